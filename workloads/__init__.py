@@ -1,0 +1,150 @@
+"""Seeded synthetic workloads: the layer shapes and the input generators.
+
+This module holds data only (shapes, distributions, seeds) and no arithmetic
+of the method: output shapes are written out as given in the workload
+statements, and both the HIP path and the oracle receive the arrays made here.
+
+Workloads (one entry per layer; block workloads are their layers in order,
+each layer with its own seeded input of the shape its chain implies):
+
+1. single Conv fp32: N=1, 3->16, 32x32, 3x3, s1 p1, fused ReLU
+2. ResNet-style bottleneck 3x3 fp16: N=32, 256->256, 14x14, s1 p1, bias,
+   residual of the output's shape, then ReLU
+3. stem 7x7 s2 p3 fp16 3->64 on 224x224 (-> 112x112), and a 1x1 pointwise
+   64->256 on 56x56, bias + ReLU
+4. depthwise-separable fp32: N=64, C=240, 28x28: depthwise 5x5 s1 p2 with
+   hard-swish, depthwise 3x3 s2 p1, pointwise 1x1 240->80, bias
+5. dilated grouped fp16: N=8, 256->256, 40x40, 3x3, dilation 2, pad 2,
+   groups 32, sigmoid; then ConvTranspose W=[256,64,2,2] stride 2 ->
+   64x80x80 with bias
+
+Distributions: x ~ U[-1,1]; w ~ N(0, 2/fan_in) (He-normal, fan_in = weight
+dim 1 * KH * KW); bias ~ U[-0.1,0.1]; residual ~ U[-1,1].  Values are drawn in
+float64 and rounded once (round-to-nearest-even) to the layer's element type.
+Seeds: 20261202 + 1000*workload + 10*layer + t, t = 0 x, 1 w, 2 bias, 3 residual.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+SEED_BASE = 20261202
+
+
+@dataclass(frozen=True)
+class Layer:
+    name: str
+    workload: int
+    index: int
+    dtype: str  # "f32" or "f16"
+    n: int
+    c_in: int
+    h: int
+    w: int
+    c_out: int
+    kh: int
+    kw: int
+    out_shape: tuple  # as stated by the workload (N, C, H, W)
+    groups: int = 1
+    stride: tuple = (1, 1)
+    dilation: tuple = (1, 1)
+    pads: tuple = (0, 0, 0, 0)  # top, left, bottom, right
+    out_pad: tuple = (0, 0)
+    transpose: bool = False
+    act: str = "identity"
+    alpha: float = 0.0
+    beta: float = 0.0
+    bias: bool = True
+    residual: bool = False
+    note: str = ""
+
+    @property
+    def np_dtype(self):
+        return np.float16 if self.dtype == "f16" else np.float32
+
+    @property
+    def w_shape(self):
+        if self.transpose:
+            return (self.c_in, self.c_out // self.groups, self.kh, self.kw)
+        return (self.c_out, self.c_in // self.groups, self.kh, self.kw)
+
+    @property
+    def x_shape(self):
+        return (self.n, self.c_in, self.h, self.w)
+
+    def with_batch(self, n: int) -> "Layer":
+        """Same layer at another batch size (output shape follows the batch)."""
+        return replace(self, n=n, out_shape=(n,) + tuple(self.out_shape[1:]))
+
+
+LAYERS = [
+    Layer("w1_conv3x3_f32", 1, 0, "f32", 1, 3, 32, 32, 16, 3, 3, (1, 16, 32, 32),
+          pads=(1, 1, 1, 1), act="relu"),
+    Layer("w2_bottleneck3x3_f16", 2, 0, "f16", 32, 256, 14, 14, 256, 3, 3,
+          (32, 256, 14, 14), pads=(1, 1, 1, 1), act="relu", residual=True),
+    Layer("w3a_stem7x7s2_f16", 3, 0, "f16", 32, 3, 224, 224, 64, 7, 7, (32, 64, 112, 112),
+          stride=(2, 2), pads=(3, 3, 3, 3), act="relu"),
+    Layer("w3b_pointwise_f16", 3, 1, "f16", 32, 64, 56, 56, 256, 1, 1, (32, 256, 56, 56),
+          act="relu"),
+    Layer("w4a_depthwise5x5_f32", 4, 0, "f32", 64, 240, 28, 28, 240, 5, 5, (64, 240, 28, 28),
+          groups=240, pads=(2, 2, 2, 2), act="hard_swish"),
+    Layer("w4b_depthwise3x3s2_f32", 4, 1, "f32", 64, 240, 28, 28, 240, 3, 3,
+          (64, 240, 14, 14), groups=240, stride=(2, 2), pads=(1, 1, 1, 1)),
+    Layer("w4c_pointwise_f32", 4, 2, "f32", 64, 240, 14, 14, 80, 1, 1, (64, 80, 14, 14)),
+    Layer("w5a_dilated_grouped_f16", 5, 0, "f16", 8, 256, 40, 40, 256, 3, 3, (8, 256, 40, 40),
+          groups=32, dilation=(2, 2), pads=(2, 2, 2, 2), act="sigmoid"),
+    Layer("w5b_convtranspose2x2s2_f16", 5, 1, "f16", 8, 256, 40, 40, 64, 2, 2, (8, 64, 80, 80),
+          stride=(2, 2), transpose=True),
+]
+
+BY_NAME = {l.name: l for l in LAYERS}
+
+
+def workload_layers(wl: int):
+    return [l for l in LAYERS if l.workload == wl]
+
+
+def seed(layer: Layer, t: int) -> int:
+    return SEED_BASE + 1000 * layer.workload + 10 * layer.index + t
+
+
+def fan_in(layer: Layer) -> int:
+    ws = layer.w_shape
+    return ws[1] * ws[2] * ws[3]
+
+
+@dataclass
+class Inputs:
+    x: np.ndarray
+    w: np.ndarray
+    b: np.ndarray | None
+    r: np.ndarray | None
+    extra: dict = field(default_factory=dict)
+
+
+def make_inputs(layer: Layer, seeds: tuple | None = None) -> Inputs:
+    """The layer's seeded inputs, drawn in float64 and rounded once to its dtype.
+
+    Draws fill arrays in C order, so a smaller batch is a prefix of the full
+    batch's x and residual."""
+    dt = layer.np_dtype
+    s = seeds or tuple(seed(layer, t) for t in range(4))
+    x = np.random.default_rng(s[0]).uniform(-1.0, 1.0, layer.x_shape).astype(dt)
+    std = math.sqrt(2.0 / fan_in(layer))
+    w = (np.random.default_rng(s[1]).standard_normal(layer.w_shape) * std).astype(dt)
+    b = (np.random.default_rng(s[2]).uniform(-0.1, 0.1, (layer.c_out,)).astype(dt)
+         if layer.bias else None)
+    r = (np.random.default_rng(s[3]).uniform(-1.0, 1.0, layer.out_shape).astype(dt)
+         if layer.residual else None)
+    return Inputs(x, w, b, r)
+
+
+def random_tensor(rng: np.random.Generator, shape, dtype, lo=-1.0, hi=1.0):
+    return rng.uniform(lo, hi, shape).astype(dtype)
+
+
+def integer_tensor(rng: np.random.Generator, shape, dtype, lo=-2, hi=2):
+    """Small integers: exact in fp16 and fp32, so sums are exact in any order."""
+    return rng.integers(lo, hi + 1, shape).astype(dtype)
