@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2-D convolution forward on one MI355X.
+
+A step is one forward pass of the headline workload: the ResNet-style
+bottleneck 3x3 layer, fp16 operands with fp32 accumulation, N=32, 256->256
+channels, 14x14, stride 1, pad 1, bias + residual + ReLU, with every operand
+resident in HBM before the timed region starts.  The operand sets rotate over
+>= 1 GiB of device memory so that no call finds its inputs in the 256 MB
+Infinity Cache.  Every other workload layer is timed the same way and reported
+in "layers" (TFLOP/s, GB/s of algorithmic bytes, fraction of its roofline).
+
+Prints one JSON line.  Options: --gpus N (only 1 is supported: the build runs on
+one GPU), --steps K, --warmup W, --no-cpu-baseline, --layers a,b,...,
+--headline-only, --copy-calib BYTES (runs only a plain device copy of that size,
+for calibrating the HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HEADLINE = "w2_bottleneck3x3_f16"
+METRIC = "conv fwd TFLOP/s (2*MACs/s) and HBM GB/s per layer config, % of roofline"
+PEAK = {  # MI355X published peaks
+    "f16_mfma_tflops": 2500.0,
+    "f32_tflops": 157.3,
+    "hbm_gbs": 8000.0,
+}
+ROTATE_BYTES = 1 << 30
+
+
+def esize(dt):
+    return 2 if dt == "f16" else 4
+
+
+def layer_stats(layer):
+    """MACs (as 'Convolutions' section 2.3 counts them; ConvT: x*w products)
+    and algorithmic bytes (x, w, bias, residual and y once each)."""
+    N, C, H, W = layer.out_shape
+    if layer.transpose:
+        macs = layer.n * layer.c_in * layer.h * layer.w * (layer.c_out // layer.groups) * \
+            layer.kh * layer.kw
+    else:
+        macs = N * layer.c_out * H * W * (layer.c_in // layer.groups) * layer.kh * layer.kw
+    es = esize(layer.dtype)
+    nbytes = (math.prod(layer.x_shape) + math.prod(layer.w_shape) + N * C * H * W) * es
+    if layer.bias:
+        nbytes += layer.c_out * es
+    if layer.residual:
+        nbytes += N * C * H * W * es
+    return macs, nbytes
+
+
+def roof(layer, macs, nbytes):
+    """Binding roof: min(compute peak, AI * HBM peak)."""
+    flops = 2 * macs
+    peak_c = PEAK["f16_mfma_tflops"] if layer.dtype == "f16" else PEAK["f32_tflops"]
+    t_c = flops / (peak_c * 1e12)
+    t_m = nbytes / (PEAK["hbm_gbs"] * 1e9)
+    if layer.groups == layer.c_in and layer.groups > 1 and not layer.transpose:
+        bound = "hbm"  # depthwise runs on the VALU without MFMA; bandwidth binds
+        t_c = 0.0
+    else:
+        bound = "mfma" if t_c >= t_m else "hbm"
+    return bound, max(t_c, t_m)
+
+
+def build_problem(cf, layer):
+    return cf.make_problem(layer.n, layer.c_in, layer.h, layer.w, layer.c_out, layer.kh,
+                           layer.kw, groups=layer.groups, stride=layer.stride,
+                           dilation=layer.dilation, pads=layer.pads, out_pad=layer.out_pad,
+                           transpose=layer.transpose, act=layer.act, bias=layer.bias,
+                           residual=layer.residual)
+
+
+def time_layer(cf, torch, layer, steps, warmup):
+    p = build_problem(cf, layer)
+    variant = cf.conv_describe_variant(p, layer.dtype)
+    inp = workloads.make_inputs(layer)
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    base = [dev(inp.x), dev(inp.w), dev(inp.b), dev(inp.r)]
+    ydt = torch.float16 if layer.dtype == "f16" else torch.float32
+    macs, nbytes = layer_stats(layer)
+    nsets = max(1, min(256, math.ceil(ROTATE_BYTES / nbytes)))
+    sets = []
+    for i in range(nsets):
+        cl = [None if t is None else (t if i == 0 else t.clone()) for t in base]
+        y = torch.empty(layer.out_shape, dtype=ydt, device="cuda")
+        sets.append(cl + [y])
+    whole, _ = cf.conv_scratch_size(p, layer.dtype)
+    scratch = torch.empty(max(whole // 4, 4), dtype=torch.float32, device="cuda") if whole else None
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fn = cf.conv_transpose_forward if layer.transpose else cf.conv_forward
+
+    def call(i):
+        x, w, b, r, y = sets[i % nsets]
+        fn(p, layer.dtype, x, w, b, r, y, scratch, whole, sh)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        call(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e-3  # s
+    total = ev[0].elapsed_time(ev[steps]) * 1e-3
+    del sets
+    torch.cuda.empty_cache()
+    bound, t_roof = roof(layer, macs, nbytes)
+    avg = float(per.mean())
+    med = float(np.median(per))
+    return {
+        "name": layer.name, "variant": variant, "dtype": layer.dtype,
+        "rotating_sets": nsets, "us_avg": avg * 1e6, "us_median": med * 1e6,
+        "us_total_per_step": total / steps * 1e6, "wall_s": wall,
+        "tflops": 2 * macs / avg / 1e12, "gbs": nbytes / avg / 1e9,
+        "macs": macs, "alg_bytes": nbytes, "bound": bound,
+        "roof_us": t_roof * 1e6, "roof_frac": t_roof / avg, "total_s": total,
+    }
+
+
+def cpu_baseline(layer, budget_s=10.0):
+    """The fp64 oracle (plain C loops, OpenMP over output planes) on the host
+    cores, over the whole headline layer, repeated until ~budget_s of work."""
+    import oracle  # CPU baseline leg only
+
+    inp = workloads.make_inputs(layer)
+    t, l, b, r = layer.pads
+    g = oracle.Geom(layer.n, layer.c_in, layer.h, layer.w, layer.c_out, layer.kh, layer.kw,
+                    groups=layer.groups, sh=layer.stride[0], sw=layer.stride[1],
+                    dh=layer.dilation[0], dw=layer.dilation[1], pt=t, pl=l, pb=b, pr=r,
+                    act=layer.act)
+    macs, _ = layer_stats(layer)
+    runs, spent = 0, 0.0
+    while spent < budget_s and runs < 20:
+        t0 = time.perf_counter()
+        oracle.conv2d(g, inp.x, inp.w, inp.b, inp.r)
+        spent += time.perf_counter() - t0
+        runs += 1
+    return {
+        "value": 2 * macs * runs / spent / 1e12, "unit": "TFLOP/s",
+        "cores": oracle.max_threads(), "kind": "oracle",
+        "sample": f"whole headline layer (N={layer.n}), fp64 direct loops with |w*x| scale, "
+                  f"{runs} run(s), {spent:.1f} s",
+    }
+
+
+def traffic_from_profiles(kernel_src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"^traffic: (.*)$", txt, re.M)
+    if not m:
+        return None
+    kv = dict(item.split("=", 1) for item in m.group(1).split())
+    if kv.get("source_sha") != kernel_src_hash:
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "convolution_forward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", default="")
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by batch or output channel, see DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import convolution_forward_amd as cf
+
+    if args.copy_calib:
+        n = args.copy_calib // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n * 4}))
+        return
+
+    cf.lib()  # fail loudly if the native library is missing
+    names = [HEADLINE] if args.headline_only else (
+        args.layers.split(",") if args.layers else [l.name for l in workloads.LAYERS])
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
+    results = {}
+    for nm in names:
+        results[nm] = time_layer(cf, torch, workloads.BY_NAME[nm], args.steps, args.warmup)
+        print(f"# {nm}: {results[nm]['variant']} {results[nm]['us_avg']:.2f} us "
+              f"{results[nm]['tflops']:.1f} TFLOP/s {results[nm]['gbs']:.0f} GB/s "
+              f"{100 * results[nm]['roof_frac']:.1f}% of {results[nm]['bound']} roof",
+              file=sys.stderr, flush=True)
+    h = results[HEADLINE]
+    layer = workloads.BY_NAME[HEADLINE]
+    macs, nbytes = layer_stats(layer)
+    value = 2 * macs / (h["total_s"] / args.steps) / 1e12
+    traffic = traffic_from_profiles(kernel_source_hash())
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["total_s"] / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded U[-1,1] inputs, He-normal weights, U[-0.1,0.1] bias, "
+                "U[-1,1] residual)",
+        "config": {"workload": "ResNet-style bottleneck 3x3 fp16 (fp32 accumulate), N=32, "
+                               "Cin=Cout=256, 14x14, stride 1, pad 1, bias + residual + ReLU",
+                   "variant": h["variant"], "rotating_sets": h["rotating_sets"],
+                   "hbm_gbs_alg": round(h["gbs"], 1)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(2 * macs / (h["us_avg"] * 1e-6) / 1e12, 3),
+            "peak": PEAK["f16_mfma_tflops"],
+            "unit": "TFLOP/s",
+            "frac": round(2 * macs / (h["us_avg"] * 1e-6) / 1e12 / PEAK["f16_mfma_tflops"], 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(layer),
+        "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
+                    if k not in ("total_s", "wall_s")} for r in results.values()],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

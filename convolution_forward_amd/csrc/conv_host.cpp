@@ -1,0 +1,512 @@
+// Host half of the C ABI (include/conv.h): problem validation with checked
+// int64 arithmetic, auto_pad resolution, the shape-only variant planner, scratch
+// sizing, overlap checks and the chunked launch sequence.
+//
+// "Convolution, pooling and resize" (OneGpu docs), "Layout and operands": sizes
+// are checked before anything is recorded; scratch is caller-supplied, reported
+// for the whole batch and for one image, and a smaller buffer runs the batch in
+// chunks of whole images without changing a bit; scratch may share an arena with
+// the operands as long as its range overlaps none of them.  "Variants": the
+// variant depends on the layer class; the split-k cut depends only on the shape.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "conv.h"
+#include "internal.h"
+
+using namespace convfwd;
+
+namespace {
+
+constexpr int64_t kMaxElems = 2147483647LL;  // every operand indexable with int32
+constexpr int kMaxSplits = 16;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_add_overflow(a, b, r); }
+
+// floor((in + pb + pe - d(k-1) - 1)/s) + 1, or -1 when no window fits / overflow.
+int64_t conv_extent(int64_t in, int64_t k, int64_t s, int64_t d, int64_t pb, int64_t pe) {
+  int64_t span, dk;
+  if (!mul_ok(d, k - 1, &dk)) return -1;
+  if (!add_ok(in, pb, &span) || !add_ok(span, pe, &span)) return -1;
+  span = span - dk - 1;
+  if (span < 0) return -1;
+  return span / s + 1;
+}
+
+// s(in-1) + op + d(k-1) + 1 - pb - pe, or -1.
+int64_t convt_extent(int64_t in, int64_t k, int64_t s, int64_t d, int64_t pb, int64_t pe,
+                     int64_t op) {
+  int64_t a, dk, o;
+  if (!mul_ok(s, in - 1, &a) || !mul_ok(d, k - 1, &dk)) return -1;
+  if (!add_ok(a, op, &o) || !add_ok(o, dk + 1, &o)) return -1;
+  o = o - pb - pe;
+  return o >= 1 ? o : -1;
+}
+
+struct Geo {
+  int64_t n, ci, h, w, co, kh, kw, g, sh, sw, dh, dw, pt, pl, pb, pr, oph, opw;
+  int64_t ho, wo, cig, cog;
+  int64_t x_elems, w_elems, y_elems;
+  bool transpose;
+};
+
+int validate(const conv_problem* p, int dtype, Geo* g) {
+  if (!p) return CONV_ERR_ARG;
+  if (dtype != CONV_F32 && dtype != CONV_F16) return CONV_ERR_ARG;
+  if (p->transpose != 0 && p->transpose != 1) return CONV_ERR_ARG;
+  if (p->activation < CONV_ACT_IDENTITY || p->activation > CONV_ACT_LEAKY_RELU)
+    return CONV_ERR_ARG;
+  if ((p->has_bias != 0 && p->has_bias != 1) || (p->has_residual != 0 && p->has_residual != 1))
+    return CONV_ERR_ARG;
+  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_HALO)
+    return CONV_ERR_ARG;
+  if (p->split_override < 0 || p->split_override > kMaxSplits) return CONV_ERR_ARG;
+  if (p->x_off < 0 || p->w_off < 0 || p->b_off < 0 || p->r_off < 0 || p->y_off < 0)
+    return CONV_ERR_ARG;
+
+  Geo q{};
+  q.n = p->n; q.ci = p->c_in; q.h = p->h; q.w = p->w; q.co = p->c_out;
+  q.kh = p->kh; q.kw = p->kw; q.g = p->groups;
+  q.sh = p->stride_h; q.sw = p->stride_w; q.dh = p->dil_h; q.dw = p->dil_w;
+  q.pt = p->pad_top; q.pl = p->pad_left; q.pb = p->pad_bottom; q.pr = p->pad_right;
+  q.oph = p->out_pad_h; q.opw = p->out_pad_w;
+  q.transpose = p->transpose == 1;
+  if (q.n < 1 || q.ci < 1 || q.h < 1 || q.w < 1 || q.co < 1 || q.kh < 1 || q.kw < 1 || q.g < 1)
+    return CONV_ERR_SHAPE;
+  if (q.ci % q.g || q.co % q.g) return CONV_ERR_SHAPE;
+  if (q.sh < 1 || q.sw < 1 || q.dh < 1 || q.dw < 1) return CONV_ERR_SHAPE;
+  if (q.pt < 0 || q.pl < 0 || q.pb < 0 || q.pr < 0) return CONV_ERR_SHAPE;
+  const int64_t lim = kMaxElems;
+  if (q.n > lim || q.ci > lim || q.h > lim || q.w > lim || q.co > lim || q.kh > lim ||
+      q.kw > lim || q.sh > lim || q.sw > lim || q.dh > lim || q.dw > lim || q.pt > lim ||
+      q.pl > lim || q.pb > lim || q.pr > lim)
+    return CONV_ERR_SHAPE;
+  if (q.transpose) {
+    if (q.oph < 0 || q.oph >= q.sh || q.opw < 0 || q.opw >= q.sw) return CONV_ERR_SHAPE;
+    q.ho = convt_extent(q.h, q.kh, q.sh, q.dh, q.pt, q.pb, q.oph);
+    q.wo = convt_extent(q.w, q.kw, q.sw, q.dw, q.pl, q.pr, q.opw);
+  } else {
+    if (q.oph != 0 || q.opw != 0) return CONV_ERR_SHAPE;
+    q.ho = conv_extent(q.h, q.kh, q.sh, q.dh, q.pt, q.pb);
+    q.wo = conv_extent(q.w, q.kw, q.sw, q.dw, q.pl, q.pr);
+  }
+  if (q.ho < 1 || q.wo < 1) return CONV_ERR_SHAPE;
+  q.cig = q.ci / q.g;
+  q.cog = q.co / q.g;
+  int64_t t;
+  if (!mul_ok(q.n, q.ci, &t) || !mul_ok(t, q.h, &t) || !mul_ok(t, q.w, &t) || t > lim)
+    return CONV_ERR_SHAPE;
+  q.x_elems = t;
+  if (!mul_ok(q.transpose ? q.ci : q.co, q.transpose ? q.cog : q.cig, &t) ||
+      !mul_ok(t, q.kh, &t) || !mul_ok(t, q.kw, &t) || t > lim)
+    return CONV_ERR_SHAPE;
+  q.w_elems = t;
+  if (!mul_ok(q.n, q.co, &t) || !mul_ok(t, q.ho, &t) || !mul_ok(t, q.wo, &t) || t > lim)
+    return CONV_ERR_SHAPE;
+  q.y_elems = t;
+  if (q.transpose) {  // float32 columns of one image must be indexable too
+    if (!mul_ok(q.co, q.kh, &t) || !mul_ok(t, q.kw, &t) || !mul_ok(t, q.h, &t) ||
+        !mul_ok(t, q.w, &t) || t > lim)
+      return CONV_ERR_SHAPE;
+  }
+  // pointer arithmetic on offsets must not overflow
+  int64_t end;
+  if (!add_ok(p->x_off, q.x_elems, &end) || !add_ok(p->w_off, q.w_elems, &end) ||
+      !add_ok(p->y_off, q.y_elems, &end) || !add_ok(p->b_off, q.co, &end) ||
+      !add_ok(p->r_off, q.y_elems, &end))
+    return CONV_ERR_SHAPE;
+  *g = q;
+  return CONV_OK;
+}
+
+struct Plan {
+  int variant;
+  int splits;          // implicit GEMM split-k ranges
+  int ksteps;
+  int steps_per_split;
+  uint64_t scratch_per_image;
+  uint64_t scratch_whole;
+  // depthwise tiling
+  int toh, tow, tih, tiw, tiles_w, tiles;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
+
+// Depthwise output tile: whole plane when the staged input fits, else smaller
+// tiles; the staged region stays under 48 KiB of LDS.
+bool plan_depthwise(const Geo& g, Plan* pl) {
+  int64_t toh = std::min<int64_t>(g.ho, 64), tow = std::min<int64_t>(g.wo, 64);
+  for (;;) {
+    int64_t tih = (toh - 1) * g.sh + (g.kh - 1) * g.dh + 1;
+    int64_t tiw = (tow - 1) * g.sw + (g.kw - 1) * g.dw + 1;
+    if (tih * tiw * 4 <= 48 * 1024) {
+      pl->toh = (int)toh; pl->tow = (int)tow; pl->tih = (int)tih; pl->tiw = (int)tiw;
+      pl->tiles_w = (int)ceil_div(g.wo, tow);
+      int64_t tiles = ceil_div(g.ho, toh) * pl->tiles_w;
+      if (tiles > 65535) return false;
+      pl->tiles = (int)tiles;
+      return true;
+    }
+    if (toh == 1 && tow == 1) return false;  // window alone exceeds LDS
+    if (toh >= tow && toh > 1) toh = (toh + 1) / 2; else tow = (tow + 1) / 2;
+  }
+}
+
+int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
+  memset(pl, 0, sizeof(*pl));
+  pl->splits = 1;
+  int v = p->variant_override;
+  if (g.transpose) {
+    if (v != CONV_VARIANT_AUTO && v != CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
+    pl->variant = CONV_VARIANT_TRANSPOSE_GEMM_COL2IM;
+    if (p->split_override > 1) return CONV_ERR_ARG;
+    pl->scratch_per_image = (uint64_t)(g.co * g.kh * g.kw * g.h * g.w) * 4u;
+    const int ept = dtype == CONV_F16 ? 8 : 4;
+    pl->ksteps = (int)ceil_div(g.cig, 4 * ept);
+    pl->steps_per_split = pl->ksteps;
+    if (ceil_div(g.co * g.kh * g.kw / g.g, IG_TILE_C) > 65535 || g.g > 65535) return CONV_ERR_SHAPE;
+  } else {
+    if (v == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_POINTWISE_GEMM || v == CONV_VARIANT_IMPLICIT_GEMM_HALO)
+      return CONV_ERR_ARG;  // not applicable to this shape in this build
+    if (v == CONV_VARIANT_AUTO) v = depthwise_applicable(g) ? CONV_VARIANT_DEPTHWISE_DIRECT
+                                                             : CONV_VARIANT_IMPLICIT_GEMM;
+    if (v == CONV_VARIANT_DEPTHWISE_DIRECT) {
+      if (!depthwise_applicable(g)) return CONV_ERR_ARG;
+      if (p->split_override > 1) return CONV_ERR_ARG;
+      if (!plan_depthwise(g, pl)) return CONV_ERR_SHAPE;
+    } else {
+      // implicit GEMM: k-blocks of 64 bytes; split only small grids with long k
+      const int ept = dtype == CONV_F16 ? 8 : 4;
+      const int64_t kg = g.cig * g.kh * g.kw;
+      const int64_t steps = ceil_div(kg, 4 * ept);
+      const int64_t tiles = ceil_div(g.n * g.ho * g.wo, IG_TILE_P) * ceil_div(g.cog, IG_TILE_C) * g.g;
+      int64_t r = 1;
+      if (p->split_override >= 1) {
+        r = std::min<int64_t>(p->split_override, steps);
+      } else if (tiles < 256 && steps >= 8) {
+        r = std::min<int64_t>({(int64_t)kMaxSplits, ceil_div(512, tiles), steps / 4});
+        if (r < 2) r = 1;
+      }
+      const int64_t per = ceil_div(steps, r);
+      r = ceil_div(steps, per);
+      pl->splits = (int)r;
+      pl->ksteps = (int)steps;
+      pl->steps_per_split = (int)per;
+      if (ceil_div(g.cog, IG_TILE_C) > 65535 || g.g * r > 65535) return CONV_ERR_SHAPE;
+      if (r > 1) pl->scratch_per_image = (uint64_t)(r * g.co * g.ho * g.wo) * 4u;
+    }
+    pl->variant = v;
+  }
+  pl->scratch_whole = pl->scratch_per_image * (uint64_t)g.n;
+  return CONV_OK;
+}
+
+const char* variant_name(int v) {
+  switch (v) {
+    case CONV_VARIANT_IMPLICIT_GEMM: return "implicit_gemm";
+    case CONV_VARIANT_POINTWISE_GEMM: return "pointwise_gemm";
+    case CONV_VARIANT_DEPTHWISE_DIRECT: return "depthwise_direct";
+    case CONV_VARIANT_TRANSPOSE_GEMM_COL2IM: return "transpose_gemm_col2im";
+    case CONV_VARIANT_IMPLICIT_GEMM_HALO: return "implicit_gemm_halo";
+    default: return "unknown";
+  }
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+// Every host-side check of a forward call; fills the geometry, the plan and the
+// image chunk size.  Nothing is enqueued.
+int check_call(const conv_problem* p, int dtype, bool transpose, const void* x, const void* w,
+               const void* bias, const void* residual, const void* y, const void* scratch,
+               uint64_t scratch_bytes, Geo* gout, Plan* plout, int64_t* chunk_out) {
+  Geo g;
+  if (!p) return CONV_ERR_ARG;
+  if ((p->transpose == 1) != transpose) return CONV_ERR_ARG;
+  int st = validate(p, dtype, &g);
+  if (st) return st;
+  Plan pl;
+  st = make_plan(p, dtype, g, &pl);
+  if (st) return st;
+  if (!x || !w || !y) return CONV_ERR_ARG;
+  if (p->has_bias && !bias) return CONV_ERR_ARG;
+  if (p->has_residual && !residual) return CONV_ERR_ARG;
+
+  const size_t es = dtype == CONV_F16 ? 2 : 4;
+  int64_t chunk = g.n;
+  if (pl.scratch_per_image > 0) {
+    if (!scratch) return CONV_ERR_SCRATCH;
+    if (reinterpret_cast<uintptr_t>(scratch) % 16) return CONV_ERR_ARG;
+    if (scratch_bytes < pl.scratch_per_image) return CONV_ERR_SCRATCH;
+    chunk = std::min<int64_t>(g.n, (int64_t)(scratch_bytes / pl.scratch_per_image));
+  }
+
+  const char* xb = static_cast<const char*>(x) + p->x_off * es;
+  const char* wb = static_cast<const char*>(w) + p->w_off * es;
+  const char* bb = p->has_bias ? static_cast<const char*>(bias) + p->b_off * es : nullptr;
+  const char* rb = p->has_residual ? static_cast<const char*>(residual) + p->r_off * es : nullptr;
+  const char* yb = static_cast<const char*>(y) + p->y_off * es;
+
+  // overlap rules ("Layout and operands": the scratch may live in the operands'
+  // arena as long as its range overlaps no operand)
+  Range rx{(uintptr_t)xb, (uintptr_t)xb + g.x_elems * es};
+  Range rw{(uintptr_t)wb, (uintptr_t)wb + g.w_elems * es};
+  Range rbias{(uintptr_t)bb, bb ? (uintptr_t)bb + g.co * es : (uintptr_t)bb};
+  Range rr{(uintptr_t)rb, rb ? (uintptr_t)rb + g.y_elems * es : (uintptr_t)rb};
+  Range ry{(uintptr_t)yb, (uintptr_t)yb + g.y_elems * es};
+  if (overlaps(ry, rx) || overlaps(ry, rw) || (bb && overlaps(ry, rbias))) return CONV_ERR_OVERLAP;
+  if (rb && overlaps(ry, rr) && !(ry.lo == rr.lo && ry.hi == rr.hi)) return CONV_ERR_OVERLAP;
+  if (pl.scratch_per_image > 0) {
+    Range rs{(uintptr_t)scratch, (uintptr_t)scratch + (uint64_t)chunk * pl.scratch_per_image};
+    if (overlaps(rs, rx) || overlaps(rs, rw) || (bb && overlaps(rs, rbias)) ||
+        (rb && overlaps(rs, rr)) || overlaps(rs, ry))
+      return CONV_ERR_OVERLAP;
+  }
+
+  *gout = g;
+  *plout = pl;
+  *chunk_out = chunk;
+  return CONV_OK;
+}
+
+int run(const conv_problem* p, int dtype, bool transpose, const void* x, const void* w,
+        const void* bias, const void* residual, void* y, void* scratch, uint64_t scratch_bytes,
+        void* stream) {
+  Geo g;
+  Plan pl;
+  int64_t chunk;
+  const int st = check_call(p, dtype, transpose, x, w, bias, residual, y, scratch, scratch_bytes,
+                            &g, &pl, &chunk);
+  if (st) return st;
+  const size_t es = dtype == CONV_F16 ? 2 : 4;
+  const char* xb = static_cast<const char*>(x) + p->x_off * es;
+  const char* wb = static_cast<const char*>(w) + p->w_off * es;
+  const char* bb = p->has_bias ? static_cast<const char*>(bias) + p->b_off * es : nullptr;
+  const char* rb = p->has_residual ? static_cast<const char*>(residual) + p->r_off * es : nullptr;
+  char* yb = static_cast<char*>(y) + p->y_off * es;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dtype dt = dtype == CONV_F16 ? F16 : F32;
+  const int64_t x_img = g.ci * g.h * g.w, y_img = g.co * g.ho * g.wo;
+
+  for (int64_t i0 = 0; i0 < g.n; i0 += chunk) {
+    const int cn = (int)std::min<int64_t>(chunk, g.n - i0);
+    const char* xc = xb + i0 * x_img * es;
+    const char* rc = rb ? rb + i0 * y_img * es : nullptr;
+    char* yc = yb + i0 * y_img * es;
+    hipError_t e = hipSuccess;
+    if (pl.variant == CONV_VARIANT_DEPTHWISE_DIRECT) {
+      DepthwiseArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.kh = (int)g.kh; a.kw = (int)g.kw; a.mult = (int)(g.co / g.ci);
+      a.sh = (int)g.sh; a.sw = (int)g.sw; a.dh = (int)g.dh; a.dw = (int)g.dw;
+      a.pt = (int)g.pt; a.pl = (int)g.pl; a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.toh = pl.toh; a.tow = pl.tow; a.tih = pl.tih; a.tiw = pl.tiw;
+      a.tiles_w = pl.tiles_w; a.tiles = pl.tiles;
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_depthwise(dt, a, s);
+    } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {
+      IgemmArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.planes = static_cast<float*>(scratch);
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.kh = (int)g.kh; a.kw = (int)g.kw; a.groups = (int)g.g;
+      a.sh = (int)g.sh; a.sw = (int)g.sw; a.dh = (int)g.dh; a.dw = (int)g.dw;
+      a.pt = (int)g.pt; a.pl = (int)g.pl; a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.cig = (int)g.cig; a.cog = (int)g.cog; a.kg = (int)(g.cig * g.kh * g.kw);
+      a.pix = (int)(cn * g.ho * g.wo);
+      a.ksteps = pl.ksteps; a.steps_per_split = pl.steps_per_split; a.splits = pl.splits;
+      a.wtrans = 0;
+      const int ept = dt == F16 ? 8 : 4;
+      a.wvec = (a.kg % ept == 0) && (reinterpret_cast<uintptr_t>(wb) % 16 == 0);
+      a.mode = pl.splits > 1 ? OUT_RAW : OUT_FUSED;
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      a.plane_stride = (long long)cn * y_img;
+      e = launch_igemm(dt, a, s);
+      if (e == hipSuccess && pl.splits > 1) {
+        ReduceArgs r{};
+        r.planes = static_cast<const float*>(scratch);
+        r.plane_stride = (long long)cn * y_img;
+        r.splits = pl.splits;
+        r.bias = bb; r.res = rc; r.y = yc;
+        r.total = (long long)cn * y_img;
+        r.hw = (int)(g.ho * g.wo); r.c_out = (int)g.co;
+        r.act = p->activation; r.alpha = p->act_alpha; r.beta = p->act_beta;
+        e = launch_reduce(dt, r, s);
+      }
+    } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) {
+      // GEMM: cols[n][g*M + m][h][w] = sum_ci w[g*cig + ci][m] * x[n][g*cig + ci][h][w],
+      // M = (Cout/G)*KH*KW; the matrix kernel runs it as a 1x1 conv with transposed
+      // weight rows into raw float32 planes.
+      const int64_t M = g.cog * g.kh * g.kw;
+      IgemmArgs a{};
+      a.x = xc; a.wt = wb; a.bias = nullptr; a.res = nullptr; a.y = nullptr;
+      a.planes = static_cast<float*>(scratch);
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w;
+      a.c_out = (int)(M * g.g); a.kh = 1; a.kw = 1; a.groups = (int)g.g;
+      a.sh = 1; a.sw = 1; a.dh = 1; a.dw = 1; a.pt = 0; a.pl = 0;
+      a.ho = (int)g.h; a.wo = (int)g.w;
+      a.cig = (int)g.cig; a.cog = (int)M; a.kg = (int)g.cig;
+      a.pix = (int)(cn * g.h * g.w);
+      a.ksteps = pl.ksteps; a.steps_per_split = pl.steps_per_split; a.splits = 1;
+      a.wtrans = 1; a.wvec = 0; a.mode = OUT_RAW;
+      a.plane_stride = 0;
+      e = launch_igemm(dt, a, s);
+      if (e == hipSuccess) {
+        Col2imArgs c{};
+        c.cols = static_cast<const float*>(scratch);
+        c.bias = bb; c.res = rc; c.y = yc;
+        c.n = cn; c.h = (int)g.h; c.w = (int)g.w; c.c_out = (int)g.co; c.cog = (int)g.cog;
+        c.kh = (int)g.kh; c.kw = (int)g.kw; c.sh = (int)g.sh; c.sw = (int)g.sw;
+        c.dh = (int)g.dh; c.dw = (int)g.dw; c.pt = (int)g.pt; c.pl = (int)g.pl;
+        c.ho = (int)g.ho; c.wo = (int)g.wo;
+        c.total = (long long)cn * y_img;
+        c.act = p->activation; c.alpha = p->act_alpha; c.beta = p->act_beta;
+        e = launch_col2im(dt, c, s);
+      }
+    } else {
+      return CONV_ERR_ARG;
+    }
+    if (e != hipSuccess) return CONV_ERR_DEVICE;
+  }
+  return CONV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv_output_extent(const conv_problem* p, int64_t* ho, int64_t* wo) {
+  if (!p || !ho || !wo) return CONV_ERR_ARG;
+  Geo g;
+  int st = validate(p, CONV_F32, &g);
+  if (st) return st;
+  *ho = g.ho;
+  *wo = g.wo;
+  return CONV_OK;
+}
+
+int conv_resolve_auto_pad(conv_problem* p, int auto_pad, const int64_t* output_shape_hw) {
+  if (!p) return CONV_ERR_ARG;
+  if (auto_pad < CONV_AUTO_PAD_NOTSET || auto_pad > CONV_AUTO_PAD_VALID) return CONV_ERR_ARG;
+  const int64_t in[2] = {p->h, p->w}, k[2] = {p->kh, p->kw}, s[2] = {p->stride_h, p->stride_w},
+                d[2] = {p->dil_h, p->dil_w}, op[2] = {p->out_pad_h, p->out_pad_w};
+  for (int i = 0; i < 2; ++i)
+    if (in[i] < 1 || k[i] < 1 || s[i] < 1 || d[i] < 1 || in[i] > kMaxElems || k[i] > kMaxElems ||
+        s[i] > kMaxElems || d[i] > kMaxElems)
+      return CONV_ERR_SHAPE;
+  int64_t pb[2] = {p->pad_top, p->pad_left}, pe[2] = {p->pad_bottom, p->pad_right};
+  for (int i = 0; i < 2; ++i) {
+    const int64_t keff = d[i] * (k[i] - 1) + 1;
+    if (!p->transpose) {
+      if (auto_pad == CONV_AUTO_PAD_NOTSET) continue;
+      if (auto_pad == CONV_AUTO_PAD_VALID) { pb[i] = pe[i] = 0; continue; }
+      const int64_t out = (in[i] + s[i] - 1) / s[i];
+      int64_t total = (out - 1) * s[i] + keff - in[i];
+      if (total < 0) total = 0;
+      const int64_t lo = total / 2, hi = total - total / 2;
+      pb[i] = auto_pad == CONV_AUTO_PAD_SAME_UPPER ? lo : hi;
+      pe[i] = auto_pad == CONV_AUTO_PAD_SAME_UPPER ? hi : lo;
+    } else {
+      if (auto_pad == CONV_AUTO_PAD_VALID) { pb[i] = pe[i] = 0; continue; }
+      int64_t out;
+      if (output_shape_hw) out = output_shape_hw[i];
+      else if (auto_pad == CONV_AUTO_PAD_NOTSET) continue;
+      else out = s[i] * in[i];
+      if (op[i] < 0 || op[i] >= s[i] || out < 1) return CONV_ERR_SHAPE;
+      const int64_t total = s[i] * (in[i] - 1) + op[i] + keff - out;
+      if (total < 0) return CONV_ERR_SHAPE;
+      const int64_t lo = total / 2, hi = total - total / 2;
+      pb[i] = auto_pad == CONV_AUTO_PAD_SAME_UPPER ? lo : hi;
+      pe[i] = auto_pad == CONV_AUTO_PAD_SAME_UPPER ? hi : lo;
+    }
+  }
+  p->pad_top = pb[0]; p->pad_left = pb[1]; p->pad_bottom = pe[0]; p->pad_right = pe[1];
+  return CONV_OK;
+}
+
+int conv_scratch_size(const conv_problem* p, int dtype, uint64_t* whole, uint64_t* per_image) {
+  if (!whole || !per_image) return CONV_ERR_ARG;
+  Geo g;
+  int st = validate(p, dtype, &g);
+  if (st) return st;
+  Plan pl;
+  st = make_plan(p, dtype, g, &pl);
+  if (st) return st;
+  *whole = pl.scratch_whole;
+  *per_image = pl.scratch_per_image;
+  return CONV_OK;
+}
+
+int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t len) {
+  if (!buf) return CONV_ERR_ARG;
+  Geo g;
+  int st = validate(p, dtype, &g);
+  if (st) return st;
+  Plan pl;
+  st = make_plan(p, dtype, g, &pl);
+  if (st) return st;
+  const char* dn = dtype == CONV_F16 ? "f16" : "f32";
+  char tmp[128];
+  switch (pl.variant) {
+    case CONV_VARIANT_IMPLICIT_GEMM:
+      snprintf(tmp, sizeof tmp, "implicit_gemm.%s.t%dx%d.split%d", dn, IG_TILE_P, IG_TILE_C,
+               pl.splits);
+      break;
+    case CONV_VARIANT_DEPTHWISE_DIRECT:
+      snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
+      break;
+    default:
+      snprintf(tmp, sizeof tmp, "%s.%s", variant_name(pl.variant), dn);
+  }
+  const size_t need = strlen(tmp) + 1;
+  if (len < need) return CONV_ERR_ARG;
+  memcpy(buf, tmp, need);
+  return CONV_OK;
+}
+
+int conv_forward(const conv_problem* p, int dtype, const void* x, const void* w,
+                 const void* bias, const void* residual, void* y, void* scratch,
+                 uint64_t scratch_bytes, void* stream) {
+  return run(p, dtype, false, x, w, bias, residual, y, scratch, scratch_bytes, stream);
+}
+
+int conv_transpose_forward(const conv_problem* p, int dtype, const void* x, const void* w,
+                           const void* bias, const void* residual, void* y, void* scratch,
+                           uint64_t scratch_bytes, void* stream) {
+  return run(p, dtype, true, x, w, bias, residual, y, scratch, scratch_bytes, stream);
+}
+
+int conv_check(const conv_problem* p, int dtype, const void* x, const void* w,
+               const void* bias, const void* residual, const void* y, const void* scratch,
+               uint64_t scratch_bytes) {
+  if (!p) return CONV_ERR_ARG;
+  Geo g;
+  Plan pl;
+  int64_t chunk;
+  return check_call(p, dtype, p->transpose == 1, x, w, bias, residual, y, scratch, scratch_bytes,
+                    &g, &pl, &chunk);
+}
+
+const char* conv_status_string(int status) {
+  switch (status) {
+    case CONV_OK: return "ok";
+    case CONV_ERR_ARG: return "invalid argument";
+    case CONV_ERR_SHAPE: return "invalid shape or size limit exceeded";
+    case CONV_ERR_OVERLAP: return "operand or scratch ranges overlap";
+    case CONV_ERR_SCRATCH: return "scratch buffer too small for one image";
+    case CONV_ERR_DEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Internal interface between the host planner (conv_host.cpp) and the gfx950
+// kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace convfwd {
+
+enum Dtype { F32 = 0, F16 = 1 };
+
+// Output modes of the matrix kernels.
+enum OutMode {
+  OUT_FUSED = 0,  // bias, residual, activation, store y in the operand dtype
+  OUT_RAW = 1     // raw float32 sums into a plane of the scratch (split k, ConvT columns)
+};
+
+// Geometry and operands of one implicit-GEMM launch (one image chunk).
+// Element pointers already include the problem's element offsets.
+struct IgemmArgs {
+  const void* x;
+  const void* wt;      // weights
+  const void* bias;      // nullptr when absent
+  const void* res;       // nullptr when absent
+  void* y;               // OUT_FUSED target
+  float* planes;         // OUT_RAW target: plane r at planes + r * plane_stride
+  int n, c_in, h, w;     // input (n = images in this chunk)
+  int c_out, kh, kw, groups;
+  int sh, sw, dh, dw, pt, pl;
+  int ho, wo;
+  int cig, cog;          // channels per group (cog = GEMM columns per group)
+  int kg;                // reduction length per group
+  int pix;               // n * ho * wo
+  int ksteps;            // k-blocks per group
+  int steps_per_split;   // k-blocks per split range
+  int splits;            // R
+  int wtrans;            // 1: weight element (k, col) at w[(g*cig + k) * cog + col]
+  int wvec;              // 1: weight rows may be read 16 bytes at a time
+  int mode;              // OutMode
+  int act;
+  float alpha, beta;
+  long long plane_stride;  // elements per raw plane
+};
+
+struct HaloArgs {
+  const void* x;
+  const void* wt;      // weights
+  const void* bias;
+  const void* res;
+  void* y;
+  float* planes;
+  int n, c_in, h, w, c_out, kh, kw, groups;
+  int sh, sw, dh, dw, pt, pl;
+  int ho, wo;
+  int cig, cog;
+  int chunks;            // channel chunks per group
+  int chunks_per_split;
+  int splits;
+  int mode;
+  int act;
+  float alpha, beta;
+  long long plane_stride;
+};
+
+struct DepthwiseArgs {
+  const void* x;
+  const void* wt;      // weights
+  const void* bias;
+  const void* res;
+  void* y;
+  int n, c_in, h, w, c_out, kh, kw;
+  int mult;              // c_out / c_in
+  int sh, sw, dh, dw, pt, pl;
+  int ho, wo;
+  int toh, tow;          // output tile
+  int tih, tiw;          // staged input tile (with halo)
+  int tiles_w, tiles;    // tiles per plane along w, total per plane
+  int act;
+  float alpha, beta;
+};
+
+// Split-k reduction and epilogue: y = act(sum_r planes[r] + bias + res).
+struct ReduceArgs {
+  const float* planes;
+  long long plane_stride;
+  int splits;
+  const void* bias;
+  const void* res;
+  void* y;
+  long long total;       // output elements in this chunk
+  int hw;                // ho * wo
+  int c_out;
+  int act;
+  float alpha, beta;
+};
+
+// Gathering col2im + epilogue for ConvTranspose.
+struct Col2imArgs {
+  const float* cols;     // [n][groups * cog * kh * kw][h][w]
+  const void* bias;
+  const void* res;
+  void* y;
+  int n, h, w, c_out, cog, kh, kw;
+  int sh, sw, dh, dw, pt, pl;
+  int ho, wo;
+  long long total;
+  int act;
+  float alpha, beta;
+};
+
+// Tile shape of the generic implicit GEMM kernel.
+constexpr int IG_TILE_P = 64;   // output pixels per workgroup
+constexpr int IG_TILE_C = 64;   // output channels per workgroup
+constexpr int IG_KSTEP_BYTES = 64;  // k-block: 32 halves or 16 floats
+
+// Halo kernel (f16): whole-image pixel tiles, channel chunks of 32.
+constexpr int HALO_CHUNK = 32;
+
+hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
+hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
+hipError_t launch_reduce(Dtype dt, const ReduceArgs& a, hipStream_t s);
+hipError_t launch_col2im(Dtype dt, const Col2imArgs& a, hipStream_t s);
+
+}  // namespace convfwd

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Covers the workload layers (reduced batch, full comparison; full size, sampled
+outputs), a seeded sweep of small shapes over every variant, activation and
+option, bit-exact index-mapping probes, integer exactness, determinism,
+chunking, forced split-k and forced variants, element offsets and residual
+aliasing.
+"""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+
+import convolution_forward_amd as cf
+import oracle
+import workloads
+from gpu_harness import assert_parity, geom_from_layer, oracle_ref, run_gpu
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cf.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+REDUCED_N = {
+    "w1_conv3x3_f32": 1, "w2_bottleneck3x3_f16": 2, "w3a_stem7x7s2_f16": 1,
+    "w3b_pointwise_f16": 1, "w4a_depthwise5x5_f32": 2, "w4b_depthwise3x3s2_f32": 2,
+    "w4c_pointwise_f32": 3, "w5a_dilated_grouped_f16": 1, "w5b_convtranspose2x2s2_f16": 1,
+}
+
+
+@pytest.mark.parametrize("name", [l.name for l in workloads.LAYERS])
+def test_workload_layer_reduced_batch(name):
+    layer = workloads.BY_NAME[name]
+    lr = layer.with_batch(REDUCED_N[name])
+    _say(f"[parity] {name} n={lr.n}")
+    inp = workloads.make_inputs(lr)
+    g = geom_from_layer(lr)
+    y = run_gpu(g, lr.dtype, inp.x, inp.w, inp.b, inp.r, transpose=lr.transpose)
+    assert y.shape == lr.out_shape
+    yr, sr = oracle_ref(g, inp.x, inp.w, inp.b, inp.r, transpose=lr.transpose)
+    q = assert_parity(lr.dtype, y, yr, sr, inp.b, inp.r, what=name)
+    _say(f"  max err / bound = {q:.3g}")
+
+
+@pytest.mark.parametrize("name", [l.name for l in workloads.LAYERS])
+def test_workload_layer_full_size_sampled(name):
+    """Full workload size, in the launch configuration the benchmark times;
+    outputs sampled (corners, edges and random interior points)."""
+    layer = workloads.BY_NAME[name]
+    _say(f"[parity-full] {name} n={layer.n}")
+    inp = workloads.make_inputs(layer)
+    g = geom_from_layer(layer)
+    y = run_gpu(g, layer.dtype, inp.x, inp.w, inp.b, inp.r, transpose=layer.transpose)
+    assert y.shape == layer.out_shape
+    if layer.transpose:
+        yr, sr = oracle_ref(g, inp.x, inp.w, inp.b, inp.r, transpose=True)
+        assert_parity(layer.dtype, y, yr, sr, inp.b, inp.r, what=name)
+        return
+    rng = np.random.default_rng(7)
+    N, C, H, W = layer.out_shape
+    pts = set()
+    for n in (0, N - 1):
+        for c in (0, C - 1):
+            for h in (0, H - 1):
+                for w in (0, W - 1):
+                    pts.add(((n * C + c) * H + h) * W + w)
+    pts.update(int(v) for v in rng.choice(y.size, 4000, replace=False))
+    idx = np.array(sorted(pts), np.int64)
+    yr, sr = oracle.conv2d_points(g, inp.x, inp.w, inp.b, inp.r, idx)
+    yg = y.ravel()[idx]
+    sp = sr.copy()
+    if inp.b is not None:
+        sp += np.abs(inp.b.astype(np.float64))[(idx // (H * W)) % C]
+    if inp.r is not None:
+        sp += np.abs(inp.r.astype(np.float64).ravel()[idx])
+    assert_parity(layer.dtype, yg, yr, sp, what=name)
+
+
+def _sweep_cases():
+    rng = np.random.default_rng(2026)
+    acts = list(cf.ACTIVATIONS)
+    cases = []
+    while len(cases) < 48:
+        G = int(rng.choice([1, 1, 1, 2, 4]))
+        cig = int(rng.choice([1, 2, 3, 5, 8, 16, 19, 40]))
+        cog = int(rng.choice([1, 3, 8, 17, 64, 70]))
+        if G > 1 and cig * G > 64:
+            G = 1
+        kh, kw = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        g = oracle.Geom(int(rng.integers(1, 4)), cig * G, int(rng.integers(1, 20)),
+                        int(rng.integers(1, 20)), cog * G, kh, kw, groups=G,
+                        sh=int(rng.integers(1, 4)), sw=int(rng.integers(1, 4)),
+                        dh=int(rng.integers(1, 3)), dw=int(rng.integers(1, 3)),
+                        pt=int(rng.integers(0, 3)), pl=int(rng.integers(0, 3)),
+                        pb=int(rng.integers(0, 3)), pr=int(rng.integers(0, 3)),
+                        act=acts[len(cases) % len(acts)])
+        if g.act == "clip":
+            g.alpha, g.beta = -0.3, 0.4
+        elif g.act == "leaky_relu":
+            g.alpha = 0.1
+        elif g.act == "hard_sigmoid":
+            g.alpha, g.beta = 0.2, 0.5
+        try:
+            oracle.out_shape(g)
+        except ValueError:
+            continue
+        dtype = ("f32", "f16")[len(cases) % 2]
+        cases.append((g, dtype, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"{c[1]}-{c[0].act}")
+def test_random_shapes(case):
+    g, dtype, has_b, has_r = case
+    _say(f"[sweep] {dtype} {g}")
+    rng = np.random.default_rng(g.n * 1000 + g.c_in * 10 + g.kh)
+    npdt = np.float16 if dtype == "f16" else np.float32
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+    w = (rng.standard_normal((g.c_out, g.c_in // g.groups, g.kh, g.kw)) * 0.3).astype(npdt)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(npdt) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    variants = ["auto", "implicit_gemm"]
+    if g.c_in // g.groups == 1:
+        variants.append("depthwise_direct")
+    for v in variants:
+        y = run_gpu(g, dtype, x, w, b, r, variant=v)
+        assert_parity(dtype, y, yr, sr, b, r, what=f"{v}")
+
+
+def _convt_cases():
+    return [
+        (oracle.Geom(2, 16, 5, 7, 8, 3, 3, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1, oph=1, opw=0), "f16"),
+        (oracle.Geom(1, 8, 4, 4, 6, 4, 4, groups=2, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1), "f32"),
+        (oracle.Geom(3, 40, 3, 6, 12, 2, 3, sh=2, sw=3, dh=1, dw=2, pt=0, pl=1, pb=0, pr=0,
+                     act="tanh"), "f16"),
+        (oracle.Geom(1, 5, 6, 5, 3, 3, 1, sh=1, sw=2, dh=2, pt=2, pl=0, pb=1, pr=0, opw=1,
+                     act="sigmoid"), "f32"),
+        (oracle.Geom(2, 64, 8, 8, 64, 2, 2, groups=4, sh=2, sw=2, act="relu"), "f16"),
+    ]
+
+
+@pytest.mark.parametrize("case", _convt_cases())
+def test_conv_transpose_shapes(case):
+    g, dtype = case
+    _say(f"[convt] {dtype} {g}")
+    rng = np.random.default_rng(g.c_in * 7 + g.kh)
+    npdt = np.float16 if dtype == "f16" else np.float32
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+    w = (rng.standard_normal((g.c_in, g.c_out // g.groups, g.kh, g.kw)) * 0.3).astype(npdt)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt)
+    r = rng.uniform(-1, 1, oracle.out_shape(g, transpose=True)).astype(npdt)
+    yr, sr = oracle.conv_transpose2d(g, x, w, b, r)
+    y = run_gpu(g, dtype, x, w, b, r, transpose=True)
+    assert_parity(dtype, y, yr, sr, b, r, what="convt")
+    # chunked through a one-image scratch: same bits
+    y1 = run_gpu(g, dtype, x, w, b, r, transpose=True, scratch_images=1)
+    assert np.array_equal(y.view(np.uint16 if dtype == "f16" else np.uint32),
+                          y1.view(np.uint16 if dtype == "f16" else np.uint32))
+
+
+def test_convt_checkerboard_counts():
+    """All-ones input and kernel, stride 2 ('Convolutions' exercise 3): exact."""
+    for k in (3, 4):
+        g = oracle.Geom(1, 1, 6, 6, 1, k, k, sh=2, sw=2)
+        y = run_gpu(g, "f32", np.ones((1, 1, 6, 6), np.float32), np.ones((1, 1, k, k), np.float32),
+                    transpose=True)
+        yr, _ = oracle.conv_transpose2d(g, np.ones((1, 1, 6, 6)), np.ones((1, 1, k, k)))
+        assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_index_mapping_one_hot_probes(dtype):
+    """Integer-coded inputs and one-hot weights: every output must be exactly the
+    addressed input value (or 0 in padding), for each tap of the window."""
+    npdt = np.float16 if dtype == "f16" else np.float32
+    for g in [oracle.Geom(2, 3, 9, 11, 4, 3, 2, sh=2, sw=1, dh=1, dw=2, pt=2, pl=1, pb=0, pr=2),
+              oracle.Geom(1, 4, 7, 6, 4, 2, 3, groups=2, sh=1, sw=3, dh=3, dw=1, pt=1, pl=0, pb=3, pr=1),
+              oracle.Geom(1, 6, 8, 8, 12, 3, 3, groups=6, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1)]:
+        x = (np.arange(g.n * g.c_in * g.h * g.w) % 1000 + 1).reshape(g.n, g.c_in, g.h, g.w)
+        x = x.astype(npdt)
+        assert np.all(x.astype(np.float64) == np.arange(x.size).reshape(x.shape) % 1000 + 1)
+        cig = g.c_in // g.groups
+        for c, u, v in itertools.product(range(cig), range(g.kh), range(g.kw)):
+            w = np.zeros((g.c_out, cig, g.kh, g.kw), npdt)
+            w[:, c, u, v] = 1
+            y = run_gpu(g, dtype, x, w)
+            yr, _ = oracle.conv2d(g, x, w)
+            assert np.array_equal(y.astype(np.float64), yr), (g, c, u, v)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_integer_inputs_exact(dtype):
+    """Small integers: every partial sum is exact in float32, so the GPU must
+    equal the oracle exactly (identity activation, no bias)."""
+    npdt = np.float16 if dtype == "f16" else np.float32
+    rng = np.random.default_rng(5)
+    for g, variant, splits in [
+        (oracle.Geom(2, 32, 9, 9, 40, 3, 3, pt=1, pl=1, pb=1, pr=1), "implicit_gemm", 0),
+        (oracle.Geom(1, 64, 6, 6, 16, 3, 3, pt=1, pl=1, pb=1, pr=1), "implicit_gemm", 3),
+        (oracle.Geom(2, 8, 10, 10, 16, 5, 5, groups=8, pt=2, pl=2, pb=2, pr=2), "depthwise_direct", 0),
+    ]:
+        x = rng.integers(-2, 3, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+        w = rng.integers(-2, 3, (g.c_out, g.c_in // g.groups, g.kh, g.kw)).astype(npdt)
+        y = run_gpu(g, dtype, x, w, variant=variant, splits=splits)
+        yr, _ = oracle.conv2d(g, x, w)
+        assert np.array_equal(y.astype(np.float64), yr.astype(npdt).astype(np.float64))
+
+
+def _bits(a):
+    return a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+
+
+@pytest.mark.parametrize("name", ["w2_bottleneck3x3_f16", "w4a_depthwise5x5_f32",
+                                  "w5a_dilated_grouped_f16", "w1_conv3x3_f32"])
+def test_determinism_rerun(name):
+    layer = workloads.BY_NAME[name].with_batch(2)
+    inp = workloads.make_inputs(layer)
+    g = geom_from_layer(layer)
+    y1 = run_gpu(g, layer.dtype, inp.x, inp.w, inp.b, inp.r)
+    y2 = run_gpu(g, layer.dtype, inp.x, inp.w, inp.b, inp.r)
+    assert np.array_equal(_bits(y1), _bits(y2))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_split_k_forced_and_chunked(dtype):
+    """Late-layer shape (small grid, long k): auto split, forced whole-k, forced
+    R; chunking through a one-image scratch gives the same bits."""
+    npdt = np.float16 if dtype == "f16" else np.float32
+    g = oracle.Geom(3, 128, 7, 7, 96, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu")
+    rng = np.random.default_rng(9)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+    w = (rng.standard_normal((g.c_out, g.c_in, 3, 3)) * 0.03).astype(npdt)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt)
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(npdt)
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    p = cf.make_problem(3, 128, 7, 7, 96, 3, 3, pads=(1, 1, 1, 1))
+    assert "split1" not in cf.conv_describe_variant(p, dtype)
+    outs = {}
+    for splits in (0, 1, 2, 5, 16):
+        y = run_gpu(g, dtype, x, w, b, r, splits=splits)
+        assert_parity(dtype, y, yr, sr, b, r, what=f"splits={splits}")
+        outs[splits] = y
+        if splits != 1:
+            yc = run_gpu(g, dtype, x, w, b, r, splits=splits, scratch_images=1)
+            assert np.array_equal(_bits(y), _bits(yc)), splits
+
+
+def test_offsets_and_alias():
+    """Unaligned element offsets (arena placement) give the same bits, and y may
+    alias the residual exactly."""
+    layer = workloads.BY_NAME["w2_bottleneck3x3_f16"].with_batch(1)
+    inp = workloads.make_inputs(layer)
+    g = geom_from_layer(layer)
+    y0 = run_gpu(g, "f16", inp.x, inp.w, inp.b, inp.r)
+    y1 = run_gpu(g, "f16", inp.x, inp.w, inp.b, inp.r, offsets=(3, 5, 1, 7, 9))
+    assert np.array_equal(_bits(y0), _bits(y1))
+    y2 = run_gpu(g, "f16", inp.x, inp.w, inp.b, inp.r, offsets=(0, 0, 0, 4, 4),
+                 alias_residual=True)
+    assert np.array_equal(_bits(y0), _bits(y2))
+    dl = workloads.BY_NAME["w4b_depthwise3x3s2_f32"].with_batch(1)
+    di = workloads.make_inputs(dl)
+    dg = geom_from_layer(dl)
+    assert np.array_equal(_bits(run_gpu(dg, "f32", di.x, di.w, di.b)),
+                          _bits(run_gpu(dg, "f32", di.x, di.w, di.b, offsets=(1, 2, 3, 0, 5))))
