@@ -123,8 +123,14 @@ int validate(const conv_problem* p, int dtype, Geo* g) {
   return CONV_OK;
 }
 
+struct HaloShape {
+  int oct, tr, tcb, cb, tih, tiw, n_ct, n_rt;
+  bool rowshift;  // the 3x3 stride-1 narrow-image kernel
+};
+
 struct Plan {
   int variant;
+  HaloShape halo;
   int splits;          // implicit GEMM split-k ranges
   int ksteps;
   int steps_per_split;
@@ -132,6 +138,7 @@ struct Plan {
   uint64_t scratch_whole;
   // depthwise tiling
   int toh, tow, tih, tiw, tiles_w, tiles;
+  int dw_planes;  // > 0: whole-plane register-blocked path with this many planes per workgroup
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -139,8 +146,34 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 
 // Depthwise output tile: whole plane when the staged input fits, else smaller
-// tiles; the staged region stays under 48 KiB of LDS.
+// tiles; the staged region stays under 48 KiB of LDS.  Kernel/stride pairs with a
+// compiled register-blocked path and whole planes of at most 16 KiB take the
+// whole-plane kernel: several planes per workgroup, enough 2x2 output blocks to
+// give every thread a few.
 bool plan_depthwise(const Geo& g, Plan* pl) {
+  pl->dw_planes = 0;
+  const bool compiled = g.dh == 1 && g.dw == 1 && g.sh == g.sw && g.kh == g.kw &&
+                        ((g.kh == 3 && g.sh <= 2) || (g.kh == 5 && g.sh <= 2) ||
+                         (g.kh == 7 && g.sh == 1));
+  if (compiled) {
+    const int64_t tih = (g.ho - 1) * g.sh + g.kh;
+    const int64_t tiw = (g.wo - 1) * g.sw + g.kw + 1;  // one pad column in the row pitch
+    const int64_t mult = g.co / g.ci;
+    const int64_t plane_bytes = (tih * tiw + mult * g.kh * g.kw) * 4;
+    if (plane_bytes <= 16 * 1024) {
+      const int64_t blocks = ceil_div(g.ho, 2) * ceil_div(g.wo, 2);
+      int64_t P = std::min<int64_t>(32 * 1024 / plane_bytes, std::max<int64_t>(1, 1024 / blocks));
+      P = std::max<int64_t>(1, std::min<int64_t>(P, g.n * g.ci));
+      pl->dw_planes = (int)P;
+      pl->tih = (int)tih;
+      pl->tiw = (int)tiw;
+      pl->toh = (int)g.ho;
+      pl->tow = (int)g.wo;
+      pl->tiles = 1;
+      pl->tiles_w = 1;
+      return ceil_div(g.n * g.ci, P) <= 2147483647LL;
+    }
+  }
   int64_t toh = std::min<int64_t>(g.ho, 64), tow = std::min<int64_t>(g.wo, 64);
   for (;;) {
     int64_t tih = (toh - 1) * g.sh + (g.kh - 1) * g.dh + 1;
@@ -158,6 +191,75 @@ bool plan_depthwise(const Geo& g, Plan* pl) {
   }
 }
 
+// Halo implicit GEMM (float16): kernel 3x3 or 1x1, channels per group a multiple
+// of 8, output rows at most 64 wide.  Picks the chunk width, the channel tile and
+// the rows per workgroup so that the staged tile fits one LDS buffer, every wave
+// owns at most HALO_MAXT MFMA tiles and every thread stages at most HALO_MAXI
+// items.  Shape-only.
+bool plan_halo(const Geo& g, int dtype, HaloShape* hs) {
+  if (dtype != CONV_F16 || g.transpose) return false;
+  // 3x3, stride 1, dilation 1, whole image of at most 14 x 14 outputs per
+  // workgroup, chunk pairs of 64 channels: the row-shift kernel.
+  if (g.kh == 3 && g.kw == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 &&
+      g.cig % 64 == 0 && g.ho <= 14 && g.wo <= 14) {
+    HaloShape s{};
+    s.rowshift = true;
+    s.oct = 4;
+    s.cb = 2;
+    s.tcb = 1;
+    s.tr = g.ho <= 8 ? 8 : 14;
+    s.tih = s.tr + 2;
+    s.tiw = 16;
+    s.n_ct = (int)ceil_div(g.cog, 32);
+    s.n_rt = 1;
+    if ((int64_t)s.n_ct * g.n * g.g > 2147483647LL) return false;
+    *hs = s;
+    return true;
+  }
+  if (!((g.kh == 3 && g.kw == 3) || (g.kh == 1 && g.kw == 1))) return false;
+  if (g.cig % 8 || g.wo > 64) return false;
+  HaloShape s{};
+  s.oct = g.cig % 32 == 0 ? 4 : (g.cig % 16 == 0 ? 2 : 1);
+  s.cb = g.cog > 16 ? 2 : 1;
+  s.tcb = (int)ceil_div(g.wo, 16);
+  s.n_ct = (int)ceil_div(g.cog, 16 * s.cb);
+  // Largest row tile that fits, then halve it while the grid is under two
+  // workgroups per CU (256 CUs): a second resident workgroup hides the first's
+  // staging latency.
+  // MFMA tiles per wave: the 3x3 kernels with 16- or 32-channel chunks would
+  // spill registers beyond 4 (resp. 7) tiles at two waves per SIMD.
+  const int64_t max_tiles = (g.kh * g.kw == 9 && s.oct == 4) ? 4
+                          : (g.kh * g.kw == 9 && s.oct == 2) ? 7 : HALO_MAXT;
+  int64_t best = 0;
+  for (int64_t tr = g.ho; tr >= 1; --tr) {
+    const int64_t rb = tr * s.tcb;
+    const int64_t per_wave = s.cb == 2 ? ceil_div(rb, 2) : ceil_div(rb, 4);
+    if (per_wave > max_tiles) continue;
+    const int64_t tih = (tr - 1) * g.sh + (g.kh - 1) * g.dh + 1;
+    const int64_t tiw = (s.tcb * 16 - 1) * g.sw + (g.kw - 1) * g.dw + 1;
+    const int64_t items = tih * tiw * s.oct;
+    if (items > 256 * HALO_MAXI) continue;
+    const int64_t bytes = items * 16 + g.kh * g.kw * 16 * s.cb * s.oct * 16;
+    if (bytes > HALO_BUF_BYTES) continue;
+    best = tr;
+    break;
+  }
+  if (best == 0) return false;
+  while (best > 1 && (int64_t)s.n_ct * ceil_div(g.ho, best) * g.n * g.g < 512) {
+    const int64_t half = ceil_div(best, 2);
+    if (ceil_div(g.ho, half) == ceil_div(g.ho, best)) break;
+    best = half;
+  }
+  s.tr = (int)best;
+  s.tih = (int)((best - 1) * g.sh + (g.kh - 1) * g.dh + 1);
+  s.tiw = (int)((s.tcb * 16 - 1) * g.sw + (g.kw - 1) * g.dw + 1);
+  s.n_rt = (int)ceil_div(g.ho, best);
+  const int64_t grid = (int64_t)s.n_ct * s.n_rt * g.n * g.g;
+  if (grid > 2147483647LL) return false;
+  *hs = s;
+  return true;
+}
+
 int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
   memset(pl, 0, sizeof(*pl));
   pl->splits = 1;
@@ -173,11 +275,21 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (ceil_div(g.co * g.kh * g.kw / g.g, IG_TILE_C) > 65535 || g.g > 65535) return CONV_ERR_SHAPE;
   } else {
     if (v == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
-    if (v == CONV_VARIANT_POINTWISE_GEMM || v == CONV_VARIANT_IMPLICIT_GEMM_HALO)
-      return CONV_ERR_ARG;  // not applicable to this shape in this build
-    if (v == CONV_VARIANT_AUTO) v = depthwise_applicable(g) ? CONV_VARIANT_DEPTHWISE_DIRECT
-                                                             : CONV_VARIANT_IMPLICIT_GEMM;
-    if (v == CONV_VARIANT_DEPTHWISE_DIRECT) {
+    if (v == CONV_VARIANT_POINTWISE_GEMM) return CONV_ERR_ARG;  // not built for this shape
+    HaloShape hs{};
+    const bool halo_ok = plan_halo(g, dtype, &hs);
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO && !halo_ok) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_AUTO) {
+      if (depthwise_applicable(g)) v = CONV_VARIANT_DEPTHWISE_DIRECT;
+      else if (halo_ok && p->split_override <= 1 &&
+               (int64_t)hs.n_ct * hs.n_rt * g.n * g.g >= (hs.rowshift ? 32 : 128))
+        v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
+      else v = CONV_VARIANT_IMPLICIT_GEMM;
+    }
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
+      if (p->split_override > 1) return CONV_ERR_ARG;
+      pl->halo = hs;
+    } else if (v == CONV_VARIANT_DEPTHWISE_DIRECT) {
       if (!depthwise_applicable(g)) return CONV_ERR_ARG;
       if (p->split_override > 1) return CONV_ERR_ARG;
       if (!plan_depthwise(g, pl)) return CONV_ERR_SHAPE;
@@ -313,7 +425,23 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.toh = pl.toh; a.tow = pl.tow; a.tih = pl.tih; a.tiw = pl.tiw;
       a.tiles_w = pl.tiles_w; a.tiles = pl.tiles;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      e = launch_depthwise(dt, a, s);
+      a.planes = pl.dw_planes;
+      a.xvec = reinterpret_cast<uintptr_t>(xc) % (dt == F16 ? 8 : 16) == 0 && (g.h * g.w) % 4 == 0;
+      e = pl.dw_planes > 0 ? launch_depthwise_plane(dt, a, s) : launch_depthwise(dt, a, s);
+    } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
+      HaloArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.kh = (int)g.kh; a.kw = (int)g.kw; a.groups = (int)g.g;
+      a.sh = (int)g.sh; a.sw = (int)g.sw; a.dh = (int)g.dh; a.dw = (int)g.dw;
+      a.pt = (int)g.pt; a.pl = (int)g.pl; a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.cig = (int)g.cig; a.cog = (int)g.cog;
+      a.oct = pl.halo.oct; a.tr = pl.halo.tr; a.tcb = pl.halo.tcb; a.cb = pl.halo.cb;
+      a.tih = pl.halo.tih; a.tiw = pl.halo.tiw; a.n_ct = pl.halo.n_ct; a.n_rt = pl.halo.n_rt;
+      a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0;
+      a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0;
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = pl.halo.rowshift ? launch_rowshift(a, s) : launch_halo(a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {
       IgemmArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -463,7 +591,17 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                pl.splits);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
-      snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
+      if (pl.dw_planes > 0)
+        snprintf(tmp, sizeof tmp, "depthwise_direct.%s.planes%d.b2x2", dn, pl.dw_planes);
+      else
+        snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
+      break;
+    case CONV_VARIANT_IMPLICIT_GEMM_HALO:
+      if (pl.halo.rowshift)
+        snprintf(tmp, sizeof tmp, "implicit_gemm_halo.%s.rowshift.r%d.n32", dn, pl.halo.tr);
+      else
+        snprintf(tmp, sizeof tmp, "implicit_gemm_halo.%s.r%dx%d.n%d.c%d", dn, pl.halo.tr,
+                 pl.halo.tcb * 16, pl.halo.cb * 16, pl.halo.oct * 8);
       break;
     default:
       snprintf(tmp, sizeof tmp, "%s.%s", variant_name(pl.variant), dn);

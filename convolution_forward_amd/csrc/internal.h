@@ -45,22 +45,24 @@ struct IgemmArgs {
 
 struct HaloArgs {
   const void* x;
-  const void* wt;      // weights
+  const void* wt;        // weights
   const void* bias;
   const void* res;
   void* y;
-  float* planes;
   int n, c_in, h, w, c_out, kh, kw, groups;
   int sh, sw, dh, dw, pt, pl;
   int ho, wo;
   int cig, cog;
-  int chunks;            // channel chunks per group
-  int chunks_per_split;
-  int splits;
-  int mode;
+  int oct;               // channel octets per chunk (chunk = 8*oct channels)
+  int tr;                // output rows per workgroup
+  int tcb;               // 16-column blocks per output row (covers the full width)
+  int cb;                // 16-channel blocks per workgroup (1 or 2)
+  int tih, tiw;          // staged input tile (rows, cols)
+  int n_ct, n_rt;        // channel tiles per group, row tiles per image
+  int wvec;              // weight rows may be read 16 bytes at a time
+  int xvec;              // input planes may be read 8 bytes at a time
   int act;
   float alpha, beta;
-  long long plane_stride;
 };
 
 struct DepthwiseArgs {
@@ -76,6 +78,8 @@ struct DepthwiseArgs {
   int toh, tow;          // output tile
   int tih, tiw;          // staged input tile (with halo)
   int tiles_w, tiles;    // tiles per plane along w, total per plane
+  int planes;            // whole-plane path: input planes per workgroup
+  int xvec;              // whole-plane path: planes may be read 16 (f32) / 8 (f16) bytes at a time
   int act;
   float alpha, beta;
 };
@@ -114,11 +118,17 @@ constexpr int IG_TILE_P = 64;   // output pixels per workgroup
 constexpr int IG_TILE_C = 64;   // output channels per workgroup
 constexpr int IG_KSTEP_BYTES = 64;  // k-block: 32 halves or 16 floats
 
-// Halo kernel (f16): whole-image pixel tiles, channel chunks of 32.
-constexpr int HALO_CHUNK = 32;
+// Halo kernel (f16): LDS bytes per pipeline buffer (input tile + weight tile);
+// two buffers are allocated statically.
+constexpr int HALO_BUF_BYTES = 40 * 1024;
+constexpr int HALO_MAXT = 8;  // 16x16 MFMA output tiles per wave
+constexpr int HALO_MAXI = 8;  // staged (position, octet) input items per thread
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
+hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
+hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
+hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_reduce(Dtype dt, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_col2im(Dtype dt, const Col2imArgs& a, hipStream_t s);
 

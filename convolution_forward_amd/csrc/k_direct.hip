@@ -71,6 +71,163 @@ hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Depthwise, whole-plane fast path (dilation 1, kernel and stride fixed at
+// compile time): a workgroup stages P consecutive input planes (contiguous in
+// NCHW, read with 16-byte loads) into zero-padded LDS tiles together with their
+// weights, then each thread computes 2x2 output blocks from an input patch held
+// in registers, so every staged value feeds several FMAs.  Each output is still
+// one float32 FMA chain over the window in (kh, kw) row-major order.
+// ---------------------------------------------------------------------------
+template <typename T, int KH, int KW, int SH, int SW>
+__global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArgs a) {
+  constexpr int BH = 2, BW = 2;
+  constexpr int PH = (BH - 1) * SH + KH, PW = (BW - 1) * SW + KW;  // input patch
+  extern __shared__ float smem_dw[];
+  const int P = a.planes;                 // input planes per workgroup
+  const int tsz = a.tih * a.tiw;          // floats per plane tile (tiw = row pitch)
+  float* tile = smem_dw;
+  float* wl = smem_dw + P * tsz;          // P * mult * KH * KW weights
+  const int plane0 = blockIdx.x * P;
+  const int nplanes = a.n * a.c_in;
+  const int np = min(P, nplanes - plane0);
+  const int hw = a.h * a.w;
+  const T* __restrict__ xp = static_cast<const T*>(a.x) + (long long)plane0 * hw;
+
+  for (int i = threadIdx.x; i < P * tsz; i += 256) tile[i] = 0.0f;
+  const int nw = np * a.mult * KH * KW;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nw; i += 256) {
+    // planes of one workgroup may wrap from the last channel of an image to the
+    // first of the next: index the weights by each plane's channel
+    const int pl = i / (a.mult * KH * KW), r = i - pl * (a.mult * KH * KW);
+    const int ci = (plane0 + pl) % a.c_in;
+    wl[i] = to_f32(static_cast<const T*>(a.wt)[(long long)ci * a.mult * KH * KW + r]);
+  }
+  // planes: 4 consecutive pixels per item
+  const int g4 = (hw + 3) / 4;
+  for (int q = threadIdx.x; q < np * g4; q += 256) {
+    const int pl = q / g4, f0 = 4 * (q - pl * g4);
+    float v[4];
+    if (a.xvec && f0 + 4 <= hw) {
+      if constexpr (sizeof(T) == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(xp + (long long)pl * hw + f0);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(xp + (long long)pl * hw + f0);
+        const _Float16* h = reinterpret_cast<const _Float16*>(&t);
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) v[k4] = (float)h[k4];
+      }
+    } else {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        v[k4] = f0 + k4 < hw ? to_f32(xp[(long long)pl * hw + f0 + k4]) : 0.0f;
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int f = f0 + k4;
+      if (f >= hw) break;
+      const int ih = f / a.w, iw = f - (f / a.w) * a.w;
+      const int tr = ih + a.pt, tc = iw + a.pl;
+      if (tr < a.tih && tc < a.tiw - 1) tile[pl * tsz + tr * a.tiw + tc] = v[k4];
+    }
+  }
+  __syncthreads();
+
+  const T* bias = static_cast<const T*>(a.bias);
+  const T* res = static_cast<const T*>(a.res);
+  T* y = static_cast<T*>(a.y);
+  const int nbh = (a.ho + BH - 1) / BH, nbw = (a.wo + BW - 1) / BW;
+  const int per_plane = nbh * nbw;
+  for (int b = threadIdx.x; b < np * per_plane; b += 256) {
+    const int pl = b / per_plane, r = b - pl * per_plane;
+    const int bh = r / nbw, bw = r - (r / nbw) * nbw;
+    const int oh0 = bh * BH, ow0 = bw * BW;
+    const float* src = tile + pl * tsz + (oh0 * SH) * a.tiw + ow0 * SW;
+    float patch[PH][PW];
+#pragma unroll
+    for (int i = 0; i < PH; ++i)
+#pragma unroll
+      for (int j = 0; j < PW; ++j) {
+        // the last block of a row/column may reach past the tile: clamp the read
+        // (those outputs are not stored)
+        const int rr = min(oh0 * SH + i, a.tih - 1) - oh0 * SH;
+        const int cc = min(ow0 * SW + j, a.tiw - 1) - ow0 * SW;
+        patch[i][j] = src[rr * a.tiw + cc];
+      }
+    const int plane = plane0 + pl;
+    const int n = plane / a.c_in, ci = plane - n * a.c_in;
+    for (int jm = 0; jm < a.mult; ++jm) {
+      const int co = ci * a.mult + jm;
+      const float* wv = wl + (pl * a.mult + jm) * KH * KW;
+      float acc[BH][BW];
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+#pragma unroll
+        for (int j = 0; j < BW; ++j) acc[i][j] = 0.0f;
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+          const float wk = wv[kh * KW + kw];
+#pragma unroll
+          for (int i = 0; i < BH; ++i)
+#pragma unroll
+            for (int j = 0; j < BW; ++j)
+              acc[i][j] = fmaf(patch[i * SH + kh][j * SW + kw], wk, acc[i][j]);
+        }
+      // residuals first (y may alias the residual exactly), then the stores
+      const long long obase = ((long long)n * a.c_out + co) * a.ho * a.wo;
+      long long oidx[BH][BW];
+      bool ok[BH][BW];
+      float rv[BH][BW];
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+#pragma unroll
+        for (int j = 0; j < BW; ++j) {
+          ok[i][j] = oh0 + i < a.ho && ow0 + j < a.wo;
+          oidx[i][j] = obase + (ok[i][j] ? (long long)(oh0 + i) * a.wo + ow0 + j : 0);
+          rv[i][j] = (res && ok[i][j]) ? to_f32(res[oidx[i][j]]) : 0.0f;
+        }
+      const float bv = bias ? to_f32(bias[co]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+#pragma unroll
+        for (int j = 0; j < BW; ++j) {
+          if (!ok[i][j]) continue;
+          float v = acc[i][j];
+          if (bias) v = v + bv;
+          if (res) v = v + rv[i][j];
+          y[oidx[i][j]] = from_f32<T>(apply_act(v, a.act, a.alpha, a.beta));
+        }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_dw_plane_t(const DepthwiseArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n * a.c_in + a.planes - 1) / a.planes));
+  const size_t lds = ((size_t)a.planes * a.tih * a.tiw + (size_t)a.planes * a.mult * a.kh * a.kw) *
+                     sizeof(float);
+#define DW_CASE(KH_, KW_, SH_, SW_)                                                        \
+  if (a.kh == KH_ && a.kw == KW_ && a.sh == SH_ && a.sw == SW_) {                          \
+    hipLaunchKernelGGL((depthwise_plane_kernel<T, KH_, KW_, SH_, SW_>), grid, dim3(256), lds, s, a); \
+    return hipGetLastError();                                                              \
+  }
+  DW_CASE(3, 3, 1, 1)
+  DW_CASE(3, 3, 2, 2)
+  DW_CASE(5, 5, 1, 1)
+  DW_CASE(5, 5, 2, 2)
+  DW_CASE(7, 7, 1, 1)
+#undef DW_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, hipStream_t s) {
+  return dt == F16 ? launch_dw_plane_t<_Float16>(a, s) : launch_dw_plane_t<float>(a, s);
+}
+
+// ---------------------------------------------------------------------------
 // Split-k reduction.  The R raw planes hold disjoint k ranges of the same
 // outputs.  Lanes are grouped R' = next_pow2(R) at a time: lane (q, r) reads
 // plane r of output q, and a xor butterfly over the group adds the planes in a

@@ -199,32 +199,53 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
     }
   }
 
-  // Epilogue: lane holds pixels 4*(lane/16) + e of row block i, channel lane % 16 of block j.
+  // Epilogue: lane holds pixels 4*(lane/16) + e of row block i, channel lane % 16 of
+  // block j.  Every residual of the lane is read before any store: y may alias the
+  // residual exactly and each element is read and written by this lane only, so
+  // hoisting the reads keeps the result and lets them overlap.
   const T* bias = static_cast<const T*>(a.bias);
   const T* res = static_cast<const T*>(a.res);
   T* y = static_cast<T*>(a.y);
+  long long oidx[2][2][4];
+  bool ok[2][2][4];
+  float rv[2][2][4];
+  float bv[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = tile_c0 + wc * 32 + j * 16 + (lane & 15);
-    if (col >= a.cog) continue;
-    const int co = grp * a.cog + col;
+    const bool col_ok = col < a.cog;
+    const int co = grp * a.cog + (col_ok ? col : 0);
+    bv[j] = (bias && col_ok && a.mode != OUT_RAW) ? to_f32(bias[co]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pp = tile_p0 + wr * 32 + i * 16 + (lane >> 4) * 4 + e;
-        if (pp >= a.pix) continue;
-        const int n_o = pp / hw_out;
-        const int rem = pp - n_o * hw_out;
-        const long long oidx = ((long long)n_o * a.c_out + co) * hw_out + rem;
-        const float v = acc[i][j][e];
-        if (a.mode == OUT_RAW)
-          a.planes[(long long)split * a.plane_stride + oidx] = v;
-        else
-          y[oidx] = epilogue_one<T>(v, bias, res, co, oidx, a.act, a.alpha, a.beta);
+        ok[j][i][e] = col_ok && pp < a.pix;
+        const int ppc = ok[j][i][e] ? pp : 0;
+        const int n_o = ppc / hw_out;
+        const int rem = ppc - n_o * hw_out;
+        oidx[j][i][e] = ((long long)n_o * a.c_out + co) * hw_out + rem;
+        rv[j][i][e] = (res && ok[j][i][e] && a.mode != OUT_RAW) ? to_f32(res[oidx[j][i][e]]) : 0.f;
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!ok[j][i][e]) continue;
+        float v = acc[i][j][e];
+        if (a.mode == OUT_RAW) {
+          a.planes[(long long)split * a.plane_stride + oidx[j][i][e]] = v;
+        } else {
+          if (bias) v = v + bv[j];
+          if (res) v = v + rv[j][i][e];
+          y[oidx[j][i][e]] = from_f32<T>(apply_act(v, a.act, a.alpha, a.beta));
+        }
+      }
 }
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s) {

@@ -7,6 +7,7 @@ chunking, forced split-k and forced variants, element offsets and residual
 aliasing.
 """
 import itertools
+import re
 import sys
 
 import numpy as np
@@ -51,7 +52,7 @@ def test_workload_layer_reduced_batch(name):
     y = run_gpu(g, lr.dtype, inp.x, inp.w, inp.b, inp.r, transpose=lr.transpose)
     assert y.shape == lr.out_shape
     yr, sr = oracle_ref(g, inp.x, inp.w, inp.b, inp.r, transpose=lr.transpose)
-    q = assert_parity(lr.dtype, y, yr, sr, inp.b, inp.r, what=name)
+    q = assert_parity(lr.dtype, y, yr, sr, inp.b, inp.r, what=name, act=lr.act)
     _say(f"  max err / bound = {q:.3g}")
 
 
@@ -67,7 +68,7 @@ def test_workload_layer_full_size_sampled(name):
     assert y.shape == layer.out_shape
     if layer.transpose:
         yr, sr = oracle_ref(g, inp.x, inp.w, inp.b, inp.r, transpose=True)
-        assert_parity(layer.dtype, y, yr, sr, inp.b, inp.r, what=name)
+        assert_parity(layer.dtype, y, yr, sr, inp.b, inp.r, what=name, act=layer.act)
         return
     rng = np.random.default_rng(7)
     N, C, H, W = layer.out_shape
@@ -86,7 +87,7 @@ def test_workload_layer_full_size_sampled(name):
         sp += np.abs(inp.b.astype(np.float64))[(idx // (H * W)) % C]
     if inp.r is not None:
         sp += np.abs(inp.r.astype(np.float64).ravel()[idx])
-    assert_parity(layer.dtype, yg, yr, sp, what=name)
+    assert_parity(layer.dtype, yg, yr, sp, what=name, act=layer.act)
 
 
 def _sweep_cases():
@@ -136,9 +137,122 @@ def test_random_shapes(case):
     variants = ["auto", "implicit_gemm"]
     if g.c_in // g.groups == 1:
         variants.append("depthwise_direct")
+    if _applicable(g, dtype, "implicit_gemm_halo"):
+        variants.append("implicit_gemm_halo")
     for v in variants:
         y = run_gpu(g, dtype, x, w, b, r, variant=v)
-        assert_parity(dtype, y, yr, sr, b, r, what=f"{v}")
+        assert_parity(dtype, y, yr, sr, b, r, what=f"{v}", act=g.act)
+
+
+def _applicable(g, dtype, variant):
+    from gpu_harness import problem_from
+    try:
+        cf.conv_describe_variant(problem_from(g, variant=variant), dtype)
+        return True
+    except cf.ConvError:
+        return False
+
+
+HALO_CASES = [
+    # (geometry, bias, residual)
+    (oracle.Geom(2, 64, 14, 14, 64, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu"), True, True),
+    (oracle.Geom(3, 32, 7, 7, 48, 3, 3, pt=1, pl=1, pb=1, pr=1, act="silu"), True, False),
+    (oracle.Geom(1, 96, 15, 17, 40, 3, 3, sh=2, sw=2, pt=1, pl=0, pb=2, pr=1), False, True),
+    (oracle.Geom(2, 16, 20, 30, 16, 3, 3, dh=2, dw=3, pt=2, pl=3, pb=2, pr=3, act="tanh"),
+     True, False),
+    (oracle.Geom(1, 24, 9, 64, 20, 3, 3, sh=1, sw=1, pt=0, pl=1, pb=0, pr=1), True, True),
+    (oracle.Geom(2, 64, 10, 56, 64, 3, 3, groups=8, dh=2, dw=2, pt=2, pl=2, pb=2, pr=2,
+                 act="sigmoid"), True, False),
+    (oracle.Geom(2, 64, 12, 50, 256, 1, 1, act="relu"), True, False),
+    (oracle.Geom(1, 48, 5, 5, 33, 1, 1, sh=2, sw=2, pt=1, pl=1, pb=0, pr=0), True, True),
+    (oracle.Geom(4, 256, 14, 14, 256, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu"), True, True),
+]
+
+
+@pytest.mark.parametrize("case", HALO_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}")
+def test_halo_variant(case):
+    g, has_b, has_r = case
+    _say(f"[halo] {g}")
+    assert _applicable(g, "f16", "implicit_gemm_halo")
+    rng = np.random.default_rng(g.c_in + 31 * g.w)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, g.c_in // g.groups, g.kh, g.kw)) *
+         np.sqrt(2.0 / (g.c_in // g.groups * g.kh * g.kw))).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f16", x, w, b, r, variant="implicit_gemm_halo")
+    assert_parity("f16", y, yr, sr, b, r, what="halo", act=g.act)
+    # same bits when chunked over images (no scratch: every image is independent)
+    # and with misaligned weights (element-load path)
+    y2 = run_gpu(g, "f16", x, w, b, r, variant="implicit_gemm_halo", offsets=(1, 3, 0, 0, 2))
+    assert np.array_equal(_bits(y), _bits(y2))
+
+
+ROWSHIFT_CASES = [
+    (oracle.Geom(2, 64, 14, 14, 64, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu"), True, True),
+    (oracle.Geom(3, 128, 7, 7, 40, 3, 3, pt=1, pl=1, pb=1, pr=1, act="silu"), True, False),
+    (oracle.Geom(1, 64, 12, 11, 96, 3, 3, pt=0, pl=2, pb=2, pr=0), False, True),
+    (oracle.Geom(2, 128, 10, 10, 64, 3, 3, groups=2, pt=1, pl=0, pb=1, pr=1, act="tanh"),
+     True, False),
+    (oracle.Geom(1, 192, 16, 16, 32, 3, 3), True, True),  # no pads: 14 x 14 out
+    (oracle.Geom(2, 64, 5, 4, 48, 3, 3, pt=2, pl=2, pb=1, pr=2, act="hard_swish"), True, True),
+]
+
+
+@pytest.mark.parametrize("case", ROWSHIFT_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}")
+def test_rowshift_variant(case):
+    g, has_b, has_r = case
+    _say(f"[rowshift] {g}")
+    from gpu_harness import problem_from
+    assert "rowshift" in cf.conv_describe_variant(problem_from(g, variant="implicit_gemm_halo"),
+                                                  "f16")
+    rng = np.random.default_rng(g.c_in + 17 * g.w + g.h)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, g.c_in // g.groups, 3, 3)) *
+         np.sqrt(2.0 / (g.c_in // g.groups * 9))).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    v = "implicit_gemm_halo"
+    y = run_gpu(g, "f16", x, w, b, r, variant=v)
+    assert_parity("f16", y, yr, sr, b, r, what="rowshift", act=g.act)
+    y2 = run_gpu(g, "f16", x, w, b, r, variant=v, offsets=(5, 1, 2, 0, 3))  # misaligned w
+    assert np.array_equal(_bits(y), _bits(y2))
+    y3 = run_gpu(g, "f16", x, w, b, r, variant=v)
+    assert np.array_equal(_bits(y), _bits(y3))
+
+
+DEPTHWISE_CASES = [
+    (oracle.Geom(3, 5, 9, 11, 10, 3, 3, groups=5, pt=1, pl=1, pb=1, pr=1, act="relu"), "f32"),
+    (oracle.Geom(2, 7, 13, 13, 7, 7, 7, groups=7, pt=3, pl=3, pb=3, pr=3), "f32"),
+    (oracle.Geom(4, 6, 15, 14, 6, 5, 5, groups=6, sh=2, sw=2, pt=2, pl=2, pb=2, pr=1,
+                 act="hard_swish"), "f32"),
+    (oracle.Geom(2, 24, 28, 28, 24, 3, 3, groups=24, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1), "f16"),
+    (oracle.Geom(5, 3, 7, 6, 9, 5, 5, groups=3, pt=2, pl=2, pb=2, pr=2, act="sigmoid"), "f16"),
+    (oracle.Geom(1, 4, 30, 30, 4, 3, 3, groups=4, pt=0, pl=0, pb=0, pr=0), "f32"),
+]
+
+
+@pytest.mark.parametrize("case", DEPTHWISE_CASES, ids=lambda c: f"{c[1]}-{c[0].kh}x{c[0].kw}s{c[0].sh}")
+def test_depthwise_variants(case):
+    """Whole-plane and tiled depthwise paths against the oracle; same bits when
+    the input is misaligned (element loads) and from run to run."""
+    g, dtype = case
+    _say(f"[depthwise] {dtype} {g}")
+    npdt = np.float16 if dtype == "f16" else np.float32
+    rng = np.random.default_rng(g.c_out * 13 + g.kh)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+    w = (rng.standard_normal((g.c_out, 1, g.kh, g.kw)) * 0.3).astype(npdt)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt)
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(npdt)
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, dtype, x, w, b, r)
+    assert_parity(dtype, y, yr, sr, b, r, what="depthwise", act=g.act)
+    y2 = run_gpu(g, dtype, x, w, b, r, offsets=(1, 0, 0, 2, 3))
+    assert np.array_equal(_bits(y), _bits(y2))
+    y3 = run_gpu(g, dtype, x, w, b, r, variant="implicit_gemm")
+    assert_parity(dtype, y3, yr, sr, b, r, what="depthwise-as-igemm", act=g.act)
 
 
 def _convt_cases():
@@ -165,7 +279,7 @@ def test_conv_transpose_shapes(case):
     r = rng.uniform(-1, 1, oracle.out_shape(g, transpose=True)).astype(npdt)
     yr, sr = oracle.conv_transpose2d(g, x, w, b, r)
     y = run_gpu(g, dtype, x, w, b, r, transpose=True)
-    assert_parity(dtype, y, yr, sr, b, r, what="convt")
+    assert_parity(dtype, y, yr, sr, b, r, what="convt", act=g.act)
     # chunked through a one-image scratch: same bits
     y1 = run_gpu(g, dtype, x, w, b, r, transpose=True, scratch_images=1)
     assert np.array_equal(y.view(np.uint16 if dtype == "f16" else np.uint32),
@@ -248,11 +362,11 @@ def test_split_k_forced_and_chunked(dtype):
     r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(npdt)
     yr, sr = oracle.conv2d(g, x, w, b, r)
     p = cf.make_problem(3, 128, 7, 7, 96, 3, 3, pads=(1, 1, 1, 1))
-    assert "split1" not in cf.conv_describe_variant(p, dtype)
+    assert int(re.search(r"split(\d+)", cf.conv_describe_variant(p, dtype)).group(1)) > 1
     outs = {}
     for splits in (0, 1, 2, 5, 16):
         y = run_gpu(g, dtype, x, w, b, r, splits=splits)
-        assert_parity(dtype, y, yr, sr, b, r, what=f"splits={splits}")
+        assert_parity(dtype, y, yr, sr, b, r, what=f"splits={splits}", act=g.act)
         outs[splits] = y
         if splits != 1:
             yc = run_gpu(g, dtype, x, w, b, r, splits=splits, scratch_images=1)
