@@ -32,6 +32,42 @@ __device__ __forceinline__ float apply_act(float v, int act, float alpha, float 
   }
 }
 
+template <int ACT>
+__device__ __forceinline__ float act_t(float v, float alpha, float beta) {
+  if constexpr (ACT == 1) return v > 0.0f ? v : 0.0f;
+  else if constexpr (ACT == 2) return tanhf(v);
+  else if constexpr (ACT == 3) return 1.0f / (1.0f + expf(-v));
+  else if constexpr (ACT == 4) return v / (1.0f + expf(-v));
+  else if constexpr (ACT == 5) return fminf(fmaxf(alpha * v + beta, 0.0f), 1.0f);
+  else if constexpr (ACT == 6) return v * fminf(fmaxf(v * (1.0f / 6.0f) + 0.5f, 0.0f), 1.0f);
+  else if constexpr (ACT == 7) return fminf(fmaxf(v, alpha), beta);
+  else if constexpr (ACT == 8) return v >= 0.0f ? v : alpha * v;
+  else return v;
+}
+
+// Activation over a thread's whole batch of outputs: one uniform branch, then a
+// branch-free loop (an activation switch per element would multiply the code by
+// the batch size).
+template <int N>
+__device__ __forceinline__ void act_array(float (&v)[N], int act, float alpha, float beta) {
+  switch (act) {
+#define CONVFWD_ACT_CASE(A)                                                   \
+  case A:                                                                     \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = act_t<A>(v[i], alpha, beta); \
+    break;
+    CONVFWD_ACT_CASE(1)
+    CONVFWD_ACT_CASE(2)
+    CONVFWD_ACT_CASE(3)
+    CONVFWD_ACT_CASE(4)
+    CONVFWD_ACT_CASE(5)
+    CONVFWD_ACT_CASE(6)
+    CONVFWD_ACT_CASE(7)
+    CONVFWD_ACT_CASE(8)
+#undef CONVFWD_ACT_CASE
+    default: break;
+  }
+}
+
 // One output element: v is the float32 sum; idx the flat NCHW output index.
 template <typename T>
 __device__ __forceinline__ T epilogue_one(float v, const T* bias, const T* res, int co,

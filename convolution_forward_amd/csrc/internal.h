@@ -61,6 +61,7 @@ struct HaloArgs {
   int n_ct, n_rt;        // channel tiles per group, row tiles per image
   int wvec;              // weight rows may be read 16 bytes at a time
   int xvec;              // input planes may be read 8 bytes at a time
+  int ovec;              // output / residual planes may be written / read 8 bytes at a time
   int act;
   float alpha, beta;
 };

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArg
   }
   __syncthreads();
 
-  const T* bias = static_cast<const T*>(a.bias);
+  const T* __restrict__ bias = static_cast<const T*>(a.bias);
   const T* res = static_cast<const T*>(a.res);
   T* y = static_cast<T*>(a.y);
   const int nbh = (a.ho + BH - 1) / BH, nbw = (a.wo + BW - 1) / BW;
@@ -187,19 +187,31 @@ __global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArg
         for (int j = 0; j < BW; ++j) {
           ok[i][j] = oh0 + i < a.ho && ow0 + j < a.wo;
           oidx[i][j] = obase + (ok[i][j] ? (long long)(oh0 + i) * a.wo + ow0 + j : 0);
-          rv[i][j] = (res && ok[i][j]) ? to_f32(res[oidx[i][j]]) : 0.0f;
+          rv[i][j] = 0.0f;
         }
+      if (res) {  // uniform; clamped indices keep every load unconditional
+#pragma unroll
+        for (int i = 0; i < BH; ++i)
+#pragma unroll
+          for (int j = 0; j < BW; ++j) rv[i][j] = to_f32(res[oidx[i][j]]);
+      }
       const float bv = bias ? to_f32(bias[co]) : 0.0f;
+      float v[BH * BW];
 #pragma unroll
       for (int i = 0; i < BH; ++i)
 #pragma unroll
         for (int j = 0; j < BW; ++j) {
-          if (!ok[i][j]) continue;
-          float v = acc[i][j];
-          if (bias) v = v + bv;
-          if (res) v = v + rv[i][j];
-          y[oidx[i][j]] = from_f32<T>(apply_act(v, a.act, a.alpha, a.beta));
+          float s = acc[i][j];
+          if (bias) s = s + bv;
+          if (res) s = s + rv[i][j];
+          v[i * BW + j] = s;
         }
+      act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+      for (int i = 0; i < BH; ++i)
+#pragma unroll
+        for (int j = 0; j < BW; ++j)
+          if (ok[i][j]) y[oidx[i][j]] = from_f32<T>(v[i * BW + j]);
     }
   }
 }

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
 
   // items per thread (uniform across the workgroup): a scalar branch per item
   const int ni = (in_items + 255) / 256;
-  auto load_chunk = [&](int c) {
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
     const long long coff = (long long)c * CH * hw_in;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     }
   };
 
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
     unsigned char* base = smem + buf * HALO_BUF_BYTES;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
@@ -162,13 +162,14 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     }
     if (w_live) {
       // the item holds w[co][8 channels][KHW taps]; element e*KHW + t is channel e, tap t
-      const _Float16* h = reinterpret_cast<const _Float16*>(rw);
       unsigned char* wb = base + in_bytes;
 #pragma unroll
       for (int t = 0; t < KHW; ++t) {
         half8_t v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = w_ok ? h[e * KHW + t] : _Float16(0);
+        for (int e = 0; e < 8; ++e)
+          v[e] = w_ok ? __builtin_bit_cast(half8_t, rw[(e * KHW + t) / 8])[(e * KHW + t) % 8]
+                      : _Float16(0);
         const int pos = t * TN + w_co_l;
         *reinterpret_cast<half8_t*>(wb + (pos * OCT + swz<OCT>(pos, w_o)) * 16) = v;
       }
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   for (int i = 0; i < NT; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int lg = lane >> 4;
-  auto compute_chunk = [&](int buf) {
+  auto compute_chunk = [&](int buf) __attribute__((always_inline)) {
     const unsigned char* base = smem + buf * HALO_BUF_BYTES;
     const unsigned char* wb = base + in_bytes;
 #pragma unroll
@@ -239,44 +240,64 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds pixels 4*(lane/16)+e of the tile's 16 columns ----
-  // Residuals are read for every tile of the lane before any store (y may alias
-  // the residual exactly; each element is read and written by this lane only).
-  const _Float16* bias = static_cast<const _Float16*>(a.bias);
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
-  const int col_l = co0 + cbw * 16 + (lane & 15);
-  if (col_l >= a.cog) return;
-  const int co = g * a.cog + col_l;
-  const long long hw_out = (long long)a.ho * a.wo;
-  const float bv = bias ? (float)bias[co] : 0.f;
-  long long oidx[NT][4];
-  bool ok[NT][4];
-  float rv[NT][4];
+  // ---- epilogue: the accumulators (lane: pixels 4*(lane/16)+e of a 16-column
+  // block, output channel lane % 16) are laid out [channel][row][column] in LDS,
+  // then every thread finishes outputs in memory order, so residual reads and
+  // stores are contiguous along output rows. ----
+  const int TNc = a.cb * 16;
+  const int rows = min(a.tr, a.ho - oh0);
+  const int tile_px = rows * a.wo;
+  float* outt = reinterpret_cast<float*>(smem);  // [TNc][rows * wo]; the loop ended on a barrier
+  float* bsm = reinterpret_cast<float*>(smem + 2 * HALO_BUF_BYTES) - 32;
+  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  if (tid < TNc) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
+    if (i >= ntile) continue;
     const int rb = rb0 + i * rbs;
     const int r = rb / a.tcb, cblk = rb - (rb / a.tcb) * a.tcb;
-    const int oh = oh0 + r;
+    if (r >= rows) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ow = cblk * 16 + 4 * lg + e;
-      ok[i][e] = i < ntile && oh < a.ho && ow < a.wo;
-      oidx[i][e] = ((long long)n * a.c_out + co) * hw_out +
-                   (ok[i][e] ? (long long)oh * a.wo + ow : 0);
-      rv[i][e] = (res && ok[i][e]) ? (float)res[oidx[i][e]] : 0.f;
+      if (ow < a.wo) outt[(cbw * 16 + (lane & 15)) * tile_px + r * a.wo + ow] = acc[i][e];
     }
   }
+  __syncthreads();
+  const _Float16* res = static_cast<const _Float16*>(a.res);
+  _Float16* y = static_cast<_Float16*>(a.y);
+  const int cvalid = min(TNc, a.cog - co0);
+  const int total = cvalid * tile_px;
+  const long long hw_out = (long long)a.ho * a.wo;
+  const long long cbase = ((long long)n * a.c_out + g * a.cog + co0) * hw_out + (long long)oh0 * a.wo;
+  // every residual of the thread is read before its first store (y may alias the
+  // residual exactly; every element is read and written by one thread only); the
+  // bias went to LDS before the barrier
+  constexpr int EPT = 32;  // at most 32 channels x 256 pixels per workgroup tile
+  long long oidx[EPT];
+  float v[EPT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int k2 = 0; k2 < EPT; ++k2) {
+    const int idx = min(tid + 256 * k2, total - 1);
+    const int cl = idx / tile_px, rem = idx - cl * tile_px;
+    oidx[k2] = cbase + (long long)cl * hw_out + rem;
+  }
+  if (res) {  // uniform; loads from clamped indices so none sits behind a branch
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!ok[i][e]) continue;
-      float v = acc[i][e];
-      if (bias) v = v + bv;
-      if (res) v = v + rv[i][e];
-      y[oidx[i][e]] = (_Float16)apply_act(v, a.act, a.alpha, a.beta);
-    }
+    for (int k2 = 0; k2 < EPT; ++k2) v[k2] = (float)res[oidx[k2]];
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < EPT; ++k2) {
+    const int idx = min(tid + 256 * k2, total - 1);
+    float s = outt[idx];
+    if (a.bias) s = s + bsm[idx / tile_px];
+    if (res) s = s + v[k2];
+    v[k2] = s;
+  }
+  act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+  for (int k2 = 0; k2 < EPT; ++k2)
+    if (tid + 256 * k2 < total) y[oidx[k2]] = (_Float16)v[k2];
 }
 
 template <int KH, int KW, int OCT>

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
 
   vec_t ra, rb;
 
-  auto gather = [&](int step) {
+  auto gather = [&](int step) __attribute__((always_inline)) {
     const int k0 = step * KSTEP + squart * EPT;
     // A: decode k0 once, then walk (ci, kh, kw) in weight-row order.
     {
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
     }
   };
 
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf) __attribute__((always_inline)) {
     *reinterpret_cast<vec_t*>(&As[buf][srow * IG_ROW + squart * 16]) = ra;
     *reinterpret_cast<vec_t*>(&Bs[buf][srow * IG_ROW + squart * 16]) = rb;
   };
@@ -226,26 +226,48 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
         const int n_o = ppc / hw_out;
         const int rem = ppc - n_o * hw_out;
         oidx[j][i][e] = ((long long)n_o * a.c_out + co) * hw_out + rem;
-        rv[j][i][e] = (res && ok[j][i][e] && a.mode != OUT_RAW) ? to_f32(res[oidx[j][i][e]]) : 0.f;
+        rv[j][i][e] = 0.f;
       }
     }
   }
+  if (res && a.mode != OUT_RAW) {  // uniform; every load unconditional (clamped index)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[j][i][e] = to_f32(res[oidx[j][i][e]]);
+  }
+  if (a.mode == OUT_RAW) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ok[j][i][e]) a.planes[(long long)split * a.plane_stride + oidx[j][i][e]] = acc[i][j][e];
+    return;
+  }
+  float v[16];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (!ok[j][i][e]) continue;
-        float v = acc[i][j][e];
-        if (a.mode == OUT_RAW) {
-          a.planes[(long long)split * a.plane_stride + oidx[j][i][e]] = v;
-        } else {
-          if (bias) v = v + bv[j];
-          if (res) v = v + rv[j][i][e];
-          y[oidx[j][i][e]] = from_f32<T>(apply_act(v, a.act, a.alpha, a.beta));
-        }
+        float s = acc[i][j][e];
+        if (bias) s = s + bv[j];
+        if (res) s = s + rv[j][i][e];
+        v[(j * 2 + i) * 4 + e] = s;
       }
+  act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok[j][i][e]) y[oidx[j][i][e]] = from_f32<T>(v[(j * 2 + i) * 4 + e]);
 }
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s) {

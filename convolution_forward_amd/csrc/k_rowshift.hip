@@ -31,6 +31,8 @@
 //    that no pixel maps to (the padding border) are zeroed once.
 // Per output the taps of a 16-channel slice are accumulated in (kh, kw) row-major
 // order, slices in increasing channel order within each wave.
+#include <type_traits>
+
 #include "epilogue.h"
 #include "internal.h"
 
@@ -56,7 +58,8 @@ struct RsLayout {
   static constexpr int NPOS = TROWS * RS_COLS;
   static constexpr int IN_BYTES = NPOS * RS_CH * 2;  // 8 octets of 16 bytes per position
   static constexpr int STAGE = IN_BYTES + RS_WBYTES;
-  static constexpr int TOTAL = 2 * STAGE;            // double buffer
+  static constexpr int SINK = 2 * STAGE;             // 16 bytes that dead staging writes hit
+  static constexpr int TOTAL = 2 * STAGE + 16;        // double buffer + sink
   static constexpr int MAX_GROUPS = 16 * 16 / 4;     // 4-pixel groups of an input plane
   static constexpr int NI = (8 * MAX_GROUPS + 255) / 256;
   static constexpr int NW = (32 * 72 + 255) / 256;   // 16-byte weight vectors per thread
@@ -142,11 +145,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     w_lds[i] = L::IN_BYTES + col * RS_WROW + piece * 16;
   }
 
-  u32x2_t rin[L::NI][8];  // [item][channel]: 4 pixels
-  u32x4_t rwv[L::NW];
+  u32x2_t rin[2][L::NI][8];  // two staged stages in flight: [set][item][channel], 4 pixels
+  u32x4_t rwv[2][L::NW];
   const int nstages = a.cig / RS_CH;
 
-  auto load_stage = [&](int s) {
+  auto load_stage = [&](int s, int set) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
     if (a.xvec) {
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         const _Float16* src = ximg + xoff + in_off[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          rin[i][e] = *reinterpret_cast<const u32x2_t*>(src + (long long)e * hw);
+          rin[set][i][e] = *reinterpret_cast<const u32x2_t*>(src + (long long)e * hw);
       }
     } else {  // input not 8-byte aligned or planes not a multiple of 4: element loads
 #pragma unroll
@@ -167,42 +170,47 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           half4_t h;
 #pragma unroll
           for (int k4 = 0; k4 < 4; ++k4) h[k4] = src[(long long)e * hw + min(k4, left)];
-          rin[i][e] = __builtin_bit_cast(u32x2_t, h);
+          rin[set][i][e] = __builtin_bit_cast(u32x2_t, h);
         }
       }
     }
     if (a.wvec) {
 #pragma unroll
       for (int i = 0; i < L::NW; ++i)
-        rwv[i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
+        rwv[set][i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < L::NW; ++i) {
         half8_t h;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = wg[woff + w_off[i] + e];
-        rwv[i] = __builtin_bit_cast(u32x4_t, h);
+        rwv[set][i] = __builtin_bit_cast(u32x4_t, h);
       }
     }
   };
 
-  auto store_stage = [&](int buf) {
+  // Branch-free: dead items and pixels past the plane write the sink, so no
+  // store sits behind a branch (which would make the compiler wait for every
+  // outstanding load there, including the stage just prefetched).
+  auto store_stage = [&](int buf, int set) __attribute__((always_inline)) {
     unsigned char* base = smem + buf * L::STAGE;
 #pragma unroll
     for (int i = 0; i < L::NI; ++i) {
-      if (!in_live[i]) continue;
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         half8_t v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, rin[i][e])[k4];
-        if (in_lds[i][k4] >= 0) *reinterpret_cast<half8_t*>(base + in_lds[i][k4]) = v;
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, rin[set][i][e])[k4];
+        const bool live = in_live[i] && in_lds[i][k4] >= 0;
+        unsigned char* dst = live ? base + in_lds[i][k4] : smem + L::SINK;
+        *reinterpret_cast<half8_t*>(dst) = v;
       }
     }
 #pragma unroll
     for (int i = 0; i < L::NW; ++i) {
-      const u32x4_t v = w_ok[i] ? rwv[i] : u32x4_t{0, 0, 0, 0};
-      if (w_live[i]) *reinterpret_cast<u32x4_t*>(base + w_lds[i]) = v;
+      const u32x4_t v = w_ok[i] ? rwv[set][i] : u32x4_t{0, 0, 0, 0};
+      unsigned char* dst = w_live[i] ? base + w_lds[i] : smem + L::SINK;
+      *reinterpret_cast<u32x4_t*>(dst) = v;
     }
   };
 
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int pcol = lane & 15;
   const int oct = 2 * wave + grp;    // octet of the stage's 64 channels
 
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf) __attribute__((always_inline)) {
     const unsigned char* in = smem + buf * L::STAGE;
     // B: this lane's 8 channels x 9 taps (144 contiguous bytes of output channel lane % 32)
     const unsigned char* wb =
@@ -226,15 +234,13 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 #pragma unroll
     for (int v = 0; v < 9; ++v) raw[v] = *reinterpret_cast<const u32x4_t*>(wb + 16 * v);
     u32x4_t bf[9];
-    {
-      const _Float16* h = reinterpret_cast<const _Float16*>(raw);
 #pragma unroll
-      for (int t = 0; t < 9; ++t) {
-        half8_t v;
+    for (int t = 0; t < 9; ++t) {
+      half8_t v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = h[e * 9 + t];
-        bf[t] = __builtin_bit_cast(u32x4_t, v);
-      }
+      for (int e = 0; e < 8; ++e)  // element e*9+t of the 72 halves (compile-time index)
+        v[e] = __builtin_bit_cast(half8_t, raw[(e * 9 + t) / 8])[(e * 9 + t) % 8];
+      bf[t] = __builtin_bit_cast(u32x4_t, v);
     }
     // A: the row pair starting at input row t feeds output row pair (t - kh) / 2 at tap row kh
 #pragma unroll
@@ -261,61 +267,114 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     *reinterpret_cast<u32x4_t*>(smem + st * L::STAGE + off * 16) = u32x4_t{0, 0, 0, 0};
   }
   __syncthreads();
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < nstages; ++s) {
-    const bool more = s + 1 < nstages;
-    load_stage(more ? s + 1 : s);  // the last iteration re-reads harmlessly
-    compute(s & 1);
-    if (more) store_stage((s + 1) & 1);
+  // Prefetch distance 2: loads for stage s+2 are issued while stage s multiplies
+  // and reach LDS one step later, after stage s+1 has multiplied.  Register set
+  // and LDS buffer follow the stage's parity, fixed at compile time in a loop
+  // unrolled by two, and every load is unconditional (clamped stage index), so
+  // the wait before a store counts exactly the loads issued since.
+  auto step = [&](int s, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    load_stage(min(s + 2, nstages - 1), P);  // set P: stage s was stored last step
+    compute(P);                              // buffer P holds stage s
+    store_stage(P ^ 1, P ^ 1);               // stage s+1 (set P^1) into buffer P^1
     __syncthreads();
-  }
-
-  // ---- the four waves' partial sums, added in wave order per row pair ----
-  floatx16_t* red = reinterpret_cast<floatx16_t*>(smem);  // [wave][NP][64 lanes]
-#pragma unroll
-  for (int q = 0; q < NP; ++q) red[(wave * NP + q) * 64 + lane] = acc[q];
+  };
+  load_stage(0, 0);
+  load_stage(min(1, nstages - 1), 1);
+  store_stage(0, 0);
   __syncthreads();
+  int s = 0;
+  for (; s + 1 < nstages; s += 2) {
+    step(s, std::integral_constant<int, 0>{});
+    step(s + 1, std::integral_constant<int, 1>{});
+  }
+  if (s < nstages) step(s, std::integral_constant<int, 0>{});
 
-  const _Float16* bias = static_cast<const _Float16*>(a.bias);
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
-  const int col_l = co0 + (lane & 31);
-  const int co = g * a.cog + col_l;
-  const long long hw_out = (long long)a.ho * a.wo;
-  const long long ybase = ((long long)n * a.c_out + co) * hw_out;
-  for (int q = wave; q < NP; q += 4) {
-    floatx16_t v = red[q * 64 + lane];
+  // ---- each wave's partial sums go to its own [channel][pixel] LDS area; the
+  // epilogue adds the four in wave order, ((w0 + w1) + w2) + w3, and runs in
+  // memory order, 4 contiguous outputs per item (a fragment spans 32 output
+  // planes, so storing from the fragment layout would scatter). ----
+  const int howo = a.ho * a.wo;
+  const int area = 32 * howo;  // floats per wave area
+  float* part = reinterpret_cast<float*>(smem);
+  float* bsm = reinterpret_cast<float*>(smem + L::SINK) - 32;  // bias of the 32 channels
+  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const floatx16_t o = red[(w * NP + q) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = v[i] + o[i];
-    }
-    if (col_l >= a.cog) continue;
-    // Residuals are read for the whole tile before any store: y may alias the
-    // residual exactly, and each element is read and written by this lane only,
-    // so hoisting the reads keeps the result and lets them overlap.
-    long long oidx[16];
-    bool ok[16];
-    float rv[16];
+  for (int q = 0; q < NP; ++q)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int p = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);  // pixel of the row pair
       const int oh = 2 * q + p / 16, ow = p % 16;
-      ok[i] = oh < a.ho && ow < a.wo;
-      oidx[i] = ybase + (long long)(ok[i] ? oh : 0) * a.wo + (ok[i] ? ow : 0);
-      rv[i] = (res && ok[i]) ? (float)res[oidx[i]] : 0.f;
+      if (oh < a.ho && ow < a.wo)
+        part[wave * area + (lane & 31) * howo + oh * a.wo + ow] = acc[q][i];
     }
-    const float bv = bias ? (float)bias[co] : 0.f;
+  if (tid < 32) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
+  __syncthreads();
+
+  const _Float16* res = static_cast<const _Float16*>(a.res);
+  _Float16* y = static_cast<_Float16*>(a.y);
+  const int cvalid = min(32, a.cog - co0);
+  const int total = cvalid * howo;
+  const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
+  constexpr int MAXQ = (32 * 14 * 14 / 4 + 255) / 256;  // 4-output items per thread at most
+  const bool vec = a.ovec;  // howo % 4 == 0 and y / residual 8-byte aligned (uniform)
+  if (vec) {
+    const int nq = total / 4;
+    float v[MAXQ * 4];
+    if (res) {  // uniform; clamped items keep every load unconditional
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (!ok[i]) continue;
-      float v2 = v[i];
-      if (bias) v2 = v2 + bv;
-      if (res) v2 = v2 + rv[i];
-      y[oidx[i]] = (_Float16)apply_act(v2, a.act, a.alpha, a.beta);
+      for (int k = 0; k < MAXQ; ++k) {
+        const int it = min(tid + 256 * k, nq - 1);
+        const u32x2_t r = *reinterpret_cast<const u32x2_t*>(res + obase + 4 * it);
+        const half4_t h = __builtin_bit_cast(half4_t, r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * k + e] = (float)h[e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+      const int it = min(tid + 256 * k, nq - 1);
+      const float bv = bsm[(4 * it) / howo];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * it + e;
+        float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
+        if (bias) s = s + bv;
+        if (res) s = s + v[4 * k + e];
+        v[4 * k + e] = s;
+      }
+    }
+    act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+    for (int k = 0; k < MAXQ; ++k) {
+      const int it = tid + 256 * k;
+      if (it < nq) {
+        half4_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[4 * k + e];
+        *reinterpret_cast<u32x2_t*>(y + obase + 4 * it) = __builtin_bit_cast(u32x2_t, h);
+      }
+    }
+  } else {
+    constexpr int EPT = (32 * 14 * 14 + 255) / 256;
+    float v[EPT];
+    if (res) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) v[k] = (float)res[obase + min(tid + 256 * k, total - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int idx = min(tid + 256 * k, total - 1);
+      float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
+      if (bias) s = s + bsm[idx / howo];
+      if (res) s = s + v[k];
+      v[k] = s;
+    }
+    act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int idx = tid + 256 * k;
+      if (idx < total) y[obase + idx] = (_Float16)v[k];
     }
   }
 }
