@@ -17,6 +17,7 @@ for calibrating the HBM byte counters).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -104,39 +105,70 @@ def time_layer(cf, torch, layer, steps, warmup):
     scratch = torch.empty(max(whole // 4, 4), dtype=torch.float32, device="cuda") if whole else None
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    fn = cf.conv_transpose_forward if layer.transpose else cf.conv_forward
+    fn = cf.lib().conv_transpose_forward if layer.transpose else cf.lib().conv_forward
+    pref = ctypes.byref(p)
+    dt = 1 if layer.dtype == "f16" else 0
+    sp = None if scratch is None else scratch.data_ptr()
+    args = [[None if t is None else t.data_ptr() for t in st] for st in sets]
 
     def call(i):
-        x, w, b, r, y = sets[i % nsets]
-        fn(p, layer.dtype, x, w, b, r, y, scratch, whole, sh)
+        x, w, b, r, y = args[i % nsets]
+        st = fn(pref, dt, x, w, b, r, y, sp, whole, sh)
+        if st:
+            raise cf.ConvError(st, "conv_forward")
 
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
+    # Host submission (ctypes + validation + launch) is timed on its own; for
+    # the device timing a GPU-side delay first holds the stream while all K
+    # calls are enqueued, so the events measure the kernels back to back, not
+    # the host's launch rate.
     t0 = time.perf_counter()
-    ev[0].record(stream)
     for i in range(steps):
         call(i)
-        ev[i + 1].record(stream)
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(sleep_cycles(torch, host_us * steps * 1.5 + 2000.0))
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e-3  # s
-    total = ev[0].elapsed_time(ev[steps]) * 1e-3
+    total = ev0.elapsed_time(ev1) * 1e-3  # s
     del sets
     torch.cuda.empty_cache()
     bound, t_roof = roof(layer, macs, nbytes)
-    avg = float(per.mean())
-    med = float(np.median(per))
+    avg = total / steps
     return {
         "name": layer.name, "variant": variant, "dtype": layer.dtype,
-        "rotating_sets": nsets, "us_avg": avg * 1e6, "us_median": med * 1e6,
-        "us_total_per_step": total / steps * 1e6, "wall_s": wall,
+        "rotating_sets": nsets, "us_avg": avg * 1e6, "host_us_per_call": host_us,
+        "wall_s": wall,
         "tflops": 2 * macs / avg / 1e12, "gbs": nbytes / avg / 1e9,
         "macs": macs, "alg_bytes": nbytes, "bound": bound,
         "roof_us": t_roof * 1e6, "roof_frac": t_roof / avg, "total_s": total,
     }
+
+
+_SLEEP_RATE = None
+
+
+def sleep_cycles(torch, us):
+    """Argument of torch.cuda._sleep that holds the stream for about `us`."""
+    global _SLEEP_RATE
+    if _SLEEP_RATE is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_RATE = 2_000_000 / max(a.elapsed_time(b) * 1e3, 1.0)  # cycles per us
+    return int(_SLEEP_RATE * us)
 
 
 def cpu_baseline(layer, budget_s=10.0):

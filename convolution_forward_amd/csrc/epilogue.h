@@ -68,6 +68,17 @@ __device__ __forceinline__ void act_array(float (&v)[N], int act, float alpha, f
   }
 }
 
+// Workgroups are handed to the 8 XCDs round robin (workgroup b runs on XCD b % 8),
+// and each XCD has its own L2.  This maps the launch index to a logical index such
+// that every XCD receives one contiguous range of logical indices: tiles that
+// share an operand (consecutive logical indices) then share an L2 instead of
+// fetching that operand once per XCD.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_logical(int bid, int total) {
+  const int x = bid & 7, q = total >> 3, r = total & 7;
+  const int first = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return first + (bid >> 3);
+}
+
 // One output element: v is the float32 sum; idx the flat NCHW output index.
 template <typename T>
 __device__ __forceinline__ T epilogue_one(float v, const T* bias, const T* res, int co,

@@ -64,9 +64,9 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // block -> (co tile, row tile, image, group); co tile varies fastest so that
-  // neighbouring workgroups (spread over the XCDs) share an input image.
-  int bid = blockIdx.x;
+  // logical tile -> (co tile, row tile, image, group); co tile varies fastest, so
+  // the co tiles of one input tile run on one XCD and share its L2.
+  int bid = xcd_logical(blockIdx.x, gridDim.x);
   const int ct = bid % a.n_ct;
   bid /= a.n_ct;
   const int rt = bid % a.n_rt;

@@ -89,13 +89,17 @@ template <int R>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef RsLayout<R> L;
   constexpr int NP = L::NP;
+  // epilogue areas (4 waves x 32 channels x (R * 14 + 1) floats) and the bias
+  // slots below the sink reuse the two stage buffers
+  static_assert(4 * 32 * (R * 14 + 1) * 4 + 32 * 4 <= L::SINK, "epilogue does not fit");
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  int bid = blockIdx.x;
+  // logical tile: co tile fastest, so an image's co tiles run on one XCD
+  int bid = xcd_logical(blockIdx.x, gridDim.x);
   const int ct = bid % a.n_ct;
   bid /= a.n_ct;
   const int n = bid % a.n;
@@ -295,7 +299,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // memory order, 4 contiguous outputs per item (a fragment spans 32 output
   // planes, so storing from the fragment layout would scatter). ----
   const int howo = a.ho * a.wo;
-  const int area = 32 * howo;  // floats per wave area
+  const int pitch = howo + 1;   // odd channel pitch: a fragment's 32 channels hit distinct banks
+  const int area = 32 * pitch;  // floats per wave area
   float* part = reinterpret_cast<float*>(smem);
   float* bsm = reinterpret_cast<float*>(smem + L::SINK) - 32;  // bias of the 32 channels
   const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       const int p = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);  // pixel of the row pair
       const int oh = 2 * q + p / 16, ow = p % 16;
       if (oh < a.ho && ow < a.wo)
-        part[wave * area + (lane & 31) * howo + oh * a.wo + ow] = acc[q][i];
+        part[wave * area + (lane & 31) * pitch + oh * a.wo + ow] = acc[q][i];
     }
   if (tid < 32) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
   __syncthreads();
@@ -334,10 +339,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 #pragma unroll
     for (int k = 0; k < MAXQ; ++k) {
       const int it = min(tid + 256 * k, nq - 1);
-      const float bv = bsm[(4 * it) / howo];
+      const int c = (4 * it) / howo;  // 4 outputs never straddle planes (howo % 4 == 0)
+      const float bv = bsm[c];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int idx = 4 * it + e;
+        const int idx = 4 * it + e + c;  // channel c's area starts c floats later
         float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
         if (bias) s = s + bv;
         if (res) s = s + v[4 * k + e];
@@ -364,9 +370,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const int idx = min(tid + 256 * k, total - 1);
+      const int o = min(tid + 256 * k, total - 1);
+      const int c = o / howo;
+      const int idx = o + c;
       float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
-      if (bias) s = s + bsm[idx / howo];
+      if (bias) s = s + bsm[c];
       if (res) s = s + v[k];
       v[k] = s;
     }
