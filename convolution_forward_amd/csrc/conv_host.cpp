@@ -138,10 +138,34 @@ struct Plan {
   uint64_t scratch_whole;
   // depthwise tiling
   int toh, tow, tih, tiw, tiles_w, tiles;
-  int dw_planes;  // > 0: whole-plane register-blocked path with this many planes per workgroup
+  int dw_planes;  // > 0: whole-plane path with this many planes per group
+  int dw_bh;      // whole-plane path: outputs per thread along a column
+  int dw_wave;    // whole-plane path: one wave per plane
+  int dw_lm;      // one-wave path: LDS column of input column 0
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// LDS floats of the whole-plane depthwise kernel: P staged planes, output tile
+// (16-byte aligned), weights, double-buffered bias, one sink float.
+int64_t dw_lds_floats(int64_t P, int64_t tpp, int64_t mult, int64_t howo, int64_t k) {
+  const int64_t out0 = (P * tpp + 3) / 4 * 4;
+  return out0 + P * mult * howo + P * mult * k * k + 2 * P * mult + 1;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
 
 bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 
@@ -153,25 +177,60 @@ bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 bool plan_depthwise(const Geo& g, Plan* pl) {
   pl->dw_planes = 0;
   const bool compiled = g.dh == 1 && g.dw == 1 && g.sh == g.sw && g.kh == g.kw &&
-                        ((g.kh == 3 && g.sh <= 2) || (g.kh == 5 && g.sh <= 2) ||
-                         (g.kh == 7 && g.sh == 1));
+                        ((g.sh == 1 && (g.kh == 3 || g.kh == 5 || g.kh == 7)) ||
+                         (g.sh == 2 && (g.kh == 3 || g.kh == 5))) &&
+                        (g.h * g.w) % 4 == 0;
   if (compiled) {
-    const int64_t tih = (g.ho - 1) * g.sh + g.kh;
-    const int64_t tiw = (g.wo - 1) * g.sw + g.kw + 1;  // one pad column in the row pitch
     const int64_t mult = g.co / g.ci;
-    const int64_t plane_bytes = (tih * tiw + mult * g.kh * g.kw) * 4;
-    if (plane_bytes <= 16 * 1024) {
-      const int64_t blocks = ceil_div(g.ho, 2) * ceil_div(g.wo, 2);
-      int64_t P = std::min<int64_t>(32 * 1024 / plane_bytes, std::max<int64_t>(1, 1024 / blocks));
-      P = std::max<int64_t>(1, std::min<int64_t>(P, g.n * g.ci));
+    const int64_t hw = g.h * g.w, howo = g.ho * g.wo;
+    // one wave per plane: small planes, at most 64 output columns per row block
+    {
+      const int64_t bh = g.sh == 1 ? 14 : 4;
+      const int64_t nrb = ceil_div(g.ho, bh);
+      if (hw <= 1024 && mult * howo <= 1024 && mult <= 64 && g.wo <= 64) {
+        const int64_t lm = (g.pl + 3) / 4 * 4;
+        int64_t tiw = std::max<int64_t>(lm + g.w, lm - g.pl + (g.wo - 1) * g.sw + g.kw);
+        tiw = (tiw + 3) / 4 * 4;
+        // two row blocks 32 banks apart when the pitch allows it
+        for (int64_t t = tiw; t < tiw + 64; t += 4)
+          if ((bh * g.sh * t) % 64 == 32) { tiw = t; break; }
+        const int64_t tih = std::max<int64_t>(g.h + g.pt, (nrb * bh - 1) * g.sh + g.kh);
+        pl->dw_wave = 1;
+        pl->dw_planes = 1;
+        pl->dw_bh = (int)bh;
+        pl->dw_lm = (int)lm;
+        pl->tih = (int)tih;
+        pl->tiw = (int)tiw;
+        pl->toh = (int)g.ho;
+        pl->tow = (int)g.wo;
+        pl->tiles = 1;
+        pl->tiles_w = 1;
+        return true;
+      }
+    }
+    const int64_t bh = g.sh == 1 ? 4 : 2;
+    const int64_t nrb = ceil_div(g.ho, bh);
+    const int64_t tih = std::max<int64_t>(g.h + g.pt, (nrb * bh - 1) * g.sh + g.kh);
+    const int64_t tiw = std::max<int64_t>(g.w + g.pl, (g.wo - 1) * g.sw + g.kw);
+    // whole planes per group: every thread stages at most 4 items of 4 inputs,
+    // 2 weights and 1 bias, and finishes at most 4 items of 4 outputs; the
+    // group's LDS stays under 64 KiB
+    int64_t P = std::min<int64_t>({4096 / hw, 4096 / (mult * howo), 256 / mult,
+                                   512 / (mult * g.kh * g.kw), g.n * g.ci});
+    for (; P >= 1; --P) {
+      const int64_t lds = dw_lds_floats(P, tih * tiw, mult, howo, g.kh) * 4;
+      if (lds <= 64 * 1024) break;
+    }
+    if (P >= 1) {
       pl->dw_planes = (int)P;
+      pl->dw_bh = (int)bh;
       pl->tih = (int)tih;
       pl->tiw = (int)tiw;
       pl->toh = (int)g.ho;
       pl->tow = (int)g.wo;
       pl->tiles = 1;
       pl->tiles_w = 1;
-      return ceil_div(g.n * g.ci, P) <= 2147483647LL;
+      return true;
     }
   }
   int64_t toh = std::min<int64_t>(g.ho, 64), tow = std::min<int64_t>(g.wo, 64);
@@ -425,9 +484,60 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.toh = pl.toh; a.tow = pl.tow; a.tih = pl.tih; a.tiw = pl.tiw;
       a.tiles_w = pl.tiles_w; a.tiles = pl.tiles;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      a.planes = pl.dw_planes;
-      a.xvec = reinterpret_cast<uintptr_t>(xc) % (dt == F16 ? 8 : 16) == 0 && (g.h * g.w) % 4 == 0;
-      e = pl.dw_planes > 0 ? launch_depthwise_plane(dt, a, s) : launch_depthwise(dt, a, s);
+      const int vb = dt == F16 ? 8 : 16;
+      // the whole-plane kernel reads x with vector loads only; a misaligned x
+      // runs the tiled kernel (same sums in the same order)
+      if (pl.dw_wave && reinterpret_cast<uintptr_t>(xc) % vb == 0) {
+        const int64_t mult = g.co / g.ci, howo = g.ho * g.wo;
+        a.planes = 1;
+        a.bh = pl.dw_bh;
+        a.nrb = (int)ceil_div(g.ho, pl.dw_bh);
+        a.lm = pl.dw_lm;
+        a.tpp = pl.tih * pl.tiw;
+        a.oofs = a.tpp;  // tiw % 4 == 0
+        a.bofs = (int)(a.oofs + (mult * howo + 3) / 4 * 4);
+        a.sofs = (int)(a.bofs + (mult + 3) / 4 * 4);
+        a.xvec = 1;
+        a.ovec = reinterpret_cast<uintptr_t>(yc) % vb == 0 &&
+                 (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % vb == 0) && howo % 4 == 0;
+        a.mg_w = make_magic((unsigned)g.w);
+        a.mg_wo = make_magic((unsigned)g.wo);
+        a.mg_howo = make_magic((unsigned)howo);
+        const size_t lds = (size_t)(a.sofs + 4) * 4;
+        const int64_t planes = cn * g.ci;
+        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16, (160 * 1024) / (int64_t)lds));
+        const int64_t rounds = ceil_div(planes, (int64_t)device_cus() * per_cu);
+        e = launch_depthwise_wave(dt, a, (int)ceil_div(planes, rounds), lds, s);
+      } else if (pl.dw_planes > 0 && !pl.dw_wave && reinterpret_cast<uintptr_t>(xc) % vb == 0) {
+        const int64_t P = pl.dw_planes, mult = g.co / g.ci, howo = g.ho * g.wo;
+        a.planes = (int)P;
+        a.ngroups = (int)ceil_div(cn * g.ci, P);
+        a.bh = pl.dw_bh;
+        a.nrb = (int)ceil_div(g.ho, pl.dw_bh);
+        a.tpp = pl.tih * pl.tiw;
+        a.oofs = (int)((P * a.tpp + 3) / 4 * 4);
+        a.wofs = (int)(a.oofs + P * mult * howo);
+        a.bofs = (int)(a.wofs + P * mult * g.kh * g.kw);
+        a.sofs = (int)(a.bofs + 2 * P * mult);
+        a.xvec = 1;
+        a.ovec = reinterpret_cast<uintptr_t>(yc) % vb == 0 &&
+                 (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % vb == 0) && howo % 4 == 0;
+        a.mg_hw = make_magic((unsigned)(g.h * g.w));
+        a.mg_w = make_magic((unsigned)g.w);
+        a.mg_pu = make_magic((unsigned)(a.nrb * g.wo));
+        a.mg_wo = make_magic((unsigned)g.wo);
+        a.mg_howo = make_magic((unsigned)howo);
+        const size_t lds = (size_t)dw_lds_floats(P, a.tpp, mult, howo, g.kh) * 4;
+        // persistent grid: as many workgroups as fit the chip, each taking an
+        // equal number of groups
+        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / (int64_t)lds));
+        const int64_t slots = (int64_t)device_cus() * per_cu;
+        const int64_t rounds = ceil_div(a.ngroups, slots);
+        const int grid = (int)ceil_div(a.ngroups, rounds);
+        e = launch_depthwise_plane(dt, a, grid, lds, s);
+      } else {
+        e = launch_depthwise(dt, a, s);
+      }
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
       HaloArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -593,8 +703,11 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                pl.splits);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
-      if (pl.dw_planes > 0)
-        snprintf(tmp, sizeof tmp, "depthwise_direct.%s.planes%d.b2x2", dn, pl.dw_planes);
+      if (pl.dw_wave)
+        snprintf(tmp, sizeof tmp, "depthwise_direct.%s.wave.col%d", dn, pl.dw_bh);
+      else if (pl.dw_planes > 0)
+        snprintf(tmp, sizeof tmp, "depthwise_direct.%s.planes%d.col%d", dn, pl.dw_planes,
+                 pl.dw_bh);
       else
         snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
       break;

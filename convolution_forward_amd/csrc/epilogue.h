@@ -68,6 +68,11 @@ __device__ __forceinline__ void act_array(float (&v)[N], int act, float alpha, f
   }
 }
 
+// floor(n / d) for a launch-constant divisor (see make_magic); n < 2^31.
+__device__ __forceinline__ unsigned mdiv(unsigned n, Magic g) {
+  return (__umulhi(g.m, n) + n) >> g.s;
+}
+
 // Workgroups are handed to the 8 XCDs round robin (workgroup b runs on XCD b % 8),
 // and each XCD has its own L2.  This maps the launch index to a logical index such
 // that every XCD receives one contiguous range of logical indices: tiles that

@@ -66,6 +66,24 @@ struct HaloArgs {
   float alpha, beta;
 };
 
+// Division by a launch constant d >= 1 as multiply-high, add and shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1):
+// floor(n / d) = (umulhi(m, n) + n) >> l, exact for every 0 <= n < 2^31.
+struct Magic {
+  unsigned m;
+  int s;
+};
+
+inline Magic make_magic(unsigned d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  Magic g;
+  g.m = (unsigned)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  g.s = l;
+  return g;
+}
+
 struct DepthwiseArgs {
   const void* x;
   const void* wt;      // weights
@@ -79,8 +97,17 @@ struct DepthwiseArgs {
   int toh, tow;          // output tile
   int tih, tiw;          // staged input tile (with halo)
   int tiles_w, tiles;    // tiles per plane along w, total per plane
-  int planes;            // whole-plane path: input planes per workgroup
-  int xvec;              // whole-plane path: planes may be read 16 (f32) / 8 (f16) bytes at a time
+  // whole-plane path
+  int planes;            // input planes per group (P)
+  int ngroups;           // groups of P planes in this chunk
+  int bh;                // outputs per thread (one column, BH rows)
+  int nrb;               // row blocks per plane: ceil(ho / bh)
+  int tpp;               // LDS floats per staged plane (tih * tiw)
+  int oofs, wofs, bofs, sofs;  // LDS float offsets: output tile, weights, bias, sink
+  int lm;                // one-wave path: LDS column of input column 0 (a multiple of 4)
+  int xvec;              // x may be read 16 (f32) / 8 (f16) bytes at a time, h * w % 4 == 0
+  int ovec;              // y and residual 16 / 8-byte aligned and ho * wo % 4 == 0
+  Magic mg_hw, mg_w, mg_pu, mg_wo, mg_howo;  // h*w, w, nrb*wo, wo, ho*wo
   int act;
   float alpha, beta;
 };
@@ -129,7 +156,10 @@ hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
-hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
+hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
+                                  hipStream_t s);
+hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
+                                 hipStream_t s);
 hipError_t launch_reduce(Dtype dt, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_col2im(Dtype dt, const Col2imArgs& a, hipStream_t s);
 

@@ -71,172 +71,501 @@ hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Depthwise, whole-plane fast path (dilation 1, kernel and stride fixed at
-// compile time): a workgroup stages P consecutive input planes (contiguous in
-// NCHW, read with 16-byte loads) into zero-padded LDS tiles together with their
-// weights, then each thread computes 2x2 output blocks from an input patch held
-// in registers, so every staged value feeds several FMAs.  Each output is still
-// one float32 FMA chain over the window in (kh, kw) row-major order.
+// Depthwise, whole-plane path (dilation 1, kernel and stride fixed at compile
+// time).  A persistent workgroup walks groups of P consecutive input planes
+// (n, ci): P planes are one contiguous run of x, and their P * mult output
+// planes one contiguous run of y.
+//  * The next group's input is loaded into registers (16-byte loads in memory
+//    order) while the current group is computed, so HBM reads overlap the
+//    arithmetic of the previous group.
+//  * The staged planes sit in zero-bordered LDS tiles; the border is written
+//    once and never overwritten.
+//  * A thread computes BH outputs of one output column: consecutive lanes take
+//    consecutive columns, so every LDS read of the window is conflict free
+//    (stride 1) or 2-way (stride 2).  Each output is one float32 FMA chain over
+//    the window in (kh, kw) row-major order.
+//  * Raw sums go to an LDS output tile in y's memory order; the epilogue (bias,
+//    residual, activation) then runs on 4 contiguous outputs per item with
+//    vector loads and stores.
+// Index arithmetic divides only by launch constants, as multiply-high + shift.
 // ---------------------------------------------------------------------------
-template <typename T, int KH, int KW, int SH, int SW>
-__global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArgs a) {
-  constexpr int BH = 2, BW = 2;
-  constexpr int PH = (BH - 1) * SH + KH, PW = (BW - 1) * SW + KW;  // input patch
-  extern __shared__ float smem_dw[];
-  const int P = a.planes;                 // input planes per workgroup
-  const int tsz = a.tih * a.tiw;          // floats per plane tile (tiw = row pitch)
-  float* tile = smem_dw;
-  float* wl = smem_dw + P * tsz;          // P * mult * KH * KW weights
-  const int plane0 = blockIdx.x * P;
-  const int nplanes = a.n * a.c_in;
-  const int np = min(P, nplanes - plane0);
-  const int hw = a.h * a.w;
-  const T* __restrict__ xp = static_cast<const T*>(a.x) + (long long)plane0 * hw;
+constexpr int DW_NI = 4;  // 4-element input items per thread and group (P * H * W <= 4096)
+constexpr int DW_NE = 4;  // 4-output epilogue items per thread and group
+constexpr int DW_NW = 2;  // weights per thread and group (P * mult * K * K <= 512)
 
-  for (int i = threadIdx.x; i < P * tsz; i += 256) tile[i] = 0.0f;
-  const int nw = np * a.mult * KH * KW;
-  __syncthreads();
-  for (int i = threadIdx.x; i < nw; i += 256) {
-    // planes of one workgroup may wrap from the last channel of an image to the
-    // first of the next: index the weights by each plane's channel
-    const int pl = i / (a.mult * KH * KW), r = i - pl * (a.mult * KH * KW);
-    const int ci = (plane0 + pl) % a.c_in;
-    wl[i] = to_f32(static_cast<const T*>(a.wt)[(long long)ci * a.mult * KH * KW + r]);
-  }
-  // planes: 4 consecutive pixels per item
-  const int g4 = (hw + 3) / 4;
-  for (int q = threadIdx.x; q < np * g4; q += 256) {
-    const int pl = q / g4, f0 = 4 * (q - pl * g4);
-    float v[4];
-    if (a.xvec && f0 + 4 <= hw) {
-      if constexpr (sizeof(T) == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(xp + (long long)pl * hw + f0);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-      } else {
-        const uint2 t = *reinterpret_cast<const uint2*>(xp + (long long)pl * hw + f0);
-        const _Float16* h = reinterpret_cast<const _Float16*>(&t);
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) v[k4] = (float)h[k4];
-      }
-    } else {
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-        v[k4] = f0 + k4 < hw ? to_f32(xp[(long long)pl * hw + f0 + k4]) : 0.0f;
-    }
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int f = f0 + k4;
-      if (f >= hw) break;
-      const int ih = f / a.w, iw = f - (f / a.w) * a.w;
-      const int tr = ih + a.pt, tc = iw + a.pl;
-      if (tr < a.tih && tc < a.tiw - 1) tile[pl * tsz + tr * a.tiw + tc] = v[k4];
-    }
-  }
-  __syncthreads();
+template <typename T>
+struct DwVec;  // 4 elements of the operand type
+template <>
+struct DwVec<float> {
+  typedef float4 type;
+};
+template <>
+struct DwVec<_Float16> {
+  typedef uint2 type;
+};
 
-  const T* __restrict__ bias = static_cast<const T*>(a.bias);
-  const T* res = static_cast<const T*>(a.res);
-  T* y = static_cast<T*>(a.y);
-  const int nbh = (a.ho + BH - 1) / BH, nbw = (a.wo + BW - 1) / BW;
-  const int per_plane = nbh * nbw;
-  for (int b = threadIdx.x; b < np * per_plane; b += 256) {
-    const int pl = b / per_plane, r = b - pl * per_plane;
-    const int bh = r / nbw, bw = r - (r / nbw) * nbw;
-    const int oh0 = bh * BH, ow0 = bw * BW;
-    const float* src = tile + pl * tsz + (oh0 * SH) * a.tiw + ow0 * SW;
-    float patch[PH][PW];
+template <typename T>
+__device__ __forceinline__ void dw_unpack(const typename DwVec<T>::type& v, float (&f)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  } else {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 h = __builtin_bit_cast(h4, v);
 #pragma unroll
-    for (int i = 0; i < PH; ++i)
-#pragma unroll
-      for (int j = 0; j < PW; ++j) {
-        // the last block of a row/column may reach past the tile: clamp the read
-        // (those outputs are not stored)
-        const int rr = min(oh0 * SH + i, a.tih - 1) - oh0 * SH;
-        const int cc = min(ow0 * SW + j, a.tiw - 1) - ow0 * SW;
-        patch[i][j] = src[rr * a.tiw + cc];
-      }
-    const int plane = plane0 + pl;
-    const int n = plane / a.c_in, ci = plane - n * a.c_in;
-    for (int jm = 0; jm < a.mult; ++jm) {
-      const int co = ci * a.mult + jm;
-      const float* wv = wl + (pl * a.mult + jm) * KH * KW;
-      float acc[BH][BW];
-#pragma unroll
-      for (int i = 0; i < BH; ++i)
-#pragma unroll
-        for (int j = 0; j < BW; ++j) acc[i][j] = 0.0f;
-#pragma unroll
-      for (int kh = 0; kh < KH; ++kh)
-#pragma unroll
-        for (int kw = 0; kw < KW; ++kw) {
-          const float wk = wv[kh * KW + kw];
-#pragma unroll
-          for (int i = 0; i < BH; ++i)
-#pragma unroll
-            for (int j = 0; j < BW; ++j)
-              acc[i][j] = fmaf(patch[i * SH + kh][j * SW + kw], wk, acc[i][j]);
-        }
-      // residuals first (y may alias the residual exactly), then the stores
-      const long long obase = ((long long)n * a.c_out + co) * a.ho * a.wo;
-      long long oidx[BH][BW];
-      bool ok[BH][BW];
-      float rv[BH][BW];
-#pragma unroll
-      for (int i = 0; i < BH; ++i)
-#pragma unroll
-        for (int j = 0; j < BW; ++j) {
-          ok[i][j] = oh0 + i < a.ho && ow0 + j < a.wo;
-          oidx[i][j] = obase + (ok[i][j] ? (long long)(oh0 + i) * a.wo + ow0 + j : 0);
-          rv[i][j] = 0.0f;
-        }
-      if (res) {  // uniform; clamped indices keep every load unconditional
-#pragma unroll
-        for (int i = 0; i < BH; ++i)
-#pragma unroll
-          for (int j = 0; j < BW; ++j) rv[i][j] = to_f32(res[oidx[i][j]]);
-      }
-      const float bv = bias ? to_f32(bias[co]) : 0.0f;
-      float v[BH * BW];
-#pragma unroll
-      for (int i = 0; i < BH; ++i)
-#pragma unroll
-        for (int j = 0; j < BW; ++j) {
-          float s = acc[i][j];
-          if (bias) s = s + bv;
-          if (res) s = s + rv[i][j];
-          v[i * BW + j] = s;
-        }
-      act_array(v, a.act, a.alpha, a.beta);
-#pragma unroll
-      for (int i = 0; i < BH; ++i)
-#pragma unroll
-        for (int j = 0; j < BW; ++j)
-          if (ok[i][j]) y[oidx[i][j]] = from_f32<T>(v[i * BW + j]);
-    }
+    for (int k = 0; k < 4; ++k) f[k] = (float)h[k];
   }
 }
 
 template <typename T>
-static hipError_t launch_dw_plane_t(const DepthwiseArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n * a.c_in + a.planes - 1) / a.planes));
-  const size_t lds = ((size_t)a.planes * a.tih * a.tiw + (size_t)a.planes * a.mult * a.kh * a.kw) *
-                     sizeof(float);
-#define DW_CASE(KH_, KW_, SH_, SW_)                                                        \
-  if (a.kh == KH_ && a.kw == KW_ && a.sh == SH_ && a.sw == SW_) {                          \
-    hipLaunchKernelGGL((depthwise_plane_kernel<T, KH_, KW_, SH_, SW_>), grid, dim3(256), lds, s, a); \
-    return hipGetLastError();                                                              \
+__device__ __forceinline__ typename DwVec<T>::type dw_pack(const float (&f)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    return float4{f[0], f[1], f[2], f[3]};
+  } else {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h[k] = (_Float16)f[k];
+    return __builtin_bit_cast(uint2, h);
   }
-  DW_CASE(3, 3, 1, 1)
-  DW_CASE(3, 3, 2, 2)
-  DW_CASE(5, 5, 1, 1)
-  DW_CASE(5, 5, 2, 2)
-  DW_CASE(7, 7, 1, 1)
+}
+
+template <typename T, int K, int S, int BH, bool RES>
+__global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArgs a) {
+  typedef typename DwVec<T>::type V;
+  constexpr int PR = (BH - 1) * S + K;  // input rows of one thread's window column
+  extern __shared__ float smem_dw[];
+  const int tid = threadIdx.x;
+  const int P = a.planes;
+  const int hw = a.h * a.w;
+  const int howo = a.ho * a.wo;
+  const int mult = a.mult;
+  const int nplanes = a.n * a.c_in;
+  float* tile = smem_dw;           // P planes x tpp floats
+  float* outt = smem_dw + a.oofs;  // P * mult * howo raw sums (16-byte aligned)
+  float* wl = smem_dw + a.wofs;    // P * mult * K * K weights
+  float* bl = smem_dw + a.bofs;    // 2 x P * mult bias (double buffered)
+  float* sink = smem_dw + a.sofs;  // target of dead LDS writes
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  const T* __restrict__ wt = static_cast<const T*>(a.wt);
+  const T* __restrict__ bias = static_cast<const T*>(a.bias);
+  const T* res = static_cast<const T*>(a.res);
+  T* y = static_cast<T*>(a.y);
+
+  // ---- prefetched per group: input items (4 consecutive elements of the
+  // group's contiguous run, one vector load each), weights and bias ----
+  float xin[DW_NI][4];
+  float wreg[DW_NW];
+  float breg = 0.0f;
+  const int mkk = mult * K * K;
+  auto load = [&](int grp) __attribute__((always_inline)) {
+    const int plane0 = grp * P;
+    const int np = min(P, nplanes - plane0);
+    const long long base = (long long)plane0 * hw;
+    const int lastv = np * hw - 4;  // hw % 4 == 0: the last full vector
+#pragma unroll
+    for (int i = 0; i < DW_NI; ++i) {
+      const int e = min(4 * (tid + 256 * i), lastv);
+      dw_unpack<T>(*reinterpret_cast<const V*>(x + base + e), xin[i]);
+    }
+    // weights of the group's planes, indexed by each plane's channel (a group
+    // may wrap from the last channel of one image to the first of the next)
+#pragma unroll
+    for (int i = 0; i < DW_NW; ++i) {
+      const int q = min(tid + 256 * i, np * mkk - 1);
+      const int pl = q / mkk, r = q - pl * mkk;
+      wreg[i] = to_f32(wt[(long long)((plane0 + pl) % a.c_in) * mkk + r]);
+    }
+    if (bias) {
+      const int q = min(tid, np * mult - 1);
+      const int pl = q / mult, jm = q - pl * mult;
+      breg = to_f32(bias[((plane0 + pl) % a.c_in) * mult + jm]);
+    }
+  };
+  auto stage = [&](int grp) __attribute__((always_inline)) {
+    const int cnt = min(P, nplanes - grp * P) * hw;
+#pragma unroll
+    for (int i = 0; i < DW_NI; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const unsigned e = 4 * (tid + 256 * i) + k;
+        const unsigned pl = mdiv(e, a.mg_hw);
+        const unsigned rem = e - pl * hw;
+        const unsigned ih = mdiv(rem, a.mg_w);
+        const unsigned iw = rem - ih * a.w;
+        float* dst = (int)e < cnt ? tile + pl * a.tpp + (ih + a.pt) * a.tiw + iw + a.pl : sink;
+        *dst = xin[i][k];
+      }
+  };
+
+  // zero every tile once: the border (padding) is never written again
+  for (int i = tid; i < P * a.tpp; i += 256) tile[i] = 0.0f;
+  int grp = blockIdx.x;
+  if (grp < a.ngroups) load(grp);
+  __syncthreads();
+
+  const int pu = a.nrb * a.wo;  // units (BH outputs of one column) per input plane
+  for (int it = 0; grp < a.ngroups; grp += gridDim.x, ++it) {
+    const int plane0 = grp * P;
+    const int np = min(P, nplanes - plane0);
+    stage(grp);
+#pragma unroll
+    for (int i = 0; i < DW_NW; ++i) {
+      const int q = tid + 256 * i;
+      *(q < np * mkk ? wl + q : sink) = wreg[i];
+    }
+    float* bcur = bl + (it & 1) * P * mult;
+    *(tid < np * mult ? bcur + tid : sink) = breg;
+    __syncthreads();
+    if (grp + (int)gridDim.x < a.ngroups) load(grp + gridDim.x);  // prefetch (uniform)
+
+    // ---- compute: unit = (plane, row block, output column) ----
+    for (int u = tid; u < np * pu; u += 256) {
+      const unsigned pl = mdiv(u, a.mg_pu);
+      const unsigned r = u - pl * pu;
+      const unsigned rb = mdiv(r, a.mg_wo);
+      const unsigned ow = r - rb * a.wo;
+      const float* src = tile + pl * a.tpp + (rb * BH * S) * a.tiw + ow * S;
+      float patch[PR][K];
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+#pragma unroll
+        for (int j = 0; j < K; ++j) patch[i][j] = src[i * a.tiw + j];
+      for (int jm = 0; jm < mult; ++jm) {
+        const float* wv = wl + (pl * mult + jm) * K * K;
+        float acc[BH];
+#pragma unroll
+        for (int i = 0; i < BH; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+          for (int kw = 0; kw < K; ++kw) {
+            const float wk = wv[kh * K + kw];
+#pragma unroll
+            for (int i = 0; i < BH; ++i) acc[i] = fmaf(patch[i * S + kh][kw], wk, acc[i]);
+          }
+        float* o = outt + (pl * mult + jm) * howo + ow;
+#pragma unroll
+        for (int i = 0; i < BH; ++i) {
+          const int oh = rb * BH + i;
+          float* dst = oh < a.ho ? o + oh * a.wo : sink;
+          *dst = acc[i];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- epilogue over the group's contiguous outputs ----
+    const int tot = np * mult * howo;
+    const long long obase = (long long)plane0 * mult * howo;
+    if (a.ovec) {  // howo % 4 == 0, y / residual 16 / 8-byte aligned
+      const int nq = tot / 4;
+      if constexpr (RES) {
+        // every residual read before any store (y may alias the residual)
+        float v[DW_NE * 4];
+#pragma unroll
+        for (int k = 0; k < DW_NE; ++k) {
+          float f[4];
+          dw_unpack<T>(*reinterpret_cast<const V*>(res + obase + 4 * min(tid + 256 * k, nq - 1)), f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * k + e] = f[e];
+        }
+#pragma unroll
+        for (int k = 0; k < DW_NE; ++k) {
+          const int q = min(tid + 256 * k, nq - 1);
+          const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
+          const float bv = bcur[mdiv(4 * q, a.mg_howo)];
+          const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * k + e] = (sv[e] + bv) + v[4 * k + e];
+        }
+        act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+        for (int k = 0; k < DW_NE; ++k) {
+          const int q = tid + 256 * k;
+          if (q < nq) {
+            const float f[4] = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+            *reinterpret_cast<V*>(y + obase + 4 * q) = dw_pack<T>(f);
+          }
+        }
+      } else {
+        for (int q = tid; q < nq; q += 256) {
+          const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
+          const float bv = bcur[mdiv(4 * q, a.mg_howo)];
+          float f[4] = {s4.x + bv, s4.y + bv, s4.z + bv, s4.w + bv};
+          act_array(f, a.act, a.alpha, a.beta);
+          *reinterpret_cast<V*>(y + obase + 4 * q) = dw_pack<T>(f);
+        }
+      }
+    } else {
+      if constexpr (RES) {
+        float v[DW_NE * 4];
+#pragma unroll
+        for (int k = 0; k < DW_NE * 4; ++k) v[k] = to_f32(res[obase + min(tid + 256 * k, tot - 1)]);
+#pragma unroll
+        for (int k = 0; k < DW_NE * 4; ++k) {
+          const int o = min(tid + 256 * k, tot - 1);
+          v[k] = (outt[o] + bcur[mdiv(o, a.mg_howo)]) + v[k];
+        }
+        act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+        for (int k = 0; k < DW_NE * 4; ++k) {
+          const int o = tid + 256 * k;
+          if (o < tot) y[obase + o] = from_f32<T>(v[k]);
+        }
+      } else {
+        for (int o = tid; o < tot; o += 256) {
+          float f[1] = {outt[o] + bcur[mdiv(o, a.mg_howo)]};
+          act_array(f, a.act, a.alpha, a.beta);
+          y[obase + o] = from_f32<T>(f[0]);
+        }
+      }
+    }
+    // the next group overwrites the tiles and weights only after every thread has
+    // passed the barrier after the compute; the bias is double buffered
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Depthwise, one wave per plane (planes of at most 1024 elements, at most 64
+// output columns per row block).  Workgroups are single wavefronts, so nothing
+// waits on other waves: each wave walks its own sequence of planes, prefetching
+// the next plane into registers while it computes the current one.
+//  * The plane sits in a zero-bordered LDS tile; input column 0 is placed at a
+//    16-byte aligned column so a 4-element item is one LDS vector write.
+//  * Lane (row block, output column) streams the PR input rows its BH outputs
+//    need, reading K values per row once; row r adds to output i with tap row
+//    kh = r - i * S.  Rows arrive in increasing order, so every output is still
+//    one float32 FMA chain in (kh, kw) row-major order.
+//  * The plane's weights are wave-uniform (scalar loads, no LDS).
+//  * Raw sums go to an LDS tile in y's memory order; the epilogue runs on 4
+//    contiguous outputs per item.
+// ---------------------------------------------------------------------------
+constexpr int DWW_NI = 4;  // 4-element input items per lane (H * W <= 1024)
+constexpr int DWW_NE = 4;  // 4-output epilogue items per lane (mult * Ho * Wo <= 1024)
+
+template <typename T, int K, int S, int BH, bool RES>
+__global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs a) {
+  typedef typename DwVec<T>::type V;
+  constexpr int PR = (BH - 1) * S + K;  // input rows of one lane's output column
+  extern __shared__ float smem_dw[];
+  const int lane = threadIdx.x;
+  const int hw = a.h * a.w;
+  const int howo = a.ho * a.wo;
+  const int mult = a.mult;
+  const int nplanes = a.n * a.c_in;
+  float* tile = smem_dw;           // tih x tiw; input column iw sits at column lm + iw
+  float* outt = smem_dw + a.oofs;  // mult * howo raw sums (16-byte aligned)
+  float* bl = smem_dw + a.bofs;    // mult bias values
+  float* sink = smem_dw + a.sofs;  // 4 floats (16-byte aligned) that dead writes hit
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  const T* __restrict__ wt = static_cast<const T*>(a.wt);
+  const T* __restrict__ bias = static_cast<const T*>(a.bias);
+  const T* res = static_cast<const T*>(a.res);
+  T* y = static_cast<T*>(a.y);
+
+  float xin[DWW_NI][4];
+  auto load = [&](int p) __attribute__((always_inline)) {
+    const long long base = (long long)p * hw;
+#pragma unroll
+    for (int i = 0; i < DWW_NI; ++i) {
+      const int e = min(4 * (lane + 64 * i), hw - 4);  // hw % 4 == 0
+      dw_unpack<T>(*reinterpret_cast<const V*>(x + base + e), xin[i]);
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+    if (a.w % 4 == 0) {  // uniform: an item never straddles two rows
+#pragma unroll
+      for (int i = 0; i < DWW_NI; ++i) {
+        const unsigned e = 4 * (lane + 64 * i);
+        const unsigned ih = mdiv(e, a.mg_w);
+        const unsigned iw = e - ih * a.w;
+        float* dst = (int)e < hw ? tile + (ih + a.pt) * a.tiw + a.lm + iw : sink;
+        *reinterpret_cast<float4*>(dst) = float4{xin[i][0], xin[i][1], xin[i][2], xin[i][3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DWW_NI; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const unsigned e = 4 * (lane + 64 * i) + k;
+          const unsigned ih = mdiv(e, a.mg_w);
+          const unsigned iw = e - ih * a.w;
+          float* dst = (int)e < hw ? tile + (ih + a.pt) * a.tiw + a.lm + iw : sink;
+          *dst = xin[i][k];
+        }
+    }
+  };
+
+  for (int i = lane; i < a.tpp; i += 64) tile[i] = 0.0f;  // border stays zero
+  int p = blockIdx.x;
+  if (p < nplanes) load(p);
+  __syncthreads();
+
+  const int units = a.nrb * a.wo;
+  for (; p < nplanes; p += gridDim.x) {
+    stage();
+    const int ci = p % a.c_in;
+    if (lane < mult) bl[lane] = bias ? to_f32(bias[ci * mult + lane]) : 0.0f;
+    __syncthreads();
+    if (p + (int)gridDim.x < nplanes) load(p + gridDim.x);  // prefetch (uniform)
+
+    for (int u = lane; u < units; u += 64) {
+      const unsigned rb = mdiv(u, a.mg_wo);
+      const unsigned ow = u - rb * a.wo;
+      const float* src = tile + (rb * BH * S) * a.tiw + ow * S + (a.lm - a.pl);
+      for (int jm = 0; jm < mult; ++jm) {
+        const T* wc = wt + (long long)(ci * mult + jm) * (K * K);  // wave-uniform
+        float wk[K * K];
+#pragma unroll
+        for (int j = 0; j < K * K; ++j) wk[j] = to_f32(wc[j]);
+        float acc[BH];
+#pragma unroll
+        for (int i = 0; i < BH; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < PR; ++r) {
+          float rv[K];
+#pragma unroll
+          for (int kw = 0; kw < K; ++kw) rv[kw] = src[r * a.tiw + kw];
+#pragma unroll
+          for (int i = 0; i < BH; ++i) {
+            const int kh = r - i * S;
+            if (kh < 0 || kh >= K) continue;  // compile time
+#pragma unroll
+            for (int kw = 0; kw < K; ++kw) acc[i] = fmaf(rv[kw], wk[kh * K + kw], acc[i]);
+          }
+        }
+        float* o = outt + jm * howo + ow;
+#pragma unroll
+        for (int i = 0; i < BH; ++i) {
+          const int oh = rb * BH + i;
+          *(oh < a.ho ? o + oh * a.wo : sink) = acc[i];
+        }
+      }
+    }
+    __syncthreads();
+
+    const int tot = mult * howo;
+    const long long obase = (long long)p * tot;
+    if (a.ovec) {  // howo % 4 == 0, y / residual 16 / 8-byte aligned
+      const int nq = tot / 4;
+      if constexpr (RES) {
+        float v[DWW_NE * 4];  // every residual read before any store (y may alias it)
+#pragma unroll
+        for (int k = 0; k < DWW_NE; ++k) {
+          float f[4];
+          dw_unpack<T>(*reinterpret_cast<const V*>(res + obase + 4 * min(lane + 64 * k, nq - 1)), f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * k + e] = f[e];
+        }
+#pragma unroll
+        for (int k = 0; k < DWW_NE; ++k) {
+          const int q = min(lane + 64 * k, nq - 1);
+          const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
+          const float bv = bl[mdiv(4 * q, a.mg_howo)];
+          const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * k + e] = (sv[e] + bv) + v[4 * k + e];
+        }
+        act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+        for (int k = 0; k < DWW_NE; ++k) {
+          const int q = lane + 64 * k;
+          if (q < nq) {
+            const float f[4] = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+            *reinterpret_cast<V*>(y + obase + 4 * q) = dw_pack<T>(f);
+          }
+        }
+      } else {
+        for (int q = lane; q < nq; q += 64) {
+          const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
+          const float bv = bl[mdiv(4 * q, a.mg_howo)];
+          float f[4] = {s4.x + bv, s4.y + bv, s4.z + bv, s4.w + bv};
+          act_array(f, a.act, a.alpha, a.beta);
+          *reinterpret_cast<V*>(y + obase + 4 * q) = dw_pack<T>(f);
+        }
+      }
+    } else {
+      if constexpr (RES) {
+        float v[DWW_NE * 4];
+#pragma unroll
+        for (int k = 0; k < DWW_NE * 4; ++k) v[k] = to_f32(res[obase + min(lane + 64 * k, tot - 1)]);
+#pragma unroll
+        for (int k = 0; k < DWW_NE * 4; ++k) {
+          const int o = min(lane + 64 * k, tot - 1);
+          v[k] = (outt[o] + bl[mdiv(o, a.mg_howo)]) + v[k];
+        }
+        act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+        for (int k = 0; k < DWW_NE * 4; ++k) {
+          const int o = lane + 64 * k;
+          if (o < tot) y[obase + o] = from_f32<T>(v[k]);
+        }
+      } else {
+        for (int o = lane; o < tot; o += 64) {
+          float f[1] = {outt[o] + bl[mdiv(o, a.mg_howo)]};
+          act_array(f, a.act, a.alpha, a.beta);
+          y[obase + o] = from_f32<T>(f[0]);
+        }
+      }
+    }
+    // one wave: its LDS accesses are ordered, so the next plane may overwrite
+    // the tiles right away
+  }
+}
+
+template <typename T>
+static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, int grid, size_t lds, hipStream_t s) {
+#define DWW_CASE(K_, S_, BH_)                                                            \
+  if (a.kh == K_ && a.sh == S_ && a.bh == BH_) {                                         \
+    if (a.res)                                                                           \
+      hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, true>), dim3(grid), dim3(64), \
+                         lds, s, a);                                                     \
+    else                                                                                 \
+      hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, false>), dim3(grid), dim3(64), \
+                         lds, s, a);                                                     \
+    return hipGetLastError();                                                            \
+  }
+  DWW_CASE(3, 1, 14)
+  DWW_CASE(3, 2, 4)
+  DWW_CASE(5, 1, 14)
+  DWW_CASE(5, 2, 4)
+  DWW_CASE(7, 1, 14)
+#undef DWW_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
+                                 hipStream_t s) {
+  return dt == F16 ? launch_dw_wave_t<_Float16>(a, grid, lds, s)
+                   : launch_dw_wave_t<float>(a, grid, lds, s);
+}
+
+template <typename T>
+static hipError_t launch_dw_plane_t(const DepthwiseArgs& a, int grid, size_t lds,
+                                    hipStream_t s) {
+#define DW_CASE(K_, S_, BH_)                                                             \
+  if (a.kh == K_ && a.sh == S_ && a.bh == BH_) {                                         \
+    if (a.res)                                                                           \
+      hipLaunchKernelGGL((depthwise_plane_kernel<T, K_, S_, BH_, true>), dim3(grid), dim3(256), \
+                         lds, s, a);                                                     \
+    else                                                                                 \
+      hipLaunchKernelGGL((depthwise_plane_kernel<T, K_, S_, BH_, false>), dim3(grid), dim3(256), \
+                         lds, s, a);                                                     \
+    return hipGetLastError();                                                            \
+  }
+  DW_CASE(3, 1, 4)
+  DW_CASE(3, 2, 2)
+  DW_CASE(5, 1, 4)
+  DW_CASE(5, 2, 2)
+  DW_CASE(7, 1, 4)
 #undef DW_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, hipStream_t s) {
-  return dt == F16 ? launch_dw_plane_t<_Float16>(a, s) : launch_dw_plane_t<float>(a, s);
+hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
+                                  hipStream_t s) {
+  return dt == F16 ? launch_dw_plane_t<_Float16>(a, grid, lds, s)
+                   : launch_dw_plane_t<float>(a, grid, lds, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -231,6 +231,10 @@ DEPTHWISE_CASES = [
     (oracle.Geom(2, 24, 28, 28, 24, 3, 3, groups=24, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1), "f16"),
     (oracle.Geom(5, 3, 7, 6, 9, 5, 5, groups=3, pt=2, pl=2, pb=2, pr=2, act="sigmoid"), "f16"),
     (oracle.Geom(1, 4, 30, 30, 4, 3, 3, groups=4, pt=0, pl=0, pb=0, pr=0), "f32"),
+    # groups of planes that wrap from one image into the next, partial last group
+    (oracle.Geom(7, 13, 20, 20, 13, 3, 3, groups=13, pt=1, pl=1, pb=1, pr=1), "f32"),
+    # more plane groups than resident workgroups: each workgroup walks several
+    (oracle.Geom(30, 70, 64, 64, 70, 3, 3, groups=70, pt=1, pl=1, pb=1, pr=1), "f32"),
 ]
 
 
