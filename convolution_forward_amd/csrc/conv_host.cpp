@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "conv.h"
 #include "internal.h"
@@ -155,16 +156,16 @@ int64_t dw_lds_floats(int64_t P, int64_t tpp, int64_t mult, int64_t howo, int64_
 
 // Compute units of the current device (cached per device).
 int device_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
       v = 256;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
@@ -187,7 +188,7 @@ bool plan_depthwise(const Geo& g, Plan* pl) {
     {
       const int64_t bh = g.sh == 1 ? 14 : 4;
       const int64_t nrb = ceil_div(g.ho, bh);
-      if (hw <= 1024 && mult * howo <= 1024 && mult <= 64 && g.wo <= 64) {
+      if (hw <= 1024 && mult * howo <= 1024 && mult * g.kh * g.kw <= 64 && g.wo <= 64) {
         const int64_t lm = (g.pl + 3) / 4 * 4;
         int64_t tiw = std::max<int64_t>(lm + g.w, lm - g.pl + (g.wo - 1) * g.sw + g.kw);
         tiw = (tiw + 3) / 4 * 4;
@@ -496,7 +497,8 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         a.tpp = pl.tih * pl.tiw;
         a.oofs = a.tpp;  // tiw % 4 == 0
         a.bofs = (int)(a.oofs + (mult * howo + 3) / 4 * 4);
-        a.sofs = (int)(a.bofs + (mult + 3) / 4 * 4);
+        a.wofs = (int)(a.bofs + (mult + 3) / 4 * 4);
+        a.sofs = (int)(a.wofs + mult * ((g.kh * g.kw + 3) / 4 * 4));
         a.xvec = 1;
         a.ovec = reinterpret_cast<uintptr_t>(yc) % vb == 0 &&
                  (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % vb == 0) && howo % 4 == 0;
@@ -504,10 +506,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         a.mg_wo = make_magic((unsigned)g.wo);
         a.mg_howo = make_magic((unsigned)howo);
         const size_t lds = (size_t)(a.sofs + 4) * 4;
-        const int64_t planes = cn * g.ci;
-        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16, (160 * 1024) / (int64_t)lds));
-        const int64_t rounds = ceil_div(planes, (int64_t)device_cus() * per_cu);
-        e = launch_depthwise_wave(dt, a, (int)ceil_div(planes, rounds), lds, s);
+        e = launch_depthwise_wave(dt, a, cn * g.ci, device_cus(), lds, s);
       } else if (pl.dw_planes > 0 && !pl.dw_wave && reinterpret_cast<uintptr_t>(xc) % vb == 0) {
         const int64_t P = pl.dw_planes, mult = g.co / g.ci, howo = g.ho * g.wo;
         a.planes = (int)P;

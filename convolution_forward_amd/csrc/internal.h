@@ -158,8 +158,8 @@ hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
                                   hipStream_t s);
-hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
-                                 hipStream_t s);
+hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, long long planes, int cus,
+                                 size_t lds, hipStream_t s);
 hipError_t launch_reduce(Dtype dt, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_col2im(Dtype dt, const Col2imArgs& a, hipStream_t s);
 

@@ -5,6 +5,9 @@
 //    shuffle tree, then bias, residual, activation);
 //  - the gathering col2im + epilogue of ConvTranspose (one thread per output
 //    element, taps visited in row-major order, no atomics).
+#include <mutex>
+#include <type_traits>
+
 #include "epilogue.h"
 #include "internal.h"
 
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArg
 constexpr int DWW_NI = 4;  // 4-element input items per lane (H * W <= 1024)
 constexpr int DWW_NE = 4;  // 4-output epilogue items per lane (mult * Ho * Wo <= 1024)
 
-template <typename T, int K, int S, int BH, bool RES>
+template <typename T, int K, int S, int BH, bool RES, bool OVEC>
 __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs a) {
   typedef typename DwVec<T>::type V;
   constexpr int PR = (BH - 1) * S + K;  // input rows of one lane's output column
@@ -356,6 +359,8 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
   float* tile = smem_dw;           // tih x tiw; input column iw sits at column lm + iw
   float* outt = smem_dw + a.oofs;  // mult * howo raw sums (16-byte aligned)
   float* bl = smem_dw + a.bofs;    // mult bias values
+  constexpr int KKP = (K * K + 3) / 4 * 4;
+  float* wl = smem_dw + a.wofs;    // mult rows of K * K weights, KKP floats apart
   float* sink = smem_dw + a.sofs;  // 4 floats (16-byte aligned) that dead writes hit
   const T* __restrict__ x = static_cast<const T*>(a.x);
   const T* __restrict__ wt = static_cast<const T*>(a.wt);
@@ -363,7 +368,11 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
   const T* res = static_cast<const T*>(a.res);
   T* y = static_cast<T*>(a.y);
 
+  // prefetched per plane: the input (4-element items), the bias of output
+  // plane (p, lane) for lane < mult and weight `lane` of the plane's
+  // mult * K * K <= 64 weights
   float xin[DWW_NI][4];
+  float bin = 0.0f, win = 0.0f;
   auto load = [&](int p) __attribute__((always_inline)) {
     const long long base = (long long)p * hw;
 #pragma unroll
@@ -371,6 +380,9 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
       const int e = min(4 * (lane + 64 * i), hw - 4);  // hw % 4 == 0
       dw_unpack<T>(*reinterpret_cast<const V*>(x + base + e), xin[i]);
     }
+    const int ci = p % a.c_in;
+    if (bias) bin = to_f32(bias[ci * mult + min(lane, mult - 1)]);
+    win = to_f32(wt[(long long)ci * (mult * K * K) + min(lane, mult * K * K - 1)]);
   };
   auto stage = [&]() __attribute__((always_inline)) {
     if (a.w % 4 == 0) {  // uniform: an item never straddles two rows
@@ -404,8 +416,11 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
   const int units = a.nrb * a.wo;
   for (; p < nplanes; p += gridDim.x) {
     stage();
-    const int ci = p % a.c_in;
-    if (lane < mult) bl[lane] = bias ? to_f32(bias[ci * mult + lane]) : 0.0f;
+    if (lane < mult) bl[lane] = bin;
+    if (lane < mult * K * K) {  // weight rows padded to whole 16-byte vectors
+      const int jm = lane / (K * K), t = lane - jm * (K * K);
+      wl[jm * KKP + t] = win;
+    }
     __syncthreads();
     if (p + (int)gridDim.x < nplanes) load(p + gridDim.x);  // prefetch (uniform)
 
@@ -414,10 +429,16 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
       const unsigned ow = u - rb * a.wo;
       const float* src = tile + (rb * BH * S) * a.tiw + ow * S + (a.lm - a.pl);
       for (int jm = 0; jm < mult; ++jm) {
-        const T* wc = wt + (long long)(ci * mult + jm) * (K * K);  // wave-uniform
-        float wk[K * K];
+        // the plane's weights: one LDS address for every lane (broadcast reads)
+        float wk[KKP];
 #pragma unroll
-        for (int j = 0; j < K * K; ++j) wk[j] = to_f32(wc[j]);
+        for (int j = 0; j < KKP / 4; ++j) {
+          const float4 w4 = *reinterpret_cast<const float4*>(wl + jm * KKP + 4 * j);
+          wk[4 * j] = w4.x;
+          wk[4 * j + 1] = w4.y;
+          wk[4 * j + 2] = w4.z;
+          wk[4 * j + 3] = w4.w;
+        }
         float acc[BH];
 #pragma unroll
         for (int i = 0; i < BH; ++i) acc[i] = 0.0f;
@@ -446,7 +467,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
 
     const int tot = mult * howo;
     const long long obase = (long long)p * tot;
-    if (a.ovec) {  // howo % 4 == 0, y / residual 16 / 8-byte aligned
+    if constexpr (OVEC) {  // howo % 4 == 0, y / residual 16 / 8-byte aligned
       const int nq = tot / 4;
       if constexpr (RES) {
         float v[DWW_NE * 4];  // every residual read before any store (y may alias it)
@@ -476,7 +497,11 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
           }
         }
       } else {
-        for (int q = lane; q < nq; q += 64) {
+        // items past the end repeat the last item (same value, same address):
+        // a fixed number of stores lets the wait before the next staging skip them
+#pragma unroll
+        for (int k = 0; k < DWW_NE; ++k) {
+          const int q = min(lane + 64 * k, nq - 1);
           const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
           const float bv = bl[mdiv(4 * q, a.mg_howo)];
           float f[4] = {s4.x + bv, s4.y + bv, s4.z + bv, s4.w + bv};
@@ -501,10 +526,17 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
           if (o < tot) y[obase + o] = from_f32<T>(v[k]);
         }
       } else {
-        for (int o = lane; o < tot; o += 64) {
-          float f[1] = {outt[o] + bl[mdiv(o, a.mg_howo)]};
+#pragma unroll
+        for (int k = 0; k < DWW_NE; ++k) {
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int o = min(lane + 64 * (4 * k + e), tot - 1);
+            f[e] = outt[o] + bl[mdiv(o, a.mg_howo)];
+          }
           act_array(f, a.act, a.alpha, a.beta);
-          y[obase + o] = from_f32<T>(f[0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[obase + min(lane + 64 * (4 * k + e), tot - 1)] = from_f32<T>(f[e]);
         }
       }
     }
@@ -513,17 +545,54 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
   }
 }
 
+// Resident workgroups per CU of kernel f with lds bytes of dynamic LDS (cached).
+static int resident_per_cu(const void* f, int threads, size_t lds) {
+  struct Entry {
+    const void* f;
+    size_t lds;
+    int n;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  static std::mutex mu;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].f == f && cache[i].lds == lds) return cache[i].n;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds) != hipSuccess || n < 1) n = 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (used < 64) cache[used++] = Entry{f, lds, n};
+  return n;
+}
+
+// Persistent grid over `items` work items: as many workgroups as are resident,
+// each taking an equal number of items.
+static int persistent_grid(long long items, int per_cu, int cus) {
+  const long long slots = (long long)per_cu * cus;
+  const long long rounds = (items + slots - 1) / slots;
+  return (int)((items + rounds - 1) / rounds);
+}
+
 template <typename T>
-static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, int grid, size_t lds, hipStream_t s) {
+static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, long long planes, int cus, size_t lds,
+                                   hipStream_t s) {
+#define DWW_LAUNCH(K_, S_, BH_, R_, O_)                                                  \
+  {                                                                                      \
+    const void* f = reinterpret_cast<const void*>(&depthwise_wave_kernel<T, K_, S_, BH_, R_, O_>); \
+    const int grid = persistent_grid(planes, resident_per_cu(f, 64, lds), cus);          \
+    hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, R_, O_>), dim3(grid), dim3(64), lds, \
+                       s, a);                                                            \
+    return hipGetLastError();                                                            \
+  }
 #define DWW_CASE(K_, S_, BH_)                                                            \
   if (a.kh == K_ && a.sh == S_ && a.bh == BH_) {                                         \
-    if (a.res)                                                                           \
-      hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, true>), dim3(grid), dim3(64), \
-                         lds, s, a);                                                     \
-    else                                                                                 \
-      hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, false>), dim3(grid), dim3(64), \
-                         lds, s, a);                                                     \
-    return hipGetLastError();                                                            \
+    if (a.res) {                                                                         \
+      if (a.ovec) DWW_LAUNCH(K_, S_, BH_, true, true) else DWW_LAUNCH(K_, S_, BH_, true, false) \
+    } else {                                                                             \
+      if (a.ovec) DWW_LAUNCH(K_, S_, BH_, false, true) else DWW_LAUNCH(K_, S_, BH_, false, false) \
+    }                                                                                    \
   }
   DWW_CASE(3, 1, 14)
   DWW_CASE(3, 2, 4)
@@ -531,13 +600,14 @@ static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, int grid, size_t lds,
   DWW_CASE(5, 2, 4)
   DWW_CASE(7, 1, 14)
 #undef DWW_CASE
+#undef DWW_LAUNCH
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
-                                 hipStream_t s) {
-  return dt == F16 ? launch_dw_wave_t<_Float16>(a, grid, lds, s)
-                   : launch_dw_wave_t<float>(a, grid, lds, s);
+hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, long long planes, int cus,
+                                 size_t lds, hipStream_t s) {
+  return dt == F16 ? launch_dw_wave_t<_Float16>(a, planes, cus, lds, s)
+                   : launch_dw_wave_t<float>(a, planes, cus, lds, s);
 }
 
 template <typename T>
