@@ -170,6 +170,14 @@ int device_cus() {
 
 bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 
+// Pointwise GEMM on x as it lies: 1x1, stride 1, no padding, one group, float16,
+// whole channel octets and planes of whole 4-pixel groups.
+bool pointwise_applicable(const Geo& g, int dtype) {
+  return !g.transpose && dtype == CONV_F16 && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
+         g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
+         (g.h * g.w) % 4 == 0 && g.h * g.w >= 4;
+}
+
 // Depthwise output tile: whole plane when the staged input fits, else smaller
 // tiles; the staged region stays under 48 KiB of LDS.  Kernel/stride pairs with a
 // compiled register-blocked path and whole planes of at most 16 KiB take the
@@ -335,7 +343,15 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (ceil_div(g.co * g.kh * g.kw / g.g, IG_TILE_C) > 65535 || g.g > 65535) return CONV_ERR_SHAPE;
   } else {
     if (v == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
-    if (v == CONV_VARIANT_POINTWISE_GEMM) return CONV_ERR_ARG;  // not built for this shape
+    const bool pw_ok = pointwise_applicable(g, dtype);
+    if (v == CONV_VARIANT_POINTWISE_GEMM && !pw_ok) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_AUTO && pw_ok && p->split_override <= 1) v = CONV_VARIANT_POINTWISE_GEMM;
+    if (v == CONV_VARIANT_POINTWISE_GEMM) {
+      if (p->split_override > 1) return CONV_ERR_ARG;
+      pl->variant = v;
+      pl->scratch_whole = 0;
+      return CONV_OK;
+    }
     HaloShape hs{};
     const bool halo_ok = plan_halo(g, dtype, &hs);
     if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO && !halo_ok) return CONV_ERR_ARG;
@@ -537,6 +553,20 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       } else {
         e = launch_depthwise(dt, a, s);
       }
+    } else if (pl.variant == CONV_VARIANT_POINTWISE_GEMM) {
+      PwArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
+      a.n_pt = (int)ceil_div(g.h * g.w, 128);
+      a.n_ct = (int)ceil_div(g.co, 128);
+      a.ntiles = (int)((int64_t)cn * a.n_pt * a.n_ct);
+      a.nchunks = (int)ceil_div(g.ci, 64);
+      a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0;
+      a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0;
+      a.ovec = reinterpret_cast<uintptr_t>(yc) % 8 == 0 &&
+               (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0);
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_pointwise(a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
       HaloArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -700,6 +730,9 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
     case CONV_VARIANT_IMPLICIT_GEMM:
       snprintf(tmp, sizeof tmp, "implicit_gemm.%s.t%dx%d.split%d", dn, IG_TILE_P, IG_TILE_C,
                pl.splits);
+      break;
+    case CONV_VARIANT_POINTWISE_GEMM:
+      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t128x128.k64", dn);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
       if (pl.dw_wave)

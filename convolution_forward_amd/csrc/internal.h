@@ -66,6 +66,21 @@ struct HaloArgs {
   float alpha, beta;
 };
 
+// Pointwise (1x1, stride 1, no padding, one group) GEMM on x as it lies.
+struct PwArgs {
+  const void* x;
+  const void* wt;
+  const void* bias;
+  const void* res;
+  void* y;
+  int n, c_in, hw, c_out;
+  int n_pt, n_ct;        // 128-pixel tiles per image, 128-channel tiles
+  int ntiles, nchunks;   // tiles in this chunk of images, 64-channel chunks of c_in
+  int xvec, wvec, ovec;  // x 8-byte, w 16-byte, y / residual 8-byte aligned
+  int act;
+  float alpha, beta;
+};
+
 // Division by a launch constant d >= 1 as multiply-high, add and shift
 // (Granlund and Montgomery, "Division by invariant integers using
 // multiplication", 1994, with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1):
@@ -154,6 +169,7 @@ constexpr int HALO_MAXI = 8;  // staged (position, octet) input items per thread
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
+hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,

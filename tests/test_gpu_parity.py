@@ -200,6 +200,43 @@ ROWSHIFT_CASES = [
 ]
 
 
+POINTWISE_CASES = [
+    # (geometry, bias, residual): channel chunks with tails, channel tiles with
+    # tails, pixel tiles with tails, several images, every epilogue term
+    (oracle.Geom(2, 64, 12, 12, 256, 1, 1, act="relu"), True, False),
+    (oracle.Geom(3, 24, 10, 6, 40, 1, 1, act="silu"), True, True),
+    (oracle.Geom(1, 136, 16, 9, 200, 1, 1), False, True),
+    (oracle.Geom(4, 72, 2, 2, 130, 1, 1, act="hard_swish"), True, True),
+    (oracle.Geom(2, 256, 7, 4, 64, 1, 1, act="tanh"), True, False),
+]
+
+
+@pytest.mark.parametrize("case", POINTWISE_CASES, ids=lambda c: f"{c[0].c_in}to{c[0].c_out}x{c[0].h}x{c[0].w}")
+def test_pointwise_variant(case):
+    """The 1x1 GEMM on x as it lies against the oracle; identical bits with
+    misaligned operands (element loads and stores) and with y aliasing the
+    residual."""
+    g, has_b, has_r = case
+    _say(f"[pointwise] {g}")
+    from gpu_harness import problem_from
+    assert cf.conv_describe_variant(problem_from(g), "f16").startswith("pointwise_gemm.f16")
+    rng = np.random.default_rng(g.c_in + 31 * g.c_out + g.h)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, g.c_in, 1, 1)) * np.sqrt(2.0 / g.c_in)).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f16", x, w, b, r)
+    assert_parity("f16", y, yr, sr, b, r, what="pointwise", act=g.act)
+    y2 = run_gpu(g, "f16", x, w, b, r, offsets=(1, 3, 1, 1, 1))
+    assert np.array_equal(_bits(y), _bits(y2))
+    if has_r:
+        y3 = run_gpu(g, "f16", x, w, b, r, offsets=(0, 0, 0, 4, 4), alias_residual=True)
+        assert np.array_equal(_bits(y), _bits(y3))
+    y4 = run_gpu(g, "f16", x, w, b, r, variant="implicit_gemm")
+    assert_parity("f16", y4, yr, sr, b, r, what="pointwise-as-igemm", act=g.act)
+
+
 @pytest.mark.parametrize("case", ROWSHIFT_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}")
 def test_rowshift_variant(case):
     g, has_b, has_r = case
