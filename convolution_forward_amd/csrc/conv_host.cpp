@@ -565,6 +565,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0;
       a.ovec = reinterpret_cast<uintptr_t>(yc) % 8 == 0 &&
                (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0);
+      a.o16 = reinterpret_cast<uintptr_t>(yc) % 16 == 0 && (g.h * g.w) % 8 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_pointwise(a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {

@@ -20,9 +20,10 @@
 //    reads into rows padded to 144 bytes.
 //  * Persistent workgroups walk (tile, chunk) pairs; the next pair's operands
 //    are loaded into registers while the current chunk multiplies.
-//  * Epilogue straight from the accumulators: a lane holds 4 consecutive pixels
-//    of one output channel, so bias, residual and activation run in float32 and
-//    one 8-byte store writes the 4 outputs.
+//  * Epilogue: a lane holds 4 consecutive pixels of one output channel; bias,
+//    residual and activation run in float32 on them, the float16 results go to
+//    an LDS output tile [channel][pixel] in the freed staging area, and whole
+//    256-byte rows of it leave with 16-byte stores.
 // Per output the sum runs over the channels in increasing order in steps of 32
 // (the MFMA's internal order within a step).
 #include <atomic>
@@ -47,14 +48,17 @@ constexpr int PW_XBYTES = PW_TP * PW_KC * 2;
 constexpr int PW_WROW = PW_KC * 2 + 16;    // padded LDS bytes per output channel
 constexpr int PW_WBYTES = PW_TC * PW_WROW;
 constexpr int PW_NW = PW_TC * (PW_KC / 8) / 256;  // 16-byte weight vectors per thread
+constexpr int PW_OROW = PW_TP * 2 + 16;    // LDS bytes per output-tile row (float16)
+static_assert(PW_TC * PW_OROW <= PW_XBYTES + PW_WBYTES, "output tile reuses the staging area");
 
 // octet slot at pixel row p: the 16 rows of an MFMA block land on distinct banks
 __device__ __forceinline__ int pw_slot(int p, int o) { return o ^ ((p >> 1) & 7); }
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PW_XBYTES + PW_WBYTES];
+template <bool O16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pointwise_f16_kernel(const PwArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PW_XBYTES + PW_WBYTES + PW_TC * 4];
   unsigned char* xs = smem;
   unsigned char* ws = smem + PW_XBYTES;
 
@@ -70,6 +74,8 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
 
   u32x2_t xr[8];       // 8 channels x 4 pixels
   u32x4_t wr[PW_NW];   // weight vectors
+  _Float16 br = 0.0f;  // bias of tile channel tid (tid < 128), converted when staged
+  float* bsm = reinterpret_cast<float*>(smem + PW_XBYTES + PW_WBYTES);
 
   // work item = tile * nchunks + chunk; tile = (image, pixel tile, channel tile),
   // channel tile fastest
@@ -106,6 +112,7 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
         xr[e] = __builtin_bit_cast(u32x2_t, h);
       }
     }
+    if (a.bias) br = static_cast<const _Float16*>(a.bias)[min(co0 + (tid & 127), a.c_out - 1)];
     // w: row co0 + q / 8, 16-byte piece q % 8 of the chunk
 #pragma unroll
     for (int i = 0; i < PW_NW; ++i) {
@@ -136,6 +143,7 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
       const int p = 4 * sg + j;
       *reinterpret_cast<half8_t*>(xs + p * 128 + 16 * pw_slot(p, so)) = v;
     }
+    if (tid < PW_TC) bsm[tid] = (float)br;
 #pragma unroll
     for (int i = 0; i < PW_NW; ++i) {
       const int q = tid + 256 * i;
@@ -175,27 +183,37 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
     }
   };
 
-  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  const void* bias = a.bias;
   const _Float16* res = static_cast<const _Float16*>(a.res);
   _Float16* y = static_cast<_Float16*>(a.y);
+  // Epilogue.  Phase 1, per lane from the accumulators: bias, residual and
+  // activation in float32, rounded to float16 into the LDS output tile
+  // [channel][pixel] (which reuses the staging area).  Phase 2: full rows of the
+  // tile leave with 16-byte stores.  Every residual read happens in phase 1,
+  // before the barrier that precedes any store (y may alias the residual).
   auto epilogue = [&](int item) __attribute__((always_inline)) {
     int n, p0, co0, c0;
     decode(item, n, p0, co0, c0);
-    const int pbase = p0 + 64 * wp + 4 * (lane >> 4);
-    const int cbase = co0 + 64 * wc + (lane & 15);
-    float bv[4];
+    const int pl0 = 64 * wp + 4 * (lane >> 4);  // tile pixel of the lane's first value
+    const int cl0 = 64 * wc + (lane & 15);      // tile channel of the lane's block 0
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      bv[cb] = bias ? (float)bias[min(cbase + 16 * cb, a.c_out - 1)] : 0.0f;
-    // residual reads first (y may alias the residual); clamped, unconditional
-    float rv[4][4][4];
-    if (res) {
+    for (int pb = 0; pb < 4; ++pb) {
+      float v[16];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
+      for (int cb = 0; cb < 4; ++cb) {
+        const float bv = bsm[cl0 + 16 * cb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float t = acc[pb][cb][i];
+          if (bias) t = t + bv;
+          v[4 * cb + i] = t;
+        }
+      }
+      if (res) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const int p = min(pbase + 16 * pb, hw - 4);
-          const int co = min(cbase + 16 * cb, a.c_out - 1);
+          const int p = min(p0 + pl0 + 16 * pb, hw - 4);
+          const int co = min(co0 + cl0 + 16 * cb, a.c_out - 1);
           const _Float16* src = res + ((long long)n * a.c_out + co) * hw + p;
           half4_t h;
           if (a.ovec) {  // uniform: y and residual 8-byte aligned
@@ -205,45 +223,60 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
             for (int i = 0; i < 4; ++i) h[i] = src[i];
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rv[pb][cb][i] = (float)h[i];
-        }
-    }
-    float v[64];
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = acc[pb][cb][i];
-          if (bias) s = s + bv[cb];
-          if (res) s = s + rv[pb][cb][i];
-          v[16 * pb + 4 * cb + i] = s;
-        }
-    act_array(v, a.act, a.alpha, a.beta);
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int p = pbase + 16 * pb;
-        const int co = cbase + 16 * cb;
-        if (p < hw && co < a.c_out) {  // hw % 4 == 0: 4 pixels are valid together
-          half4_t h;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[16 * pb + 4 * cb + i];
-          _Float16* dst = y + ((long long)n * a.c_out + co) * hw + p;
-          if (a.ovec) {
-            *reinterpret_cast<u32x2_t*>(dst) = __builtin_bit_cast(u32x2_t, h);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = h[i];
-          }
+          for (int i = 0; i < 4; ++i) v[4 * cb + i] = v[4 * cb + i] + (float)h[i];
         }
       }
+      act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        half4_t h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[4 * cb + i];
+        *reinterpret_cast<half4_t*>(smem + (cl0 + 16 * cb) * PW_OROW + 2 * (pl0 + 16 * pb)) = h;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    // phase 2: 128 rows of 16 vectors of 8 pixels
+    const int pvalid = min(PW_TP, hw - p0);  // a multiple of 4 (of 8 when O16)
+    if constexpr (O16) {
+      // vectors past the tile's valid rows or pixels repeat the last valid vector
+      // of the tile (same value, same address): the store count is fixed, so
+      // the wait before the next staging does not include these stores
+      const int rlast = min(PW_TC, a.c_out - co0) - 1;
+#pragma unroll
+      for (int k = 0; k < PW_TC * PW_TP / 8 / 256; ++k) {
+        const int q = tid + 256 * k;
+        const int row = min(q >> 4, rlast), px = min(8 * (q & 15), pvalid - 8);
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(smem + row * PW_OROW + 2 * px);
+        *reinterpret_cast<u32x4_t*>(y + ((long long)n * a.c_out + co0 + row) * hw + p0 + px) = d;
+      }
+    } else {
+#pragma unroll 1
+      for (int k = 0; k < PW_TC * PW_TP / 8 / 256; ++k) {
+        const int q = tid + 256 * k;
+        const int row = q >> 4, px = 8 * (q & 15);
+        const int co = co0 + row;
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(smem + row * PW_OROW + 2 * px);
+        _Float16* dst = y + ((long long)n * a.c_out + co) * hw + p0 + px;
+        if (co < a.c_out && px < pvalid) {
+          if (a.ovec) {
+            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{d[0], d[1]};
+            if (px + 8 <= pvalid) *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{d[2], d[3]};
+          } else {
+            const half8_t h = __builtin_bit_cast(half8_t, d);
+            const int cnt = min(8, pvalid - px);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e < cnt) dst[e] = h[e];
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next staging overwrites the output tile
   };
 
   const int nitems = a.ntiles * a.nchunks;
@@ -264,12 +297,13 @@ __global__ __launch_bounds__(256) void pointwise_f16_kernel(const PwArgs a) {
   }
 }
 
-hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s) {
+template <bool O16>
+static hipError_t launch_pw_t(const PwArgs& a, int cus, hipStream_t s) {
   // persistent: as many workgroups as are resident, each taking an equal share
   static std::atomic<int> per_cu{0};
   int r = per_cu.load(std::memory_order_relaxed);
   if (r == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<O16>, 256, 0) !=
             hipSuccess || r < 1)
       r = 1;
     per_cu.store(r, std::memory_order_relaxed);
@@ -277,8 +311,12 @@ hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s) {
   const long long slots = (long long)r * cus;
   const long long rounds = (a.ntiles + slots - 1) / slots;
   const int grid = (int)((a.ntiles + rounds - 1) / rounds);
-  hipLaunchKernelGGL(pointwise_f16_kernel, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(pointwise_f16_kernel<O16>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s) {
+  return a.o16 ? launch_pw_t<true>(a, cus, s) : launch_pw_t<false>(a, cus, s);
 }
 
 }  // namespace convfwd
