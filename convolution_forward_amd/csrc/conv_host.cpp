@@ -143,6 +143,7 @@ struct Plan {
   int dw_bh;      // whole-plane path: outputs per thread along a column
   int dw_wave;    // whole-plane path: one wave per plane
   int dw_lm;      // one-wave path: LDS column of input column 0
+  int pw_tc;      // pointwise: output channels per tile
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -349,6 +350,7 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (v == CONV_VARIANT_POINTWISE_GEMM) {
       if (p->split_override > 1) return CONV_ERR_ARG;
       pl->variant = v;
+      pl->pw_tc = g.co > 64 ? 128 : 64;
       pl->scratch_whole = 0;
       return CONV_OK;
     }
@@ -558,7 +560,8 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
       a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
       a.n_pt = (int)ceil_div(g.h * g.w, 128);
-      a.n_ct = (int)ceil_div(g.co, 128);
+      a.tc = pl.pw_tc;
+      a.n_ct = (int)ceil_div(g.co, a.tc);
       a.ntiles = (int)((int64_t)cn * a.n_pt * a.n_ct);
       a.nchunks = (int)ceil_div(g.ci, 64);
       a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0;
@@ -733,7 +736,7 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                pl.splits);
       break;
     case CONV_VARIANT_POINTWISE_GEMM:
-      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t128x128.k64", dn);
+      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t128x%d.k64", dn, pl.pw_tc);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
       if (pl.dw_wave)

@@ -78,6 +78,7 @@ struct PwArgs {
   int ntiles, nchunks;   // tiles in this chunk of images, 64-channel chunks of c_in
   int xvec, wvec, ovec;  // x 8-byte, w 16-byte, y / residual 8-byte aligned
   int o16;               // y 16-byte aligned and h * w % 8 == 0
+  int tc;                // output channels per tile: 64 or 128
   int act;
   float alpha, beta;
 };

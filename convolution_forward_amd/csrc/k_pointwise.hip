@@ -26,6 +26,7 @@
 //    256-byte rows of it leave with 16-byte stores.
 // Per output the sum runs over the channels in increasing order in steps of 32
 // (the MFMA's internal order within a step).
+#include <algorithm>
 #include <atomic>
 
 #include "epilogue.h"
@@ -42,22 +43,25 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int PW_TP = 128;                 // pixels per tile
-constexpr int PW_TC = 128;                 // output channels per tile
 constexpr int PW_KC = 64;                  // input channels per chunk
 constexpr int PW_XBYTES = PW_TP * PW_KC * 2;
 constexpr int PW_WROW = PW_KC * 2 + 16;    // padded LDS bytes per output channel
-constexpr int PW_WBYTES = PW_TC * PW_WROW;
-constexpr int PW_NW = PW_TC * (PW_KC / 8) / 256;  // 16-byte weight vectors per thread
 constexpr int PW_OROW = PW_TP * 2 + 16;    // LDS bytes per output-tile row (float16)
-static_assert(PW_TC * PW_OROW <= PW_XBYTES + PW_WBYTES, "output tile reuses the staging area");
 
 // octet slot at pixel row p: the 16 rows of an MFMA block land on distinct banks
 __device__ __forceinline__ int pw_slot(int p, int o) { return o ^ ((p >> 1) & 7); }
 
 }  // namespace
 
-template <bool O16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void pointwise_f16_kernel(const PwArgs a) {
+template <bool O16, int PW_TC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PW_TC == 128 ? 3 : 4)))
+void pointwise_f16_kernel(const PwArgs a) {
+  constexpr int PW_WBYTES = PW_TC * PW_WROW;
+  constexpr int PW_NW = PW_TC * (PW_KC / 8) / 256;  // 16-byte weight vectors per thread
+  static_assert(PW_TC * PW_OROW <= PW_XBYTES + PW_WBYTES, "output tile reuses the staging area");
+  constexpr int WCN = PW_TC / 64;  // waves along the output channels (64 each)
+  constexpr int WPN = 4 / WCN;     // waves along the pixels
+  constexpr int PB = PW_TP / WPN / 16;  // 16-pixel MFMA blocks per wave
   __shared__ __attribute__((aligned(16))) unsigned char smem[PW_XBYTES + PW_WBYTES + PW_TC * 4];
   unsigned char* xs = smem;
   unsigned char* ws = smem + PW_XBYTES;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         xr[e] = __builtin_bit_cast(u32x2_t, h);
       }
     }
-    if (a.bias) br = static_cast<const _Float16*>(a.bias)[min(co0 + (tid & 127), a.c_out - 1)];
+    if (a.bias) br = static_cast<const _Float16*>(a.bias)[min(co0 + (tid % PW_TC), a.c_out - 1)];
     // w: row co0 + q / 8, 16-byte piece q % 8 of the chunk
 #pragma unroll
     for (int i = 0; i < PW_NW; ++i) {
@@ -153,10 +157,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   };
 
-  const int wp = wave & 1, wc = wave >> 1;  // wave's 64-pixel and 64-channel halves
-  floatx4_t acc[4][4];
+  const int wp = wave % WPN, wc = wave / WPN;  // wave's pixel and channel ranges
+  floatx4_t acc[PB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < PB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -164,10 +168,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
     for (int ks = 0; ks < PW_KC / 32; ++ks) {
       const int o = 4 * ks + (lane >> 4);
-      half8_t af[4], bf[4];
+      half8_t af[PB], bf[4];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const int p = 64 * wp + 16 * pb + (lane & 15);
+      for (int pb = 0; pb < PB; ++pb) {
+        const int p = 16 * PB * wp + 16 * pb + (lane & 15);
         af[pb] = *reinterpret_cast<const half8_t*>(xs + p * 128 + 16 * pw_slot(p, o));
       }
 #pragma unroll
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
         bf[cb] = *reinterpret_cast<const half8_t*>(ws + c * PW_WROW + 16 * o);
       }
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb)
+      for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
           acc[pb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[pb], bf[cb], acc[pb][cb], 0, 0, 0);
@@ -194,10 +198,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   auto epilogue = [&](int item) __attribute__((always_inline)) {
     int n, p0, co0, c0;
     decode(item, n, p0, co0, c0);
-    const int pl0 = 64 * wp + 4 * (lane >> 4);  // tile pixel of the lane's first value
+    const int pl0 = 16 * PB * wp + 4 * (lane >> 4);  // tile pixel of the lane's first value
     const int cl0 = 64 * wc + (lane & 15);      // tile channel of the lane's block 0
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
+    for (int pb = 0; pb < PB; ++pb) {
       float v[16];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < PB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
@@ -297,26 +301,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   }
 }
 
-template <bool O16>
+template <bool O16, int TC>
 static hipError_t launch_pw_t(const PwArgs& a, int cus, hipStream_t s) {
-  // persistent: as many workgroups as are resident, each taking an equal share
+  // persistent: one workgroup per resident slot (an uneven last round measured
+  // faster than fewer workgroups with equal shares)
   static std::atomic<int> per_cu{0};
   int r = per_cu.load(std::memory_order_relaxed);
   if (r == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<O16>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<O16, TC>, 256, 0) !=
             hipSuccess || r < 1)
       r = 1;
     per_cu.store(r, std::memory_order_relaxed);
   }
-  const long long slots = (long long)r * cus;
-  const long long rounds = (a.ntiles + slots - 1) / slots;
-  const int grid = (int)((a.ntiles + rounds - 1) / rounds);
-  hipLaunchKernelGGL(pointwise_f16_kernel<O16>, dim3(grid), dim3(256), 0, s, a);
+  const int grid = (int)std::min<long long>((long long)r * cus, a.ntiles);
+  hipLaunchKernelGGL((pointwise_f16_kernel<O16, TC>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s) {
-  return a.o16 ? launch_pw_t<true>(a, cus, s) : launch_pw_t<false>(a, cus, s);
+  if (a.tc == 64) return a.o16 ? launch_pw_t<true, 64>(a, cus, s) : launch_pw_t<false, 64>(a, cus, s);
+  return a.o16 ? launch_pw_t<true, 128>(a, cus, s) : launch_pw_t<false, 128>(a, cus, s);
 }
 
 }  // namespace convfwd
