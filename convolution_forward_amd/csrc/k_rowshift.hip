@@ -22,6 +22,8 @@
 //    moved 1 and 2 lanes down inside each 16-lane DPP row (row_shl), which holds
 //    one image row: a 14-wide output row plus its 2-column reach fits 16 lanes, so
 //    the lanes that shift in zeros only feed output columns >= Wo, never stored.
+//    The MFMAs run taps outermost and row pairs innermost, so back-to-back MFMAs
+//    accumulate into different row pairs.
 //  * The stage's weights are copied as they lie (64 channels x 9 taps contiguous
 //    per output channel in OIHW) with coalesced 16-byte reads into padded LDS
 //    rows; a lane's B data for all 9 taps (8 channels x 9 taps, 144 contiguous
@@ -85,13 +87,14 @@ __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c)
 
 }  // namespace
 
-template <int R>
+template <int R, bool XV, bool WV>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef RsLayout<R> L;
   constexpr int NP = L::NP;
   // epilogue areas (4 waves x 32 channels x (R * 14 + 1) floats) and the bias
   // slots below the sink reuse the two stage buffers
-  static_assert(4 * 32 * (R * 14 + 1) * 4 + 32 * 4 <= L::SINK, "epilogue does not fit");
+  // plus one junk float per thread and the bias slots below the sink
+  static_assert(4 * 32 * (R * 14 + 1) * 4 + 256 * 4 + 32 * 4 <= L::SINK, "epilogue does not fit");
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
   const int tid = threadIdx.x;
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   auto load_stage = [&](int s, int set) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
-    if (a.xvec) {
+    if constexpr (XV) {  // 8-byte aligned planes of whole 4-pixel groups
 #pragma unroll
       for (int i = 0; i < L::NI; ++i) {
         const _Float16* src = ximg + xoff + in_off[i];
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         }
       }
     }
-    if (a.wvec) {
+    if constexpr (WV) {  // 16-byte aligned weights
 #pragma unroll
       for (int i = 0; i < L::NW; ++i)
         rwv[set][i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
@@ -246,59 +249,100 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         v[e] = __builtin_bit_cast(half8_t, raw[(e * 9 + t) / 8])[(e * 9 + t) % 8];
       bf[t] = __builtin_bit_cast(u32x4_t, v);
     }
-    // A: the row pair starting at input row t feeds output row pair (t - kh) / 2 at tap row kh
+    // A: the row pair starting at input row t; output row pair q takes it at
+    // tap row kh = t - 2q.  Taps outermost, row pairs innermost: consecutive
+    // MFMAs go to NP different accumulators, so none waits for its previous
+    // result, and every output still sees its taps in (kh, kw) row-major order.
 #pragma unroll
-    for (int t = 0; t < 2 * NP + 1; ++t) {
-      const int pos = (t + prow) * RS_COLS + pcol;
-      const u32x4_t f0 = *reinterpret_cast<const u32x4_t*>(in + (pos * 8 + slot8(pos, oct)) * 16);
-      const u32x4_t f1 = row_shift<1>(f0);
-      const u32x4_t f2 = row_shift<2>(f0);
+    for (int kh = 0; kh < 3; ++kh) {
+      u32x4_t fr[NP];  // row pair 2q + kh of every output row pair q
 #pragma unroll
-      for (int kh = 0; kh < 3; ++kh) {
-        if ((t - kh) < 0 || ((t - kh) & 1)) continue;  // compile-time
-        const int q = (t - kh) >> 1;
-        if (q >= NP) continue;
-        acc[q] = mfma32(f0, bf[kh * 3 + 0], acc[q]);
-        acc[q] = mfma32(f1, bf[kh * 3 + 1], acc[q]);
-        acc[q] = mfma32(f2, bf[kh * 3 + 2], acc[q]);
+      for (int q = 0; q < NP; ++q) {
+        const int pos = (2 * q + kh + prow) * RS_COLS + pcol;
+        fr[q] = *reinterpret_cast<const u32x4_t*>(in + (pos * 8 + slot8(pos, oct)) * 16);
       }
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          const u32x4_t f = kw == 0 ? fr[q] : kw == 1 ? row_shift<1>(fr[q]) : row_shift<2>(fr[q]);
+          acc[q] = mfma32(f, bf[kh * 3 + kw], acc[q]);
+        }
+      __builtin_amdgcn_sched_barrier(0);  // one tap row's fragments live at a time
     }
   };
 
-  // zero both stages' input regions once: padding positions are never written
+  const int howo = a.ho * a.wo;
+  const int total_c = min(32, a.cog - co0) * howo;  // outputs of this tile
+  const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
+  const _Float16* res = static_cast<const _Float16*>(a.res);
+  constexpr int MAXQ = (32 * 14 * 14 / 4 + 255) / 256;  // 4-output items per thread at most
+  constexpr int EPT = (32 * 14 * 14 + 255) / 256;       // single outputs per thread at most
+  const bool vec = a.ovec;  // howo % 4 == 0 and y / residual 8-byte aligned (uniform)
+  u32x2_t rq[MAXQ];         // residual (vector path), prefetched during the last step
+  auto load_residual = [&]() __attribute__((always_inline)) {
+    if (res && vec) {  // uniform; clamped items keep every load unconditional
+      const int nq = total_c / 4;
+#pragma unroll
+      for (int k = 0; k < MAXQ; ++k)
+        rq[k] = *reinterpret_cast<const u32x2_t*>(res + obase + 4 * min(tid + 256 * k, nq - 1));
+    }
+  };
+
+  // Prefetch distance 2: loads for stage s+2 are issued while stage s multiplies
+  // and reach LDS one step later, after stage s+1 has multiplied.  Register set
+  // and LDS buffer follow the stage's parity, fixed at compile time in a loop
+  // unrolled by two; the last steps load (M = 1) or also store (M = 2) nothing.
+  auto step = [&](int s, auto parity, auto mode) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr int M = decltype(mode)::value;
+    if constexpr (M == 0) load_stage(s + 2, P);  // set P: stage s was stored last step
+    if constexpr (M == 2) load_residual();        // the epilogue's residual
+    // the scheduler must not sink these loads below the multiplications (which
+    // would shorten the prefetch to nothing) nor hoist the regrouping of set P^1
+    // into them (which waits for that set early)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(P);                                   // buffer P holds stage s
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (M <= 1) store_stage(P ^ 1, P ^ 1);  // stage s+1 (set P^1) into buffer P^1
+    __syncthreads();
+  };
+  typedef std::integral_constant<int, 0> P0;
+  typedef std::integral_constant<int, 1> P1;
+  typedef std::integral_constant<int, 0> LOAD;
+  typedef std::integral_constant<int, 1> STORE_ONLY;
+  typedef std::integral_constant<int, 2> LAST;
+  load_stage(0, 0);
+  load_stage(min(1, nstages - 1), 1);
+  // zero both stages' input regions while the first loads fly: padding
+  // positions are never written again
   for (int q = tid; q < 2 * (L::IN_BYTES / 16); q += 256) {
     const int st = q / (L::IN_BYTES / 16), off = q - st * (L::IN_BYTES / 16);
     *reinterpret_cast<u32x4_t*>(smem + st * L::STAGE + off * 16) = u32x4_t{0, 0, 0, 0};
   }
   __syncthreads();
-  // Prefetch distance 2: loads for stage s+2 are issued while stage s multiplies
-  // and reach LDS one step later, after stage s+1 has multiplied.  Register set
-  // and LDS buffer follow the stage's parity, fixed at compile time in a loop
-  // unrolled by two, and every load is unconditional (clamped stage index), so
-  // the wait before a store counts exactly the loads issued since.
-  auto step = [&](int s, auto parity) __attribute__((always_inline)) {
-    constexpr int P = decltype(parity)::value;
-    load_stage(min(s + 2, nstages - 1), P);  // set P: stage s was stored last step
-    compute(P);                              // buffer P holds stage s
-    store_stage(P ^ 1, P ^ 1);               // stage s+1 (set P^1) into buffer P^1
-    __syncthreads();
-  };
-  load_stage(0, 0);
-  load_stage(min(1, nstages - 1), 1);
   store_stage(0, 0);
   __syncthreads();
   int s = 0;
-  for (; s + 1 < nstages; s += 2) {
-    step(s, std::integral_constant<int, 0>{});
-    step(s + 1, std::integral_constant<int, 1>{});
+  for (; s + 3 < nstages; s += 2) {  // both steps prefetch a stage
+    step(s, P0{}, LOAD{});
+    step(s + 1, P1{}, LOAD{});
   }
-  if (s < nstages) step(s, std::integral_constant<int, 0>{});
+  if (nstages - s == 3) {
+    step(s, P0{}, LOAD{});
+    step(s + 1, P1{}, STORE_ONLY{});
+    step(s + 2, P0{}, LAST{});
+  } else if (nstages - s == 2) {
+    step(s, P0{}, STORE_ONLY{});
+    step(s + 1, P1{}, LAST{});
+  } else {
+    step(s, P0{}, LAST{});
+  }
 
   // ---- each wave's partial sums go to its own [channel][pixel] LDS area; the
   // epilogue adds the four in wave order, ((w0 + w1) + w2) + w3, and runs in
   // memory order, 4 contiguous outputs per item (a fragment spans 32 output
   // planes, so storing from the fragment layout would scatter). ----
-  const int howo = a.ho * a.wo;
   const int pitch = howo + 1;   // odd channel pitch: a fragment's 32 channels hit distinct banks
   const int area = 32 * pitch;  // floats per wave area
   float* part = reinterpret_cast<float*>(smem);
@@ -310,28 +354,23 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     for (int i = 0; i < 16; ++i) {
       const int p = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);  // pixel of the row pair
       const int oh = 2 * q + p / 16, ow = p % 16;
-      if (oh < a.ho && ow < a.wo)
-        part[wave * area + (lane & 31) * pitch + oh * a.wo + ow] = acc[q][i];
+      // columns past the row (and rows past the image) go to this lane's junk
+      // slot: no branch, no two lanes on one address
+      const bool ok = oh < a.ho && ow < a.wo;
+      part[ok ? wave * area + (lane & 31) * pitch + oh * a.wo + ow : 4 * area + tid] = acc[q][i];
     }
   if (tid < 32) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
   __syncthreads();
 
-  const _Float16* res = static_cast<const _Float16*>(a.res);
   _Float16* y = static_cast<_Float16*>(a.y);
-  const int cvalid = min(32, a.cog - co0);
-  const int total = cvalid * howo;
-  const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
-  constexpr int MAXQ = (32 * 14 * 14 / 4 + 255) / 256;  // 4-output items per thread at most
-  const bool vec = a.ovec;  // howo % 4 == 0 and y / residual 8-byte aligned (uniform)
+  const int total = total_c;
   if (vec) {
     const int nq = total / 4;
     float v[MAXQ * 4];
-    if (res) {  // uniform; clamped items keep every load unconditional
+    if (res) {  // prefetched before the last multiplication step
 #pragma unroll
       for (int k = 0; k < MAXQ; ++k) {
-        const int it = min(tid + 256 * k, nq - 1);
-        const u32x2_t r = *reinterpret_cast<const u32x2_t*>(res + obase + 4 * it);
-        const half4_t h = __builtin_bit_cast(half4_t, r);
+        const half4_t h = __builtin_bit_cast(half4_t, rq[k]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * k + e] = (float)h[e];
       }
@@ -362,9 +401,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       }
     }
   } else {
-    constexpr int EPT = (32 * 14 * 14 + 255) / 256;
     float v[EPT];
-    if (res) {
+    if (res) {  // every residual read before any store (y may alias it)
 #pragma unroll
       for (int k = 0; k < EPT; ++k) v[k] = (float)res[obase + min(tid + 256 * k, total - 1)];
     }
@@ -389,12 +427,20 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups));
+#define RS_LAUNCH(R_)                                                                        \
+  {                                                                                          \
+    if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, true>), grid, dim3(256), 0, s, a); \
+    else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, false>), grid, dim3(256), 0, s, a); \
+    else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, false, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((rowshift_kernel<R_, false, false>), grid, dim3(256), 0, s, a);           \
+  }
   if (a.ho <= 8)
-    hipLaunchKernelGGL(rowshift_kernel<8>, grid, dim3(256), 0, s, a);
+    RS_LAUNCH(8)
   else if (a.ho <= 14)
-    hipLaunchKernelGGL(rowshift_kernel<14>, grid, dim3(256), 0, s, a);
+    RS_LAUNCH(14)
   else
     return hipErrorInvalidValue;
+#undef RS_LAUNCH
   return hipGetLastError();
 }
 
