@@ -63,7 +63,7 @@ int validate(const conv_problem* p, int dtype, Geo* g) {
     return CONV_ERR_ARG;
   if ((p->has_bias != 0 && p->has_bias != 1) || (p->has_residual != 0 && p->has_residual != 1))
     return CONV_ERR_ARG;
-  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_HALO)
+  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_ROWBAND)
     return CONV_ERR_ARG;
   if (p->split_override < 0 || p->split_override > kMaxSplits) return CONV_ERR_ARG;
   if (p->x_off < 0 || p->w_off < 0 || p->b_off < 0 || p->r_off < 0 || p->y_off < 0)
@@ -144,6 +144,7 @@ struct Plan {
   int dw_wave;    // whole-plane path: one wave per plane
   int dw_lm;      // one-wave path: LDS column of input column 0
   int pw_tc;      // pointwise: output channels per tile
+  int rb_band_rows;  // row band: output rows per workgroup
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -170,6 +171,17 @@ int device_cus() {
 }
 
 bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
+
+// Row-band implicit GEMM: float16, one group, stride 2 both ways, no dilation,
+// kernel rows of at most 8 taps, at most 24 (ci, kh) groups, output rows of at
+// most 128; the new input rows of one output row fit one 16-byte item per
+// thread, the first KH rows four, and the ring holds KH rows plus three rows'
+// worth of prefetched ones.
+bool rowband_applicable(const Geo& g, int dtype) {
+  return !g.transpose && dtype == CONV_F16 && g.g == 1 && g.sh == 2 && g.sw == 2 && g.dh == 1 &&
+         g.dw == 1 && g.kw <= 8 && g.ci * g.kh <= 24 && g.kh + 4 * g.sh <= 16 && g.wo <= 128 &&
+         g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024;
+}
 
 // Pointwise GEMM on x as it lies: 1x1, stride 1, no padding, one group, float16,
 // whole channel octets and planes of whole 4-pixel groups.
@@ -347,6 +359,20 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     const bool pw_ok = pointwise_applicable(g, dtype);
     if (v == CONV_VARIANT_POINTWISE_GEMM && !pw_ok) return CONV_ERR_ARG;
     if (v == CONV_VARIANT_AUTO && pw_ok && p->split_override <= 1) v = CONV_VARIANT_POINTWISE_GEMM;
+    const bool rb_ok = rowband_applicable(g, dtype);
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_ROWBAND && !rb_ok) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_AUTO && rb_ok && p->split_override <= 1) v = CONV_VARIANT_IMPLICIT_GEMM_ROWBAND;
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_ROWBAND) {
+      if (p->split_override > 1) return CONV_ERR_ARG;
+      pl->variant = v;
+      // bands of output rows: one round of workgroups at full size (the ring
+      // refill per band costs KH rows)
+      const int64_t tiles = g.n * ceil_div(g.co, 64);
+      int64_t bands = std::max<int64_t>(1, std::min<int64_t>(g.ho, ceil_div(256, tiles)));
+      pl->rb_band_rows = (int)ceil_div(g.ho, bands);
+      pl->scratch_whole = 0;
+      return CONV_OK;
+    }
     if (v == CONV_VARIANT_POINTWISE_GEMM) {
       if (p->split_override > 1) return CONV_ERR_ARG;
       pl->variant = v;
@@ -405,6 +431,7 @@ const char* variant_name(int v) {
     case CONV_VARIANT_DEPTHWISE_DIRECT: return "depthwise_direct";
     case CONV_VARIANT_TRANSPOSE_GEMM_COL2IM: return "transpose_gemm_col2im";
     case CONV_VARIANT_IMPLICIT_GEMM_HALO: return "implicit_gemm_halo";
+    case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND: return "implicit_gemm_rowband";
     default: return "unknown";
   }
 }
@@ -555,6 +582,31 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       } else {
         e = launch_depthwise(dt, a, s);
       }
+    } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_ROWBAND) {
+      RowbandArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.kh = (int)g.kh; a.kw = (int)g.kw; a.sh = (int)g.sh; a.pt = (int)g.pt; a.pl = (int)g.pl;
+      a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.n_ct = (int)ceil_div(g.co, 64);
+      a.band_rows = pl.rb_band_rows;
+      a.n_band = (int)ceil_div(g.ho, a.band_rows);
+      const int64_t need = std::max<int64_t>(g.pl + g.w, 2 * (g.wo - 1) + 8);
+      a.rpitch = (int)((need + 1) / 2 * 2);
+      // the ring area also stages the tile's weights once at the start
+      a.ring_bytes = (int)((std::max<int64_t>((int64_t)g.ci * 16 * a.rpitch, 64 * g.ci * g.kh * g.kw) * 2 +
+                            15) / 16 * 16);
+      a.vec = reinterpret_cast<uintptr_t>(xc) % 16 == 0 && reinterpret_cast<uintptr_t>(yc) % 16 == 0 &&
+              g.w % 8 == 0 && g.wo % 8 == 0;
+      {
+        const int64_t per_co = g.ci * g.kh * g.kw;
+        // every tile's run starts at a multiple of 64 channels: whole vectors when
+        // the base is aligned and each tile's length is a multiple of 8 halves
+        a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0 &&
+                 (std::min<int64_t>(64, g.co) * per_co) % 8 == 0 && ((g.co % 64) * per_co) % 8 == 0;
+      }
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_rowband(a, s);
     } else if (pl.variant == CONV_VARIANT_POINTWISE_GEMM) {
       PwArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -737,6 +789,9 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
       break;
     case CONV_VARIANT_POINTWISE_GEMM:
       snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t128x%d.k64", dn, pl.pw_tc);
+      break;
+    case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND:
+      snprintf(tmp, sizeof tmp, "implicit_gemm_rowband.%s.rows%d", dn, pl.rb_band_rows);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
       if (pl.dw_wave)

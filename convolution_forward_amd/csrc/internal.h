@@ -83,6 +83,24 @@ struct PwArgs {
   float alpha, beta;
 };
 
+// Row-band implicit GEMM for stride-2 layers with few input channels.
+struct RowbandArgs {
+  const void* x;
+  const void* wt;
+  const void* bias;
+  const void* res;
+  void* y;
+  int n, c_in, h, w, c_out, kh, kw;
+  int sh, pt, pl, ho, wo;
+  int n_ct, n_band, band_rows;  // 64-channel tiles, bands of output rows per image
+  int rpitch;                   // halves per LDS ring row (even)
+  int ring_bytes;               // c_in * 16 rows * rpitch * 2
+  int vec;                      // x, y 16-byte aligned, w % 8 == 0 and wo % 8 == 0
+  int wvec;                     // weights 16-byte aligned, tile runs whole vectors
+  int act;
+  float alpha, beta;
+};
+
 // Division by a launch constant d >= 1 as multiply-high, add and shift
 // (Granlund and Montgomery, "Division by invariant integers using
 // multiplication", 1994, with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1):
@@ -172,6 +190,7 @@ constexpr int HALO_MAXI = 8;  // staged (position, octet) input items per thread
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s);
+hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s);
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,

@@ -1,0 +1,304 @@
+// Implicit-GEMM convolution for stride-2 layers with few input channels (the
+// stem of an image network: 3 channels, 7x7, stride 2), gfx950, float16
+// operands, float32 accumulation ("Convolution, pooling and resize", "Variants":
+// the input window is gathered while the tile is staged; no column matrix).
+//
+// The reduction index is k = (ci, kh, kw) with kw padded to 8: for one (ci, kh)
+// the 8 taps of output column ow read input columns 2*ow - pl + 0..7, which are 8
+// consecutive halves of one staged input row.  So an MFMA operand fragment (8
+// consecutive k of one output pixel) is four 4-byte LDS reads of a row, with no
+// column matrix and no per-element gather.  The weight matrix, laid out the same
+// way (tap kw = 7 is zero), is loaded once into registers.
+//
+//  * A workgroup owns a band of output rows of one image and up to 64 output
+//    channels.  Input rows live in a ring of LDS rows per channel; output row oh
+//    needs input rows 2*oh - pt .. 2*oh - pt + KH - 1, so each new output row
+//    brings in only 2 new input rows, loaded (16-byte reads) while the previous
+//    row multiplies.  Rows above or below the image are zero rows; columns
+//    outside it stay zero from the start.
+//  * MFMA v_mfma_f32_32x32x16_f16: A = 32 output pixels x 16 k (two (ci, kh)
+//    groups), B = 16 k x 32 output channels.  With 64 channels a wave owns one
+//    32-channel block and two 32-pixel blocks of the row; with 32 channels, one
+//    pixel block (rows of at most 128 outputs).
+//  * Epilogue: bias and activation in float32, float16 into an LDS row tile
+//    [channel][pixel], then whole output rows leave with 16-byte stores.
+// Per output the sum runs over (ci, kh) groups in pairs, each pair inside one
+// MFMA; the order is fixed by the shape.
+#include <type_traits>
+
+#include "epilogue.h"
+#include "internal.h"
+
+namespace convfwd {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int RB_RING = 16;        // input rows kept per channel (power of two)
+constexpr int RB_MAXST = 12;       // MFMA k-steps (pairs of (ci, kh) groups) at most
+constexpr int RB_OPITCH = 128 * 2 + 16;  // LDS bytes per output-tile row (float16)
+constexpr int RB_FILL = 4;         // items per thread for the first KH rows (<= 1024 items)
+constexpr int RB_NSTV = 64 * 16 / 256;  // output vectors per thread and row (<= 64 x 128)
+
+}  // namespace
+
+template <int CB, bool VEC>
+__global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_rb[];
+  // ring: [ci][slot][rp halves]; output tile [64][RB_OPITCH bytes]; bias [64]
+  _Float16* ring = reinterpret_cast<_Float16*>(smem_rb);
+  unsigned char* otile = smem_rb + a.ring_bytes;
+  float* bsm = reinterpret_cast<float*>(otile + 64 * RB_OPITCH);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rp = a.rpitch;  // halves per ring row (even)
+
+  // work: (image, channel tile, band of output rows)
+  int bid = blockIdx.x;
+  const int band = bid % a.n_band;
+  bid /= a.n_band;
+  const int ct = bid % a.n_ct;
+  const int n = bid / a.n_ct;
+  const int co0 = ct * 64;
+  const int r0 = band * a.band_rows;
+  const int r1 = min(r0 + a.band_rows, a.ho);
+
+  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x) + (long long)n * a.c_in * a.h * a.w;
+  const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt);
+  static_assert(64 * 2 * RB_MAXST * 8 <= 64 * 1024, "weights staging");
+
+  // ---- wave roles: channel block cbw; CB pixel blocks pb0 .. pb0 + CB - 1 of 32 ----
+  const int cbw = CB == 2 ? (wave & 1) : 0;
+  const int pb0 = CB == 2 ? 2 * (wave >> 1) : wave;
+  // ---- weights: B fragment of k-step st: lane l holds the 8 taps of group
+  // g = 2 st + l / 32 for output channel co0 + 32 cbw + l % 32 ----
+  const int groups = a.c_in * a.kh;  // (ci, kh) groups
+  // the tile's weights ([<= 64 channels][groups * kw] contiguous) pass through the
+  // ring area with coalesced 16-byte reads when aligned, element reads otherwise
+  {
+    const int per_co = groups * a.kw;
+    const int cn = min(64, a.c_out - co0);
+    const int total = cn * per_co;  // halves
+    _Float16* wl = ring;
+    const _Float16* src = w + (long long)co0 * per_co;
+    if (a.wvec) {  // w 16-byte aligned and the tile's run a whole number of vectors
+      for (int q = tid; q < total / 8; q += 256)
+        reinterpret_cast<u32x4_t*>(wl)[q] = *reinterpret_cast<const u32x4_t*>(src + 8 * q);
+    } else {
+      for (int q = tid; q < total; q += 256) wl[q] = src[q];
+    }
+  }
+  __syncthreads();
+  u32x4_t wf[RB_MAXST];
+#pragma unroll
+  for (int st = 0; st < RB_MAXST; ++st) {
+    const int g = 2 * st + (lane >> 5);
+    const int cl = 32 * cbw + (lane & 31);  // channel within the tile
+    const bool okg = g < groups && co0 + cl < a.c_out;
+    const _Float16* wrow = ring + (okg ? cl * (groups * a.kw) + g * a.kw : 0);
+    half8_t v;
+#pragma unroll
+    for (int kw = 0; kw < 8; ++kw) v[kw] = (okg && kw < a.kw) ? wrow[min(kw, a.kw - 1)] : (_Float16)0.0f;
+    wf[st] = __builtin_bit_cast(u32x4_t, v);
+  }
+  __syncthreads();  // the ring area is zeroed next
+  if (tid < 64) bsm[tid] = (a.bias && co0 + tid < a.c_out)
+                               ? (float)static_cast<const _Float16*>(a.bias)[co0 + tid] : 0.0f;
+
+  // zero the ring: columns outside the image are never written again
+  for (int i = tid; i < a.ring_bytes / 16; i += 256)
+    reinterpret_cast<u32x4_t*>(smem_rb)[i] = u32x4_t{0, 0, 0, 0};
+  __syncthreads();
+
+  // ---- input rows: item = (row r of a batch of rows, channel, 8-column vector) ----
+  const int nv = (a.w + 7) / 8;  // vectors per input row
+  // one item of the batch of rows starting at input row ir0 (clamped into the
+  // batch and the image; rows outside the image read as zero)
+  auto load_item = [&](int ir0, int q, int items) __attribute__((always_inline)) {
+    q = min(q, items - 1);
+    const int v = q % nv, rc = q / nv;
+    const int ci = rc % a.c_in, r = rc / a.c_in;
+    const int ir = ir0 + r;
+    const _Float16* src = x + ((long long)ci * a.h + min(max(ir, 0), a.h - 1)) * a.w + 8 * v;
+    u32x4_t d;
+    if constexpr (VEC) {  // w % 8 == 0, 16-byte aligned rows
+      d = *reinterpret_cast<const u32x4_t*>(src);
+    } else {
+      half8_t h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = src[min(e, a.w - 1 - 8 * v)];
+      d = __builtin_bit_cast(u32x4_t, h);
+    }
+    return (ir >= 0 && ir < a.h) ? d : u32x4_t{0, 0, 0, 0};
+  };
+  // ...and its store into the ring (input column c at ring column c + pl)
+  auto store_item = [&](int ir0, int q, int items, u32x4_t d) __attribute__((always_inline)) {
+    if (q < items) {
+      const int v = q % nv, rc = q / nv;
+      const int ci = rc % a.c_in, r = rc / a.c_in;
+      const int slot = (ir0 + r) & (RB_RING - 1);
+      _Float16* dst = ring + (ci * RB_RING + slot) * rp + a.pl + 8 * v;
+      const half8_t h = __builtin_bit_cast(half8_t, d);
+      const int cnt = min(8, a.w - 8 * v);  // the row's last vector may be partial
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < cnt) dst[e] = h[e];
+    }
+  };
+  // first input row of the sh new rows that output row o brings in
+  auto new_rows = [&](int o) __attribute__((always_inline)) { return o * a.sh - a.pt + a.kh - a.sh; };
+  const int step_items = a.sh * a.c_in * nv;  // <= 256: one item per thread
+
+  // the KH rows of the band's first output row (at most RB_FILL items per thread)
+  {
+    const int first = r0 * a.sh - a.pt;
+    const int items = a.kh * a.c_in * nv;
+    u32x4_t t[RB_FILL];
+#pragma unroll
+    for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + 256 * k, items);
+#pragma unroll
+    for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + 256 * k, items, t[k]);
+  }
+  // prefetch ring of three: the new rows of output row o sit in lr[(o - r0) % 3]
+  u32x4_t lr[3];
+  lr[1] = load_item(new_rows(r0 + 1), tid, step_items);
+  lr[2] = load_item(new_rows(r0 + 2), tid, step_items);
+  lr[0] = load_item(new_rows(r0 + 3), tid, step_items);
+
+  const int half = lane >> 5;  // k-group parity of this lane
+  // per k-step: this lane's (ci, kh) group as a ring row base and a tap row
+  int gbase[RB_MAXST], gkh[RB_MAXST];
+#pragma unroll
+  for (int st = 0; st < RB_MAXST; ++st) {
+    const int g = min(2 * st + half, groups - 1);  // the padded group multiplies zero weights
+    const int ci = g / a.kh;
+    gkh[st] = g - ci * a.kh;
+    gbase[st] = ci * RB_RING * rp;
+  }
+  int pxo[CB];  // ring column offset of this lane's output column in each pixel block
+#pragma unroll
+  for (int j = 0; j < CB; ++j) pxo[j] = 2 * min(32 * (pb0 + j) + (lane & 31), a.wo - 1);
+  const _Float16* __restrict__ res = static_cast<const _Float16*>(a.res);
+  _Float16* y = static_cast<_Float16*>(a.y);
+  const long long ybase = ((long long)n * a.c_out + co0) * a.ho * a.wo;
+
+  // one output row; J = (oh - r0) % 3 at compile time picks the prefetch registers
+  auto row = [&](int oh, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    // the next output row's new input rows go to ring slots this row does not use
+    store_item(new_rows(oh + 1), tid, step_items, lr[(J + 1) % 3]);
+    __syncthreads();  // rows of oh present; the previous row's tile has left
+    // those registers now take the rows of output row oh + 4 (three rows ahead)
+    lr[(J + 1) % 3] = load_item(new_rows(oh + 4), tid, step_items);
+
+    // ---- MFMA: k-step st covers groups 2 st (lanes 0-31) and 2 st + 1 (32-63) ----
+    floatx16_t acc[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+    const int ir_base = oh * a.sh - a.pt;
+#pragma unroll
+    for (int st = 0; st < RB_MAXST; ++st) {
+      if (2 * st >= groups) continue;  // uniform
+      const int slot = (ir_base + gkh[st]) & (RB_RING - 1);
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const unsigned int* src =
+            reinterpret_cast<const unsigned int*>(ring + gbase[st] + slot * rp + pxo[j]);
+        u32x4_t f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = src[e];
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, f),
+                                                        __builtin_bit_cast(half8_t, wf[st]),
+                                                        acc[j], 0, 0, 0);
+      }
+    }
+
+    // ---- epilogue: lane l holds channel 32 cbw + l % 32 and, in pixel block
+    // pb0 + j, output columns 32 (pb0 + j) + 8 (i / 4) + 4 (l / 32) + i % 4 ----
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = 32 * cbw + (lane & 31);
+      const int pxb = 32 * (pb0 + j);
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float t = acc[j][i];
+        if (a.bias) t = t + bsm[c];
+        v[i] = t;
+      }
+      if (res) {  // residual read in the fragment layout (clamped, before any store)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ow = min(pxb + 8 * (i / 4) + 4 * half + (i % 4), a.wo - 1);
+          v[i] = v[i] + (float)res[ybase + ((long long)min(c, a.c_out - co0 - 1) * a.ho + oh) * a.wo + ow];
+        }
+      }
+      act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half4_t h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[4 * q + i];
+        *reinterpret_cast<half4_t*>(otile + c * RB_OPITCH + 2 * (pxb + 8 * q + 4 * half)) = h;
+      }
+    }
+    __syncthreads();
+    // ---- whole rows of the tile: 16-byte vectors of 8 output columns ----
+    const int cn = min(32 * CB, a.c_out - co0);
+    const int vpr = (a.wo + 7) / 8;
+    if constexpr (VEC) {  // wo % 8 == 0: whole vectors; past the end the last one
+      // repeats (same value, same address), so the store count is fixed
+#pragma unroll
+      for (int k = 0; k < RB_NSTV; ++k) {
+        const int q = min(tid + 256 * k, cn * vpr - 1);
+        const int c = q / vpr, v = q - (q / vpr) * vpr;
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + c * RB_OPITCH + 16 * v);
+        *reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v) = d;
+      }
+    } else {
+      for (int q = tid; q < cn * vpr; q += 256) {
+        const int c = q / vpr, v = q - (q / vpr) * vpr;
+        const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(
+                                                          otile + c * RB_OPITCH + 16 * v));
+        _Float16* dst = y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v;
+        const int cnt = min(8, a.wo - 8 * v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < cnt) dst[e] = h[e];
+      }
+    }
+  };
+
+  for (int oh = r0; oh < r1; oh += 3) {  // unrolled by three: prefetch sets at compile time
+    row(oh, std::integral_constant<int, 0>{});
+    if (oh + 1 >= r1) break;
+    row(oh + 1, std::integral_constant<int, 1>{});
+    if (oh + 2 >= r1) break;
+    row(oh + 2, std::integral_constant<int, 2>{});
+  }
+}
+
+hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.n * a.n_ct * a.n_band));
+  const size_t lds = (size_t)a.ring_bytes + 64 * RB_OPITCH + 64 * 4;
+  const bool two = a.c_out > 32;
+  if (a.vec) {
+    if (two) hipLaunchKernelGGL((rowband_kernel<2, true>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<1, true>), grid, dim3(256), lds, s, a);
+  } else {
+    if (two) hipLaunchKernelGGL((rowband_kernel<2, false>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<1, false>), grid, dim3(256), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace convfwd

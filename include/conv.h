@@ -101,8 +101,11 @@ typedef enum {
     CONV_VARIANT_POINTWISE_GEMM = 2,    /* 1x1, stride 1, no pad: GEMM on x as it lies */
     CONV_VARIANT_DEPTHWISE_DIRECT = 3,  /* one input channel per group, direct, no MFMA */
     CONV_VARIANT_TRANSPOSE_GEMM_COL2IM = 4, /* ConvTranspose: GEMM + gathering col2im */
-    CONV_VARIANT_IMPLICIT_GEMM_HALO = 5 /* implicit GEMM with the input halo tile staged
-                                           once per channel chunk and reused for all taps */
+    CONV_VARIANT_IMPLICIT_GEMM_HALO = 5, /* implicit GEMM with the input halo tile staged
+                                            once per channel chunk and reused for all taps */
+    CONV_VARIANT_IMPLICIT_GEMM_ROWBAND = 6 /* stride 2, few input channels (image stems):
+                                              a ring of staged input rows per output-row
+                                              band, kw taps read as consecutive halves */
 } conv_variant;
 
 /* The problem: shape, explicit pads, stride, dilation, groups, fused activation

@@ -211,6 +211,41 @@ POINTWISE_CASES = [
 ]
 
 
+ROWBAND_CASES = [
+    # (geometry, bias, residual): stem-like stride-2 layers with few input channels
+    (oracle.Geom(2, 3, 30, 28, 64, 7, 7, sh=2, sw=2, pt=3, pl=3, pb=3, pr=3, act="relu"), True, False),
+    (oracle.Geom(3, 3, 17, 23, 40, 7, 7, sh=2, sw=2, pt=3, pl=3, pb=3, pr=3), True, True),
+    (oracle.Geom(2, 4, 20, 16, 24, 5, 5, sh=2, sw=2, pt=2, pl=2, pb=1, pr=2, act="hard_swish"),
+     False, True),
+    (oracle.Geom(1, 8, 33, 40, 64, 3, 3, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1, act="sigmoid"), True, False),
+    (oracle.Geom(2, 3, 64, 64, 128, 7, 7, sh=2, sw=2, pt=3, pl=3, pb=3, pr=3, act="relu"), True, False),
+]
+
+
+@pytest.mark.parametrize("case", ROWBAND_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}k{c[0].kh}")
+def test_rowband_variant(case):
+    """The row-band stride-2 kernel against the oracle; identical bits with
+    misaligned operands and with y aliasing the residual."""
+    g, has_b, has_r = case
+    _say(f"[rowband] {g}")
+    from gpu_harness import problem_from
+    assert cf.conv_describe_variant(problem_from(g), "f16").startswith("implicit_gemm_rowband")
+    rng = np.random.default_rng(g.c_in * 7 + g.h + 5 * g.c_out)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, g.c_in, g.kh, g.kw)) *
+         np.sqrt(2.0 / (g.c_in * g.kh * g.kw))).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f16", x, w, b, r)
+    assert_parity("f16", y, yr, sr, b, r, what="rowband", act=g.act)
+    y2 = run_gpu(g, "f16", x, w, b, r, offsets=(1, 3, 1, 1, 1))
+    assert np.array_equal(_bits(y), _bits(y2))
+    if has_r:
+        y3 = run_gpu(g, "f16", x, w, b, r, offsets=(0, 0, 0, 8, 8), alias_residual=True)
+        assert np.array_equal(_bits(y), _bits(y3))
+
+
 @pytest.mark.parametrize("case", POINTWISE_CASES, ids=lambda c: f"{c[0].c_in}to{c[0].c_out}x{c[0].h}x{c[0].w}")
 def test_pointwise_variant(case):
     """The 1x1 GEMM on x as it lies against the oracle; identical bits with

@@ -260,8 +260,8 @@ def test_variant_names_for_workloads():
     assert names["w4b_depthwise3x3s2_f32"].startswith("depthwise_direct.f32")
     assert names["w5b_convtranspose2x2s2_f16"].startswith("transpose_gemm_col2im.f16")
     assert names["w3b_pointwise_f16"].startswith("pointwise_gemm.f16")
-    for n in ("w1_conv3x3_f32", "w2_bottleneck3x3_f16", "w3a_stem7x7s2_f16",
-              "w5a_dilated_grouped_f16"):
+    assert names["w3a_stem7x7s2_f16"].startswith("implicit_gemm_rowband.f16")
+    for n in ("w1_conv3x3_f32", "w2_bottleneck3x3_f16", "w5a_dilated_grouped_f16"):
         assert names[n].startswith("implicit_gemm"), names[n]
     buf_small = cf.conv_describe_variant  # too-small buffer path
     import ctypes
