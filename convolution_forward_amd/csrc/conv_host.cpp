@@ -145,6 +145,7 @@ struct Plan {
   int dw_lm;      // one-wave path: LDS column of input column 0
   int pw_tc;      // pointwise: output channels per tile
   int rb_band_rows;  // row band: output rows per workgroup
+  int ct_fused;      // transpose: kernel = stride = 2 taps gathered by the GEMM epilogue
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -183,12 +184,34 @@ bool rowband_applicable(const Geo& g, int dtype) {
          g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024;
 }
 
+// Work items (tile, 64-channel chunk) of the pointwise kernel; its int item
+// arithmetic needs them well below 2^31.
+int64_t pw_items(int64_t n, int64_t pixel_tiles, int64_t channel_tiles, int64_t ci) {
+  int64_t t;
+  if (!mul_ok(n, pixel_tiles, &t) || !mul_ok(t, channel_tiles, &t) ||
+      !mul_ok(t, ceil_div(ci, 64), &t))
+    return INT64_MAX;
+  return t;
+}
+
 // Pointwise GEMM on x as it lies: 1x1, stride 1, no padding, one group, float16,
 // whole channel octets and planes of whole 4-pixel groups.
 bool pointwise_applicable(const Geo& g, int dtype) {
   return !g.transpose && dtype == CONV_F16 && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
          g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
-         (g.h * g.w) % 4 == 0 && g.h * g.w >= 4;
+         (g.h * g.w) % 4 == 0 && g.h * g.w >= 4 &&
+         pw_items(g.n, ceil_div(g.h * g.w, 128), ceil_div(g.co, 64), g.ci) < (1LL << 30);
+}
+
+// ConvTranspose whose kernel equals its stride of 2 with no padding: each output
+// takes exactly one tap, so the GEMM's epilogue can scatter its tile straight
+// into y (float16, one group, no residual, input rows of whole 4-pixel groups
+// that fit a 128-pixel tile).
+bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
+  return g.transpose && dtype == CONV_F16 && g.g == 1 && g.kh == 2 && g.kw == 2 && g.sh == 2 &&
+         g.sw == 2 && g.dh == 1 && g.dw == 1 && g.pt == 0 && g.pl == 0 && g.pb == 0 &&
+         g.pr == 0 && g.oph == 0 && g.opw == 0 && !residual && g.w % 4 == 0 && g.w <= 128 &&
+         pw_items(g.n, ceil_div(g.h * g.w, (128 / g.w) * g.w), ceil_div(4 * g.co, 128), g.ci) < (1LL << 30);
 }
 
 // Depthwise output tile: whole plane when the staged input fits, else smaller
@@ -349,6 +372,15 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (v != CONV_VARIANT_AUTO && v != CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
     pl->variant = CONV_VARIANT_TRANSPOSE_GEMM_COL2IM;
     if (p->split_override > 1) return CONV_ERR_ARG;
+    if (transpose_fused_applicable(g, dtype, p->has_residual == 1)) {
+      pl->ct_fused = 1;
+      // 64-row tiles when 128-row ones would leave compute units idle
+      const int64_t tiles128 =
+          g.n * ceil_div(g.h * g.w, (128 / g.w) * g.w) * ceil_div(4 * g.co, 128);
+      pl->pw_tc = tiles128 < device_cus() ? 64 : 128;
+      pl->scratch_whole = 0;
+      return CONV_OK;
+    }
     pl->scratch_per_image = (uint64_t)(g.co * g.kh * g.kw * g.h * g.w) * 4u;
     const int ept = dtype == CONV_F16 ? 8 : 4;
     pl->ksteps = (int)ceil_div(g.cig, 4 * ept);
@@ -612,15 +644,14 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
       a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
       a.n_pt = (int)ceil_div(g.h * g.w, 128);
+      a.tp = 128;
       a.tc = pl.pw_tc;
       a.n_ct = (int)ceil_div(g.co, a.tc);
       a.ntiles = (int)((int64_t)cn * a.n_pt * a.n_ct);
       a.nchunks = (int)ceil_div(g.ci, 64);
-      a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0;
-      a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0;
-      a.ovec = reinterpret_cast<uintptr_t>(yc) % 8 == 0 &&
-               (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0);
-      a.o16 = reinterpret_cast<uintptr_t>(yc) % 16 == 0 && (g.h * g.w) % 8 == 0;
+      a.vec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && reinterpret_cast<uintptr_t>(wb) % 16 == 0 &&
+              reinterpret_cast<uintptr_t>(yc) % 16 == 0 &&
+              (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0) && (g.h * g.w) % 8 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_pointwise(a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
@@ -668,6 +699,26 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         r.act = p->activation; r.alpha = p->act_alpha; r.beta = p->act_beta;
         e = launch_reduce(dt, r, s);
       }
+    } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM && pl.ct_fused) {
+      // GEMM rows m = 4 co + 2 kh + kw over whole input rows of one image; the
+      // epilogue writes y[n][co][2h + kh][2w + kw] directly
+      PwArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = nullptr; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)(4 * g.co);
+      a.ct = 1; a.w_in = (int)g.w;
+      a.ct_rows = (int)(128 / g.w);
+      a.tp = a.ct_rows * (int)g.w;
+      a.mg_vpr = make_magic((unsigned)(g.w / 4));
+      a.mg_rows = make_magic((unsigned)a.ct_rows);
+      a.n_pt = (int)ceil_div(g.h * g.w, a.tp);
+      a.tc = pl.pw_tc;
+      a.n_ct = (int)ceil_div(4 * g.co, a.tc);
+      a.ntiles = (int)((int64_t)cn * a.n_pt * a.n_ct);
+      a.nchunks = (int)ceil_div(g.ci, 64);
+      a.vec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && reinterpret_cast<uintptr_t>(wb) % 8 == 0 &&
+              reinterpret_cast<uintptr_t>(yc) % 16 == 0;
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_pointwise(a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) {
       // GEMM: cols[n][g*M + m][h][w] = sum_ci w[g*cig + ci][m] * x[n][g*cig + ci][h][w],
       // M = (Cout/G)*KH*KW; the matrix kernel runs it as a 1x1 conv with transposed
@@ -792,6 +843,12 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND:
       snprintf(tmp, sizeof tmp, "implicit_gemm_rowband.%s.rows%d", dn, pl.rb_band_rows);
+      break;
+    case CONV_VARIANT_TRANSPOSE_GEMM_COL2IM:
+      if (pl.ct_fused)
+        snprintf(tmp, sizeof tmp, "transpose_gemm_col2im.%s.fused_k2s2.t128x%d", dn, pl.pw_tc);
+      else
+        snprintf(tmp, sizeof tmp, "transpose_gemm_col2im.%s", dn);
       break;
     case CONV_VARIANT_DEPTHWISE_DIRECT:
       if (pl.dw_wave)

@@ -16,6 +16,24 @@ enum OutMode {
   OUT_RAW = 1     // raw float32 sums into a plane of the scratch (split k, ConvT columns)
 };
 
+// Division by a launch constant d >= 1 as multiply-high, add and shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1):
+// floor(n / d) = (umulhi(m, n) + n) >> l, exact for every 0 <= n < 2^31.
+struct Magic {
+  unsigned m;
+  int s;
+};
+
+inline Magic make_magic(unsigned d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  Magic g;
+  g.m = (unsigned)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  g.s = l;
+  return g;
+}
+
 // Geometry and operands of one implicit-GEMM launch (one image chunk).
 // Element pointers already include the problem's element offsets.
 struct IgemmArgs {
@@ -68,17 +86,23 @@ struct HaloArgs {
 
 // Pointwise (1x1, stride 1, no padding, one group) GEMM on x as it lies.
 struct PwArgs {
-  const void* x;
-  const void* wt;
-  const void* bias;
-  const void* res;
+  const void* x;         // [n][c_in][hw]
+  const void* wt;        // [c_out][c_in], or [c_in][c_out] with ct
+  const void* bias;      // nullptr when absent
+  const void* res;       // nullptr when absent (always with ct)
   void* y;
-  int n, c_in, hw, c_out;
-  int n_pt, n_ct;        // 128-pixel tiles per image, 128-channel tiles
+  int n, c_in, hw, c_out;  // c_out: GEMM rows (4 output channels each with ct)
+  int n_pt, n_ct;        // pixel tiles per image, row tiles
   int ntiles, nchunks;   // tiles in this chunk of images, 64-channel chunks of c_in
-  int xvec, wvec, ovec;  // x 8-byte, w 16-byte, y / residual 8-byte aligned
-  int o16;               // y 16-byte aligned and h * w % 8 == 0
-  int tc;                // output channels per tile: 64 or 128
+  int vec;               // x 8-byte, w 16-byte (ct: 8-byte), y 16-byte, residual
+                         // 8-byte aligned and hw % 8 == 0 (ct: w_in % 4 == 0)
+  int tc;                // GEMM rows per tile: 64 or 128
+  int tp;                // pixels per tile (<= 128)
+  int ct;                // ConvTranspose, kernel = stride = 2, no padding: GEMM rows are
+                         // (co, kh, kw), weights [c_in][c_out], outputs scattered into y
+  int w_in;              // ct: input row width (the tile holds whole input rows)
+  int ct_rows;           // ct: input rows per tile, tp / w_in
+  Magic mg_vpr, mg_rows; // ct: divisions by w_in / 4 and by ct_rows
   int act;
   float alpha, beta;
 };
@@ -100,24 +124,6 @@ struct RowbandArgs {
   int act;
   float alpha, beta;
 };
-
-// Division by a launch constant d >= 1 as multiply-high, add and shift
-// (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994, with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1):
-// floor(n / d) = (umulhi(m, n) + n) >> l, exact for every 0 <= n < 2^31.
-struct Magic {
-  unsigned m;
-  int s;
-};
-
-inline Magic make_magic(unsigned d) {
-  int l = 0;
-  while ((1ull << l) < d) ++l;
-  Magic g;
-  g.m = (unsigned)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
-  g.s = l;
-  return g;
-}
 
 struct DepthwiseArgs {
   const void* x;

@@ -362,6 +362,40 @@ def test_conv_transpose_shapes(case):
                           y1.view(np.uint16 if dtype == "f16" else np.uint32))
 
 
+CONVT_FUSED_CASES = [
+    # (geometry, bias): kernel = stride = 2, no padding -- the GEMM epilogue
+    # scatters straight into y.  Channel chunks with tails, channel tiles with
+    # tails, tiles of several / one input rows, ragged last tiles.
+    (oracle.Geom(1, 256, 40, 40, 64, 2, 2, sh=2, sw=2), True),
+    (oracle.Geom(2, 24, 6, 12, 10, 2, 2, sh=2, sw=2, act="relu"), True),
+    (oracle.Geom(3, 72, 9, 36, 6, 2, 2, sh=2, sw=2, act="silu"), False),
+    (oracle.Geom(1, 16, 3, 128, 66, 2, 2, sh=2, sw=2, act="sigmoid"), True),
+    (oracle.Geom(2, 8, 5, 4, 2, 2, 2, sh=2, sw=2, act="hard_swish"), True),
+    (oracle.Geom(2, 130, 7, 20, 33, 2, 2, sh=2, sw=2, act="tanh"), True),
+]
+
+
+@pytest.mark.parametrize("case", CONVT_FUSED_CASES, ids=lambda c: f"{c[0].c_in}to{c[0].c_out}x{c[0].h}x{c[0].w}")
+def test_conv_transpose_fused_k2s2(case):
+    """ConvTranspose with kernel = stride = 2 through the fused GEMM + gather
+    kernel against the oracle; identical bits with misaligned operands (element
+    loads and stores)."""
+    g, has_b = case
+    _say(f"[convt-fused] {g}")
+    from gpu_harness import problem_from
+    name = cf.conv_describe_variant(problem_from(g, transpose=True), "f16")
+    assert "fused_k2s2" in name, name
+    rng = np.random.default_rng(g.c_in * 5 + g.w + 3 * g.c_out)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_in, g.c_out, 2, 2)) * np.sqrt(2.0 / g.c_in)).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    yr, sr = oracle.conv_transpose2d(g, x, w, b, None)
+    y = run_gpu(g, "f16", x, w, b, None, transpose=True)
+    assert_parity("f16", y, yr, sr, b, None, what="convt-fused", act=g.act)
+    y2 = run_gpu(g, "f16", x, w, b, None, transpose=True, offsets=(3, 1, 1, 0, 1))
+    assert np.array_equal(_bits(y), _bits(y2))
+
+
 def test_convt_checkerboard_counts():
     """All-ones input and kernel, stride 2 ('Convolutions' exercise 3): exact."""
     for k in (3, 4):

@@ -226,10 +226,13 @@ def test_scratch_rules():
     # forced whole-k needs no scratch
     p1 = cf.make_problem(2, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1), splits=1)
     assert cf.conv_scratch_size(p1, "f32") == (0, 0)
-    # ConvTranspose columns: c_out*kh*kw*h*w floats per image
+    # ConvTranspose columns: c_out*kh*kw*h*w floats per image (float32 here; the
+    # float16 kernel = stride = 2 case is fused and needs none)
     pt = cf.make_problem(8, 256, 40, 40, 64, 2, 2, stride=(2, 2), transpose=True)
-    assert cf.conv_scratch_size(pt, "f16") == (8 * 64 * 4 * 1600 * 4, 64 * 4 * 1600 * 4)
-    assert _fwd(pt, transpose=True) == cf.CONV_ERR_SCRATCH
+    assert cf.conv_scratch_size(pt, "f32") == (8 * 64 * 4 * 1600 * 4, 64 * 4 * 1600 * 4)
+    assert cf.conv_scratch_size(pt, "f16") == (0, 0)
+    assert _fwd(pt, "f32", transpose=True) == cf.CONV_ERR_SCRATCH
+    assert _fwd(pt, "f16", transpose=True) == cf.CONV_OK
     # depthwise and unsplit implicit need none
     for l in workloads.LAYERS:
         if l.transpose:
@@ -258,7 +261,7 @@ def test_variant_names_for_workloads():
         names[l.name] = cf.conv_describe_variant(q, l.dtype)
     assert names["w4a_depthwise5x5_f32"].startswith("depthwise_direct.f32")
     assert names["w4b_depthwise3x3s2_f32"].startswith("depthwise_direct.f32")
-    assert names["w5b_convtranspose2x2s2_f16"].startswith("transpose_gemm_col2im.f16")
+    assert names["w5b_convtranspose2x2s2_f16"].startswith("transpose_gemm_col2im.f16.fused_k2s2")
     assert names["w3b_pointwise_f16"].startswith("pointwise_gemm.f16")
     assert names["w3a_stem7x7s2_f16"].startswith("implicit_gemm_rowband.f16")
     for n in ("w1_conv3x3_f32", "w2_bottleneck3x3_f16", "w5a_dilated_grouped_f16"):
@@ -269,6 +272,30 @@ def test_variant_names_for_workloads():
     q = cf.make_problem(1, 3, 32, 32, 16, 3, 3, pads=(1, 1, 1, 1))
     assert cf.lib().conv_describe_variant(ctypes.byref(q), 0, b, 4) == cf.CONV_ERR_ARG
     assert buf_small(q, "f32")
+
+
+def test_convt_fused_plan_rules():
+    """Kernel = stride = 2 without padding, float16, one group, no residual takes
+    the fused GEMM + gather path with no scratch; anything else keeps the float32
+    column matrix."""
+    base = dict(stride=(2, 2), transpose=True)
+    for co in (32, 31):
+        p = cf.make_problem(2, 64, 10, 12, co, 2, 2, **base)
+        assert "fused_k2s2" in cf.conv_describe_variant(p, "f16")
+        assert cf.conv_scratch_size(p, "f16") == (0, 0)
+    unfused = [
+        (cf.make_problem(2, 64, 10, 12, 32, 2, 2, **base), "f32"),
+        (cf.make_problem(2, 64, 10, 12, 32, 2, 2, residual=True, **base), "f16"),
+        (cf.make_problem(2, 64, 10, 12, 32, 2, 2, groups=2, **base), "f16"),
+        (cf.make_problem(2, 64, 10, 10, 32, 2, 2, **base), "f16"),        # w % 4 != 0
+        (cf.make_problem(2, 64, 10, 132, 32, 2, 2, **base), "f16"),       # w > 128
+        (cf.make_problem(2, 64, 10, 12, 32, 3, 3, **base), "f16"),
+        (cf.make_problem(2, 64, 10, 12, 32, 2, 2, pads=(1, 1, 1, 1), **base), "f16"),
+    ]
+    for q, dt in unfused:
+        d = cf.conv_describe_variant(q, dt)
+        assert d.startswith("transpose_gemm_col2im") and "fused" not in d, d
+        assert cf.conv_scratch_size(q, dt)[0] > 0
 
 
 def test_status_strings():
