@@ -668,6 +668,8 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0;
       a.ovec = reinterpret_cast<uintptr_t>(yc) % 8 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 8 == 0) &&
                (g.ho * g.wo) % 4 == 0;
+      a.o2 = reinterpret_cast<uintptr_t>(yc) % 4 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 4 == 0) &&
+             g.wo % 2 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = pl.halo.rowshift ? launch_rowshift(a, s) : launch_halo(a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {

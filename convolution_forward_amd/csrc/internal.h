@@ -80,6 +80,7 @@ struct HaloArgs {
   int wvec;              // weight rows may be read 16 bytes at a time
   int xvec;              // input planes may be read 8 bytes at a time
   int ovec;              // output / residual planes may be written / read 8 bytes at a time
+  int o2;                // row-shift kernel: y and residual 4-byte aligned, wo even
   int act;
   float alpha, beta;
 };

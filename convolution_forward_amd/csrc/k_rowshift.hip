@@ -44,6 +44,7 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
@@ -61,7 +62,8 @@ struct RsLayout {
   static constexpr int IN_BYTES = NPOS * RS_CH * 2;  // 8 octets of 16 bytes per position
   static constexpr int STAGE = IN_BYTES + RS_WBYTES;
   static constexpr int SINK = 2 * STAGE;             // 16 bytes that dead staging writes hit
-  static constexpr int TOTAL = 2 * STAGE + 16;        // double buffer + sink
+  static constexpr int BIAS = 2 * STAGE + 16;        // 32 bias floats
+  static constexpr int TOTAL = BIAS + 32 * 4;         // double buffer + sink + bias
   static constexpr int MAX_GROUPS = 16 * 16 / 4;     // 4-pixel groups of an input plane
   static constexpr int NI = (8 * MAX_GROUPS + 255) / 256;
   static constexpr int NW = (32 * 72 + 255) / 256;   // 16-byte weight vectors per thread
@@ -80,6 +82,16 @@ __device__ __forceinline__ u32x4_t row_shift(u32x4_t v) {
   return r;
 }
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes); the
+// operands are made wave-uniform so the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
@@ -91,10 +103,9 @@ template <int R, bool XV, bool WV>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef RsLayout<R> L;
   constexpr int NP = L::NP;
-  // epilogue areas (4 waves x 32 channels x (R * 14 + 1) floats) and the bias
-  // slots below the sink reuse the two stage buffers
-  // plus one junk float per thread and the bias slots below the sink
-  static_assert(4 * 32 * (R * 14 + 1) * 4 + 256 * 4 + 32 * 4 <= L::SINK, "epilogue does not fit");
+  // the epilogue's partial sums (4 waves x NP row pairs x 16 floats x 64 lanes)
+  // reuse the two stage buffers
+  static_assert(4 * NP * 16 * 64 * 4 <= L::SINK, "epilogue does not fit");
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
   const int tid = threadIdx.x;
@@ -272,20 +283,47 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     }
   };
 
+  // ---- epilogue items: item it = (channel co, output row oh, column quad) with
+  // the quad fastest, then the row (R rows), then the channel; thread t takes
+  // items t + 256 k, k < R / 2.  An item's outputs are columns 4 quad .. 4 quad + 3
+  // of one output row: consecutive lanes cover consecutive 8-byte pieces of y. ----
+  static_assert(R % 2 == 0, "items per thread");
+  constexpr int KI = R / 2;  // 32 x R x 4 items over 256 threads
   const int howo = a.ho * a.wo;
-  const int total_c = min(32, a.cog - co0) * howo;  // outputs of this tile
   const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
   const _Float16* res = static_cast<const _Float16*>(a.res);
-  constexpr int MAXQ = (32 * 14 * 14 / 4 + 255) / 256;  // 4-output items per thread at most
-  constexpr int EPT = (32 * 14 * 14 + 255) / 256;       // single outputs per thread at most
-  const bool vec = a.ovec;  // howo % 4 == 0 and y / residual 8-byte aligned (uniform)
-  u32x2_t rq[MAXQ];         // residual (vector path), prefetched during the last step
-  auto load_residual = [&]() __attribute__((always_inline)) {
-    if (res && vec) {  // uniform; clamped items keep every load unconditional
-      const int nq = total_c / 4;
+  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  float* bsm = reinterpret_cast<float*>(smem + L::BIAS);  // the tile's 32 biases
+  const bool pairs = a.o2;  // y / residual 4-byte aligned, wo even (uniform)
+  auto it_co = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) / R; };
+  auto it_oh = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) % R; };
+  const int it_ow = 4 * (tid & 3);  // 256 k % 4 == 0: the same quad for every k
+  auto e_index = [&](int k, int j) __attribute__((always_inline)) {  // flat index in the tile
+    return it_co(k) * howo + it_oh(k) * a.wo + it_ow + j;
+  };
+  auto e_valid = [&](int k, int j) __attribute__((always_inline)) {
+    return co0 + it_co(k) < a.cog && it_oh(k) < a.ho && it_ow + j < a.wo;
+  };
+  // the nearest output (pair: back = 2) inside the tile, by clamped
+  // coordinates: loads of items past the tile stay unconditional and in bounds
+  // (24-bit products: small operands, and no 64-bit multiply-add whose unused
+  // high half could land on a register still being loaded)
+  auto e_clamped = [&](int k, int j, int back) __attribute__((always_inline)) {
+    return (int)(__umul24((unsigned)min(it_co(k), a.cog - 1 - co0), (unsigned)howo) +
+                 __umul24((unsigned)min(it_oh(k), a.ho - 1), (unsigned)a.wo)) +
+           min(it_ow + j, a.wo - back);
+  };
+  unsigned rq[KI][2];  // residual pairs (pair path), prefetched during the last step
+  auto load_epilogue_operands = [&]() __attribute__((always_inline)) {
+    if (res && pairs) {  // uniform
+      // a buffer descriptor over the tile's residual: 32-bit offsets, no 64-bit
+      // address arithmetic between the loads
+      const __amdgpu_buffer_rsrc_t rr = uniform_rsrc(res + obase, min(32, a.cog - co0) * howo * 2);
 #pragma unroll
-      for (int k = 0; k < MAXQ; ++k)
-        rq[k] = *reinterpret_cast<const u32x2_t*>(res + obase + 4 * min(tid + 256 * k, nq - 1));
+      for (int k = 0; k < KI; ++k)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+          rq[k][j2] = __builtin_amdgcn_raw_buffer_load_b32(rr, 2 * e_clamped(k, 2 * j2, 2), 0, 0);
     }
   };
 
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     constexpr int P = decltype(parity)::value;
     constexpr int M = decltype(mode)::value;
     if constexpr (M == 0) load_stage(s + 2, P);  // set P: stage s was stored last step
-    if constexpr (M == 2) load_residual();        // the epilogue's residual
+    if constexpr (M == 2) load_epilogue_operands();  // bias and residual
     // the scheduler must not sink these loads below the multiplications (which
     // would shorten the prefetch to nothing) nor hoist the regrouping of set P^1
     // into them (which waits for that set early)
@@ -312,6 +350,9 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef std::integral_constant<int, 0> LOAD;
   typedef std::integral_constant<int, 1> STORE_ONLY;
   typedef std::integral_constant<int, 2> LAST;
+  // the tile's biases, loaded first (any valid address without bias) and kept
+  // in LDS for the epilogue
+  const _Float16 b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
   load_stage(0, 0);
   load_stage(min(1, nstages - 1), 1);
   // zero both stages' input regions while the first loads fly: padding
@@ -322,6 +363,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   }
   __syncthreads();
   store_stage(0, 0);
+  if (tid < 32) bsm[tid] = (float)b_in;
   __syncthreads();
   int s = 0;
   for (; s + 3 < nstages; s += 2) {  // both steps prefetch a stage
@@ -339,88 +381,76 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     step(s, P0{}, LAST{});
   }
 
-  // ---- each wave's partial sums go to its own [channel][pixel] LDS area; the
-  // epilogue adds the four in wave order, ((w0 + w1) + w2) + w3, and runs in
-  // memory order, 4 contiguous outputs per item (a fragment spans 32 output
-  // planes, so storing from the fragment layout would scatter). ----
-  const int pitch = howo + 1;   // odd channel pitch: a fragment's 32 channels hit distinct banks
-  const int area = 32 * pitch;  // floats per wave area
-  float* part = reinterpret_cast<float*>(smem);
-  float* bsm = reinterpret_cast<float*>(smem + L::SINK) - 32;  // bias of the 32 channels
-  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  // ---- the four waves' partial sums are added through LDS.  Wave w writes its
+  // 16 floats of row pair q as 4 float4 slot groups i4 (accumulator elements
+  // 4 i4 .. 4 i4 + 3: pixels 8 i4 + 4 (l / 32) + 0..3 of the pair, one output
+  // row, 4 consecutive columns); slot S = (4 q + i4) * 64 + l sits at S ^ h,
+  // h = (2 (4 q + i4) + l / 32) % 16, so that both the writes (one slot group,
+  // 64 lanes) and the item reads (one channel, 16 consecutive items) hit
+  // distinct banks.  Each item adds its four waves' float4 in wave order,
+  // ((w0 + w1) + w2) + w3. ----
+  typedef float floatx4_t __attribute__((ext_vector_type(4)));
+  floatx4_t* part = reinterpret_cast<floatx4_t*>(smem);
+  auto slot = [](int q, int i4, int l) __attribute__((always_inline)) {
+    const int sg = 4 * q + i4;
+    return (sg * 64 + l) ^ ((2 * sg + (l >> 5)) & 15);
+  };
 #pragma unroll
   for (int q = 0; q < NP; ++q)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int p = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);  // pixel of the row pair
-      const int oh = 2 * q + p / 16, ow = p % 16;
-      // columns past the row (and rows past the image) go to this lane's junk
-      // slot: no branch, no two lanes on one address
-      const bool ok = oh < a.ho && ow < a.wo;
-      part[ok ? wave * area + (lane & 31) * pitch + oh * a.wo + ow : 4 * area + tid] = acc[q][i];
-    }
-  if (tid < 32) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
+    for (int i4 = 0; i4 < 4; ++i4)
+      part[wave * (NP * 256) + slot(q, i4, lane)] =
+          floatx4_t{acc[q][4 * i4], acc[q][4 * i4 + 1], acc[q][4 * i4 + 2], acc[q][4 * i4 + 3]};
   __syncthreads();
 
   _Float16* y = static_cast<_Float16*>(a.y);
-  const int total = total_c;
-  if (vec) {
-    const int nq = total / 4;
-    float v[MAXQ * 4];
-    if (res) {  // prefetched before the last multiplication step
+  float v[KI * 4];
 #pragma unroll
-      for (int k = 0; k < MAXQ; ++k) {
-        const half4_t h = __builtin_bit_cast(half4_t, rq[k]);
+  for (int k = 0; k < KI; ++k) {
+    // item (co, oh, quad): row pair oh / 2, slot group 2 (oh % 2) + quad / 2,
+    // lane 32 (quad % 2) + co
+    const int oh = it_oh(k), quad = tid & 3;
+    const int sl = slot(oh >> 1, 2 * (oh & 1) + (quad >> 1), 32 * (quad & 1) + it_co(k));
+    floatx4_t t = part[sl];
+    t = t + part[NP * 256 + sl];
+    t = t + part[2 * NP * 256 + sl];
+    t = t + part[3 * NP * 256 + sl];
+    const float bv = bsm[it_co(k)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * k + e] = (float)h[e];
-      }
+    for (int j = 0; j < 4; ++j) v[4 * k + j] = bias ? t[j] + bv : t[j];
+  }
+  if (res) {
+    if (pairs) {  // prefetched before the last multiplication step
+#pragma unroll
+      for (int k = 0; k < KI; ++k)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const half2_t h = __builtin_bit_cast(half2_t, rq[k][j2]);
+          v[4 * k + 2 * j2] = v[4 * k + 2 * j2] + (float)h[0];
+          v[4 * k + 2 * j2 + 1] = v[4 * k + 2 * j2 + 1] + (float)h[1];
+        }
+    } else {  // every residual read before any store (y may alias it)
+#pragma unroll
+      for (int k = 0; k < KI; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[4 * k + j] = v[4 * k + j] + (float)res[obase + e_clamped(k, j, 1)];
     }
+  }
+  act_array(v, a.act, a.alpha, a.beta);
 #pragma unroll
-    for (int k = 0; k < MAXQ; ++k) {
-      const int it = min(tid + 256 * k, nq - 1);
-      const int c = (4 * it) / howo;  // 4 outputs never straddle planes (howo % 4 == 0)
-      const float bv = bsm[c];
+  for (int k = 0; k < KI; ++k) {
+    if (pairs) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = 4 * it + e + c;  // channel c's area starts c floats later
-        float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
-        if (bias) s = s + bv;
-        if (res) s = s + v[4 * k + e];
-        v[4 * k + e] = s;
-      }
-    }
-    act_array(v, a.act, a.alpha, a.beta);
+      for (int j2 = 0; j2 < 2; ++j2)
+        if (e_valid(k, 2 * j2)) {  // wo even: both of the pair exist
+          const half2_t h = {(_Float16)v[4 * k + 2 * j2], (_Float16)v[4 * k + 2 * j2 + 1]};
+          *reinterpret_cast<half2_t*>(y + obase + e_index(k, 2 * j2)) = h;
+        }
+    } else {
 #pragma unroll
-    for (int k = 0; k < MAXQ; ++k) {
-      const int it = tid + 256 * k;
-      if (it < nq) {
-        half4_t h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[4 * k + e];
-        *reinterpret_cast<u32x2_t*>(y + obase + 4 * it) = __builtin_bit_cast(u32x2_t, h);
-      }
-    }
-  } else {
-    float v[EPT];
-    if (res) {  // every residual read before any store (y may alias it)
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) v[k] = (float)res[obase + min(tid + 256 * k, total - 1)];
-    }
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const int o = min(tid + 256 * k, total - 1);
-      const int c = o / howo;
-      const int idx = o + c;
-      float s = ((part[idx] + part[area + idx]) + part[2 * area + idx]) + part[3 * area + idx];
-      if (bias) s = s + bsm[c];
-      if (res) s = s + v[k];
-      v[k] = s;
-    }
-    act_array(v, a.act, a.alpha, a.beta);
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const int idx = tid + 256 * k;
-      if (idx < total) y[obase + idx] = (_Float16)v[k];
+      for (int j = 0; j < 4; ++j)
+        if (e_valid(k, j)) y[obase + e_index(k, j)] = (_Float16)v[4 * k + j];
     }
   }
 }
