@@ -63,7 +63,7 @@ int validate(const conv_problem* p, int dtype, Geo* g) {
     return CONV_ERR_ARG;
   if ((p->has_bias != 0 && p->has_bias != 1) || (p->has_residual != 0 && p->has_residual != 1))
     return CONV_ERR_ARG;
-  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_ROWBAND)
+  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_GROUPED)
     return CONV_ERR_ARG;
   if (p->split_override < 0 || p->split_override > kMaxSplits) return CONV_ERR_ARG;
   if (p->x_off < 0 || p->w_off < 0 || p->b_off < 0 || p->r_off < 0 || p->y_off < 0)
@@ -182,6 +182,15 @@ bool rowband_applicable(const Geo& g, int dtype) {
   return !g.transpose && dtype == CONV_F16 && g.g == 1 && g.sh == 2 && g.sw == 2 && g.dh == 1 &&
          g.dw == 1 && g.kw <= 8 && g.ci * g.kh <= 24 && g.kh + 4 * g.sh <= 16 && g.wo <= 128 &&
          g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024;
+}
+
+// Grouped implicit GEMM: float16, 8 input channels per group, at most 32 output
+// channels per group, at most 10 taps, planes of at most 4096 pixels whose
+// padded copy (16 bytes per position) fits 48 KiB of LDS.
+bool grouped_applicable(const Geo& g, int dtype) {
+  return !g.transpose && dtype == CONV_F16 && g.g > 1 && g.cig == 8 && g.cog <= 32 &&
+         g.kh * g.kw <= 10 && g.h * g.w <= 4096 &&
+         (g.h + g.pt + g.pb) * (g.w + g.pl + g.pr) * 16 <= 48 * 1024 && g.n * g.g <= 2147483647LL;
 }
 
 // Work items (tile, 64-channel chunk) of the pointwise kernel; its int item
@@ -391,6 +400,15 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     const bool pw_ok = pointwise_applicable(g, dtype);
     if (v == CONV_VARIANT_POINTWISE_GEMM && !pw_ok) return CONV_ERR_ARG;
     if (v == CONV_VARIANT_AUTO && pw_ok && p->split_override <= 1) v = CONV_VARIANT_POINTWISE_GEMM;
+    const bool gc_ok = grouped_applicable(g, dtype);
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_GROUPED && !gc_ok) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_AUTO && gc_ok && p->split_override <= 1) v = CONV_VARIANT_IMPLICIT_GEMM_GROUPED;
+    if (v == CONV_VARIANT_IMPLICIT_GEMM_GROUPED) {
+      if (p->split_override > 1) return CONV_ERR_ARG;
+      pl->variant = v;
+      pl->scratch_whole = 0;
+      return CONV_OK;
+    }
     const bool rb_ok = rowband_applicable(g, dtype);
     if (v == CONV_VARIANT_IMPLICIT_GEMM_ROWBAND && !rb_ok) return CONV_ERR_ARG;
     if (v == CONV_VARIANT_AUTO && rb_ok && p->split_override <= 1) v = CONV_VARIANT_IMPLICIT_GEMM_ROWBAND;
@@ -464,6 +482,7 @@ const char* variant_name(int v) {
     case CONV_VARIANT_TRANSPOSE_GEMM_COL2IM: return "transpose_gemm_col2im";
     case CONV_VARIANT_IMPLICIT_GEMM_HALO: return "implicit_gemm_halo";
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND: return "implicit_gemm_rowband";
+    case CONV_VARIANT_IMPLICIT_GEMM_GROUPED: return "implicit_gemm_grouped";
     default: return "unknown";
   }
 }
@@ -701,6 +720,19 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         r.act = p->activation; r.alpha = p->act_alpha; r.beta = p->act_beta;
         e = launch_reduce(dt, r, s);
       }
+    } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_GROUPED) {
+      GroupedArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.groups = (int)g.g; a.cog = (int)g.cog;
+      a.kh = (int)g.kh; a.kw = (int)g.kw; a.sh = (int)g.sh; a.sw = (int)g.sw;
+      a.dh = (int)g.dh; a.dw = (int)g.dw; a.pt = (int)g.pt; a.pl = (int)g.pl;
+      a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.hp = (int)(g.h + g.pt + g.pb); a.wp = (int)(g.w + g.pl + g.pr);
+      a.xs_bytes = a.hp * a.wp * 16;
+      a.vec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0;
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_grouped(a, s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM && pl.ct_fused) {
       // GEMM rows m = 4 co + 2 kh + kw over whole input rows of one image; the
       // epilogue writes y[n][co][2h + kh][2w + kw] directly
@@ -845,6 +877,9 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND:
       snprintf(tmp, sizeof tmp, "implicit_gemm_rowband.%s.rows%d", dn, pl.rb_band_rows);
+      break;
+    case CONV_VARIANT_IMPLICIT_GEMM_GROUPED:
+      snprintf(tmp, sizeof tmp, "implicit_gemm_grouped.%s.c8.n%d", dn, (int)std::min<int64_t>(32, g.cog));
       break;
     case CONV_VARIANT_TRANSPOSE_GEMM_COL2IM:
       if (pl.ct_fused)

@@ -85,6 +85,24 @@ struct HaloArgs {
   float alpha, beta;
 };
 
+// Grouped convolution, 8 input channels per group: one workgroup per (image,
+// group) with the padded input planes staged whole.
+struct GroupedArgs {
+  const void* x;
+  const void* wt;
+  const void* bias;
+  const void* res;
+  void* y;
+  int n, c_in, h, w, c_out, groups, cog;
+  int kh, kw, sh, sw, dh, dw, pt, pl;
+  int ho, wo;
+  int hp, wp;            // padded plane: h + pt + pb rows, w + pl + pr columns
+  int xs_bytes;          // LDS bytes of the staged plane (16 per position)
+  int vec;               // x 8-byte aligned and h * w % 4 == 0
+  int act;
+  float alpha, beta;
+};
+
 // Pointwise (1x1, stride 1, no padding, one group) GEMM on x as it lies.
 struct PwArgs {
   const void* x;         // [n][c_in][hw]
@@ -198,6 +216,7 @@ hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s);
+hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,

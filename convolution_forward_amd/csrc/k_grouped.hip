@@ -1,0 +1,220 @@
+// Grouped convolution with 8 input channels per group, float16 operands,
+// float32 accumulation, gfx950 ("Convolution, pooling and resize", "Variants":
+// the implicit GEMM gathers its window while staging, no column matrix; each
+// group is its own GEMM, "Convolutions", section 2.3 on grouped convolution):
+//
+//   y[n, g*cog + co, oh, ow] = act( sum_{kh,kw,ci} w[g*cog + co, ci, kh, kw] *
+//        x[n, g*8 + ci, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw] + bias + res )
+//
+// One workgroup per (image, group).  The group's 8 input planes, zero padded,
+// are staged once in LDS channel-innermost (a 16-byte octet per position), so
+// every tap of every output pixel is one b128 read: the window is never
+// materialised.  The GEMM per group is M = cog (<= 32 output channels) x
+// N = Ho*Wo pixels x K = taps*8, run as v_mfma_f32_32x32x16_f16 with A = the
+// weights (output-channel rows; k = two taps of 8 channels) held in registers
+// for the whole workgroup and B = 32 output pixels (k = the same two taps).
+// The sixteen waves (four per SIMD, so that one wave's latencies hide behind
+// another's work) take 32-pixel blocks in turn; the epilogue runs straight from
+// the accumulators (lane l: pixel l % 32, channels 4 (l / 32) + i + 8 (i / 4)).
+// Per output the sum runs over the taps in pairs (k-step order), each pair in
+// the MFMA's internal order.
+#include <algorithm>
+
+#include "epilogue.h"
+#include "internal.h"
+
+namespace convfwd {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int GC_MAXTAPS = 10;  // k-steps of two taps: at most 5
+constexpr int GC_NT = 1024;     // threads per workgroup: 16 waves, 4 per SIMD
+
+}  // namespace
+
+// KS: k-steps (taps <= 2 KS).  CB: 8-channel row groups of the output
+// channels (cog <= 8 CB).  VEC: x 8-byte aligned and h * w % 4 == 0.
+template <int KS, int CB, bool VEC>
+__global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u32x4_t* xs = reinterpret_cast<u32x4_t*>(smem);                      // [pos] octets
+  u32x4_t* wl = reinterpret_cast<u32x4_t*>(smem + a.xs_bytes);          // [co][tap] octets
+  float* bsm = reinterpret_cast<float*>(smem + a.xs_bytes + 32 * GC_MAXTAPS * 16);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = blockIdx.x / a.groups, g = blockIdx.x - n * a.groups;
+  const int hw = a.h * a.w, howo = a.ho * a.wo;
+  const int taps = a.kh * a.kw;
+  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x) + ((long long)n * a.c_in + g * 8) * hw;
+  const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt) + (long long)g * a.cog * 8 * taps;
+  const _Float16* bias = static_cast<const _Float16*>(a.bias);
+  const _Float16* res = static_cast<const _Float16*>(a.res);
+  _Float16* y = static_cast<_Float16*>(a.y);
+  const long long obase = ((long long)n * a.c_out + g * a.cog) * howo;
+
+  // ---- loads: 4 consecutive pixels of the 8 planes per item (items beyond the
+  // plane clamp to its last group; their LDS writes repeat that group's) ----
+  const int groups4 = (hw + 3) / 4;
+  constexpr int NI = 4096 / 4 / GC_NT;  // items per thread (planes up to 4096 pixels)
+  u32x2_t xr[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = min(tid + GC_NT * i, groups4 - 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (VEC) {
+        xr[i][e] = *reinterpret_cast<const u32x2_t*>(x + (long long)e * hw + 4 * q);
+      } else {
+        half4_t h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = x[(long long)e * hw + min(4 * q + j, hw - 1)];
+        xr[i][e] = __builtin_bit_cast(u32x2_t, h);
+      }
+    }
+  }
+  // weights (cog x 8 x taps halves, contiguous) and bias: one element per item
+  const int nw = a.cog * 8 * taps;  // <= 32 x 8 x 10
+  constexpr int WN = (32 * 8 * GC_MAXTAPS + GC_NT - 1) / GC_NT;
+  _Float16 wv[WN];
+#pragma unroll
+  for (int i = 0; i < WN; ++i) wv[i] = w[min(tid + GC_NT * i, nw - 1)];
+  const _Float16 bv_in = *(bias ? bias + g * a.cog + min(tid, a.cog - 1) : x);
+
+  // ---- zero the staged plane (padding positions stay zero) and the weight
+  // octets (taps past the last and channels past cog stay zero) ----
+  const int npos = a.hp * a.wp;
+  for (int q = tid; q < npos; q += GC_NT) xs[q] = u32x4_t{0, 0, 0, 0};
+  for (int q = tid; q < 32 * GC_MAXTAPS; q += GC_NT) wl[q] = u32x4_t{0, 0, 0, 0};
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = tid + GC_NT * i;
+    if (q < groups4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = 4 * q + j;
+        if (f < hw) {
+          half8_t v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, xr[i][e])[j];
+          const int ih = f / a.w, iw = f - ih * a.w;
+          xs[(ih + a.pt) * a.wp + iw + a.pl] = __builtin_bit_cast(u32x4_t, v);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const int q = tid + GC_NT * i;  // element (co, ci, tap) of the group's weights
+    if (q < nw) {
+      const int co = q / (8 * taps), r = q - co * 8 * taps;
+      const int ci = r / taps, t = r - ci * taps;
+      reinterpret_cast<_Float16*>(wl + co * GC_MAXTAPS + t)[ci] = wv[i];
+    }
+  }
+  if (tid < 32) bsm[tid] = (float)bv_in;
+  __syncthreads();
+
+  // ---- A fragments: lane l holds output channel l % 32, taps 2 ks + l / 32 ----
+  const int hi = lane >> 5;
+  u32x4_t af[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) af[ks] = wl[(lane & 31) * GC_MAXTAPS + 2 * ks + hi];
+  // tap offsets in the staged plane for this lane's half of each k-step
+  int tofs[KS];
+  bool tok[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int t = 2 * ks + hi;
+    tok[ks] = t < taps;
+    const int kh = t / a.kw, kw = t - kh * a.kw;
+    tofs[ks] = tok[ks] ? kh * a.dh * a.wp + kw * a.dw : 0;
+  }
+
+  // NB 32-pixel blocks per pass (independent accumulators; one block for 32
+  // output channels, which need all 16 accumulator elements); wave w takes
+  // passes w, w + 16, ...  Lane l: pixel l % 32 of each block, output channels
+  // 8 (i / 4) + 4 (l / 32) + i % 4 for accumulator element i < 4 CB.
+  _Float16* __restrict__ yg = y + obase;
+  const _Float16* rg = res ? res + obase : nullptr;
+  const int nblk = (howo + 31) / 32;
+  constexpr int NB = CB >= 4 ? 1 : 2;
+  for (int b0 = NB * wave; b0 < nblk; b0 += NB * (GC_NT / 64)) {
+    floatx16_t acc[NB];
+    int pix[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      pix[u] = 32 * (b0 + u) + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int p = min(pix[u], howo - 1);
+        const int oh = p / a.wo, ow = p - oh * a.wo;
+        const u32x4_t v = xs[oh * a.sh * a.wp + ow * a.sw + tofs[ks]];
+        const u32x4_t bf = tok[ks] ? v : u32x4_t{0, 0, 0, 0};
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, af[ks]),
+                                                        __builtin_bit_cast(half8_t, bf), acc[u], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float v[4 * CB];
+#pragma unroll
+      for (int i = 0; i < 4 * CB; ++i) {
+        const int co = 8 * (i / 4) + 4 * hi + (i & 3);
+        v[i] = bias ? acc[u][i] + bsm[co] : acc[u][i];
+      }
+      if (rg) {
+#pragma unroll
+        for (int i = 0; i < 4 * CB; ++i) {
+          const int co = min(8 * (i / 4) + 4 * hi + (i & 3), a.cog - 1);
+          v[i] = v[i] + (float)rg[co * howo + min(pix[u], howo - 1)];
+        }
+      }
+      act_array(v, a.act, a.alpha, a.beta);
+      if (pix[u] < howo) {
+#pragma unroll
+        for (int i = 0; i < 4 * CB; ++i) {
+          const int co = 8 * (i / 4) + 4 * hi + (i & 3);
+          if (co < a.cog) yg[co * howo + pix[u]] = (_Float16)v[i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.n * a.groups));
+  const size_t lds = (size_t)a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4;
+  const int taps = a.kh * a.kw;
+  if (taps > GC_MAXTAPS) return hipErrorInvalidValue;
+#define GC_CASE(KS_, CB_)                                                                      \
+  if (a.vec) hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true>), grid, dim3(GC_NT), lds, s, a); \
+  else hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, false>), grid, dim3(GC_NT), lds, s, a);
+#define GC_KS(KS_)                          \
+  if (a.cog <= 8) { GC_CASE(KS_, 1) }       \
+  else if (a.cog <= 16) { GC_CASE(KS_, 2) } \
+  else { GC_CASE(KS_, 4) }
+  if (taps <= 2) {
+    GC_KS(1)
+  } else if (taps <= 4) {
+    GC_KS(2)
+  } else {
+    GC_KS(5)
+  }
+#undef GC_KS
+#undef GC_CASE
+  return hipGetLastError();
+}
+
+}  // namespace convfwd

@@ -103,9 +103,12 @@ typedef enum {
     CONV_VARIANT_TRANSPOSE_GEMM_COL2IM = 4, /* ConvTranspose: GEMM + gathering col2im */
     CONV_VARIANT_IMPLICIT_GEMM_HALO = 5, /* implicit GEMM with the input halo tile staged
                                             once per channel chunk and reused for all taps */
-    CONV_VARIANT_IMPLICIT_GEMM_ROWBAND = 6 /* stride 2, few input channels (image stems):
+    CONV_VARIANT_IMPLICIT_GEMM_ROWBAND = 6, /* stride 2, few input channels (image stems):
                                               a ring of staged input rows per output-row
                                               band, kw taps read as consecutive halves */
+    CONV_VARIANT_IMPLICIT_GEMM_GROUPED = 7 /* 8 input channels per group: the group's
+                                              padded planes staged whole, one workgroup
+                                              per (image, group) */
 } conv_variant;
 
 /* The problem: shape, explicit pads, stride, dilation, groups, fused activation

@@ -222,6 +222,49 @@ ROWBAND_CASES = [
 ]
 
 
+GROUPED_CASES = [
+    # (geometry, bias, residual): 8 input channels per group; dilation, stride,
+    # asymmetric pads, 1x1 / 2x2 / 3x3 taps, up to 32 output channels per group,
+    # planes whose pixel count is not a multiple of 4 (element loads)
+    (oracle.Geom(2, 16, 9, 11, 48, 3, 3, groups=2, pt=1, pl=1, pb=1, pr=1), True, False),
+    (oracle.Geom(3, 32, 12, 12, 32, 3, 3, groups=4, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1,
+                 act="relu"), True, True),
+    (oracle.Geom(1, 24, 20, 16, 96, 1, 1, groups=3, act="silu"), False, True),
+    (oracle.Geom(2, 64, 16, 16, 16, 3, 3, groups=8, dh=3, dw=2, pt=3, pl=2, pb=2, pr=3,
+                 act="hard_swish"), True, False),
+    (oracle.Geom(2, 40, 13, 14, 40, 2, 2, groups=5, pt=1, pl=0, pb=0, pr=1, act="tanh"), True, True),
+    (oracle.Geom(1, 256, 40, 40, 256, 3, 3, groups=32, dh=2, dw=2, pt=2, pl=2, pb=2, pr=2,
+                 act="sigmoid"), True, False),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=lambda c: f"g{c[0].groups}x{c[0].c_out}k{c[0].kh}x{c[0].kw}")
+def test_grouped_variant(case):
+    """The grouped (8 channels per group) implicit GEMM against the oracle;
+    identical bits with misaligned operands and with y aliasing the residual."""
+    g, has_b, has_r = case
+    _say(f"[grouped] {g}")
+    from gpu_harness import problem_from
+    assert cf.conv_describe_variant(problem_from(g), "f16").startswith("implicit_gemm_grouped")
+    rng = np.random.default_rng(g.c_in * 3 + g.h + 7 * g.c_out + g.kh)
+    cig = g.c_in // g.groups
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, cig, g.kh, g.kw)) *
+         np.sqrt(2.0 / (cig * g.kh * g.kw))).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f16", x, w, b, r)
+    assert_parity("f16", y, yr, sr, b, r, what="grouped", act=g.act)
+    y2 = run_gpu(g, "f16", x, w, b, r, offsets=(1, 3, 1, 1, 1))
+    assert np.array_equal(_bits(y), _bits(y2))
+    if has_r:
+        y3 = run_gpu(g, "f16", x, w, b, r, offsets=(0, 0, 0, 8, 8), alias_residual=True)
+        assert np.array_equal(_bits(y), _bits(y3))
+    y4 = run_gpu(g, "f16", x, w, b, r, variant="implicit_gemm")
+    assert_parity("f16", y4, yr, sr, b, r, what="grouped-as-igemm", act=g.act)
+
+
 @pytest.mark.parametrize("case", ROWBAND_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}k{c[0].kh}")
 def test_rowband_variant(case):
     """The row-band stride-2 kernel against the oracle; identical bits with
