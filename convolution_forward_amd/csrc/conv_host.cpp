@@ -206,6 +206,10 @@ int64_t pw_items(int64_t n, int64_t pixel_tiles, int64_t channel_tiles, int64_t 
 // Pointwise GEMM on x as it lies: 1x1, stride 1, no padding, one group, float16,
 // whole channel octets and planes of whole 4-pixel groups.
 bool pointwise_applicable(const Geo& g, int dtype) {
+  if (dtype == CONV_F32)  // float32: planes and weight rows of whole float4 groups
+    return !g.transpose && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 && g.pt == 0 &&
+           g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 4 == 0 &&
+           (g.h * g.w) % 4 == 0 && ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) < (1LL << 31);
   return !g.transpose && dtype == CONV_F16 && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
          g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
          (g.h * g.w) % 4 == 0 && g.h * g.w >= 4 &&
@@ -426,7 +430,7 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (v == CONV_VARIANT_POINTWISE_GEMM) {
       if (p->split_override > 1) return CONV_ERR_ARG;
       pl->variant = v;
-      pl->pw_tc = g.co > 64 ? 128 : 64;
+      pl->pw_tc = dtype == CONV_F32 ? 80 : g.co > 64 ? 128 : 64;
       pl->scratch_whole = 0;
       return CONV_OK;
     }
@@ -659,6 +663,17 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_rowband(a, s);
     } else if (pl.variant == CONV_VARIANT_POINTWISE_GEMM) {
+      if (dt == F32) {
+        PwArgs a{};
+        a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+        a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
+        a.n_pt = (int)ceil_div((int64_t)cn * g.h * g.w, 64);
+        a.n_ct = (int)ceil_div(g.co, 80);
+        a.nchunks = (int)ceil_div(g.ci, 64);
+        a.vec = reinterpret_cast<uintptr_t>(xc) % 16 == 0 && reinterpret_cast<uintptr_t>(wb) % 16 == 0;
+        a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+        e = launch_pointwise_f32(a, s);
+      } else {
       PwArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
       a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
@@ -673,6 +688,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
               (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0) && (g.h * g.w) % 8 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_pointwise(a, device_cus(), s);
+      }
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
       HaloArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -873,7 +889,7 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                pl.splits);
       break;
     case CONV_VARIANT_POINTWISE_GEMM:
-      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t128x%d.k64", dn, pl.pw_tc);
+      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t%dx%d.k64", dn, dtype == CONV_F32 ? 64 : 128, pl.pw_tc);
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND:
       snprintf(tmp, sizeof tmp, "implicit_gemm_rowband.%s.rows%d", dn, pl.rb_band_rows);

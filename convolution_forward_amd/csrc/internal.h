@@ -215,6 +215,7 @@ constexpr int HALO_MAXI = 8;  // staged (position, octet) input items per thread
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s);
+hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s);
 hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);

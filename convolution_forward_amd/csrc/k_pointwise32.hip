@@ -1,0 +1,214 @@
+// Pointwise (1x1, stride 1, no padding, one group) convolution in float32 as a
+// GEMM on the input as it lies ("Convolution, pooling and resize", "Variants":
+// the 1x1 case multiplies the weight matrix by x without gathering;
+// "Convolutions", section 2.4: a per-pixel linear map), gfx950:
+//
+//   y[n, co, p] = act( sum_ci w[co, ci] * x[n, ci, p] + bias[co] + res[n, co, p] )
+//
+//  * The pixels of all images form one axis; a tile is 64 consecutive pixels of
+//    it (planes of whole float4 groups, so a group never straddles two images)
+//    x 80 output channels.  Input channels are consumed in chunks of 64, double
+//    buffered in LDS and prefetched through registers one chunk ahead.
+//  * v_mfma_f32_16x16x4_f32 (float32 products and sums): A = weights (16 output
+//    channels x 4 k), B = x (4 k x 16 pixels).  Eight waves, two per SIMD: wave
+//    w owns pixels 16 (w % 4) .. + 15 of the tile, all five 16-channel blocks,
+//    and half h = w / 4 of every chunk; the two halves' sums are added at the
+//    end (first half + second half).  Within a half, lane group g (lanes
+//    16g..16g+15) feeds channels 32h + 8g .. + 7 to the 8 k-steps in turn, so a
+//    lane's A values of four k-steps are one 16-byte LDS read.
+//  * LDS layout: x rows of 64 floats rotated by 16 columns per lane group, w rows
+//    padded to 68 floats, so that every fragment read hits distinct banks.
+// Per output: the sum of each half runs over the chunks in order, step s of a
+// half adding channels 32h + s, 32h + 8 + s, 32h + 16 + s, 32h + 24 + s (MFMA
+// internal order); then first half + second half.
+#include <algorithm>
+
+#include "epilogue.h"
+#include "internal.h"
+
+namespace convfwd {
+
+namespace {
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int P32_TP = 64;               // pixels per tile
+constexpr int P32_TC = 80;               // output channels per tile (5 blocks)
+constexpr int P32_KC = 64;               // input channels per chunk
+constexpr int P32_XP = 64;               // LDS floats per channel row of x
+constexpr int P32_WP = 68;               // LDS floats per output-channel row of w
+constexpr int P32_XF = P32_KC * P32_XP;  // floats of one x stage
+constexpr int P32_WF = P32_TC * P32_WP;  // floats of one w stage
+constexpr int P32_NT = 512;              // threads: 8 waves, 2 per SIMD
+constexpr int P32_NX = P32_KC * P32_TP / 4 / P32_NT;                 // x float4 per thread (2)
+constexpr int P32_NW = (P32_TC * P32_KC / 4 + P32_NT - 1) / P32_NT;  // w float4 per thread (3)
+
+// column of pixel px in the LDS row of chunk channel k: rows of the four lane
+// groups (channels 8g .. 8g + 7 of each half chunk) are rotated by 16 columns
+// against each other, so the groups' reads of one step hit different banks
+__device__ __forceinline__ int xcol(int k, int px) { return (px + 16 * ((k >> 3) & 3)) & 63; }
+
+}  // namespace
+
+// VEC: x and w 16-byte aligned (planes and weight rows of whole float4 groups
+// are guaranteed by the planner); otherwise element loads.
+template <bool VEC>
+__global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
+  __shared__ __attribute__((aligned(16))) float smem[2 * (P32_XF + P32_WF) + P32_TC];
+  float* bsm = smem + 2 * (P32_XF + P32_WF);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ct = blockIdx.x % a.n_ct, pt = blockIdx.x / a.n_ct;
+  const int co0 = ct * P32_TC;
+  const long long P0 = (long long)pt * P32_TP;  // first pixel of the flattened axis
+  const long long npix = (long long)a.n * a.hw;
+  const float* __restrict__ x = static_cast<const float*>(a.x);
+  const float* __restrict__ w = static_cast<const float*>(a.wt);
+  const float* bias = static_cast<const float*>(a.bias);
+  const float* res = static_cast<const float*>(a.res);
+  float* y = static_cast<float*>(a.y);
+
+  // load items: x float4 (channel k = q / 16, pixels 4 (q % 16) ..), w float4
+  // (output channel m = q / 16, channels 4 (q % 16) ..); clamped addresses, so
+  // every load is unconditional; values past the ranges are zeroed when staged
+  long long xoff[P32_NX];
+#pragma unroll
+  for (int i = 0; i < P32_NX; ++i) {
+    const int q = tid + P32_NT * i;
+    const long long P = min(P0 + 4 * (q & 15), npix - 4);
+    const long long img = P / a.hw;
+    xoff[i] = img * a.c_in * a.hw + (P - img * a.hw);
+  }
+  floatx4_t xr[P32_NX], wr[P32_NW];
+  auto load = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < P32_NX; ++i) {
+      const int q = tid + P32_NT * i;
+      const int k = min(c0 + (q >> 4), a.c_in - 1);
+      const float* src = x + xoff[i] + (long long)k * a.hw;
+      if constexpr (VEC) {
+        xr[i] = *reinterpret_cast<const floatx4_t*>(src);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[i][j] = src[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < P32_NW; ++i) {
+      const int q = min(tid + P32_NT * i, P32_TC * P32_KC / 4 - 1);
+      const int m = min(co0 + (q >> 4), a.c_out - 1);
+      const int k = min(c0 + 4 * (q & 15), a.c_in - 4);  // c_in % 4 == 0
+      const float* src = w + (long long)m * a.c_in + k;
+      if constexpr (VEC) {
+        wr[i] = *reinterpret_cast<const floatx4_t*>(src);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wr[i][j] = src[j];
+      }
+    }
+  };
+  auto stage = [&](int buf, int c0) __attribute__((always_inline)) {
+    float* xs = smem + buf * (P32_XF + P32_WF);
+    float* ws = xs + P32_XF;
+#pragma unroll
+    for (int i = 0; i < P32_NX; ++i) {
+      const int q = tid + P32_NT * i;
+      const int k = q >> 4, px = 4 * (q & 15);
+      const bool ok = c0 + k < a.c_in && P0 + px < npix;  // whole float4 groups
+      *reinterpret_cast<floatx4_t*>(xs + k * P32_XP + xcol(k, px)) = ok ? xr[i] : floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < P32_NW; ++i) {
+      const int q = tid + P32_NT * i;
+      if (P32_NT * (i + 1) <= P32_TC * P32_KC / 4 || q < P32_TC * P32_KC / 4) {  // uniform per wave
+        const int m = q >> 4, k = 4 * (q & 15);
+        const bool ok = co0 + m < a.c_out && c0 + k < a.c_in;
+        *reinterpret_cast<floatx4_t*>(ws + m * P32_WP + k) = ok ? wr[i] : floatx4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  floatx4_t acc[5];
+#pragma unroll
+  for (int cb = 0; cb < 5; ++cb) acc[cb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  const int lg = lane >> 4, lc = lane & 15;
+  const int pb = wave & 3, kh = wave >> 2;  // pixel block, half of each chunk
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const float* xs = smem + buf * (P32_XF + P32_WF);
+    const float* ws = xs + P32_XF;
+#pragma unroll
+    for (int s4 = 0; s4 < 2; ++s4) {  // four k-steps per 16-byte A read
+      floatx4_t af[5];
+#pragma unroll
+      for (int cb = 0; cb < 5; ++cb)
+        af[cb] = *reinterpret_cast<const floatx4_t*>(ws + (16 * cb + lc) * P32_WP + 32 * kh + 8 * lg + 4 * s4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 32 * kh + 8 * lg + 4 * s4 + j;
+        const float bf = xs[k * P32_XP + xcol(k, 16 * pb + lc)];
+#pragma unroll
+        for (int cb = 0; cb < 5; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[cb][j], bf, acc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  if (tid < P32_TC) bsm[tid] = bias ? bias[min(co0 + tid, a.c_out - 1)] : 0.f;
+  const int nch = a.nchunks;
+  load(0);
+  stage(0, 0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load((c + 1) * P32_KC);  // uniform
+    compute(buf);
+    if (c + 1 < nch) stage(buf ^ 1, (c + 1) * P32_KC);
+    __syncthreads();
+  }
+
+  // the upper waves' partial sums (second half of every chunk) go through LDS
+  // to the lower waves, which add them (lower + upper) and run the epilogue:
+  // lane l holds pixel 16 pb + l % 16 and output channels 16 cb + 4 (l / 16) + i
+  floatx4_t* part = reinterpret_cast<floatx4_t*>(smem);
+  if (kh == 1) {
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb) part[(pb * 5 + cb) * 64 + lane] = acc[cb];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int cb = 0; cb < 5; ++cb) acc[cb] = acc[cb] + part[(pb * 5 + cb) * 64 + lane];
+  const long long P = P0 + 16 * pb + lc;
+  if (P < npix) {
+    const long long img = P / a.hw, pp = P - img * a.hw;
+    const long long obase = img * a.c_out * a.hw + pp;
+    float v[20];
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * cb + 4 * lg + i;
+        float t = acc[cb][i];
+        if (bias) t = t + bsm[m];
+        if (res) t = t + res[obase + (long long)min(co0 + m, a.c_out - 1) * a.hw];
+        v[4 * cb + i] = t;
+      }
+    act_array(v, a.act, a.alpha, a.beta);
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * cb + 4 * lg + i;
+        if (co0 + m < a.c_out) y[obase + (long long)(co0 + m) * a.hw] = v[4 * cb + i];
+      }
+  }
+}
+
+hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.n_pt * a.n_ct));
+  if (a.vec) hipLaunchKernelGGL((pointwise_f32_kernel<true>), grid, dim3(P32_NT), 0, s, a);
+  else hipLaunchKernelGGL((pointwise_f32_kernel<false>), grid, dim3(P32_NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace convfwd

@@ -265,6 +265,41 @@ def test_grouped_variant(case):
     assert_parity("f16", y4, yr, sr, b, r, what="grouped-as-igemm", act=g.act)
 
 
+POINTWISE_F32_CASES = [
+    # (geometry, bias, residual): float32 1x1 on x as it lies; channel chunks with
+    # tails, several channel tiles, tiles straddling images, tiny planes
+    (oracle.Geom(3, 240, 14, 14, 80, 1, 1), True, False),
+    (oracle.Geom(2, 36, 6, 10, 100, 1, 1, act="relu"), True, False),
+    (oracle.Geom(1, 132, 5, 4, 17, 1, 1, act="silu"), False, True),
+    (oracle.Geom(5, 8, 2, 2, 80, 1, 1, act="hard_swish"), True, True),
+]
+
+
+@pytest.mark.parametrize("case", POINTWISE_F32_CASES, ids=lambda c: f"{c[0].c_in}to{c[0].c_out}x{c[0].h}x{c[0].w}")
+def test_pointwise_f32_variant(case):
+    """The float32 1x1 GEMM (MFMA f32) against the oracle; identical bits with
+    misaligned operands (element loads) and with y aliasing the residual."""
+    g, has_b, has_r = case
+    _say(f"[pointwise-f32] {g}")
+    from gpu_harness import problem_from
+    assert cf.conv_describe_variant(problem_from(g), "f32").startswith("pointwise_gemm.f32")
+    rng = np.random.default_rng(g.c_in + 17 * g.c_out + g.h)
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float32)
+    w = (rng.standard_normal((g.c_out, g.c_in, 1, 1)) * np.sqrt(2.0 / g.c_in)).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float32) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float32) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f32", x, w, b, r)
+    assert_parity("f32", y, yr, sr, b, r, what="pointwise-f32", act=g.act)
+    y2 = run_gpu(g, "f32", x, w, b, r, offsets=(1, 3, 1, 1, 1))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    if has_r:
+        y3 = run_gpu(g, "f32", x, w, b, r, offsets=(0, 0, 0, 4, 4), alias_residual=True)
+        assert np.array_equal(y.view(np.uint32), y3.view(np.uint32))
+    y4 = run_gpu(g, "f32", x, w, b, r, variant="implicit_gemm")
+    assert_parity("f32", y4, yr, sr, b, r, what="pointwise-f32-as-igemm", act=g.act)
+
+
 @pytest.mark.parametrize("case", ROWBAND_CASES, ids=lambda c: f"{c[0].c_in}x{c[0].h}x{c[0].w}k{c[0].kh}")
 def test_rowband_variant(case):
     """The row-band stride-2 kernel against the oracle; identical bits with
