@@ -47,7 +47,9 @@ constexpr int RB_NSTV = 64 * 16 / 256;  // output vectors per thread and row (<=
 
 }  // namespace
 
-template <int CB, bool VEC>
+// NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; CB: 32-pixel blocks per
+// wave; VEC: whole 16-byte input and output vectors.
+template <int NST, int CB, bool VEC>
 __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_rb[];
   // ring: [ci][slot][rp halves]; output tile [64][RB_OPITCH bytes]; bias [64]
@@ -96,9 +98,9 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
     }
   }
   __syncthreads();
-  u32x4_t wf[RB_MAXST];
+  u32x4_t wf[NST];
 #pragma unroll
-  for (int st = 0; st < RB_MAXST; ++st) {
+  for (int st = 0; st < NST; ++st) {
     const int g = 2 * st + (lane >> 5);
     const int cl = 32 * cbw + (lane & 31);  // channel within the tile
     const bool okg = g < groups && co0 + cl < a.c_out;
@@ -146,10 +148,15 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
       const int slot = (ir0 + r) & (RB_RING - 1);
       _Float16* dst = ring + (ci * RB_RING + slot) * rp + a.pl + 8 * v;
       const half8_t h = __builtin_bit_cast(half8_t, d);
-      const int cnt = min(8, a.w - 8 * v);  // the row's last vector may be partial
+      if constexpr (VEC) {  // w % 8 == 0: whole vectors (the ring column offset is odd-aligned)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < cnt) dst[e] = h[e];
+        for (int e = 0; e < 8; ++e) dst[e] = h[e];
+      } else {
+        const int cnt = min(8, a.w - 8 * v);  // the row's last vector may be partial
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < cnt) dst[e] = h[e];
+      }
     }
   };
   // first input row of the sh new rows that output row o brings in
@@ -174,9 +181,9 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
 
   const int half = lane >> 5;  // k-group parity of this lane
   // per k-step: this lane's (ci, kh) group as a ring row base and a tap row
-  int gbase[RB_MAXST], gkh[RB_MAXST];
+  int gbase[NST], gkh[NST];
 #pragma unroll
-  for (int st = 0; st < RB_MAXST; ++st) {
+  for (int st = 0; st < NST; ++st) {
     const int g = min(2 * st + half, groups - 1);  // the padded group multiplies zero weights
     const int ci = g / a.kh;
     gkh[st] = g - ci * a.kh;
@@ -206,8 +213,7 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
       for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
     const int ir_base = oh * a.sh - a.pt;
 #pragma unroll
-    for (int st = 0; st < RB_MAXST; ++st) {
-      if (2 * st >= groups) continue;  // uniform
+    for (int st = 0; st < NST; ++st) {
       const int slot = (ir_base + gkh[st]) & (RB_RING - 1);
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
@@ -287,17 +293,27 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
   }
 }
 
+template <int NST>
+static void launch_rb_nst(const RowbandArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  const bool two = a.c_out > 32;
+  if (a.vec) {
+    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 2, true>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<NST, 1, true>), grid, dim3(256), lds, s, a);
+  } else {
+    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 2, false>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<NST, 1, false>), grid, dim3(256), lds, s, a);
+  }
+}
+
 hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n * a.n_ct * a.n_band));
   const size_t lds = (size_t)a.ring_bytes + 64 * RB_OPITCH + 64 * 4;
-  const bool two = a.c_out > 32;
-  if (a.vec) {
-    if (two) hipLaunchKernelGGL((rowband_kernel<2, true>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<1, true>), grid, dim3(256), lds, s, a);
-  } else {
-    if (two) hipLaunchKernelGGL((rowband_kernel<2, false>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<1, false>), grid, dim3(256), lds, s, a);
-  }
+  // k-steps: exact for the 3-channel 7x7 stem, else the maximum (padded steps
+  // multiply zero weights)
+  const int nst = (a.c_in * a.kh + 1) / 2;
+  if (nst > RB_MAXST) return hipErrorInvalidValue;
+  if (nst == 11) launch_rb_nst<11>(a, grid, lds, s);
+  else launch_rb_nst<RB_MAXST>(a, grid, lds, s);
   return hipGetLastError();
 }
 
