@@ -17,9 +17,10 @@
 //    row multiplies.  Rows above or below the image are zero rows; columns
 //    outside it stay zero from the start.
 //  * MFMA v_mfma_f32_32x32x16_f16: A = 32 output pixels x 16 k (two (ci, kh)
-//    groups), B = 16 k x 32 output channels.  With 64 channels a wave owns one
-//    32-channel block and two 32-pixel blocks of the row; with 32 channels, one
-//    pixel block (rows of at most 128 outputs).
+//    groups), B = 16 k x 32 output channels.  With 64 channels eight waves
+//    (two per SIMD) each own one 32-channel block and one 32-pixel block of the
+//    row; with 32 channels four waves own one pixel block each (rows of at most
+//    128 outputs).
 //  * Epilogue: bias and activation in float32, float16 into an LDS row tile
 //    [channel][pixel], then whole output rows leave with 16-byte stores.
 // Per output the sum runs over (ci, kh) groups in pairs, each pair inside one
@@ -42,15 +43,18 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int RB_RING = 16;        // input rows kept per channel (power of two)
 constexpr int RB_MAXST = 12;       // MFMA k-steps (pairs of (ci, kh) groups) at most
 constexpr int RB_OPITCH = 128 * 2 + 16;  // LDS bytes per output-tile row (float16)
-constexpr int RB_FILL = 4;         // items per thread for the first KH rows (<= 1024 items)
-constexpr int RB_NSTV = 64 * 16 / 256;  // output vectors per thread and row (<= 64 x 128)
+constexpr int RB_FILLI = 1024;     // items of the first KH rows at most
 
 }  // namespace
 
-// NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; CB: 32-pixel blocks per
-// wave; VEC: whole 16-byte input and output vectors.
-template <int NST, int CB, bool VEC>
-__global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
+// NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; WV: waves (8: two
+// 32-channel blocks x four 32-pixel blocks; 4: one channel block); VEC: whole
+// 16-byte input and output vectors.
+template <int NST, int WV, bool VEC>
+__global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
+  constexpr int NT = 64 * WV;
+  constexpr int RB_FILL = (RB_FILLI + NT - 1) / NT;  // items per thread for the first KH rows
+  constexpr int RB_NSTV = 64 * 16 / NT;              // output vectors per thread and row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_rb[];
   // ring: [ci][slot][rp halves]; output tile [64][RB_OPITCH bytes]; bias [64]
   _Float16* ring = reinterpret_cast<_Float16*>(smem_rb);
@@ -76,9 +80,10 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
   const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt);
   static_assert(64 * 2 * RB_MAXST * 8 <= 64 * 1024, "weights staging");
 
-  // ---- wave roles: channel block cbw; CB pixel blocks pb0 .. pb0 + CB - 1 of 32 ----
-  const int cbw = CB == 2 ? (wave & 1) : 0;
-  const int pb0 = CB == 2 ? 2 * (wave >> 1) : wave;
+  // ---- wave roles: channel block cbw, pixel block pb0 of 32 ----
+  constexpr int CB = 1;
+  const int cbw = WV == 8 ? (wave & 1) : 0;
+  const int pb0 = WV == 8 ? (wave >> 1) : wave;
   // ---- weights: B fragment of k-step st: lane l holds the 8 taps of group
   // g = 2 st + l / 32 for output channel co0 + 32 cbw + l % 32 ----
   const int groups = a.c_in * a.kh;  // (ci, kh) groups
@@ -91,10 +96,10 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
     _Float16* wl = ring;
     const _Float16* src = w + (long long)co0 * per_co;
     if (a.wvec) {  // w 16-byte aligned and the tile's run a whole number of vectors
-      for (int q = tid; q < total / 8; q += 256)
+      for (int q = tid; q < total / 8; q += NT)
         reinterpret_cast<u32x4_t*>(wl)[q] = *reinterpret_cast<const u32x4_t*>(src + 8 * q);
     } else {
-      for (int q = tid; q < total; q += 256) wl[q] = src[q];
+      for (int q = tid; q < total; q += NT) wl[q] = src[q];
     }
   }
   __syncthreads();
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
                                ? (float)static_cast<const _Float16*>(a.bias)[co0 + tid] : 0.0f;
 
   // zero the ring: columns outside the image are never written again
-  for (int i = tid; i < a.ring_bytes / 16; i += 256)
+  for (int i = tid; i < a.ring_bytes / 16; i += NT)
     reinterpret_cast<u32x4_t*>(smem_rb)[i] = u32x4_t{0, 0, 0, 0};
   __syncthreads();
 
@@ -169,9 +174,9 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
     const int items = a.kh * a.c_in * nv;
     u32x4_t t[RB_FILL];
 #pragma unroll
-    for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + 256 * k, items);
+    for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + NT * k, items);
 #pragma unroll
-    for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + 256 * k, items, t[k]);
+    for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + NT * k, items, t[k]);
   }
   // prefetch ring of three: the new rows of output row o sit in lr[(o - r0) % 3]
   u32x4_t lr[3];
@@ -259,19 +264,19 @@ __global__ __launch_bounds__(256) void rowband_kernel(const RowbandArgs a) {
     }
     __syncthreads();
     // ---- whole rows of the tile: 16-byte vectors of 8 output columns ----
-    const int cn = min(32 * CB, a.c_out - co0);
+    const int cn = min(WV == 8 ? 64 : 32, a.c_out - co0);  // channels of the tile
     const int vpr = (a.wo + 7) / 8;
     if constexpr (VEC) {  // wo % 8 == 0: whole vectors; past the end the last one
       // repeats (same value, same address), so the store count is fixed
 #pragma unroll
       for (int k = 0; k < RB_NSTV; ++k) {
-        const int q = min(tid + 256 * k, cn * vpr - 1);
+        const int q = min(tid + NT * k, cn * vpr - 1);
         const int c = q / vpr, v = q - (q / vpr) * vpr;
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + c * RB_OPITCH + 16 * v);
         *reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v) = d;
       }
     } else {
-      for (int q = tid; q < cn * vpr; q += 256) {
+      for (int q = tid; q < cn * vpr; q += NT) {
         const int c = q / vpr, v = q - (q / vpr) * vpr;
         const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(
                                                           otile + c * RB_OPITCH + 16 * v));
@@ -297,11 +302,11 @@ template <int NST>
 static void launch_rb_nst(const RowbandArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const bool two = a.c_out > 32;
   if (a.vec) {
-    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 2, true>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<NST, 1, true>), grid, dim3(256), lds, s, a);
+    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, true>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<NST, 4, true>), grid, dim3(256), lds, s, a);
   } else {
-    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 2, false>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<NST, 1, false>), grid, dim3(256), lds, s, a);
+    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, false>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<NST, 4, false>), grid, dim3(256), lds, s, a);
   }
 }
 
