@@ -126,19 +126,23 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const _Float16* __restrict__ wg =
       static_cast<const _Float16*>(a.wt) + (long long)g * a.cog * a.cig * 9;
 
-  // ---- input staging items: (octet of the stage's 64 channels, 4-pixel group) ----
+  // ---- each wave stages only its own 16 channels of every stage (octets
+  // 2 wave, 2 wave + 1) and its own 16-channel slice of the weights, which are
+  // all its multiplications read: the waves need no barrier between stages and
+  // drift freely, one's loads overlapping another's multiplications ----
+  // input staging items: (one of the wave's two octets, 4-pixel group)
   const int groups4 = (hw + 3) / 4;
-  const int in_items = 8 * groups4;
+  const int in_items = 2 * groups4;
   int in_off[L::NI];
   int in_lds[L::NI][4];
   bool in_live[L::NI];
 #pragma unroll
   for (int i = 0; i < L::NI; ++i) {
-    const int q = tid + i * 256;
+    const int q = lane + i * 64;
     in_live[i] = q < in_items;
     const int qq = in_live[i] ? q : 0;
-    const int o = qq / groups4;
-    const int grp4 = qq - o * groups4;
+    const int o = 2 * wave + qq / groups4;
+    const int grp4 = qq - (qq / groups4) * groups4;
     in_off[i] = 8 * o * hw + 4 * grp4;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -148,19 +152,20 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       in_lds[i][k4] = f < hw ? (pos * 8 + slot8(pos, o)) * 16 : -1;
     }
   }
-  // ---- weight staging vectors: (output channel, 16-byte piece of its 1152 bytes) ----
+  // weight staging vectors: (output channel, 16-byte piece of the wave's 16
+  // channels x 9 taps, 288 contiguous bytes of the channel's 1152)
   int w_off[L::NW];
   int w_lds[L::NW];
   bool w_ok[L::NW], w_live[L::NW];
+  static_assert(L::NW * 64 == 32 * 18, "one weight vector per lane and step");
 #pragma unroll
   for (int i = 0; i < L::NW; ++i) {
-    const int q = tid + i * 256;
-    w_live[i] = q < 32 * 72;
-    const int qq = w_live[i] ? q : 0;
-    const int col = qq / 72, piece = qq - (qq / 72) * 72;
-    w_ok[i] = w_live[i] && co0 + col < a.cog;
-    w_off[i] = w_ok[i] ? (int)((long long)(co0 + col) * a.cig * 9 + piece * 8) : 0;
-    w_lds[i] = L::IN_BYTES + col * RS_WROW + piece * 16;
+    const int q = lane + i * 64;
+    w_live[i] = true;
+    const int col = q / 18, piece = q - (q / 18) * 18;
+    w_ok[i] = co0 + col < a.cog;
+    w_off[i] = w_ok[i] ? (int)((long long)(co0 + col) * a.cig * 9 + 144 * wave + piece * 8) : 0;
+    w_lds[i] = L::IN_BYTES + col * RS_WROW + 288 * wave + piece * 16;
   }
 
   u32x2_t rin[2][L::NI][8];  // two staged stages in flight: [set][item][channel], 4 pixels
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     compute(P);                                   // buffer P holds stage s
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (M <= 1) store_stage(P ^ 1, P ^ 1);  // stage s+1 (set P^1) into buffer P^1
-    __syncthreads();
+    // no barrier: the wave's next multiplications read only what it stored
   };
   typedef std::integral_constant<int, 0> P0;
   typedef std::integral_constant<int, 1> P1;
@@ -395,6 +400,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     const int sg = 4 * q + i4;
     return (sg * 64 + l) ^ ((2 * sg + (l >> 5)) & 15);
   };
+  __syncthreads();  // every wave is done with the stage buffers the partials overwrite
 #pragma unroll
   for (int q = 0; q < NP; ++q)
 #pragma unroll
