@@ -87,44 +87,6 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   // ---- weights: B fragment of k-step st: lane l holds the 8 taps of group
   // g = 2 st + l / 32 for output channel co0 + 32 cbw + l % 32 ----
   const int groups = a.c_in * a.kh;  // (ci, kh) groups
-  // the tile's weights ([<= 64 channels][groups * kw] contiguous) pass through the
-  // ring area with coalesced 16-byte reads when aligned, element reads otherwise
-  {
-    const int per_co = groups * a.kw;
-    const int cn = min(64, a.c_out - co0);
-    const int total = cn * per_co;  // halves
-    _Float16* wl = ring;
-    const _Float16* src = w + (long long)co0 * per_co;
-    if (a.wvec) {  // w 16-byte aligned and the tile's run a whole number of vectors
-      for (int q = tid; q < total / 8; q += NT)
-        reinterpret_cast<u32x4_t*>(wl)[q] = *reinterpret_cast<const u32x4_t*>(src + 8 * q);
-    } else {
-      for (int q = tid; q < total; q += NT) wl[q] = src[q];
-    }
-  }
-  __syncthreads();
-  u32x4_t wf[NST];
-#pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    const int g = 2 * st + (lane >> 5);
-    const int cl = 32 * cbw + (lane & 31);  // channel within the tile
-    const bool okg = g < groups && co0 + cl < a.c_out;
-    const _Float16* wrow = ring + (okg ? cl * (groups * a.kw) + g * a.kw : 0);
-    half8_t v;
-#pragma unroll
-    for (int kw = 0; kw < 8; ++kw) v[kw] = (okg && kw < a.kw) ? wrow[min(kw, a.kw - 1)] : (_Float16)0.0f;
-    wf[st] = __builtin_bit_cast(u32x4_t, v);
-  }
-  __syncthreads();  // the ring area is zeroed next
-  if (tid < 64) bsm[tid] = (a.bias && co0 + tid < a.c_out)
-                               ? (float)static_cast<const _Float16*>(a.bias)[co0 + tid] : 0.0f;
-
-  // zero the ring: columns outside the image are never written again
-  for (int i = tid; i < a.ring_bytes / 16; i += NT)
-    reinterpret_cast<u32x4_t*>(smem_rb)[i] = u32x4_t{0, 0, 0, 0};
-  __syncthreads();
-
-  // ---- input rows: item = (row r of a batch of rows, channel, 8-column vector) ----
   const int nv = (a.w + 7) / 8;  // vectors per input row
   // one item of the batch of rows starting at input row ir0 (clamped into the
   // batch and the image; rows outside the image read as zero)
@@ -168,21 +130,67 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   auto new_rows = [&](int o) __attribute__((always_inline)) { return o * a.sh - a.pt + a.kh - a.sh; };
   const int step_items = a.sh * a.c_in * nv;  // <= 256: one item per thread
 
-  // the KH rows of the band's first output row (at most RB_FILL items per thread)
-  {
-    const int first = r0 * a.sh - a.pt;
-    const int items = a.kh * a.c_in * nv;
-    u32x4_t t[RB_FILL];
+  // ---- prologue: every load first (the band's first KH input rows, the next
+  // three output rows' new input rows, the tile's weights and biases), so their
+  // latencies overlap; then the weights pass through the ring area into
+  // registers, the ring is zeroed and the first rows are stored ----
+  const int first = r0 * a.sh - a.pt;
+  const int fill_items = a.kh * a.c_in * nv;
+  u32x4_t t[RB_FILL];
 #pragma unroll
-    for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + NT * k, items);
-#pragma unroll
-    for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + NT * k, items, t[k]);
-  }
+  for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + NT * k, fill_items);
   // prefetch ring of three: the new rows of output row o sit in lr[(o - r0) % 3]
   u32x4_t lr[3];
   lr[1] = load_item(new_rows(r0 + 1), tid, step_items);
   lr[2] = load_item(new_rows(r0 + 2), tid, step_items);
   lr[0] = load_item(new_rows(r0 + 3), tid, step_items);
+  // the tile's weights ([<= 64 channels][groups * kw] contiguous): 16-byte reads
+  // when aligned (at most RB_WV per thread), element reads otherwise
+  const int per_co = groups * a.kw;
+  const int wtotal = min(64, a.c_out - co0) * per_co;  // halves
+  const _Float16* wsrc = w + (long long)co0 * per_co;
+  constexpr int RB_WV = (64 * 2 * RB_MAXST * 8 / 8 + NT - 1) / NT;
+  u32x4_t wv[RB_WV];
+  if (a.wvec) {  // uniform: w 16-byte aligned and the tile's run a whole number of vectors
+#pragma unroll
+    for (int k = 0; k < RB_WV; ++k)
+      wv[k] = *reinterpret_cast<const u32x4_t*>(wsrc + 8 * min(tid + NT * k, wtotal / 8 - 1));
+  }
+  const float bv_in = (a.bias && co0 + (tid & 63) < a.c_out)
+                          ? (float)static_cast<const _Float16*>(a.bias)[co0 + (tid & 63)] : 0.0f;
+  {
+    _Float16* wl = ring;
+    if (a.wvec) {
+#pragma unroll
+      for (int k = 0; k < RB_WV; ++k) {
+        const int q = tid + NT * k;
+        if (q < wtotal / 8) reinterpret_cast<u32x4_t*>(wl)[q] = wv[k];
+      }
+    } else {
+      for (int q = tid; q < wtotal; q += NT) wl[q] = wsrc[q];
+    }
+  }
+  __syncthreads();
+  u32x4_t wf[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const int g = 2 * st + (lane >> 5);
+    const int cl = 32 * cbw + (lane & 31);  // channel within the tile
+    const bool okg = g < groups && co0 + cl < a.c_out;
+    const _Float16* wrow = ring + (okg ? cl * (groups * a.kw) + g * a.kw : 0);
+    half8_t v;
+#pragma unroll
+    for (int kw = 0; kw < 8; ++kw) v[kw] = (okg && kw < a.kw) ? wrow[min(kw, a.kw - 1)] : (_Float16)0.0f;
+    wf[st] = __builtin_bit_cast(u32x4_t, v);
+  }
+  __syncthreads();  // the ring area is zeroed next
+  if (tid < 64) bsm[tid] = bv_in;
+  // zero the ring: columns outside the image are never written again
+  for (int i = tid; i < a.ring_bytes / 16; i += NT)
+    reinterpret_cast<u32x4_t*>(smem_rb)[i] = u32x4_t{0, 0, 0, 0};
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + NT * k, fill_items, t[k]);
 
   const int half = lane >> 5;  // k-group parity of this lane
   // per k-step: this lane's (ci, kh) group as a ring row base and a tap row
