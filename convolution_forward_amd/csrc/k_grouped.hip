@@ -172,7 +172,8 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
 #pragma unroll
       for (int i = 0; i < 4 * CB; ++i) {
         const int co = 8 * (i / 4) + 4 * hi + (i & 3);
-        v[i] = bias ? acc[u][i] + bsm[co] : acc[u][i];
+        const float bv = bsm[co];  // read outside the condition: no branch per value
+        v[i] = bias ? acc[u][i] + bv : acc[u][i];
       }
       if (rg) {
 #pragma unroll

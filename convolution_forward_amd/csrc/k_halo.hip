@@ -290,7 +290,8 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   for (int k2 = 0; k2 < EPT; ++k2) {
     const int idx = min(tid + 256 * k2, total - 1);
     float s = outt[idx];
-    if (a.bias) s = s + bsm[idx / tile_px];
+    const float bv = bsm[idx / tile_px];  // read outside the condition
+    s = a.bias ? s + bv : s;
     if (res) s = s + v[k2];
     v[k2] = s;
   }

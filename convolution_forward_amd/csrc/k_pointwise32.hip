@@ -188,8 +188,9 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * cb + 4 * lg + i;
+        const float bv = bsm[m];  // read outside the condition: no branch per value
         float t = acc[cb][i];
-        if (bias) t = t + bsm[m];
+        t = bias ? t + bv : t;
         if (res) t = t + res[obase + (long long)min(co0 + m, a.c_out - 1) * a.hw];
         v[4 * cb + i] = t;
       }

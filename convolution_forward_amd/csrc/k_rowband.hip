@@ -247,13 +247,13 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     for (int j = 0; j < CB; ++j) {
       const int c = 32 * cbw + (lane & 31);
       const int pxb = 32 * (pb0 + j);
+      // the bias is read once, outside any branch (a read under the per-value
+      // condition became one branch and one LDS round trip per value)
+      const float bv = bsm[c];
+      const bool hb = a.bias != nullptr;
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float t = acc[j][i];
-        if (a.bias) t = t + bsm[c];
-        v[i] = t;
-      }
+      for (int i = 0; i < 16; ++i) v[i] = hb ? acc[j][i] + bv : acc[j][i];
       if (res) {  // residual read in the fragment layout (clamped, before any store)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
