@@ -12,6 +12,12 @@ namespace convfwd {
 template <typename T>
 __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
 
+// Output store marked nontemporal: y is written once and not read back by the
+// kernel, so its lines need not sit dirty in the L2 until the end-of-kernel
+// release writes them all back at once.
+template <typename V>
+__device__ __forceinline__ void store_out(V* p, V v) { __builtin_nontemporal_store(v, p); }
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 

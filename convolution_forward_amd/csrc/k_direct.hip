@@ -313,13 +313,13 @@ __global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArg
 #pragma unroll
         for (int k = 0; k < DW_NE * 4; ++k) {
           const int o = tid + 256 * k;
-          if (o < tot) y[obase + o] = from_f32<T>(v[k]);
+          if (o < tot) store_out(y + obase + o, from_f32<T>(v[k]));
         }
       } else {
         for (int o = tid; o < tot; o += 256) {
           float f[1] = {outt[o] + bcur[mdiv(o, a.mg_howo)]};
           act_array(f, a.act, a.alpha, a.beta);
-          y[obase + o] = from_f32<T>(f[0]);
+          store_out(y + obase + o, from_f32<T>(f[0]));
         }
       }
     }
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
 #pragma unroll
         for (int k = 0; k < DWW_NE * 4; ++k) {
           const int o = lane + 64 * k;
-          if (o < tot) y[obase + o] = from_f32<T>(v[k]);
+          if (o < tot) store_out(y + obase + o, from_f32<T>(v[k]));
         }
       } else {
 #pragma unroll
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
           }
           act_array(f, a.act, a.alpha, a.beta);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[obase + min(lane + 64 * (4 * k + e), tot - 1)] = from_f32<T>(f[e]);
+          for (int e = 0; e < 4; ++e) store_out(y + obase + min(lane + 64 * (4 * k + e), tot - 1), from_f32<T>(f[e]));
         }
       }
     }

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
 #pragma unroll
         for (int i = 0; i < 4 * CB; ++i) {
           const int co = 8 * (i / 4) + 4 * hi + (i & 3);
-          if (co < a.cog) yg[co * howo + pix[u]] = (_Float16)v[i];
+          if (co < a.cog) store_out(yg + co * howo + pix[u], (_Float16)v[i]);
         }
       }
     }

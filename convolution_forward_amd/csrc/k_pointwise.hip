@@ -335,7 +335,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const half8_t hv = {e0[0], e1[0], e0[1], e1[1], e0[2], e1[2], e0[3], e1[3]};
         _Float16* dst = y + (((long long)n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v;
         if constexpr (VEC) {
-          *reinterpret_cast<half8_t*>(dst) = hv;
+          store_out(reinterpret_cast<half8_t*>(dst), hv);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dst[e] = hv[e];
@@ -351,7 +351,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const int q = tid + 256 * k;
         const int row = min(q >> 4, rlast), px = min(8 * (q & 15), pvalid - 8);
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(smem + row * PW_OROW + 2 * px);
-        *reinterpret_cast<u32x4_t*>(y + ((long long)n * a.c_out + co0 + row) * hw + p0 + px) = d;
+        store_out(reinterpret_cast<u32x4_t*>(y + ((long long)n * a.c_out + co0 + row) * hw + p0 + px), d);
       }
     } else {
 #pragma unroll 1

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * cb + 4 * lg + i;
-        if (co0 + m < a.c_out) y[obase + (long long)(co0 + m) * a.hw] = v[4 * cb + i];
+        if (co0 + m < a.c_out) store_out(y + obase + (long long)(co0 + m) * a.hw, v[4 * cb + i]);
       }
   }
 }

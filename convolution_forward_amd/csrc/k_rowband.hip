@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
         const int q = min(tid + NT * k, cn * vpr - 1);
         const int c = q / vpr, v = q - (q / vpr) * vpr;
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + c * RB_OPITCH + 16 * v);
-        *reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v) = d;
+        store_out(reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v), d);
       }
     } else {
       for (int q = tid; q < cn * vpr; q += NT) {

@@ -172,12 +172,31 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   u32x4_t rwv[2][L::NW];
   const int nstages = a.cig / RS_CH;
 
-  auto load_stage = [&](int s, int set) __attribute__((always_inline)) {
+  // the loads of one stage in three parts (part 0 and 1: the two halves of the
+  // input items, part 2: the weights), so that each tap row's multiplications
+  // can carry one part
+  static_assert(L::NI % 2 == 0, "input items split in two halves");
+  auto load_part = [&](int s, int set, int part) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
-    if constexpr (XV) {  // 8-byte aligned planes of whole 4-pixel groups
+    const int i0 = part == 1 ? L::NI / 2 : 0, i1 = part == 0 ? L::NI / 2 : part == 1 ? L::NI : 0;
+    if (part == 2) {
+      if constexpr (WV) {  // 16-byte aligned weights
 #pragma unroll
-      for (int i = 0; i < L::NI; ++i) {
+        for (int i = 0; i < L::NW; ++i)
+          rwv[set][i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < L::NW; ++i) {
+          half8_t h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = wg[woff + w_off[i] + e];
+          rwv[set][i] = __builtin_bit_cast(u32x4_t, h);
+        }
+      }
+    } else if constexpr (XV) {  // 8-byte aligned planes of whole 4-pixel groups
+#pragma unroll
+      for (int i = i0; i < i1; ++i) {
         const _Float16* src = ximg + xoff + in_off[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       }
     } else {  // input not 8-byte aligned or planes not a multiple of 4: element loads
 #pragma unroll
-      for (int i = 0; i < L::NI; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const _Float16* src = ximg + xoff + in_off[i];
         const int left = hw - 1 - (in_off[i] % hw);  // last valid pixel of this group
 #pragma unroll
@@ -197,19 +216,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         }
       }
     }
-    if constexpr (WV) {  // 16-byte aligned weights
-#pragma unroll
-      for (int i = 0; i < L::NW; ++i)
-        rwv[set][i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < L::NW; ++i) {
-        half8_t h;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = wg[woff + w_off[i] + e];
-        rwv[set][i] = __builtin_bit_cast(u32x4_t, h);
-      }
-    }
+  };
+  auto load_stage = [&](int s, int set) __attribute__((always_inline)) {
+    load_part(s, set, 0);
+    load_part(s, set, 1);
+    load_part(s, set, 2);
   };
 
   // Branch-free: dead items and pixels past the plane write the sink, so no
@@ -248,7 +259,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int pcol = lane & 15;
   const int oct = 2 * wave + grp;    // octet of the stage's 64 channels
 
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // hook(kh): issued with tap row kh's multiplications (the next stage's loads)
+  auto compute = [&](int buf, auto hook) __attribute__((always_inline)) {
     const unsigned char* in = smem + buf * L::STAGE;
     // B: this lane's 8 channels x 9 taps (144 contiguous bytes of output channel lane % 32)
     const unsigned char* wb =
@@ -277,6 +289,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         const int pos = (2 * q + kh + prow) * RS_COLS + pcol;
         fr[q] = *reinterpret_cast<const u32x4_t*>(in + (pos * 8 + slot8(pos, oct)) * 16);
       }
+      hook(kh);
 #pragma unroll
       for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
@@ -284,9 +297,18 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           const u32x4_t f = kw == 0 ? fr[q] : kw == 1 ? row_shift<1>(fr[q]) : row_shift<2>(fr[q]);
           acc[q] = mfma32(f, bf[kh * 3 + kw], acc[q]);
         }
+      // the loads go out between the multiplications: a load whose issue
+      // stalls (memory pipeline full) then leaves the matrix unit busy
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3 * NP - 18, 0);
       __builtin_amdgcn_sched_barrier(0);  // one tap row's fragments live at a time
     }
   };
+  auto no_hook = [](int) __attribute__((always_inline)) {};
 
   // ---- epilogue items: item it = (channel co, output row oh, column quad) with
   // the quad fastest, then the row (R rows), then the channel; thread t takes
@@ -339,13 +361,13 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   auto step = [&](int s, auto parity, auto mode) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
     constexpr int M = decltype(mode)::value;
-    if constexpr (M == 0) load_stage(s + 2, P);  // set P: stage s was stored last step
     if constexpr (M == 2) load_epilogue_operands();  // bias and residual
-    // the scheduler must not sink these loads below the multiplications (which
-    // would shorten the prefetch to nothing) nor hoist the regrouping of set P^1
-    // into them (which waits for that set early)
+    // the scheduler must not hoist the regrouping of set P^1 into the
+    // multiplications (which waits for that set early)
     __builtin_amdgcn_sched_barrier(0);
-    compute(P);                                   // buffer P holds stage s
+    // buffer P holds stage s; stage s+2 is loaded into set P (stored last step)
+    if constexpr (M == 0) compute(P, [&](int kh) __attribute__((always_inline)) { load_part(s + 2, P, kh); });
+    else compute(P, no_hook);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (M <= 1) store_stage(P ^ 1, P ^ 1);  // stage s+1 (set P^1) into buffer P^1
     // no barrier: the wave's next multiplications read only what it stored
