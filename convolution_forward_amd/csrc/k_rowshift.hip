@@ -226,10 +226,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // Branch-free: dead items and pixels past the plane write the sink, so no
   // store sits behind a branch (which would make the compiler wait for every
   // outstanding load there, including the stage just prefetched).
-  auto store_stage = [&](int buf, int set) __attribute__((always_inline)) {
+  auto store_part = [&](int buf, int set, int part) __attribute__((always_inline)) {
     unsigned char* base = smem + buf * L::STAGE;
+    const int i0 = part == 1 ? L::NI / 2 : 0, i1 = part == 0 ? L::NI / 2 : part == 1 ? L::NI : 0;
 #pragma unroll
-    for (int i = 0; i < L::NI; ++i) {
+    for (int i = i0; i < i1; ++i) {
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         half8_t v;
@@ -240,12 +241,19 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         *reinterpret_cast<half8_t*>(dst) = v;
       }
     }
+    if (part == 2) {
 #pragma unroll
-    for (int i = 0; i < L::NW; ++i) {
-      const u32x4_t v = w_ok[i] ? rwv[set][i] : u32x4_t{0, 0, 0, 0};
-      unsigned char* dst = w_live[i] ? base + w_lds[i] : smem + L::SINK;
-      *reinterpret_cast<u32x4_t*>(dst) = v;
+      for (int i = 0; i < L::NW; ++i) {
+        const u32x4_t v = w_ok[i] ? rwv[set][i] : u32x4_t{0, 0, 0, 0};
+        unsigned char* dst = w_live[i] ? base + w_lds[i] : smem + L::SINK;
+        *reinterpret_cast<u32x4_t*>(dst) = v;
+      }
     }
+  };
+  auto store_stage = [&](int buf, int set) __attribute__((always_inline)) {
+    store_part(buf, set, 0);
+    store_part(buf, set, 1);
+    store_part(buf, set, 2);
   };
 
   floatx16_t acc[NP];
@@ -259,7 +267,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int pcol = lane & 15;
   const int oct = 2 * wave + grp;    // octet of the stage's 64 channels
 
-  // hook(kh): issued with tap row kh's multiplications (the next stage's loads)
+  // hook(kh): issued with tap row kh's multiplications (the next stages' loads
+  // and stores)
   auto compute = [&](int buf, auto hook) __attribute__((always_inline)) {
     const unsigned char* in = smem + buf * L::STAGE;
     // B: this lane's 8 channels x 9 taps (144 contiguous bytes of output channel lane % 32)
@@ -303,6 +312,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       for (int j = 0; j < 9; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // 1 VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // 1 DS write
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 3 * NP - 18, 0);
       __builtin_amdgcn_sched_barrier(0);  // one tap row's fragments live at a time
@@ -365,11 +375,19 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     // the scheduler must not hoist the regrouping of set P^1 into the
     // multiplications (which waits for that set early)
     __builtin_amdgcn_sched_barrier(0);
-    // buffer P holds stage s; stage s+2 is loaded into set P (stored last step)
-    if constexpr (M == 0) compute(P, [&](int kh) __attribute__((always_inline)) { load_part(s + 2, P, kh); });
-    else compute(P, no_hook);
+    // buffer P holds stage s; stage s+2 is loaded into set P (stored last
+    // step) and stage s+1 (set P^1) is stored into buffer P^1, a third of each
+    // with every tap row
+    if constexpr (M == 0)
+      compute(P, [&](int kh) __attribute__((always_inline)) {
+        load_part(s + 2, P, kh);
+        store_part(P ^ 1, P ^ 1, kh);
+      });
+    else if constexpr (M == 1)
+      compute(P, [&](int kh) __attribute__((always_inline)) { store_part(P ^ 1, P ^ 1, kh); });
+    else
+      compute(P, no_hook);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (M <= 1) store_stage(P ^ 1, P ^ 1);  // stage s+1 (set P^1) into buffer P^1
     // no barrier: the wave's next multiplications read only what it stored
   };
   typedef std::integral_constant<int, 0> P0;
@@ -380,8 +398,10 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // the tile's biases, loaded first (any valid address without bias) and kept
   // in LDS for the epilogue
   const _Float16 b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
+  // only stage 0 is loaded before the first multiplications: stages 1 and 2
+  // are issued with stage 0's multiplications, so that the multiplications
+  // start as soon as the first stage has arrived
   load_stage(0, 0);
-  load_stage(min(1, nstages - 1), 1);
   // zero both stages' input regions while the first loads fly: padding
   // positions are never written again
   for (int q = tid; q < 2 * (L::IN_BYTES / 16); q += 256) {
@@ -392,20 +412,29 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   store_stage(0, 0);
   if (tid < 32) bsm[tid] = (float)b_in;
   __syncthreads();
-  int s = 0;
+  // step 0: stage 1 into set 1 with the multiplications, then stage 2 into
+  // set 0 (stage indexes clamped: with fewer stages the extra loads repeat the
+  // last stage and are unused), then stage 1 into buffer 1
+  if (nstages == 1) load_epilogue_operands();
+  __builtin_amdgcn_sched_barrier(0);
+  compute(0, [&](int kh) __attribute__((always_inline)) { load_part(min(1, nstages - 1), 1, kh); });
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(min(2, nstages - 1), 0);
+  if (nstages > 1) store_stage(1, 1);
+  int s = 1;
   for (; s + 3 < nstages; s += 2) {  // both steps prefetch a stage
-    step(s, P0{}, LOAD{});
-    step(s + 1, P1{}, LOAD{});
+    step(s, P1{}, LOAD{});
+    step(s + 1, P0{}, LOAD{});
   }
   if (nstages - s == 3) {
-    step(s, P0{}, LOAD{});
-    step(s + 1, P1{}, STORE_ONLY{});
-    step(s + 2, P0{}, LAST{});
+    step(s, P1{}, LOAD{});
+    step(s + 1, P0{}, STORE_ONLY{});
+    step(s + 2, P1{}, LAST{});
   } else if (nstages - s == 2) {
-    step(s, P0{}, STORE_ONLY{});
-    step(s + 1, P1{}, LAST{});
-  } else {
-    step(s, P0{}, LAST{});
+    step(s, P1{}, STORE_ONLY{});
+    step(s + 1, P0{}, LAST{});
+  } else if (nstages - s == 1) {
+    step(s, P1{}, LAST{});
   }
 
   // ---- the four waves' partial sums are added through LDS.  Wave w writes its

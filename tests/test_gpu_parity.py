@@ -197,6 +197,9 @@ ROWSHIFT_CASES = [
      True, False),
     (oracle.Geom(1, 192, 16, 16, 32, 3, 3), True, True),  # no pads: 14 x 14 out
     (oracle.Geom(2, 64, 5, 4, 48, 3, 3, pt=2, pl=2, pb=1, pr=2, act="hard_swish"), True, True),
+    # five and six 64-channel stages: the steady-state loop of the pipeline
+    (oracle.Geom(2, 320, 6, 6, 32, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu"), False, True),
+    (oracle.Geom(1, 384, 9, 9, 64, 3, 3, pt=1, pl=1, pb=1, pr=1), True, True),
 ]
 
 
