@@ -705,6 +705,11 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
                (g.ho * g.wo) % 4 == 0;
       a.o2 = reinterpret_cast<uintptr_t>(yc) % 4 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 4 == 0) &&
              g.wo % 2 == 0;
+      // every 32-channel tile of y starts 16-byte aligned: (image, channel)
+      // plane offsets n c_out + g cog + 32 k times ho wo are multiples of 8
+      a.oflat = reinterpret_cast<uintptr_t>(yc) % 16 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 16 == 0) &&
+                g.wo % 2 == 0 && g.ho * g.wo >= 8 && (g.co * g.ho * g.wo) % 8 == 0 &&
+                (g.cog * g.ho * g.wo) % 8 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = pl.halo.rowshift ? launch_rowshift(a, s) : launch_halo(a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {

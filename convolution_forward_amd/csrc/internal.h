@@ -81,6 +81,8 @@ struct HaloArgs {
   int xvec;              // input planes may be read 8 bytes at a time
   int ovec;              // output / residual planes may be written / read 8 bytes at a time
   int o2;                // row-shift kernel: y and residual 4-byte aligned, wo even
+  int oflat;             // row-shift kernel: y and residual 16-byte aligned at every
+                         // 32-channel tile, wo even, ho * wo >= 8
   int act;
   float alpha, beta;
 };

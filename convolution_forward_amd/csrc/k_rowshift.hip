@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // the epilogue's partial sums (4 waves x NP row pairs x 16 floats x 64 lanes)
   // reuse the two stage buffers
   static_assert(4 * NP * 16 * 64 * 4 <= L::SINK, "epilogue does not fit");
+  static_assert(4 * 32 * R * (RS_COLS - 2) * 4 <= L::SINK, "flat epilogue does not fit");
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
 
   const int tid = threadIdx.x;
@@ -350,17 +351,20 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
                  __umul24((unsigned)min(it_oh(k), a.ho - 1), (unsigned)a.wo)) +
            min(it_ow + j, a.wo - back);
   };
-  unsigned rq[KI][2];  // residual pairs (pair path), prefetched during the last step
+  // flat path: the tile's outputs (its channels' planes, contiguous in y) as
+  // vectors of 8; thread t takes vectors t + 256 k, k < KV, clamped to the last
+  constexpr int KV = (32 * R * (RS_COLS - 2) / 8 + 255) / 256;
+  const bool flat = a.oflat;  // uniform
+  const int ftot = min(32, a.cog - co0) * howo;  // a multiple of 8 on the flat path
+  const int nvec = ftot >> 3;
+  u32x4_t rv[KV];  // the residual (flat path), prefetched during the last step
   auto load_epilogue_operands = [&]() __attribute__((always_inline)) {
-    if (res && pairs) {  // uniform
-      // a buffer descriptor over the tile's residual: 32-bit offsets, no 64-bit
-      // address arithmetic between the loads
-      const __amdgpu_buffer_rsrc_t rr = uniform_rsrc(res + obase, min(32, a.cog - co0) * howo * 2);
+    if (res && flat) {  // uniform
+      const __amdgpu_buffer_rsrc_t rr = uniform_rsrc(res + obase, ftot * 2);
 #pragma unroll
-      for (int k = 0; k < KI; ++k)
-#pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2)
-          rq[k][j2] = __builtin_amdgcn_raw_buffer_load_b32(rr, 2 * e_clamped(k, 2 * j2, 2), 0, 0);
+      for (int k = 0; k < KV; ++k)
+        rv[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rr, 16 * min(tid + 256 * k, nvec - 1), 0, 0));
     }
   };
 
@@ -437,6 +441,68 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     step(s, P1{}, LAST{});
   }
 
+  typedef float floatx4_t __attribute__((ext_vector_type(4)));
+  if (flat) {
+    // ---- flat epilogue (y and residual 16-byte aligned at the tile, wo even,
+    // planes of at least 8 outputs): wave w writes its partial sums as float
+    // pairs into its own float32 copy of the tile, laid out like y (channel
+    // planes of Ho x Wo); each thread then takes 8 consecutive outputs (at most
+    // two channels), adds the four waves' partials in wave order
+    // (((w0 + w1) + w2) + w3), the bias and the residual, applies the
+    // activation and writes 16 bytes. ----
+    typedef float floatx2_t __attribute__((ext_vector_type(2)));
+    float* ft = reinterpret_cast<float*>(smem);
+    const int FT = 32 * howo;  // floats per wave copy
+    const int fco = lane & 31, fh = lane >> 5;
+    __syncthreads();  // every wave is done with the stage buffers the copies overwrite
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const int p = 8 * i4 + 4 * fh + 2 * j2;  // pixel of the row pair (accumulator element 4 i4 + 2 j2)
+          const int row = 2 * q + (p >> 4), col = p & 15;
+          const bool ok = row < a.ho && col < a.wo;  // wo even: the pair is whole
+          float* dst = ok ? ft + wave * FT + fco * howo + row * a.wo + col : reinterpret_cast<float*>(smem + L::SINK);
+          *reinterpret_cast<floatx2_t*>(dst) = floatx2_t{acc[q][4 * i4 + 2 * j2], acc[q][4 * i4 + 2 * j2 + 1]};
+        }
+    __syncthreads();
+    _Float16* yt = static_cast<_Float16*>(a.y) + obase;
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+      // vectors past the tile repeat the last one (same value, same address):
+      // the store count is fixed
+      const int e0 = 8 * min(tid + 256 * k, nvec - 1);
+      const floatx4_t* src = reinterpret_cast<const floatx4_t*>(ft + e0);
+      floatx4_t lo = src[0] + src[FT / 4], hi = src[1] + src[FT / 4 + 1];
+      lo = lo + src[FT / 2];
+      hi = hi + src[FT / 2 + 1];
+      lo = lo + src[3 * FT / 4];
+      hi = hi + src[3 * FT / 4 + 1];
+      const int c0 = e0 / howo, cb = (c0 + 1) * howo;  // channel of the first output, start of the next
+      const float b0 = bsm[c0], b1 = bsm[min(c0 + 1, 31)];
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = j < 4 ? lo[j] : hi[j - 4];
+        const float bv = e0 + j < cb ? b0 : b1;
+        v[j] = bias ? t + bv : t;
+      }
+      if (res) {
+        const half8_t r8 = __builtin_bit_cast(half8_t, rv[k]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = v[j] + (float)r8[j];
+      }
+      act_array(v, a.act, a.alpha, a.beta);
+      half8_t h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
+      *reinterpret_cast<half8_t*>(yt + e0) = h;
+    }
+    return;
+  }
+
   // ---- the four waves' partial sums are added through LDS.  Wave w writes its
   // 16 floats of row pair q as 4 float4 slot groups i4 (accumulator elements
   // 4 i4 .. 4 i4 + 3: pixels 8 i4 + 4 (l / 32) + 0..3 of the pair, one output
@@ -445,7 +511,6 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // 64 lanes) and the item reads (one channel, 16 consecutive items) hit
   // distinct banks.  Each item adds its four waves' float4 in wave order,
   // ((w0 + w1) + w2) + w3. ----
-  typedef float floatx4_t __attribute__((ext_vector_type(4)));
   floatx4_t* part = reinterpret_cast<floatx4_t*>(smem);
   auto slot = [](int q, int i4, int l) __attribute__((always_inline)) {
     const int sg = 4 * q + i4;
@@ -477,7 +542,13 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     for (int j = 0; j < 4; ++j) v[4 * k + j] = bias ? t[j] + bv : t[j];
   }
   if (res) {
-    if (pairs) {  // prefetched before the last multiplication step
+    if (pairs) {  // every residual read before any store (y may alias it)
+      unsigned rq[KI][2];
+#pragma unroll
+      for (int k = 0; k < KI; ++k)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+          rq[k][j2] = *reinterpret_cast<const unsigned*>(res + obase + e_clamped(k, 2 * j2, 2));
 #pragma unroll
       for (int k = 0; k < KI; ++k)
 #pragma unroll
