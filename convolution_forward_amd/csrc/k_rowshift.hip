@@ -406,15 +406,23 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // are issued with stage 0's multiplications, so that the multiplications
   // start as soon as the first stage has arrived
   load_stage(0, 0);
-  // zero both stages' input regions while the first loads fly: padding
-  // positions are never written again
-  for (int q = tid; q < 2 * (L::IN_BYTES / 16); q += 256) {
-    const int st = q / (L::IN_BYTES / 16), off = q - st * (L::IN_BYTES / 16);
-    *reinterpret_cast<u32x4_t*>(smem + st * L::STAGE + off * 16) = u32x4_t{0, 0, 0, 0};
+  // zero the padding positions of both stages' input regions (rows and
+  // columns outside the image) while the first loads fly: staging writes only
+  // image positions, so these stay zero
+  for (int q = tid; q < 2 * L::NPOS; q += 256) {
+    const int st = q / L::NPOS, pos = q - st * L::NPOS;
+    const int r = pos / RS_COLS - a.pt, c = pos % RS_COLS - a.pl;
+    if (r < 0 || r >= a.h || c < 0 || c >= a.w) {
+#pragma unroll
+      for (int o = 0; o < 8; ++o)
+        *reinterpret_cast<u32x4_t*>(smem + st * L::STAGE + (pos * 8 + o) * 16) = u32x4_t{0, 0, 0, 0};
+    }
   }
   __syncthreads();
   store_stage(0, 0);
-  if (tid < 32) bsm[tid] = (float)b_in;
+  // without a bias the slot holds -0.0, whose addition is exact for every
+  // value (a zero keeps its sign), so the epilogue adds it unconditionally
+  if (tid < 32) bsm[tid] = bias ? (float)b_in : -0.0f;
   __syncthreads();
   // step 0: stage 1 into set 1 with the multiplications, then stage 2 into
   // set 0 (stage indexes clamped: with fewer stages the extra loads repeat the
@@ -469,6 +477,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
         }
     __syncthreads();
     _Float16* yt = static_cast<_Float16*>(a.y) + obase;
+    const float rhowo = 1.0f / (float)howo;
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
       // vectors past the tile repeat the last one (same value, same address):
@@ -480,14 +489,17 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       hi = hi + src[FT / 2 + 1];
       lo = lo + src[3 * FT / 4];
       hi = hi + src[3 * FT / 4 + 1];
-      const int c0 = e0 / howo, cb = (c0 + 1) * howo;  // channel of the first output, start of the next
+      // channel of the first output, and the start of the next: (e0 + 1/2) / howo
+      // lies at least 1 / (2 howo) from an integer, far beyond the float error
+      // for tiles of at most 32 x 14 x 14 outputs, so the truncation is exact
+      const int c0 = (int)(((float)e0 + 0.5f) * rhowo), cb = (c0 + 1) * howo;
       const float b0 = bsm[c0], b1 = bsm[min(c0 + 1, 31)];
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float t = j < 4 ? lo[j] : hi[j - 4];
         const float bv = e0 + j < cb ? b0 : b1;
-        v[j] = bias ? t + bv : t;
+        v[j] = t + bv;
       }
       if (res) {
         const half8_t r8 = __builtin_bit_cast(half8_t, rv[k]);
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     t = t + part[3 * NP * 256 + sl];
     const float bv = bsm[it_co(k)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * k + j] = bias ? t[j] + bv : t[j];
+    for (int j = 0; j < 4; ++j) v[4 * k + j] = t[j] + bv;
   }
   if (res) {
     if (pairs) {  // every residual read before any store (y may alias it)
