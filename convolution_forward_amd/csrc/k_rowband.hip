@@ -88,13 +88,28 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   // g = 2 st + l / 32 for output channel co0 + 32 cbw + l % 32 ----
   const int groups = a.c_in * a.kh;  // (ci, kh) groups
   const int nv = (a.w + 7) / 8;  // vectors per input row
+  // item q of a batch of rows: vector v of row r of channel ci (the batch's
+  // rows are consecutive input rows); decomposed once per thread, since every
+  // row step uses the same items
+  struct Item {
+    int v, ci, r;
+    bool live;
+  };
+  auto decomp = [&](int q, int items) __attribute__((always_inline)) {
+    Item it;
+    const int qc = min(q, items - 1);
+    it.v = qc % nv;
+    const int rc = qc / nv;
+    it.ci = rc % a.c_in;
+    it.r = rc / a.c_in;
+    it.live = q < items;
+    return it;
+  };
   // one item of the batch of rows starting at input row ir0 (clamped into the
   // batch and the image; rows outside the image read as zero)
-  auto load_item = [&](int ir0, int q, int items) __attribute__((always_inline)) {
-    q = min(q, items - 1);
-    const int v = q % nv, rc = q / nv;
-    const int ci = rc % a.c_in, r = rc / a.c_in;
-    const int ir = ir0 + r;
+  auto load_item = [&](int ir0, const Item& it) __attribute__((always_inline)) {
+    const int v = it.v, ci = it.ci;
+    const int ir = ir0 + it.r;
     const _Float16* src = x + ((long long)ci * a.h + min(max(ir, 0), a.h - 1)) * a.w + 8 * v;
     u32x4_t d;
     if constexpr (VEC) {  // w % 8 == 0, 16-byte aligned rows
@@ -108,11 +123,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     return (ir >= 0 && ir < a.h) ? d : u32x4_t{0, 0, 0, 0};
   };
   // ...and its store into the ring (input column c at ring column c + pl)
-  auto store_item = [&](int ir0, int q, int items, u32x4_t d) __attribute__((always_inline)) {
-    if (q < items) {
-      const int v = q % nv, rc = q / nv;
-      const int ci = rc % a.c_in, r = rc / a.c_in;
-      const int slot = (ir0 + r) & (RB_RING - 1);
+  auto store_item = [&](int ir0, const Item& it, u32x4_t d) __attribute__((always_inline)) {
+    if (it.live) {
+      const int v = it.v, ci = it.ci;
+      const int slot = (ir0 + it.r) & (RB_RING - 1);
       _Float16* dst = ring + (ci * RB_RING + slot) * rp + a.pl + 8 * v;
       const half8_t h = __builtin_bit_cast(half8_t, d);
       if constexpr (VEC) {  // w % 8 == 0: whole vectors (the ring column offset is odd-aligned)
@@ -137,13 +151,18 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   const int first = r0 * a.sh - a.pt;
   const int fill_items = a.kh * a.c_in * nv;
   u32x4_t t[RB_FILL];
+  Item fit[RB_FILL];
 #pragma unroll
-  for (int k = 0; k < RB_FILL; ++k) t[k] = load_item(first, tid + NT * k, fill_items);
+  for (int k = 0; k < RB_FILL; ++k) {
+    fit[k] = decomp(tid + NT * k, fill_items);
+    t[k] = load_item(first, fit[k]);
+  }
   // prefetch ring of three: the new rows of output row o sit in lr[(o - r0) % 3]
+  const Item sit = decomp(tid, step_items);
   u32x4_t lr[3];
-  lr[1] = load_item(new_rows(r0 + 1), tid, step_items);
-  lr[2] = load_item(new_rows(r0 + 2), tid, step_items);
-  lr[0] = load_item(new_rows(r0 + 3), tid, step_items);
+  lr[1] = load_item(new_rows(r0 + 1), sit);
+  lr[2] = load_item(new_rows(r0 + 2), sit);
+  lr[0] = load_item(new_rows(r0 + 3), sit);
   // the tile's weights ([<= 64 channels][groups * kw] contiguous): 16-byte reads
   // when aligned (at most RB_WV per thread), element reads otherwise
   const int per_co = groups * a.kw;
@@ -156,8 +175,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     for (int k = 0; k < RB_WV; ++k)
       wv[k] = *reinterpret_cast<const u32x4_t*>(wsrc + 8 * min(tid + NT * k, wtotal / 8 - 1));
   }
+  // without a bias the slot holds -0.0, whose addition is exact for every
+  // value (a zero keeps its sign), so the epilogue adds it unconditionally
   const float bv_in = (a.bias && co0 + (tid & 63) < a.c_out)
-                          ? (float)static_cast<const _Float16*>(a.bias)[co0 + (tid & 63)] : 0.0f;
+                          ? (float)static_cast<const _Float16*>(a.bias)[co0 + (tid & 63)] : -0.0f;
   {
     _Float16* wl = ring;
     if (a.wvec) {
@@ -171,17 +192,43 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     }
   }
   __syncthreads();
+  // fragment st: the a.kw taps of group g start at half h0 = cl * per_co +
+  // g * kw of the staged weights; five dwords from dword h0 / 2, funnel-shifted
+  // by 16 bits when h0 is odd, hold halves h0 .. h0 + 7; taps past a.kw and
+  // padded groups or channels are masked to zero.  The reads run ahead of any
+  // use at clamped addresses (the few halves past the weights are other LDS
+  // data, masked off).
   u32x4_t wf[NST];
-#pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    const int g = 2 * st + (lane >> 5);
+  {
     const int cl = 32 * cbw + (lane & 31);  // channel within the tile
-    const bool okg = g < groups && co0 + cl < a.c_out;
-    const _Float16* wrow = ring + (okg ? cl * (groups * a.kw) + g * a.kw : 0);
-    half8_t v;
+    const bool okc = co0 + cl < a.c_out;
+    const int hc = min(cl, a.c_out - co0 - 1) * per_co;
+    unsigned dw[NST][5];
 #pragma unroll
-    for (int kw = 0; kw < 8; ++kw) v[kw] = (okg && kw < a.kw) ? wrow[min(kw, a.kw - 1)] : (_Float16)0.0f;
-    wf[st] = __builtin_bit_cast(u32x4_t, v);
+    for (int st = 0; st < NST; ++st) {
+      const int h0 = hc + min(2 * st + (lane >> 5), groups - 1) * a.kw;
+      const unsigned* src = reinterpret_cast<const unsigned*>(ring) + (h0 >> 1);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) dw[st][i] = src[i];
+    }
+    // an empty asm that takes the values: the reads stay unconditional (the
+    // compiler would otherwise put reads behind the masking branches)
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      asm volatile("" : "+v"(dw[st][0]), "+v"(dw[st][1]), "+v"(dw[st][2]), "+v"(dw[st][3]), "+v"(dw[st][4]));
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int g = 2 * st + (lane >> 5);
+      const int h0 = hc + min(g, groups - 1) * a.kw;
+      const unsigned sh = (unsigned)(h0 & 1) * 16u;
+      const bool okg = okc && g < groups;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned keep = (2 * i + 1 < a.kw ? 0xFFFF0000u : 0u) | (2 * i < a.kw ? 0x0000FFFFu : 0u);
+        const unsigned f = __builtin_amdgcn_alignbit(dw[st][i + 1], dw[st][i], sh);
+        wf[st][i] = okg ? (f & keep) : 0u;
+      }
+    }
   }
   __syncthreads();  // the ring area is zeroed next
   if (tid < 64) bsm[tid] = bv_in;
@@ -190,15 +237,17 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     reinterpret_cast<u32x4_t*>(smem_rb)[i] = u32x4_t{0, 0, 0, 0};
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < RB_FILL; ++k) store_item(first, tid + NT * k, fill_items, t[k]);
+  for (int k = 0; k < RB_FILL; ++k) store_item(first, fit[k], t[k]);
 
   const int half = lane >> 5;  // k-group parity of this lane
   // per k-step: this lane's (ci, kh) group as a ring row base and a tap row
   int gbase[NST], gkh[NST];
+  // g / kh as (g * m) >> 16 with m = ceil(65536 / kh): exact for g < 4096 / kh
+  const unsigned mkh = (65536u + (unsigned)a.kh - 1) / (unsigned)a.kh;
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
     const int g = min(2 * st + half, groups - 1);  // the padded group multiplies zero weights
-    const int ci = g / a.kh;
+    const int ci = (int)(__umul24((unsigned)g, mkh) >> 16);
     gkh[st] = g - ci * a.kh;
     gbase[st] = ci * RB_RING * rp;
   }
@@ -213,10 +262,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   auto row = [&](int oh, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
     // the next output row's new input rows go to ring slots this row does not use
-    store_item(new_rows(oh + 1), tid, step_items, lr[(J + 1) % 3]);
+    store_item(new_rows(oh + 1), sit, lr[(J + 1) % 3]);
     __syncthreads();  // rows of oh present; the previous row's tile has left
     // those registers now take the rows of output row oh + 4 (three rows ahead)
-    lr[(J + 1) % 3] = load_item(new_rows(oh + 4), tid, step_items);
+    lr[(J + 1) % 3] = load_item(new_rows(oh + 4), sit);
 
     // ---- MFMA: k-step st covers groups 2 st (lanes 0-31) and 2 st + 1 (32-63) ----
     floatx16_t acc[CB];
@@ -250,10 +299,9 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
       // the bias is read once, outside any branch (a read under the per-value
       // condition became one branch and one LDS round trip per value)
       const float bv = bsm[c];
-      const bool hb = a.bias != nullptr;
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = hb ? acc[j][i] + bv : acc[j][i];
+      for (int i = 0; i < 16; ++i) v[i] = acc[j][i] + bv;
       if (res) {  // residual read in the fragment layout (clamped, before any store)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
