@@ -644,6 +644,9 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.kh = (int)g.kh; a.kw = (int)g.kw; a.sh = (int)g.sh; a.pt = (int)g.pt; a.pl = (int)g.pl;
       a.ho = (int)g.ho; a.wo = (int)g.wo;
       a.n_ct = (int)ceil_div(g.co, 64);
+      a.mg_nv = make_magic((unsigned)((g.w + 7) / 8));
+      a.mg_cin = make_magic((unsigned)g.ci);
+      a.mg_vpr = make_magic((unsigned)((g.wo + 7) / 8));
       a.band_rows = pl.rb_band_rows;
       a.n_band = (int)ceil_div(g.ho, a.band_rows);
       const int64_t need = std::max<int64_t>(g.pl + g.w, 2 * (g.wo - 1) + 8);

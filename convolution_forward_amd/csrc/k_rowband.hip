@@ -98,10 +98,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   auto decomp = [&](int q, int items) __attribute__((always_inline)) {
     Item it;
     const int qc = min(q, items - 1);
-    it.v = qc % nv;
-    const int rc = qc / nv;
-    it.ci = rc % a.c_in;
-    it.r = rc / a.c_in;
+    const int rc = (int)mdiv((unsigned)qc, a.mg_nv);
+    it.v = qc - rc * nv;
+    it.r = (int)mdiv((unsigned)rc, a.mg_cin);
+    it.ci = rc - it.r * a.c_in;
     it.live = q < items;
     return it;
   };
@@ -327,13 +327,13 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
 #pragma unroll
       for (int k = 0; k < RB_NSTV; ++k) {
         const int q = min(tid + NT * k, cn * vpr - 1);
-        const int c = q / vpr, v = q - (q / vpr) * vpr;
+        const int c = (int)mdiv((unsigned)q, a.mg_vpr), v = q - c * vpr;
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + c * RB_OPITCH + 16 * v);
         store_out(reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v), d);
       }
     } else {
       for (int q = tid; q < cn * vpr; q += NT) {
-        const int c = q / vpr, v = q - (q / vpr) * vpr;
+        const int c = (int)mdiv((unsigned)q, a.mg_vpr), v = q - c * vpr;
         const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(
                                                           otile + c * RB_OPITCH + 16 * v));
         _Float16* dst = y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v;
