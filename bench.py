@@ -184,7 +184,7 @@ def cpu_baseline(layer, budget_s=10.0):
                     act=layer.act)
     macs, _ = layer_stats(layer)
     runs, spent = 0, 0.0
-    while spent < budget_s and runs < 20:
+    while spent < budget_s and runs < 500:
         t0 = time.perf_counter()
         oracle.conv2d(g, inp.x, inp.w, inp.b, inp.r)
         spent += time.perf_counter() - t0
