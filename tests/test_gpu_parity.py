@@ -374,6 +374,66 @@ def test_rowshift_variant(case):
     assert np.array_equal(_bits(y), _bits(y2))
     y3 = run_gpu(g, "f16", x, w, b, r, variant=v)
     assert np.array_equal(_bits(y), _bits(y3))
+    if has_r:  # y aliasing the residual (16-byte aligned: the flat epilogue)
+        y4 = run_gpu(g, "f16", x, w, b, r, variant=v, offsets=(0, 0, 0, 8, 8), alias_residual=True)
+        assert np.array_equal(_bits(y), _bits(y4))
+
+
+def _sweep_rowshift(seed):
+    """A random 3x3 stride-1 geometry the row-shift kernel takes: whole
+    64-channel stages per group, output rows of at most 14 columns."""
+    rng = np.random.default_rng(seed)
+    groups = int(rng.choice([1, 1, 2]))
+    cig = 64 * int(rng.integers(1, 4))
+    cog = int(rng.integers(1, 7)) * 8 * (1 if groups == 1 else 1)
+    pt, pb, pl, pr = (int(v) for v in rng.integers(0, 3, 4))
+    ho, wo = int(rng.integers(2, 15)), int(rng.integers(2, 15))
+    h, w = ho + 2 - pt - pb, wo + 2 - pl - pr
+    if h < 1 or w < 1:
+        h, w, pt, pb, pl, pr = ho, wo, 1, 1, 1, 1
+    act = str(rng.choice(["identity", "relu", "silu", "tanh", "hard_swish"]))
+    g = oracle.Geom(int(rng.integers(1, 4)), cig * groups, h, w, cog * groups, 3, 3, groups=groups,
+                    pt=pt, pl=pl, pb=pb, pr=pr, act=act)
+    return g, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+
+
+def _sweep_rowband(seed):
+    """A random stride-2 geometry with few input channels (the row-band kernel)."""
+    rng = np.random.default_rng(seed)
+    k = int(rng.choice([3, 5, 7]))
+    c_in = int(rng.integers(1, 5)) if k < 7 else int(rng.integers(1, 4))
+    h, w = int(rng.integers(9, 41)), int(rng.integers(9, 41))
+    p = [int(v) for v in rng.integers(0, k // 2 + 1, 4)]
+    act = str(rng.choice(["identity", "relu", "sigmoid", "hard_swish"]))
+    g = oracle.Geom(int(rng.integers(1, 3)), c_in, h, w, int(rng.integers(1, 17)) * 8, k, k, sh=2, sw=2,
+                    pt=p[0], pl=p[1], pb=p[2], pr=p[3], act=act)
+    return g, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("kind", ["rowshift", "rowband"])
+def test_random_sweep(kind, seed):
+    """Seeded random geometries for the row-shift and row-band kernels against
+    the oracle (a case the planner gives to another kernel is skipped)."""
+    g, has_b, has_r = (_sweep_rowshift if kind == "rowshift" else _sweep_rowband)(1000 * seed + 7)
+    _say(f"[sweep {kind} {seed}] {g} bias={has_b} res={has_r}")
+    from gpu_harness import problem_from
+    v = "implicit_gemm_halo" if kind == "rowshift" else "auto"
+    try:
+        name = cf.conv_describe_variant(problem_from(g, variant=v), "f16")
+    except Exception:
+        pytest.skip("geometry not taken by the kernel")
+    if kind not in name:
+        pytest.skip(f"planned as {name}")
+    rng = np.random.default_rng(seed + 99)
+    cig = g.c_in // g.groups
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(np.float16)
+    w = (rng.standard_normal((g.c_out, cig, g.kh, g.kw)) * np.sqrt(2.0 / (cig * g.kh * g.kw))).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(np.float16) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(np.float16) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, "f16", x, w, b, r, variant=v)
+    assert_parity("f16", y, yr, sr, b, r, what=f"sweep {kind}", act=g.act)
 
 
 DEPTHWISE_CASES = [
