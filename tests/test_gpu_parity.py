@@ -410,6 +410,83 @@ def _sweep_rowband(seed):
     return g, bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
 
 
+def _sweep_more(kind, seed):
+    """Random geometries for the pointwise (f16, f32), depthwise, grouped and
+    fused ConvTranspose kernels: (geometry, dtype, bias, residual, transpose)."""
+    rng = np.random.default_rng(seed)
+    acts = ["identity", "relu", "sigmoid", "hard_swish", "silu"]
+    act = str(rng.choice(acts))
+    hb, hr = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    n = int(rng.integers(1, 4))
+    if kind == "pointwise_f16":
+        g = oracle.Geom(n, 8 * int(rng.integers(1, 25)), int(rng.integers(1, 20)), 4 * int(rng.integers(1, 10)),
+                        int(rng.integers(1, 300)), 1, 1, act=act)
+        return g, "f16", hb, hr, False
+    if kind == "pointwise_f32":
+        g = oracle.Geom(n, 4 * int(rng.integers(1, 40)), int(rng.integers(1, 16)), 4 * int(rng.integers(1, 8)),
+                        int(rng.integers(1, 200)), 1, 1, act=act)
+        return g, "f32", hb, hr, False
+    if kind == "depthwise":
+        k = int(rng.choice([3, 5, 7]))
+        s = 1 if k == 7 else int(rng.choice([1, 2]))
+        c = int(rng.integers(1, 40))
+        h, w = int(rng.integers(k, 33)), 4 * int(rng.integers(2, 9))
+        p = k // 2
+        g = oracle.Geom(n, c, h, w, c, k, k, groups=c, sh=s, sw=s, pt=p, pl=p, pb=p, pr=p, act=act)
+        return g, str(rng.choice(["f16", "f32"])), hb, hr, False
+    if kind == "grouped":
+        groups = int(rng.integers(2, 9))
+        cog = int(rng.choice([4, 8, 16, 24, 32]))
+        k = int(rng.choice([1, 2, 3]))
+        d = int(rng.choice([1, 2]))
+        s = int(rng.choice([1, 2]))
+        h, w = int(rng.integers(3, 41)), int(rng.integers(3, 41))
+        p = [int(v) for v in rng.integers(0, d * (k - 1) // 2 + 1, 4)]
+        g = oracle.Geom(n, 8 * groups, h, w, cog * groups, k, k, groups=groups, sh=s, sw=s, dh=d, dw=d,
+                        pt=p[0], pl=p[1], pb=p[2], pr=p[3], act=act)
+        return g, "f16", hb, hr, False
+    # fused ConvTranspose, kernel = stride = 2
+    g = oracle.Geom(n, 8 * int(rng.integers(1, 20)), int(rng.integers(1, 12)), 4 * int(rng.integers(1, 11)),
+                    int(rng.integers(1, 70)), 2, 2, sh=2, sw=2, act=act)  # fused path: w % 4 == 0
+    return g, "f16", hb, False, True
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("kind", ["pointwise_f16", "pointwise_f32", "depthwise", "grouped", "transpose_fused"])
+def test_random_sweep_more(kind, seed):
+    """Seeded random geometries for the remaining specialised kernels against the
+    oracle (a case the planner gives to another kernel is skipped)."""
+    g, dtype, has_b, has_r, tr = _sweep_more(kind, 7919 * seed + len(kind))
+    _say(f"[sweep {kind} {seed}] {dtype} {g} bias={has_b} res={has_r}")
+    from gpu_harness import problem_from
+    want = {"pointwise_f16": "pointwise_gemm.f16", "pointwise_f32": "pointwise_gemm.f32",
+            "depthwise": "depthwise_direct", "grouped": "implicit_gemm_grouped",
+            "transpose_fused": "transpose_gemm_col2im.f16.fused"}[kind]
+    try:
+        name = cf.conv_describe_variant(problem_from(g, transpose=tr), dtype)
+    except Exception:
+        pytest.skip("geometry not accepted")
+    if not name.startswith(want):
+        pytest.skip(f"planned as {name}")
+    npdt = np.float16 if dtype == "f16" else np.float32
+    rng = np.random.default_rng(seed + 1234)
+    cig = g.c_in // g.groups
+    x = rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)).astype(npdt)
+    if tr:
+        w = (rng.standard_normal((g.c_in, g.c_out, 2, 2)) * np.sqrt(2.0 / (4 * g.c_in))).astype(npdt)
+        b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt) if has_b else None
+        yr, sr = oracle.conv_transpose2d(g, x, w, b, None)
+        y = run_gpu(g, dtype, x, w, b, None, transpose=True)
+        assert_parity(dtype, y, yr, sr, b, None, what=f"sweep {kind}", act=g.act)
+        return
+    w = (rng.standard_normal((g.c_out, cig, g.kh, g.kw)) * np.sqrt(2.0 / (cig * g.kh * g.kw))).astype(npdt)
+    b = rng.uniform(-0.1, 0.1, g.c_out).astype(npdt) if has_b else None
+    r = rng.uniform(-1, 1, oracle.out_shape(g)).astype(npdt) if has_r else None
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    y = run_gpu(g, dtype, x, w, b, r)
+    assert_parity(dtype, y, yr, sr, b, r, what=f"sweep {kind}", act=g.act)
+
+
 @pytest.mark.parametrize("seed", range(16))
 @pytest.mark.parametrize("kind", ["rowshift", "rowband"])
 def test_random_sweep(kind, seed):
