@@ -31,6 +31,14 @@
 //  * Input planes are read as they lie: 4 consecutive pixels of 8 channel planes
 //    (8 bytes each), regrouped in registers into 4 channel octets.  Tile positions
 //    that no pixel maps to (the padding border) are zeroed once.
+//  * Pipeline: only the first stage is loaded before the multiplications start;
+//    afterwards every tap row's MFMAs carry a third of the global loads of the
+//    stage two ahead and a third of the LDS stores of the next stage, so a load
+//    whose issue stalls (memory pipeline full) leaves the matrix unit busy.
+//  * Epilogue: the waves' partial sums meet in LDS.  When y and the residual are
+//    16-byte aligned at every 32-channel tile, the copies are laid out like y
+//    and each thread finishes 8 consecutive outputs with one 16-byte residual
+//    load and one 16-byte store; otherwise 4 outputs of one row per item.
 // Per output the taps of a 16-channel slice are accumulated in (kh, kw) row-major
 // order, slices in increasing channel order within each wave.
 #include <type_traits>
