@@ -23,8 +23,6 @@
 // raw f32 sums into one plane per split-k range (reduced in range order of the
 // shape-fixed cut by a second kernel), which also serves ConvTranspose's GEMM
 // into f32 columns (wtrans: weight element (k, col) at w[(g*cig + k)*cols + col]).
-#include <type_traits>
-
 #include "epilogue.h"
 #include "internal.h"
 
@@ -114,9 +112,9 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
   const bool c_ok = bcol < a.cog;
   const T* __restrict__ wbase = static_cast<const T*>(a.wt);
 
-  vec_t ra[2], rb[2];  // two register sets: the step two ahead loads into the free one
+  vec_t ra, rb;
 
-  auto gather = [&](int set, int step) __attribute__((always_inline)) {
+  auto gather = [&](int step) __attribute__((always_inline)) {
     const int k0 = step * KSTEP + squart * EPT;
     // A: decode k0 once, then walk (ci, kh, kw) in weight-row order.
     {
@@ -133,7 +131,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
           if ((unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
             v = xg[((long long)ci * a.h + ih) * a.w + iw];
         }
-        ra[set][j] = v;
+        ra[j] = v;
         if (++kw == a.kw) {
           kw = 0;
           if (++kh == a.kh) {
@@ -147,23 +145,23 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
     if (!a.wtrans) {
       const T* wr = wbase + ((long long)grp * a.cog + bcol) * a.kg;
       if (a.wvec && c_ok && k0 + EPT <= a.kg) {
-        rb[set] = *reinterpret_cast<const vec_t*>(wr + k0);
+        rb = *reinterpret_cast<const vec_t*>(wr + k0);
       } else {
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) rb[set][j] = (c_ok && k0 + j < a.kg) ? wr[k0 + j] : T(0);
+        for (int j = 0; j < EPT; ++j) rb[j] = (c_ok && k0 + j < a.kg) ? wr[k0 + j] : T(0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
         const int k = k0 + j;
-        rb[set][j] = (c_ok && k < a.kg) ? wbase[((long long)grp * a.cig + k) * a.cog + bcol] : T(0);
+        rb[j] = (c_ok && k < a.kg) ? wbase[((long long)grp * a.cig + k) * a.cog + bcol] : T(0);
       }
     }
   };
 
-  auto stash = [&](int buf, int set) __attribute__((always_inline)) {
-    *reinterpret_cast<vec_t*>(&As[buf][srow * IG_ROW + squart * 16]) = ra[set];
-    *reinterpret_cast<vec_t*>(&Bs[buf][srow * IG_ROW + squart * 16]) = rb[set];
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    *reinterpret_cast<vec_t*>(&As[buf][srow * IG_ROW + squart * 16]) = ra;
+    *reinterpret_cast<vec_t*>(&Bs[buf][srow * IG_ROW + squart * 16]) = rb;
   };
 
   floatx4_t acc[2][2];
@@ -177,10 +175,34 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
   const int frow = lane & 15;
   const int fk = (lane >> 4) * 16;
 
-  // Epilogue operands, read before the reduction so that their latency hides
-  // behind it: lane holds pixels 4*(lane/16) + e of row block i, channel lane % 16
-  // of block j.  Every residual of the lane is read before any store: y may alias
-  // the residual exactly and each element is read and written by this lane only.
+  if (nsteps > 0) {
+    gather(step_begin);
+    stash(0);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+      const int buf = s & 1;
+      const bool more = s + 1 < nsteps;
+      if (more) gather(step_begin + s + 1);
+      vec_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const vec_t*>(&As[buf][(wr * 32 + i * 16 + frow) * IG_ROW + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const vec_t*>(&Bs[buf][(wc * 32 + j * 16 + frow) * IG_ROW + fk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mfma_step<T>(fa[i], fb[j], acc[i][j]);
+      if (more) stash(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane holds pixels 4*(lane/16) + e of row block i, channel lane % 16 of
+  // block j.  Every residual of the lane is read before any store: y may alias the
+  // residual exactly and each element is read and written by this lane only, so
+  // hoisting the reads keeps the result and lets them overlap.
   const T* bias = static_cast<const T*>(a.bias);
   const T* res = static_cast<const T*>(a.res);
   T* y = static_cast<T*>(a.y);
@@ -216,38 +238,6 @@ __global__ __launch_bounds__(256) void igemm_kernel(const IgemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) rv[j][i][e] = to_f32(res[oidx[j][i][e]]);
   }
-  // step s multiplies from LDS buffer s % 2; its register set (s % 2) takes
-  // step s + 2 meanwhile, and step s + 1 (set (s + 1) % 2) is stashed into the
-  // other buffer afterwards.  Steps run in pairs so set indexes are constants.
-  auto step = [&](int s, auto parity) __attribute__((always_inline)) {
-      constexpr int P = decltype(parity)::value;
-      const int buf = P;
-      if (s + 2 < nsteps) gather(P, step_begin + s + 2);  // uniform
-      vec_t fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const vec_t*>(&As[buf][(wr * 32 + i * 16 + frow) * IG_ROW + fk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const vec_t*>(&Bs[buf][(wc * 32 + j * 16 + frow) * IG_ROW + fk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mfma_step<T>(fa[i], fb[j], acc[i][j]);
-      if (s + 1 < nsteps) stash(P ^ 1, P ^ 1);
-      __syncthreads();
-  };
-  if (nsteps > 0) {
-    gather(0, step_begin);
-    if (nsteps > 1) gather(1, step_begin + 1);
-    stash(0, 0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-      step(s, std::integral_constant<int, 0>{});
-      if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
-    }
-  }
-
   if (a.mode == OUT_RAW) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
