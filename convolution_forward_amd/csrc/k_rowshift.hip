@@ -185,6 +185,12 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // input items, part 2: the weights), so that each tap row's multiplications
   // can carry one part
   static_assert(L::NI % 2 == 0, "input items split in two halves");
+  // buffer descriptors over the image's group of planes and the group's
+  // weights: the per-lane part of every address is a 32-bit item offset and the
+  // stage and plane parts are scalar offsets, so the loads need no vector
+  // address arithmetic between the multiplications they are issued with
+  const __amdgpu_buffer_rsrc_t x_rsrc = uniform_rsrc(ximg, a.cig * hw * 2);
+  const __amdgpu_buffer_rsrc_t w_rsrc = uniform_rsrc(wg, a.cog * a.cig * 9 * 2);
   auto load_part = [&](int s, int set, int part) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
@@ -193,7 +199,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       if constexpr (WV) {  // 16-byte aligned weights
 #pragma unroll
         for (int i = 0; i < L::NW; ++i)
-          rwv[set][i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
+          rwv[set][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        w_rsrc, 2 * w_off[i], 2 * (int)woff, 0));
       } else {
 #pragma unroll
         for (int i = 0; i < L::NW; ++i) {
@@ -206,10 +213,10 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     } else if constexpr (XV) {  // 8-byte aligned planes of whole 4-pixel groups
 #pragma unroll
       for (int i = i0; i < i1; ++i) {
-        const _Float16* src = ximg + xoff + in_off[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          rin[set][i][e] = *reinterpret_cast<const u32x2_t*>(src + (long long)e * hw);
+          rin[set][i][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                           x_rsrc, 2 * in_off[i], 2 * (int)(xoff + e * hw), 0));
       }
     } else {  // input not 8-byte aligned or planes not a multiple of 4: element loads
 #pragma unroll
