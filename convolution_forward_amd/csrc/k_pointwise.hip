@@ -65,7 +65,9 @@ __device__ __forceinline__ int pw_slot(int p, int o) { return o ^ ((p >> 1) & 7)
 // 8-byte aligned, planes of whole 8-pixel vectors; otherwise every access is
 // element-wise.  PF divides the chunk count, so a group of PF items never
 // straddles two tiles.
-template <int PW_TC, bool CT, int PF, bool VEC>
+// AK: the activation fixed at compile time (the ONNX code), or -1 for the
+// launch's code chosen at run time.
+template <int PW_TC, bool CT, int PF, bool VEC, int AK = -1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF > 2 ? 2 : PW_TC == 128 || PF > 1 ? 3 : 4)))
 void pointwise_f16_kernel(const PwArgs a) {
   constexpr int PW_WBYTES = PW_TC * PW_WROW;
@@ -292,7 +294,12 @@ void pointwise_f16_kernel(const PwArgs a) {
           for (int i = 0; i < 4; ++i) v[4 * cb + i] = v[4 * cb + i] + (float)h[i];
         }
       }
-      act_array(v, a.act, a.alpha, a.beta);
+      if constexpr (AK < 0) {
+        act_array(v, a.act, a.alpha, a.beta);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = act_t<AK>(v[i], a.alpha, a.beta);
+      }
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         half4_t h;
@@ -417,26 +424,28 @@ void pointwise_f16_kernel(const PwArgs a) {
   group(std::false_type{}, k);  // cnt is a multiple of PF
 }
 
-template <int TC, bool CT, int PF, bool VEC>
+template <int TC, bool CT, int PF, bool VEC, int AK = -1>
 static hipError_t launch_pw_t(const PwArgs& a, int cus, hipStream_t s) {
   // persistent: one workgroup per resident slot (an uneven last round measured
   // faster than fewer workgroups with equal shares)
   static std::atomic<int> per_cu{0};
   int r = per_cu.load(std::memory_order_relaxed);
   if (r == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<TC, CT, PF, VEC>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<TC, CT, PF, VEC, AK>, 256, 0) !=
             hipSuccess || r < 1)
       r = 1;
     per_cu.store(r, std::memory_order_relaxed);
   }
   long long grid = std::min<long long>((long long)r * cus, a.ntiles);
   if (grid < a.ntiles) grid = std::max<long long>(8, grid & ~7LL);  // whole XCD rounds
-  hipLaunchKernelGGL((pointwise_f16_kernel<TC, CT, PF, VEC>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((pointwise_f16_kernel<TC, CT, PF, VEC, AK>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int TC, bool CT, int PF>
 static hipError_t launch_pw_v(const PwArgs& a, int cus, hipStream_t s) {
+  // ReLU, the common case, with the activation fixed at compile time
+  if (a.vec && a.act == 1) return launch_pw_t<TC, CT, PF, true, 1>(a, cus, s);
   return a.vec ? launch_pw_t<TC, CT, PF, true>(a, cus, s) : launch_pw_t<TC, CT, PF, false>(a, cus, s);
 }
 
