@@ -99,4 +99,17 @@ __device__ __forceinline__ T epilogue_one(float v, const T* bias, const T* res, 
   return from_f32<T>(apply_act(v, act, alpha, beta));
 }
 
+// The activation fixed at compile time (AK = the ONNX code), or, for AK < 0,
+// the launch's code chosen at run time.  A fixed activation keeps the other
+// activations' code (and its registers) out of the kernel.
+template <int AK, int N>
+__device__ __forceinline__ void act_apply(float (&v)[N], int act, float alpha, float beta) {
+  if constexpr (AK < 0) {
+    act_array(v, act, alpha, beta);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = act_t<AK>(v[i], alpha, beta);
+  }
+}
+
 }  // namespace convfwd

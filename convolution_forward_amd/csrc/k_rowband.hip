@@ -50,7 +50,7 @@ constexpr int RB_FILLI = 1024;     // items of the first KH rows at most
 // NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; WV: waves (8: two
 // 32-channel blocks x four 32-pixel blocks; 4: one channel block); VEC: whole
 // 16-byte input and output vectors.
-template <int NST, int WV, bool VEC>
+template <int NST, int WV, bool VEC, int AK = -1>
 __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   constexpr int NT = 64 * WV;
   constexpr int RB_FILL = (RB_FILLI + NT - 1) / NT;  // items per thread for the first KH rows
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
           v[i] = v[i] + (float)res[ybase + ((long long)min(c, a.c_out - co0 - 1) * a.ho + oh) * a.wo + ow];
         }
       }
-      act_array(v, a.act, a.alpha, a.beta);
+      act_apply<AK>(v, a.act, a.alpha, a.beta);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         half4_t h;
@@ -357,7 +357,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
 template <int NST>
 static void launch_rb_nst(const RowbandArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const bool two = a.c_out > 32;
-  if (a.vec) {
+  if (a.vec && a.act == 1) {  // ReLU, the common case, fixed at compile time
+    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, true, 1>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<NST, 4, true, 1>), grid, dim3(256), lds, s, a);
+  } else if (a.vec) {
     if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, true>), grid, dim3(512), lds, s, a);
     else hipLaunchKernelGGL((rowband_kernel<NST, 4, true>), grid, dim3(256), lds, s, a);
   } else {

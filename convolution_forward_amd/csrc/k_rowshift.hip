@@ -107,7 +107,7 @@ __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c)
 
 }  // namespace
 
-template <int R, bool XV, bool WV>
+template <int R, bool XV, bool WV, int AK = -1>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef RsLayout<R> L;
   constexpr int NP = L::NP;
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = v[j] + (float)r8[j];
       }
-      act_array(v, a.act, a.alpha, a.beta);
+      act_apply<AK>(v, a.act, a.alpha, a.beta);
       half8_t h;
 #pragma unroll
       for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           v[4 * k + j] = v[4 * k + j] + (float)res[obase + e_clamped(k, j, 1)];
     }
   }
-  act_array(v, a.act, a.alpha, a.beta);
+  act_apply<AK>(v, a.act, a.alpha, a.beta);
 #pragma unroll
   for (int k = 0; k < KI; ++k) {
     if (pairs) {
@@ -614,7 +614,9 @@ hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups));
 #define RS_LAUNCH(R_)                                                                        \
   {                                                                                          \
-    if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, true>), grid, dim3(256), 0, s, a); \
+    if (a.xvec && a.wvec && a.act == 1) /* ReLU fixed at compile time */                   \
+      hipLaunchKernelGGL((rowshift_kernel<R_, true, true, 1>), grid, dim3(256), 0, s, a);     \
+    else if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, true>), grid, dim3(256), 0, s, a); \
     else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, false>), grid, dim3(256), 0, s, a); \
     else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, false, true>), grid, dim3(256), 0, s, a); \
     else hipLaunchKernelGGL((rowshift_kernel<R_, false, false>), grid, dim3(256), 0, s, a);           \
