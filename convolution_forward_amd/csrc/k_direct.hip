@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void depthwise_plane_kernel(const DepthwiseArg
 constexpr int DWW_NI = 4;  // 4-element input items per lane (H * W <= 1024)
 constexpr int DWW_NE = 4;  // 4-output epilogue items per lane (mult * Ho * Wo <= 1024)
 
-template <typename T, int K, int S, int BH, bool RES, bool OVEC>
+template <typename T, int K, int S, int BH, bool RES, bool OVEC, int AK = -1>
 __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs a) {
   typedef typename DwVec<T>::type V;
   constexpr int PR = (BH - 1) * S + K;  // input rows of one lane's output column
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[4 * k + e] = (sv[e] + bv) + v[4 * k + e];
         }
-        act_array(v, a.act, a.alpha, a.beta);
+        act_apply<AK>(v, a.act, a.alpha, a.beta);
 #pragma unroll
         for (int k = 0; k < DWW_NE; ++k) {
           const int q = lane + 64 * k;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
           const float4 s4 = *reinterpret_cast<const float4*>(outt + 4 * q);
           const float bv = bl[mdiv(4 * q, a.mg_howo)];
           float f[4] = {s4.x + bv, s4.y + bv, s4.z + bv, s4.w + bv};
-          act_array(f, a.act, a.alpha, a.beta);
+          act_apply<AK>(f, a.act, a.alpha, a.beta);
           *reinterpret_cast<V*>(y + obase + 4 * q) = dw_pack<T>(f);
         }
       }
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
           const int o = min(lane + 64 * k, tot - 1);
           v[k] = (outt[o] + bl[mdiv(o, a.mg_howo)]) + v[k];
         }
-        act_array(v, a.act, a.alpha, a.beta);
+        act_apply<AK>(v, a.act, a.alpha, a.beta);
 #pragma unroll
         for (int k = 0; k < DWW_NE * 4; ++k) {
           const int o = lane + 64 * k;
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(64) void depthwise_wave_kernel(const DepthwiseArgs 
             const int o = min(lane + 64 * (4 * k + e), tot - 1);
             f[e] = outt[o] + bl[mdiv(o, a.mg_howo)];
           }
-          act_array(f, a.act, a.alpha, a.beta);
+          act_apply<AK>(f, a.act, a.alpha, a.beta);
 #pragma unroll
           for (int e = 0; e < 4; ++e) store_out(y + obase + min(lane + 64 * (4 * k + e), tot - 1), from_f32<T>(f[e]));
         }
@@ -578,13 +578,23 @@ static int persistent_grid(long long items, int per_cu, int cus) {
 template <typename T>
 static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, long long planes, int cus, size_t lds,
                                    hipStream_t s) {
+#define DWW_GO(...)                                                                      \
+  {                                                                                      \
+    const void* f = reinterpret_cast<const void*>(&depthwise_wave_kernel<__VA_ARGS__>);  \
+    const int grid = persistent_grid(planes, resident_per_cu(f, 64, lds), cus);          \
+    hipLaunchKernelGGL((depthwise_wave_kernel<__VA_ARGS__>), dim3(grid), dim3(64), lds, s, a); \
+    return hipGetLastError();                                                            \
+  }
+  // identity, ReLU and hard-swish with the activation fixed at compile time on
+  // the vector-output path without residual
 #define DWW_LAUNCH(K_, S_, BH_, R_, O_)                                                  \
   {                                                                                      \
-    const void* f = reinterpret_cast<const void*>(&depthwise_wave_kernel<T, K_, S_, BH_, R_, O_>); \
-    const int grid = persistent_grid(planes, resident_per_cu(f, 64, lds), cus);          \
-    hipLaunchKernelGGL((depthwise_wave_kernel<T, K_, S_, BH_, R_, O_>), dim3(grid), dim3(64), lds, \
-                       s, a);                                                            \
-    return hipGetLastError();                                                            \
+    if constexpr (O_ && !R_) {                                                           \
+      if (a.act == 0) DWW_GO(T, K_, S_, BH_, R_, O_, 0)                                  \
+      if (a.act == 1) DWW_GO(T, K_, S_, BH_, R_, O_, 1)                                  \
+      if (a.act == 6) DWW_GO(T, K_, S_, BH_, R_, O_, 6)                                  \
+    }                                                                                    \
+    DWW_GO(T, K_, S_, BH_, R_, O_)                                                       \
   }
 #define DWW_CASE(K_, S_, BH_)                                                            \
   if (a.kh == K_ && a.sh == S_ && a.bh == BH_) {                                         \
@@ -601,6 +611,7 @@ static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, long long planes, int
   DWW_CASE(7, 1, 14)
 #undef DWW_CASE
 #undef DWW_LAUNCH
+#undef DWW_GO
   return hipErrorInvalidValue;
 }
 

@@ -40,7 +40,7 @@ constexpr int GC_NT = 1024;     // threads per workgroup: 16 waves, 4 per SIMD
 
 // KS: k-steps (taps <= 2 KS).  CB: 8-channel row groups of the output
 // channels (cog <= 8 CB).  VEC: x 8-byte aligned and h * w % 4 == 0.
-template <int KS, int CB, bool VEC>
+template <int KS, int CB, bool VEC, int AK = -1>
 __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   u32x4_t* xs = reinterpret_cast<u32x4_t*>(smem);                      // [pos] octets
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
           v[i] = v[i] + (float)rg[co * howo + min(pix[u], howo - 1)];
         }
       }
-      act_array(v, a.act, a.alpha, a.beta);
+      act_apply<AK>(v, a.act, a.alpha, a.beta);
       if (pix[u] < howo) {
 #pragma unroll
         for (int i = 0; i < 4 * CB; ++i) {
@@ -199,8 +199,13 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4;
   const int taps = a.kh * a.kw;
   if (taps > GC_MAXTAPS) return hipErrorInvalidValue;
+  // ReLU and sigmoid with the activation fixed at compile time on the vector path
 #define GC_CASE(KS_, CB_)                                                                      \
-  if (a.vec) hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true>), grid, dim3(GC_NT), lds, s, a); \
+  if (a.vec && a.act == 1)                                                                     \
+    hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true, 1>), grid, dim3(GC_NT), lds, s, a);   \
+  else if (a.vec && a.act == 3)                                                                \
+    hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true, 3>), grid, dim3(GC_NT), lds, s, a);   \
+  else if (a.vec) hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true>), grid, dim3(GC_NT), lds, s, a); \
   else hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, false>), grid, dim3(GC_NT), lds, s, a);
 #define GC_KS(KS_)                          \
   if (a.cog <= 8) { GC_CASE(KS_, 1) }       \

@@ -52,7 +52,7 @@ __device__ __forceinline__ int xcol(int k, int px) { return (px + 16 * ((k >> 3)
 
 // VEC: x and w 16-byte aligned (planes and weight rows of whole float4 groups
 // are guaranteed by the planner); otherwise element loads.
-template <bool VEC>
+template <bool VEC, int AK = -1>
 __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[2 * (P32_XF + P32_WF) + P32_TC];
   float* bsm = smem + 2 * (P32_XF + P32_WF);
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
         if (res) t = t + res[obase + (long long)min(co0 + m, a.c_out - 1) * a.hw];
         v[4 * cb + i] = t;
       }
-    act_array(v, a.act, a.alpha, a.beta);
+    act_apply<AK>(v, a.act, a.alpha, a.beta);
 #pragma unroll
     for (int cb = 0; cb < 5; ++cb)
 #pragma unroll
@@ -207,7 +207,10 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
 
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_pt * a.n_ct));
-  if (a.vec) hipLaunchKernelGGL((pointwise_f32_kernel<true>), grid, dim3(P32_NT), 0, s, a);
+  // identity and ReLU with the activation fixed at compile time on the vector path
+  if (a.vec && a.act == 0) hipLaunchKernelGGL((pointwise_f32_kernel<true, 0>), grid, dim3(P32_NT), 0, s, a);
+  else if (a.vec && a.act == 1) hipLaunchKernelGGL((pointwise_f32_kernel<true, 1>), grid, dim3(P32_NT), 0, s, a);
+  else if (a.vec) hipLaunchKernelGGL((pointwise_f32_kernel<true>), grid, dim3(P32_NT), 0, s, a);
   else hipLaunchKernelGGL((pointwise_f32_kernel<false>), grid, dim3(P32_NT), 0, s, a);
   return hipGetLastError();
 }
