@@ -6,6 +6,7 @@ option, bit-exact index-mapping probes, integer exactness, determinism,
 chunking, forced split-k and forced variants, element offsets and residual
 aliasing.
 """
+import dataclasses
 import itertools
 import re
 import sys
@@ -458,6 +459,12 @@ def test_random_sweep_more(kind, seed):
     oracle (a case the planner gives to another kernel is skipped)."""
     g, dtype, has_b, has_r, tr = _sweep_more(kind, 7919 * seed + len(kind))
     _say(f"[sweep {kind} {seed}] {dtype} {g} bias={has_b} res={has_r}")
+    _check_more(kind, g, dtype, has_b, has_r, tr, seed)
+
+
+def _check_more(kind, g, dtype, has_b, has_r, tr, seed):
+    """Plan check (skip a case the planner gives to another kernel), seeded
+    inputs, GPU call and element-wise parity against the oracle."""
     from gpu_harness import problem_from
     want = {"pointwise_f16": "pointwise_gemm.f16", "pointwise_f32": "pointwise_gemm.f32",
             "depthwise": "depthwise_direct", "grouped": "implicit_gemm_grouped",
@@ -485,6 +492,35 @@ def test_random_sweep_more(kind, seed):
     yr, sr = oracle.conv2d(g, x, w, b, r)
     y = run_gpu(g, dtype, x, w, b, r)
     assert_parity(dtype, y, yr, sr, b, r, what=f"sweep {kind}", act=g.act)
+
+
+# Geometries on the vector paths of the kernels whose common activations are
+# fixed at compile time (whole 16-byte vectors, no residual on the depthwise
+# kernel), so that each compiled activation runs at least once.
+_ACT_FIXED = [
+    ("pointwise_f16", oracle.Geom(2, 64, 8, 8, 48, 1, 1), "f16", False),
+    ("pointwise_f32", oracle.Geom(2, 24, 8, 8, 20, 1, 1), "f32", False),
+    ("depthwise", oracle.Geom(2, 6, 16, 16, 6, 3, 3, groups=6, pt=1, pl=1, pb=1, pr=1), "f32", False),
+    ("depthwise", oracle.Geom(2, 6, 16, 16, 6, 3, 3, groups=6, sh=2, sw=2, pt=1, pl=1, pb=1, pr=1),
+     "f16", False),
+    ("depthwise", oracle.Geom(2, 6, 16, 16, 6, 5, 5, groups=6, pt=2, pl=2, pb=2, pr=2), "f32", False),
+    ("depthwise", oracle.Geom(2, 6, 16, 16, 6, 5, 5, groups=6, sh=2, sw=2, pt=2, pl=2, pb=2, pr=2),
+     "f32", False),
+    ("grouped", oracle.Geom(2, 64, 16, 16, 64, 3, 3, groups=8, dh=2, dw=2, pt=2, pl=2, pb=2, pr=2), "f16",
+     False),
+    ("transpose_fused", oracle.Geom(2, 32, 8, 8, 24, 2, 2, sh=2, sw=2), "f16", True),
+]
+
+
+@pytest.mark.parametrize("act", ["identity", "relu", "sigmoid", "hard_swish"])
+@pytest.mark.parametrize("case", range(len(_ACT_FIXED)))
+def test_compiled_activations(case, act):
+    """Every activation the host may hand to a compile-time-activation kernel
+    (and one it may not), on that kernel's vector path, against the oracle."""
+    kind, g0, dtype, tr = _ACT_FIXED[case]
+    g = dataclasses.replace(g0, act=act)
+    _say(f"[act {kind} {case} {act}] {dtype} {g}")
+    _check_more(kind, g, dtype, True, False, tr, 31 * case + len(act))
 
 
 @pytest.mark.parametrize("seed", range(16))
