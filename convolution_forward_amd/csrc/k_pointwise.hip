@@ -444,7 +444,7 @@ static hipError_t launch_pw_t(const PwArgs& a, int cus, hipStream_t s) {
 
 template <int TC, bool CT, int PF>
 static hipError_t launch_pw_v(const PwArgs& a, int cus, hipStream_t s) {
-  // ReLU, the common case, with the activation fixed at compile time
+  // ReLU and identity, the common cases, with the activation fixed at compile time
   if (a.vec && a.act == 1) return launch_pw_t<TC, CT, PF, true, 1>(a, cus, s);
   if (a.vec && a.act == 0) return launch_pw_t<TC, CT, PF, true, 0>(a, cus, s);
   return a.vec ? launch_pw_t<TC, CT, PF, true>(a, cus, s) : launch_pw_t<TC, CT, PF, false>(a, cus, s);
