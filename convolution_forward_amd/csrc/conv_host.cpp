@@ -713,6 +713,10 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.oflat = reinterpret_cast<uintptr_t>(yc) % 16 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 16 == 0) &&
                 g.wo % 2 == 0 && g.ho * g.wo >= 8 && (g.co * g.ho * g.wo) % 8 == 0 &&
                 (g.cog * g.ho * g.wo) % 8 == 0;
+      a.mg_w = make_magic((unsigned)g.w);
+      a.mg_g4 = make_magic((unsigned)((g.h * g.w + 3) / 4));
+      a.mg_nct = make_magic((unsigned)a.n_ct);
+      a.mg_n = make_magic((unsigned)cn);
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = pl.halo.rowshift ? launch_rowshift(a, s) : launch_halo(a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {

@@ -83,6 +83,8 @@ struct HaloArgs {
   int o2;                // row-shift kernel: y and residual 4-byte aligned, wo even
   int oflat;             // row-shift kernel: y and residual 16-byte aligned at every
                          // 32-channel tile, wo even, ho * wo >= 8
+  Magic mg_w, mg_g4;     // row-shift kernel: divisors w and (h w + 3) / 4
+  Magic mg_nct, mg_n;    // row-shift kernel: divisors n_ct and n
   int act;
   float alpha, beta;
 };

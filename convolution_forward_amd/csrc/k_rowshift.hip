@@ -122,11 +122,13 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int wave = tid >> 6;
 
   // logical tile: co tile fastest, so an image's co tiles run on one XCD
-  int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const int ct = bid % a.n_ct;
-  bid /= a.n_ct;
-  const int n = bid % a.n;
-  const int g = bid / a.n;
+  // (divisions by the host's multiply-shift constants: the tile's first loads
+  // wait on this index arithmetic)
+  const int bid = xcd_logical(blockIdx.x, gridDim.x);
+  const int bq = (int)mdiv((unsigned)bid, a.mg_nct);
+  const int ct = bid - bq * a.n_ct;
+  const int g = (int)mdiv((unsigned)bq, a.mg_n);
+  const int n = bq - g * a.n;
   const int co0 = ct * 32;
   const int hw = a.h * a.w;
 
@@ -150,13 +152,14 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     const int q = lane + i * 64;
     in_live[i] = q < in_items;
     const int qq = in_live[i] ? q : 0;
-    const int o = 2 * wave + qq / groups4;
-    const int grp4 = qq - (qq / groups4) * groups4;
+    const int qd = (int)mdiv((unsigned)qq, a.mg_g4);
+    const int o = 2 * wave + qd;
+    const int grp4 = qq - qd * groups4;
     in_off[i] = 8 * o * hw + 4 * grp4;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       const int f = 4 * grp4 + k4;  // pixels past the plane's end (hw % 4 != 0) are skipped
-      const int ih = f / a.w, iw = f - (f / a.w) * a.w;
+      const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
       const int pos = (ih + a.pt) * RS_COLS + iw + a.pl;
       in_lds[i][k4] = f < hw ? (pos * 8 + slot8(pos, o)) * 16 : -1;
     }
