@@ -759,6 +759,9 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.hp = (int)(g.h + g.pt + g.pb); a.wp = (int)(g.w + g.pl + g.pr);
       a.xs_bytes = a.hp * a.wp * 16;
       a.vec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0;
+      a.mg_w = make_magic((unsigned)g.w);
+      a.mg_wo = make_magic((unsigned)g.wo);
+      a.mg_kw = make_magic((unsigned)g.kw);
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_grouped(a, s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM && pl.ct_fused) {

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
           half8_t v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, xr[i][e])[j];
-          const int ih = f / a.w, iw = f - ih * a.w;
+          const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
           xs[(ih + a.pt) * a.wp + iw + a.pl] = __builtin_bit_cast(u32x4_t, v);
         }
       }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   for (int ks = 0; ks < KS; ++ks) {
     const int t = 2 * ks + hi;
     tok[ks] = t < taps;
-    const int kh = t / a.kw, kw = t - kh * a.kw;
+    const int kh = (int)mdiv((unsigned)t, a.mg_kw), kw = t - kh * a.kw;
     tofs[ks] = tok[ks] ? kh * a.dh * a.wp + kw * a.dw : 0;
   }
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int p = min(pix[u], howo - 1);
-        const int oh = p / a.wo, ow = p - oh * a.wo;
+        const int oh = (int)mdiv((unsigned)p, a.mg_wo), ow = p - oh * a.wo;
         const u32x4_t v = xs[oh * a.sh * a.wp + ow * a.sw + tofs[ks]];
         const u32x4_t bf = tok[ks] ? v : u32x4_t{0, 0, 0, 0};
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, af[ks]),
