@@ -670,6 +670,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         PwArgs a{};
         a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
         a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
+        a.mg_hw = make_magic((unsigned)a.hw);
         a.n_pt = (int)ceil_div((int64_t)cn * g.h * g.w, 64);
         a.n_ct = (int)ceil_div(g.co, 80);
         a.nchunks = (int)ceil_div(g.ci, 64);

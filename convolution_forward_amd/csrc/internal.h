@@ -127,6 +127,7 @@ struct PwArgs {
   int w_in;              // ct: input row width (the tile holds whole input rows)
   int ct_rows;           // ct: input rows per tile, tp / w_in
   Magic mg_vpr, mg_rows; // ct: divisions by w_in / 4 and by ct_rows
+  Magic mg_hw;           // f32 kernel: division by h * w (pixel indexes < 2^31)
   int act;
   float alpha, beta;
 };

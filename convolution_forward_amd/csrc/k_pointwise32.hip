@@ -76,7 +76,7 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
   for (int i = 0; i < P32_NX; ++i) {
     const int q = tid + P32_NT * i;
     const long long P = min(P0 + 4 * (q & 15), npix - 4);
-    const long long img = P / a.hw;
+    const long long img = mdiv((unsigned)P, a.mg_hw);  // P < 2^31
     xoff[i] = img * a.c_in * a.hw + (P - img * a.hw);
   }
   floatx4_t xr[P32_NX], wr[P32_NW];
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
   for (int cb = 0; cb < 5; ++cb) acc[cb] = acc[cb] + part[(pb * 5 + cb) * 64 + lane];
   const long long P = P0 + 16 * pb + lc;
   if (P < npix) {
-    const long long img = P / a.hw, pp = P - img * a.hw;
+    const long long img = mdiv((unsigned)P, a.mg_hw), pp = P - img * a.hw;
     const long long obase = img * a.c_out * a.hw + pp;
     float v[20];
 #pragma unroll
