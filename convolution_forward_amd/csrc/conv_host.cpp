@@ -691,6 +691,9 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
               reinterpret_cast<uintptr_t>(yc) % 16 == 0 &&
               (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 8 == 0) && (g.h * g.w) % 8 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      a.mg_nch = make_magic((unsigned)a.nchunks);
+      a.mg_nct = make_magic((unsigned)a.n_ct);
+      a.mg_npt = make_magic((unsigned)a.n_pt);
       e = launch_pointwise(a, device_cus(), s);
       }
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
@@ -784,6 +787,9 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.vec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && reinterpret_cast<uintptr_t>(wb) % 8 == 0 &&
               reinterpret_cast<uintptr_t>(yc) % 16 == 0;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      a.mg_nch = make_magic((unsigned)a.nchunks);
+      a.mg_nct = make_magic((unsigned)a.n_ct);
+      a.mg_npt = make_magic((unsigned)a.n_pt);
       e = launch_pointwise(a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) {
       // GEMM: cols[n][g*M + m][h][w] = sum_ci w[g*cig + ci][m] * x[n][g*cig + ci][h][w],

@@ -128,6 +128,7 @@ struct PwArgs {
   int ct_rows;           // ct: input rows per tile, tp / w_in
   Magic mg_vpr, mg_rows; // ct: divisions by w_in / 4 and by ct_rows
   Magic mg_hw;           // f32 kernel: division by h * w (pixel indexes < 2^31)
+  Magic mg_nch, mg_nct, mg_npt;  // f16 kernel: divisions by nchunks, n_ct and n_pt
   int act;
   float alpha, beta;
 };

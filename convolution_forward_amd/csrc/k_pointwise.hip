@@ -107,12 +107,13 @@ void pointwise_f16_kernel(const PwArgs a) {
   // work item = tile * nchunks + chunk; tile = (image, pixel tile, row tile),
   // row tile fastest
   auto decode = [&](int item, int& n, int& p0, int& co0, int& c0) __attribute__((always_inline)) {
-    const int t = item / a.nchunks;
+    // (divisions by the host's multiply-shift constants)
+    const int t = (int)mdiv((unsigned)item, a.mg_nch);
     c0 = (item - t * a.nchunks) * PW_KC;
-    const int ct = t % a.n_ct;
-    const int r = t / a.n_ct;
-    const int pt = r % a.n_pt;
-    n = r / a.n_pt;
+    const int r = (int)mdiv((unsigned)t, a.mg_nct);
+    const int ct = t - r * a.n_ct;
+    n = (int)mdiv((unsigned)r, a.mg_npt);
+    const int pt = r - n * a.n_pt;
     p0 = pt * a.tp;
     co0 = ct * PW_TC;
   };
@@ -392,7 +393,7 @@ void pointwise_f16_kernel(const PwArgs a) {
   const int cnt = j < t_count ? (t_count - j + gx - 1) / gx * a.nchunks : 0;
   if (cnt == 0) return;
   auto item_of = [&](int k) __attribute__((always_inline)) {
-    const int kt = k / a.nchunks;
+    const int kt = (int)mdiv((unsigned)k, a.mg_nch);
     return (t_first + j + kt * gx) * a.nchunks + (k - kt * a.nchunks);
   };
   // one step: stage slot S (item k), refill it with item k + PF when REFILL,
