@@ -9,10 +9,15 @@ resident in HBM before the timed region starts.  The operand sets rotate over
 Infinity Cache.  Every other workload layer is timed the same way and reported
 in "layers" (TFLOP/s, GB/s of algorithmic bytes, fraction of its roofline).
 
+Each layer's figure is the median of --loops event-timed loops of --steps
+back-to-back calls.  The fp64 oracle is timed on the host cores beside it, per
+layer (cpu_baseline, and layers[].oracle), and per-config sums of both are
+reported in "configs".
+
 Prints one JSON line.  Options: --gpus N (only 1 is supported: the build runs on
-one GPU), --steps K, --warmup W, --no-cpu-baseline, --layers a,b,...,
---headline-only, --copy-calib BYTES (runs only a plain device copy of that size,
-for calibrating the HBM byte counters).
+one GPU), --steps K, --warmup W, --loops L, --no-cpu-baseline, --oracle-budget S,
+--layers a,b,..., --headline-only, --copy-calib BYTES (runs only a plain device
+copy of that size, for calibrating the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -87,7 +92,12 @@ def build_problem(cf, layer):
                            residual=layer.residual)
 
 
-def time_layer(cf, torch, layer, steps, warmup):
+def time_layer(cf, torch, layer, steps, warmup, loops):
+    """Event-timed loops of `steps` back-to-back calls on one stream; the
+    figure is the median loop.  Operand sets rotate over >= 1 GiB and the
+    rotation index runs on across the warmup, host-timing and device loops, so
+    a set is reused only after every other set (over 1 GiB of other operands)
+    has been touched: no call finds its inputs in the 256 MB Infinity Cache."""
     p = build_problem(cf, layer)
     variant = cf.conv_describe_variant(p, layer.dtype)
     inp = workloads.make_inputs(layer)
@@ -107,47 +117,54 @@ def time_layer(cf, torch, layer, steps, warmup):
     sh = stream.cuda_stream
     fn = cf.lib().conv_transpose_forward if layer.transpose else cf.lib().conv_forward
     pref = ctypes.byref(p)
-    dt = 1 if layer.dtype == "f16" else 0
+    dt = cf.DTYPES[layer.dtype]
     sp = None if scratch is None else scratch.data_ptr()
     args = [[None if t is None else t.data_ptr() for t in st] for st in sets]
+    counter = [0]
 
-    def call(i):
-        x, w, b, r, y = args[i % nsets]
+    def call():
+        x, w, b, r, y = args[counter[0] % nsets]
+        counter[0] += 1
         st = fn(pref, dt, x, w, b, r, y, sp, whole, sh)
         if st:
             raise cf.ConvError(st, "conv_forward")
 
-    for i in range(warmup):
-        call(i)
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
     # Host submission (ctypes + validation + launch) is timed on its own; for
     # the device timing a GPU-side delay first holds the stream while all K
     # calls are enqueued, so the events measure the kernels back to back, not
     # the host's launch rate.
     t0 = time.perf_counter()
-    for i in range(steps):
-        call(i)
+    for _ in range(steps):
+        call()
     host_us = (time.perf_counter() - t0) / steps * 1e6
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(sleep_cycles(torch, host_us * steps * 1.5 + 2000.0))
-    ev0.record(stream)
-    t0 = time.perf_counter()
-    for i in range(steps):
-        call(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total = ev0.elapsed_time(ev1) * 1e-3  # s
+    loop_s = []
+    wall = 0.0
+    for _ in range(loops):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(sleep_cycles(torch, host_us * steps * 1.5 + 2000.0))
+        ev0.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        loop_s.append(ev0.elapsed_time(ev1) * 1e-3)
     del sets
     torch.cuda.empty_cache()
     bound, t_roof = roof(layer, macs, nbytes)
+    total = float(np.median(loop_s))
     avg = total / steps
     return {
         "name": layer.name, "variant": variant, "dtype": layer.dtype,
-        "rotating_sets": nsets, "us_avg": avg * 1e6, "host_us_per_call": host_us,
-        "wall_s": wall,
+        "rotating_sets": nsets, "rotation_bytes": nsets * nbytes,
+        "us_avg": avg * 1e6, "us_loops": [round(t / steps * 1e6, 3) for t in loop_s],
+        "host_us_per_call": host_us, "wall_s": wall,
         "tflops": 2 * macs / avg / 1e12, "gbs": nbytes / avg / 1e9,
         "macs": macs, "alg_bytes": nbytes, "bound": bound,
         "roof_us": t_roof * 1e6, "roof_frac": t_roof / avg, "total_s": total,
@@ -171,9 +188,21 @@ def sleep_cycles(torch, us):
     return int(_SLEEP_RATE * us)
 
 
-def cpu_baseline(layer, budget_s=10.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_layer(layer, budget_s):
     """The fp64 oracle (plain C loops, OpenMP over output planes) on the host
-    cores, over the whole headline layer, repeated until ~budget_s of work."""
+    cores over the whole layer, repeated until about budget_s of work (at least
+    one run); the time covers y and the |w*x| scale together."""
     import oracle  # CPU baseline leg only
 
     inp = workloads.make_inputs(layer)
@@ -181,20 +210,67 @@ def cpu_baseline(layer, budget_s=10.0):
     g = oracle.Geom(layer.n, layer.c_in, layer.h, layer.w, layer.c_out, layer.kh, layer.kw,
                     groups=layer.groups, sh=layer.stride[0], sw=layer.stride[1],
                     dh=layer.dilation[0], dw=layer.dilation[1], pt=t, pl=l, pb=b, pr=r,
-                    act=layer.act)
+                    oph=layer.out_pad[0], opw=layer.out_pad[1], act=layer.act)
+    f = oracle.conv_transpose2d if layer.transpose else oracle.conv2d
     macs, _ = layer_stats(layer)
     runs, spent = 0, 0.0
-    while spent < budget_s and runs < 500:
+    while runs == 0 or (spent < budget_s and runs < 500):
         t0 = time.perf_counter()
-        oracle.conv2d(g, inp.x, inp.w, inp.b, inp.r)
+        f(g, inp.x, inp.w, inp.b, inp.r)
         spent += time.perf_counter() - t0
         runs += 1
+    return {"s_per_run": spent / runs, "runs": runs, "gflops": 2 * macs * runs / spent / 1e9}
+
+
+def cpu_baseline(results, budget_s):
+    """The oracle timed per layer on the host cores (rank 0, one GPU): whole
+    layers, each repeated for about budget_s.  Returns the headline entry and
+    attaches each layer's figures to its result."""
+    import oracle
+
+    for r in results.values():
+        r["oracle"] = oracle_layer(workloads.BY_NAME[r["name"]], budget_s)
+        print(f"# oracle {r['name']}: {r['oracle']['s_per_run']:.3f} s per run, "
+              f"{r['oracle']['gflops']:.1f} GFLOP/s", file=sys.stderr, flush=True)
+    h = results[HEADLINE]["oracle"]
     return {
-        "value": 2 * macs * runs / spent / 1e12, "unit": "TFLOP/s",
+        "value": round(h["gflops"] / 1e3, 6), "unit": "TFLOP/s",
         "cores": oracle.max_threads(), "kind": "oracle",
-        "sample": f"whole headline layer (N={layer.n}), fp64 direct loops with |w*x| scale, "
-                  f"{runs} run(s), {spent:.1f} s",
+        "cpu_model": cpu_model(),
+        "sample": f"whole headline layer (N={workloads.BY_NAME[HEADLINE].n}), fp64 direct "
+                  f"loops with the |w*x| scale, {h['runs']} run(s) of {h['s_per_run']:.3f} s; "
+                  f"every other layer likewise in layers[].oracle",
     }
+
+
+CONFIGS = {  # the five workloads as their layers
+    1: ["w1_conv3x3_f32"], 2: ["w2_bottleneck3x3_f16"],
+    3: ["w3a_stem7x7s2_f16", "w3b_pointwise_f16"],
+    4: ["w4a_depthwise5x5_f32", "w4b_depthwise3x3s2_f32", "w4c_pointwise_f32"],
+    5: ["w5a_dilated_grouped_f16", "w5b_convtranspose2x2s2_f16"],
+}
+
+
+def config_sums(results):
+    out = []
+    for cfg, names in CONFIGS.items():
+        if not all(n in results for n in names):
+            continue
+        rs = [results[n] for n in names]
+        t = sum(r["us_avg"] for r in rs)
+        flops = sum(2 * r["macs"] for r in rs)
+        nbytes = sum(r["alg_bytes"] for r in rs)
+        roof = sum(r["roof_us"] for r in rs)
+        e = {"config": cfg, "layers": names, "us": round(t, 3),
+             "tflops": round(flops / (t * 1e-6) / 1e12, 3),
+             "gbs": round(nbytes / (t * 1e-6) / 1e9, 1), "roof_us": round(roof, 3),
+             "roof_frac": round(roof / t, 4)}
+        if all("oracle" in r for r in rs):
+            os_ = sum(r["oracle"]["s_per_run"] for r in rs)
+            e["oracle_s"] = round(os_, 4)
+            e["oracle_gflops"] = round(flops / os_ / 1e9, 2)
+        out.append(e)
+    return out
 
 
 def traffic_from_profiles(kernel_src_hash):
@@ -227,6 +303,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--loops", type=int, default=5)
+    ap.add_argument("--oracle-budget", type=float, default=1.5,
+                    help="seconds of oracle work per layer for cpu_baseline")
     ap.add_argument("--layers", default="")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -234,7 +313,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the path shards by batch or output channel, see DESIGN.md)",
+                                   "(the path would shard by batch or output channel; no multi-GPU run is provided)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -252,22 +331,25 @@ def main():
         return
 
     cf.lib()  # fail loudly if the native library is missing
+    default = [l.name for l in workloads.LAYERS] + [l.name for l in workloads.EXTRA_LAYERS]
     names = [HEADLINE] if args.headline_only else (
-        args.layers.split(",") if args.layers else [l.name for l in workloads.LAYERS])
+        args.layers.split(",") if args.layers else default)
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
     results = {}
     for nm in names:
-        results[nm] = time_layer(cf, torch, workloads.BY_NAME[nm], args.steps, args.warmup)
+        results[nm] = time_layer(cf, torch, workloads.BY_NAME[nm], args.steps, args.warmup,
+                                 args.loops)
         print(f"# {nm}: {results[nm]['variant']} {results[nm]['us_avg']:.2f} us "
               f"{results[nm]['tflops']:.1f} TFLOP/s {results[nm]['gbs']:.0f} GB/s "
-              f"{100 * results[nm]['roof_frac']:.1f}% of {results[nm]['bound']} roof",
-              file=sys.stderr, flush=True)
+              f"{100 * results[nm]['roof_frac']:.1f}% of {results[nm]['bound']} roof "
+              f"(loops {results[nm]['us_loops']})", file=sys.stderr, flush=True)
     h = results[HEADLINE]
     layer = workloads.BY_NAME[HEADLINE]
     macs, nbytes = layer_stats(layer)
     value = 2 * macs / (h["total_s"] / args.steps) / 1e12
     traffic = traffic_from_profiles(kernel_source_hash())
+    cpu = None if args.no_cpu_baseline else cpu_baseline(results, args.oracle_budget)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -285,6 +367,8 @@ def main():
         "config": {"workload": "ResNet-style bottleneck 3x3 fp16 (fp32 accumulate), N=32, "
                                "Cin=Cout=256, 14x14, stride 1, pad 1, bias + residual + ReLU",
                    "variant": h["variant"], "rotating_sets": h["rotating_sets"],
+                   "rotation_bytes": h["rotation_bytes"], "loops": args.loops,
+                   "timing": f"median of {args.loops} event-timed loops of {args.steps} calls",
                    "hbm_gbs_alg": round(h["gbs"], 1)},
         "roofline": {
             "bound": "mfma",
@@ -294,7 +378,8 @@ def main():
             "frac": round(2 * macs / (h["us_avg"] * 1e-6) / 1e12 / PEAK["f16_mfma_tflops"], 4),
             "traffic": traffic,
         },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(layer),
+        "cpu_baseline": cpu,
+        "configs": config_sums(results),
         "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                     if k not in ("total_s", "wall_s")} for r in results.values()],
     }

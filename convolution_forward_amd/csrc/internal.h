@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "tiles.h"
+
 namespace convfwd {
 
 enum Dtype { F32 = 0, F16 = 1 };
@@ -193,6 +195,7 @@ struct ReduceArgs {
   long long total;       // output elements in this chunk
   int hw;                // ho * wo
   int c_out;
+  int vec;               // total and plane_stride multiples of 4 (planes 16-byte aligned)
   int act;
   float alpha, beta;
 };
@@ -211,16 +214,6 @@ struct Col2imArgs {
   float alpha, beta;
 };
 
-// Tile shape of the generic implicit GEMM kernel.
-constexpr int IG_TILE_P = 64;   // output pixels per workgroup
-constexpr int IG_TILE_C = 64;   // output channels per workgroup
-constexpr int IG_KSTEP_BYTES = 64;  // k-block: 32 halves or 16 floats
-
-// Halo kernel (f16): LDS bytes per pipeline buffer (input tile + weight tile);
-// two buffers are allocated statically.
-constexpr int HALO_BUF_BYTES = 40 * 1024;
-constexpr int HALO_MAXT = 8;  // 16x16 MFMA output tiles per wave
-constexpr int HALO_MAXI = 8;  // staged (position, octet) input items per thread
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_halo(const HaloArgs& a, hipStream_t s);

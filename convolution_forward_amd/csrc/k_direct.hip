@@ -650,48 +650,71 @@ hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, si
 }
 
 // ---------------------------------------------------------------------------
-// Split-k reduction.  The R raw planes hold disjoint k ranges of the same
-// outputs.  Lanes are grouped R' = next_pow2(R) at a time: lane (q, r) reads
-// plane r of output q, and a xor butterfly over the group adds the planes in a
-// fixed tree ((p0+p1)+(p2+p3))+...; addition is commutative, so every lane of
-// the group ends with bit-identical sums and the order depends only on R.
-// Lane r == 0 of each group applies bias, residual, activation and stores.
+// Split-k reduction ("Convolution, pooling and resize", split k: each range
+// writes a raw plane and the epilogue pass adds the planes in range order, then
+// bias, residual and activation).  Each lane owns 4 consecutive outputs, read
+// as float4, so a half wave reads 512 contiguous bytes of a plane.  The two
+// halves of a wave cover the same 128 outputs: the lower half adds planes
+// [0, h) and the upper half planes [h, R), each in range order, h = ceil(R/2);
+// one cross-half wavefront shuffle (lane xor 32) then adds the two partial
+// sums.  The order depends on R alone, so two runs give the same bits.  The
+// lower half applies bias, residual and activation and stores.
 // ---------------------------------------------------------------------------
-template <typename T, int RP>
+template <typename T>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const ReduceArgs a) {
-  constexpr int OPW = 64 / RP;  // outputs per wave
   const int lane = threadIdx.x & 63;
-  const int q = lane / RP, r = lane - q * RP;
-  const long long wave_id = (long long)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  const long long o = wave_id * OPW + q;
-  float v = 0.0f;
-  if (o < a.total && r < a.splits) v = a.planes[(long long)r * a.plane_stride + o];
+  const int upper = lane >> 5;
+  const long long wave_id = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long o0 = (wave_id * 32 + (lane & 31)) * 4;
+  const int h = (a.splits + 1) >> 1;
+  const int r0 = upper ? h : 0, r1 = upper ? a.splits : h;
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (o0 < a.total) {
+    if (a.vec) {  // total and the plane stride are multiples of 4
+      for (int r = r0; r < r1; ++r) {
+        const float4 p =
+            *reinterpret_cast<const float4*>(a.planes + (long long)r * a.plane_stride + o0);
+        if (r == r0) {
+          v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        } else {
+          v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+        }
+      }
+    } else {
+      for (int r = r0; r < r1; ++r) {
 #pragma unroll
-  for (int off = 1; off < RP; off <<= 1) v += __shfl_xor(v, off, 64);
-  if (r == 0 && o < a.total) {
-    const int co = (int)((o / a.hw) % a.c_out);
-    static_cast<T*>(a.y)[o] = epilogue_one<T>(v, static_cast<const T*>(a.bias),
-                                              static_cast<const T*>(a.res), co, o, a.act,
-                                              a.alpha, a.beta);
+        for (int i = 0; i < 4; ++i) {
+          if (o0 + i < a.total) {
+            const float p = a.planes[(long long)r * a.plane_stride + o0 + i];
+            v[i] = r == r0 ? p : v[i] + p;
+          }
+        }
+      }
+    }
+  }
+  // every lane reaches the shuffle (no early exit above)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] += __shfl_xor(v[i], 32, 64);
+  if (!upper) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long long o = o0 + i;
+      if (o < a.total) {
+        const int co = (int)((o / a.hw) % a.c_out);
+        static_cast<T*>(a.y)[o] = epilogue_one<T>(v[i], static_cast<const T*>(a.bias),
+                                                  static_cast<const T*>(a.res), co, o, a.act,
+                                                  a.alpha, a.beta);
+      }
+    }
   }
 }
 
 template <typename T>
 static hipError_t launch_reduce_t(const ReduceArgs& a, hipStream_t s) {
-  int rp = 1;
-  while (rp < a.splits) rp <<= 1;
-  const long long opw = 64 / rp;
-  const long long waves = (a.total + opw - 1) / opw;
+  if (a.splits < 2) return hipErrorInvalidValue;
+  const long long waves = (a.total + 127) / 128;
   dim3 grid((unsigned)((waves + 3) / 4));
-  switch (rp) {
-    case 1: hipLaunchKernelGGL((splitk_reduce_kernel<T, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((splitk_reduce_kernel<T, 8>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((splitk_reduce_kernel<T, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((splitk_reduce_kernel<T, 32>), grid, dim3(256), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((splitk_reduce_kernel<T>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 //   y[n, co, p] = act( sum_ci w[co, ci] * x[n, ci, p]  + bias[co] + res[n, co, p] )
 //
 // for every image n and pixel p of the H*W plane.  The same kernel runs the
-// ConvTranspose whose kernel equals its stride of 2 with no padding ("Convolution
-// arithmetic", transposed convolution: each output then takes exactly one tap):
+// ConvTranspose whose kernel equals its stride of 2 with no padding
+// ("Convolutions", section 2.5, transposed convolution: with kernel = stride the
+// copies of the kernel do not overlap, so each output takes exactly one tap):
 // GEMM rows m = 4 co + 2 kh + kw, weights [ci][m] as they lie, and the epilogue
 // scatters row m, pixel (h, w) to y[n, co, 2h + kh, 2w + kw].
 //

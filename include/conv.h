@@ -146,44 +146,68 @@ int conv_output_extent(const conv_problem* p, int64_t* ho, int64_t* wo);
 int conv_resolve_auto_pad(conv_problem* p, int auto_pad, const int64_t* output_shape_hw);
 
 /* Scratch the planned variant needs, in bytes, for the whole batch and for one
- * image ("Layout and operands": Scratch(problem, half)).  Zero for the direct,
- * pointwise and unsplit implicit variants; R float32 partial planes per image when
- * k is split into R ranges; c_out*kh*kw*h*w float32 columns per image for
- * ConvTranspose.  A scratch buffer between the two runs the batch in chunks of
- * whole images, which changes no bit of the result.  Pure host, shape-only. */
+ * image ("Convolution, pooling and resize", "Layout and operands":
+ * Scratch(problem, half) says how much a shape needs, nothing for the variants
+ * that gather windows while they multiply).  Zero for the direct, pointwise and
+ * unsplit implicit variants; R float32 partial planes per image when k is split
+ * into R ranges ("Variants", split k); c_out*kh*kw*h*w float32 columns per image
+ * for ConvTranspose other than kernel = stride = 2.  A scratch buffer between
+ * the two runs the batch in chunks of whole images, which changes no bit of the
+ * result.  Shape-only: the plan is made for gfx950's 256 compute units and
+ * never queries the HIP runtime, so every device gets the same answer. */
 int conv_scratch_size(const conv_problem* p, int dtype, uint64_t* bytes_whole_batch,
                       uint64_t* bytes_per_image);
 
-/* Name of the variant the planner picks ("DescribeVariant"), NUL-terminated,
- * e.g. "implicit_gemm_halo.f16.t224x32", "depthwise_direct.f32".  Shape-only.
- * Returns CONV_ERR_ARG when len is too small. */
+/* Name of the variant the planner picks ("Convolution, pooling and resize",
+ * "Variants": DescribeVariant names what a device runs), NUL-terminated, e.g.
+ * "implicit_gemm_halo.f16.rowshift.r14.n32", "depthwise_direct.f32.wave.col14".
+ * Shape-only (no HIP runtime call; the same string on every device).  Returns
+ * CONV_ERR_ARG when len is too small, or the validation status of the problem. */
 int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t len);
 
-/* Conv forward.  x, w, y are required device pointers; bias and residual are read
- * only when has_bias / has_residual are set (then they are required).  scratch may
- * be NULL when conv_scratch_size reports zero; it must be 16-byte aligned and must
- * not overlap any operand.  stream is a hipStream_t (NULL = default stream).
- * Requires p->transpose == 0.  Asynchronous: returns once the work is enqueued. */
+/* Conv forward: the cross-correlation above with the fused epilogue
+ * ("Convolution, pooling and resize", "Layout and operands": operands are
+ * buffers plus element offsets, the epilogue is sum, bias, residual,
+ * activation, each rounded in float32; "Variants": the layer class picks the
+ * kernel; "Convolutions" sections 2.1 and 2.4: output size, convolution as a
+ * matrix product with the window gathered, never unfolded into a column
+ * matrix).  x, w, y are required device pointers; bias and residual are read
+ * only when has_bias / has_residual are set (then they are required).  scratch
+ * may be NULL when conv_scratch_size reports zero; it must be 16-byte aligned and
+ * must not overlap any operand.  stream is a hipStream_t (NULL = default stream).
+ * Requires p->transpose == 0.  Asynchronous: returns once the work is enqueued.
+ * Errors: CONV_ERR_ARG / SHAPE / OVERLAP / SCRATCH before anything is enqueued;
+ * CONV_ERR_DEVICE if the runtime refuses a launch. */
 int conv_forward(const conv_problem* p, int dtype, const void* x, const void* w,
                  const void* bias, const void* residual, void* y, void* scratch,
                  uint64_t scratch_bytes, void* stream);
 
-/* ConvTranspose forward: same contract as conv_forward, p->transpose == 1,
- * w in [c_in, c_out/groups, kh, kw] layout, and scratch required for the float32
- * columns (conv_scratch_size). */
+/* ConvTranspose forward ("Convolution, pooling and resize", "Variants": the
+ * product of the transposed weights with the input, then a gathering col2im, one
+ * thread per output element and no atomics, with the same epilogue;
+ * "Convolutions" section 2.5 and section 6: the adjoint scatter of Conv and the
+ * output_padding that picks among the stride's preimages).  Same contract as
+ * conv_forward, with p->transpose == 1, w in [c_in, c_out/groups, kh, kw] layout,
+ * and scratch for the float32 columns when conv_scratch_size reports any (kernel
+ * = stride = 2 without padding needs none: each output takes exactly one tap). */
 int conv_transpose_forward(const conv_problem* p, int dtype, const void* x, const void* w,
                            const void* bias, const void* residual, void* y, void* scratch,
                            uint64_t scratch_bytes, void* stream);
 
-/* Pre-flight: runs every check conv_forward (p->transpose == 0) or
- * conv_transpose_forward (p->transpose == 1) would run on these arguments (shape,
- * enums, pointers, overlap, scratch) and returns the status that call would
- * return before enqueueing, without enqueueing or touching the device.  Pure host. */
+/* Pre-flight ("Convolution, pooling and resize", "Layout and operands": sizes
+ * are checked before anything is recorded, and a scratch range may share the
+ * operands' arena only where it overlaps none of them): runs every check
+ * conv_forward (p->transpose == 0) or conv_transpose_forward (p->transpose == 1)
+ * would run on these arguments (shape, enums, pointers, overlap, scratch) and
+ * returns the status that call would return before enqueueing, without
+ * enqueueing or any HIP runtime call.  Pointers are compared, never read. */
 int conv_check(const conv_problem* p, int dtype, const void* x, const void* w,
                const void* bias, const void* residual, const void* y, const void* scratch,
                uint64_t scratch_bytes);
 
-/* Static, human-readable text for a status code. */
+/* Static, human-readable text for a status code (the shape errors are the
+ * GpuKernelShapeException analog of "Convolution, pooling and resize",
+ * "Layout and operands": raised before anything is recorded). */
 const char* conv_status_string(int status);
 
 #ifdef __cplusplus

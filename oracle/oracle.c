@@ -25,7 +25,7 @@
  *    residual, activation; the nine fused activations) and section
  *    "ConvInteger" (asymmetric padding is part of the problem geometry).
  *
- * Readings where the pages are silent (restated in the design doc):
+ * Readings where the pages are silent:
  *  - padding is zero padding (ONNX Conv semantics), begin and end pads are
  *    separate;
  *  - auto_pad follows the ONNX operator definitions (parity unpinned beyond

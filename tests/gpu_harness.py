@@ -2,7 +2,7 @@
 GPU (torch only allocates device memory and provides the stream) and compare it
 with the fp64 oracle.
 
-Parity bound, per output (north-star tolerances, "Convolution, pooling and
+Parity bound, per output (the stated tolerances, "Convolution, pooling and
 resize", "Tolerances"): |y_gpu - y_oracle| <= tol * S' + u(y_oracle), where
 tol = 1e-5 for float32 and 2e-3 for float16 operands with float32 accumulation,
 S' = sum |w*x| over the output's taps plus |bias| and |residual| (the bias and

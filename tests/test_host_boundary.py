@@ -274,6 +274,36 @@ def test_variant_names_for_workloads():
     assert buf_small(q, "f32")
 
 
+def test_workload_plans_fixed():
+    """Each workload layer's variant string, as the GPU tier asserts it on the
+    device: the plan depends on the shape only."""
+    from expected_plans import EXPECTED_PLANS, layer_problem
+    for name, want in EXPECTED_PLANS.items():
+        l = workloads.BY_NAME[name]
+        assert cf.conv_describe_variant(layer_problem(cf, l), l.dtype) == want, name
+
+
+def test_planner_references_no_hip_symbol(tmp_path):
+    """The planner (validation, plan, describe, scratch, check, status text) is
+    plain C++: it compiles without the HIP headers on the include path and its
+    object references no HIP runtime symbol, so nothing it answers can depend
+    on the device a call runs on (its compute-unit count included)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None or shutil.which("nm") is None:
+        pytest.skip("no host toolchain")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "convolution_forward_amd", "csrc")
+    obj = str(tmp_path / "plan.o")
+    subprocess.check_call(["g++", "-std=c++17", "-c", "-I", os.path.join(root, "include"), "-I",
+                           csrc, os.path.join(csrc, "conv_plan.cpp"), "-o", obj])
+    undefined = subprocess.check_output(["nm", "-u", "-C", obj], text=True)
+    assert "hip" not in undefined.lower(), undefined
+    for name in ("conv_describe_variant", "conv_scratch_size", "conv_check",
+                 "conv_output_extent", "conv_resolve_auto_pad", "conv_status_string"):
+        assert name in subprocess.check_output(["nm", "-g", "--defined-only", obj], text=True)
+
+
 def test_convt_fused_plan_rules():
     """Kernel = stride = 2 without padding, float16, one group, no residual takes
     the fused GEMM + gather path with no scratch; anything else keeps the float32

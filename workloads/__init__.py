@@ -99,7 +99,16 @@ LAYERS = [
           stride=(2, 2), transpose=True),
 ]
 
-BY_NAME = {l.name: l for l in LAYERS}
+# Measured beside the five workloads: the late 3x3 layer of the RTX 4070
+# single-layer split-k table (512 -> 512 channels at 7x7, batch 1), here in
+# fp16 with bias and ReLU.  Its grid is small and its k long, so the planner
+# cuts k into ranges.
+EXTRA_LAYERS = [
+    Layer("x1_late3x3_512_7x7_f16", 6, 0, "f16", 1, 512, 7, 7, 512, 3, 3, (1, 512, 7, 7),
+          pads=(1, 1, 1, 1), act="relu"),
+]
+
+BY_NAME = {l.name: l for l in LAYERS + EXTRA_LAYERS}
 
 
 def workload_layers(wl: int):
