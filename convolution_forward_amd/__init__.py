@@ -38,7 +38,7 @@ ACT_DEFAULTS = {"hard_sigmoid": (0.2, 0.5), "leaky_relu": (0.01, 0.0)}
 EXPORTS = (
     "conv_output_extent", "conv_resolve_auto_pad", "conv_scratch_size",
     "conv_describe_variant", "conv_forward", "conv_transpose_forward",
-    "conv_check", "conv_status_string",
+    "conv_check", "conv_status_string", "conv_forward_noalloc",
 )
 
 
@@ -86,6 +86,7 @@ def lib():
         L.conv_forward.argtypes = fwd
         L.conv_transpose_forward.argtypes = fwd
         L.conv_check.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_uint64]
+        L.conv_forward_noalloc.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp]
         L.conv_status_string.argtypes = [ctypes.c_int]
         L.conv_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -196,3 +197,13 @@ def conv_transpose_forward(p, dtype, x, w, bias, residual, y, scratch=None, scra
     """Enqueue the ConvTranspose forward on `stream`."""
     return _call(lib().conv_transpose_forward, "conv_transpose_forward", p, dtype, x, w, bias,
                  residual, y, scratch, scratch_bytes, stream, check)
+
+
+def conv_forward_noalloc(p, dtype, x, w, bias, residual, y, stream=None, check=True) -> int:
+    """Enqueue Conv (p.transpose == 0) or ConvTranspose (p.transpose == 1) with the
+    library's own static scratch: no allocation, no scratch argument."""
+    st = lib().conv_forward_noalloc(ctypes.byref(p), _dt(dtype), _ptr(x), _ptr(w), _ptr(bias),
+                                    _ptr(residual), _ptr(y), stream or None)
+    if check and st:
+        raise ConvError(st, "conv_forward_noalloc")
+    return st

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "conv.h"
 #include "internal.h"
@@ -315,9 +316,52 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
 }
 
 
+// Scratch held by the library for conv_forward_noalloc: split-k planes and
+// ConvTranspose float32 columns, for callers that cannot allocate.  The array
+// is a device global, one copy per GPU, kept until the process ends.  Host code
+// never uses its name as an address: the device address of each GPU's copy is
+// taken once per device with hipGetSymbolAddress and cached below.
+constexpr uint64_t kNoallocScratchBytes = 64ull << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`, or nullptr.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
+
+int conv_forward_noalloc(const conv_problem* p, int dtype, const void* x, const void* w,
+                         const void* bias, const void* residual, void* y, void* stream) {
+  if (!p) return CONV_ERR_ARG;
+  const bool tr = p->transpose == 1;
+  uint64_t whole = 0, per = 0;
+  const int st = conv_scratch_size(p, dtype, &whole, &per);
+  if (st) return st;
+  if (per > kNoallocScratchBytes) return CONV_ERR_SCRATCH;  // one image needs more than the array
+  if (per == 0) return run(p, dtype, tr, x, w, bias, residual, y, nullptr, 0, stream);
+  void* sp = noalloc_scratch();
+  if (!sp) return CONV_ERR_DEVICE;
+  // the largest whole number of images that fits; run() chunks the batch by it
+  const uint64_t bytes = std::min<uint64_t>(whole, kNoallocScratchBytes / per * per);
+  return run(p, dtype, tr, x, w, bias, residual, y, sp, bytes, stream);
+}
 
 int conv_forward(const conv_problem* p, int dtype, const void* x, const void* w,
                  const void* bias, const void* residual, void* y, void* scratch,

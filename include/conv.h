@@ -205,6 +205,23 @@ int conv_check(const conv_problem* p, int dtype, const void* x, const void* w,
                const void* bias, const void* residual, const void* y, const void* scratch,
                uint64_t scratch_bytes);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  conv_forward (p->transpose == 0) or conv_transpose_forward
+ * (p->transpose == 1) with the same arguments except the scratch: the split-k
+ * planes and ConvTranspose columns live in a 64 MiB array the library holds per
+ * GPU (a device global, kept until the process ends), so the call allocates
+ * nothing and gives the same bits as those calls.  A batch whose scratch need
+ * exceeds 64 MiB runs in chunks of whole images (same bits); a problem whose
+ * one image needs more than 64 MiB returns CONV_ERR_SCRATCH before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array and every kernel
+ * that uses it writes all of it that it reads, so nothing needs clearing; two
+ * calls that overlap in time on one GPU (different streams, or different host
+ * threads) race on it and must be serialised by the caller.  The first call on
+ * a device resolves the array's address there (CONV_ERR_DEVICE if that fails). */
+int conv_forward_noalloc(const conv_problem* p, int dtype, const void* x, const void* w,
+                         const void* bias, const void* residual, void* y, void* stream);
+
 /* Static, human-readable text for a status code (the shape errors are the
  * GpuKernelShapeException analog of "Convolution, pooling and resize",
  * "Layout and operands": raised before anything is recorded). */
