@@ -49,7 +49,7 @@ ROTATE_BYTES = 1 << 30
 
 
 def esize(dt):
-    return 2 if dt == "f16" else 4
+    return 4 if dt == "f32" else 2
 
 
 def layer_stats(layer):
@@ -73,7 +73,8 @@ def layer_stats(layer):
 def roof(layer, macs, nbytes):
     """Binding roof: min(compute peak, AI * HBM peak)."""
     flops = 2 * macs
-    peak_c = PEAK["f16_mfma_tflops"] if layer.dtype == "f16" else PEAK["f32_tflops"]
+    # bf16 and fp16 dense MFMA share the 2.5 PFLOP/s peak
+    peak_c = PEAK["f32_tflops"] if layer.dtype == "f32" else PEAK["f16_mfma_tflops"]
     t_c = flops / (peak_c * 1e12)
     t_m = nbytes / (PEAK["hbm_gbs"] * 1e9)
     if layer.groups == layer.c_in and layer.groups > 1 and not layer.transpose:
@@ -101,9 +102,12 @@ def time_layer(cf, torch, layer, steps, warmup, loops):
     p = build_problem(cf, layer)
     variant = cf.conv_describe_variant(p, layer.dtype)
     inp = workloads.make_inputs(layer)
-    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[layer.dtype]
+    # bfloat16 inputs are bfloat16-exact float32 values: the conversion is exact
+    dev = lambda a: None if a is None else \
+        torch.from_numpy(np.ascontiguousarray(a)).cuda().to(tdt)
     base = [dev(inp.x), dev(inp.w), dev(inp.b), dev(inp.r)]
-    ydt = torch.float16 if layer.dtype == "f16" else torch.float32
+    ydt = tdt
     macs, nbytes = layer_stats(layer)
     nsets = max(1, min(256, math.ceil(ROTATE_BYTES / nbytes)))
     sets = []

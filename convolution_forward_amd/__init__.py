@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libconvfwd.so")
 
 # enums of include/conv.h
 CONV_OK, CONV_ERR_ARG, CONV_ERR_SHAPE, CONV_ERR_OVERLAP, CONV_ERR_SCRATCH, CONV_ERR_DEVICE = range(6)
-CONV_F32, CONV_F16 = 0, 1
-DTYPES = {"f32": CONV_F32, "f16": CONV_F16}
+CONV_F32, CONV_F16, CONV_BF16 = 0, 1, 2
+DTYPES = {"f32": CONV_F32, "f16": CONV_F16, "bf16": CONV_BF16}
 ACTIVATIONS = {
     "identity": 0, "relu": 1, "tanh": 2, "sigmoid": 3, "silu": 4,
     "hard_sigmoid": 5, "hard_swish": 6, "clip": 7, "leaky_relu": 8,

@@ -44,14 +44,14 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
   const int st = check_call(p, dtype, transpose, x, w, bias, residual, y, scratch, scratch_bytes,
                             &g, &pl, &chunk);
   if (st) return st;
-  const size_t es = dtype == CONV_F16 ? 2 : 4;
+  const size_t es = (size_t)dtype_size(dtype);
   const char* xb = static_cast<const char*>(x) + p->x_off * es;
   const char* wb = static_cast<const char*>(w) + p->w_off * es;
   const char* bb = p->has_bias ? static_cast<const char*>(bias) + p->b_off * es : nullptr;
   const char* rb = p->has_residual ? static_cast<const char*>(residual) + p->r_off * es : nullptr;
   char* yb = static_cast<char*>(y) + p->y_off * es;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Dtype dt = dtype == CONV_F16 ? F16 : F32;
+  const Dtype dt = dtype == CONV_F16 ? F16 : dtype == CONV_BF16 ? BF16 : F32;
   const int64_t x_img = g.ci * g.h * g.w, y_img = g.co * g.ho * g.wo;
 
   for (int64_t i0 = 0; i0 < g.n; i0 += chunk) {
@@ -70,7 +70,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.toh = pl.toh; a.tow = pl.tow; a.tih = pl.tih; a.tiw = pl.tiw;
       a.tiles_w = pl.tiles_w; a.tiles = pl.tiles;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      const int vb = dt == F16 ? 8 : 16;
+      const int vb = dt == F32 ? 16 : 8;
       // the whole-plane kernel reads x with vector loads only; a misaligned x
       // runs the tiled kernel (same sums in the same order)
       if (pl.dw_wave && reinterpret_cast<uintptr_t>(xc) % vb == 0) {
@@ -149,7 +149,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
                  (std::min<int64_t>(64, g.co) * per_co) % 8 == 0 && ((g.co % 64) * per_co) % 8 == 0;
       }
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      e = launch_rowband(a, s);
+      e = launch_rowband(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_POINTWISE_GEMM) {
       if (dt == F32) {
         PwArgs a{};
@@ -179,7 +179,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_nch = make_magic((unsigned)a.nchunks);
       a.mg_nct = make_magic((unsigned)a.n_ct);
       a.mg_npt = make_magic((unsigned)a.n_pt);
-      e = launch_pointwise(a, device_cus(), s);
+      e = launch_pointwise(dt, a, device_cus(), s);
       }
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
       HaloArgs a{};
@@ -207,7 +207,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_nct = make_magic((unsigned)a.n_ct);
       a.mg_n = make_magic((unsigned)cn);
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      e = pl.halo.rowshift ? launch_rowshift(a, s) : launch_halo(a, s);
+      e = pl.halo.rowshift ? launch_rowshift(dt, a, s) : launch_halo(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {
       IgemmArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
@@ -220,7 +220,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.pix = (int)(cn * g.ho * g.wo);
       a.ksteps = pl.ksteps; a.steps_per_split = pl.steps_per_split; a.splits = pl.splits;
       a.wtrans = 0;
-      const int ept = dt == F16 ? 8 : 4;
+      const int ept = dt == F32 ? 4 : 8;
       a.wvec = (a.kg % ept == 0) && (reinterpret_cast<uintptr_t>(wb) % 16 == 0);
       a.mode = pl.splits > 1 ? OUT_RAW : OUT_FUSED;
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
@@ -253,7 +253,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_wo = make_magic((unsigned)g.wo);
       a.mg_kw = make_magic((unsigned)g.kw);
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
-      e = launch_grouped(a, s);
+      e = launch_grouped(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM && pl.ct_fused) {
       // GEMM rows m = 4 co + 2 kh + kw over whole input rows of one image; the
       // epilogue writes y[n][co][2h + kh][2w + kw] directly
@@ -276,7 +276,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_nch = make_magic((unsigned)a.nchunks);
       a.mg_nct = make_magic((unsigned)a.n_ct);
       a.mg_npt = make_magic((unsigned)a.n_pt);
-      e = launch_pointwise(a, device_cus(), s);
+      e = launch_pointwise(dt, a, device_cus(), s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) {
       // GEMM: cols[n][g*M + m][h][w] = sum_ci w[g*cig + ci][m] * x[n][g*cig + ci][h][w],
       // M = (Cout/G)*KH*KW; the matrix kernel runs it as a 1x1 conv with transposed

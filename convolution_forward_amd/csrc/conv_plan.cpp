@@ -49,7 +49,7 @@ int64_t convt_extent(int64_t in, int64_t k, int64_t s, int64_t d, int64_t pb, in
 
 int validate(const conv_problem* p, int dtype, Geo* g) {
   if (!p) return CONV_ERR_ARG;
-  if (dtype != CONV_F32 && dtype != CONV_F16) return CONV_ERR_ARG;
+  if (dtype != CONV_F32 && dtype != CONV_F16 && dtype != CONV_BF16) return CONV_ERR_ARG;
   if (p->transpose != 0 && p->transpose != 1) return CONV_ERR_ARG;
   if (p->activation < CONV_ACT_IDENTITY || p->activation > CONV_ACT_LEAKY_RELU)
     return CONV_ERR_ARG;
@@ -138,7 +138,7 @@ bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 // thread, the first KH rows four, and the ring holds KH rows plus three rows'
 // worth of prefetched ones.
 bool rowband_applicable(const Geo& g, int dtype) {
-  return !g.transpose && dtype == CONV_F16 && g.g == 1 && g.sh == 2 && g.sw == 2 && g.dh == 1 &&
+  return !g.transpose && half16(dtype) && g.g == 1 && g.sh == 2 && g.sw == 2 && g.dh == 1 &&
          g.dw == 1 && g.kw <= 8 && g.ci * g.kh <= 24 && g.kh + 4 * g.sh <= 16 && g.wo <= 128 &&
          g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024;
 }
@@ -147,7 +147,7 @@ bool rowband_applicable(const Geo& g, int dtype) {
 // channels per group, at most 10 taps, planes of at most 4096 pixels whose
 // padded copy (16 bytes per position) fits 48 KiB of LDS.
 bool grouped_applicable(const Geo& g, int dtype) {
-  return !g.transpose && dtype == CONV_F16 && g.g > 1 && g.cig == 8 && g.cog <= 32 &&
+  return !g.transpose && half16(dtype) && g.g > 1 && g.cig == 8 && g.cog <= 32 &&
          g.kh * g.kw <= 10 && g.h * g.w <= 4096 &&
          (g.h + g.pt + g.pb) * (g.w + g.pl + g.pr) * 16 <= 48 * 1024 && g.n * g.g <= 2147483647LL;
 }
@@ -169,7 +169,7 @@ bool pointwise_applicable(const Geo& g, int dtype) {
     return !g.transpose && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 && g.pt == 0 &&
            g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 4 == 0 &&
            (g.h * g.w) % 4 == 0 && ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) < (1LL << 31);
-  return !g.transpose && dtype == CONV_F16 && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
+  return !g.transpose && half16(dtype) && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
          g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
          (g.h * g.w) % 4 == 0 && g.h * g.w >= 4 &&
          pw_items(g.n, ceil_div(g.h * g.w, 128), ceil_div(g.co, 64), g.ci) < (1LL << 30);
@@ -180,7 +180,7 @@ bool pointwise_applicable(const Geo& g, int dtype) {
 // into y (float16, one group, no residual, input rows of whole 4-pixel groups
 // that fit a 128-pixel tile).
 bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
-  return g.transpose && dtype == CONV_F16 && g.g == 1 && g.kh == 2 && g.kw == 2 && g.sh == 2 &&
+  return g.transpose && half16(dtype) && g.g == 1 && g.kh == 2 && g.kw == 2 && g.sh == 2 &&
          g.sw == 2 && g.dh == 1 && g.dw == 1 && g.pt == 0 && g.pl == 0 && g.pb == 0 &&
          g.pr == 0 && g.oph == 0 && g.opw == 0 && !residual && g.w % 4 == 0 && g.w <= 128 &&
          pw_items(g.n, ceil_div(g.h * g.w, (128 / g.w) * g.w), ceil_div(4 * g.co, 128), g.ci) < (1LL << 30);
@@ -273,7 +273,7 @@ bool plan_depthwise(const Geo& g, Plan* pl) {
 // owns at most HALO_MAXT MFMA tiles and every thread stages at most HALO_MAXI
 // items.  Shape-only.
 bool plan_halo(const Geo& g, int dtype, HaloShape* hs) {
-  if (dtype != CONV_F16 || g.transpose) return false;
+  if (!half16(dtype) || g.transpose) return false;
   // 3x3, stride 1, dilation 1, whole image of at most 14 x 14 outputs per
   // workgroup, chunk pairs of 64 channels: the row-shift kernel.
   if (g.kh == 3 && g.kw == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 &&
@@ -354,7 +354,7 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
       return CONV_OK;
     }
     pl->scratch_per_image = (uint64_t)(g.co * g.kh * g.kw * g.h * g.w) * 4u;
-    const int ept = dtype == CONV_F16 ? 8 : 4;
+    const int ept = half16(dtype) ? 8 : 4;
     pl->ksteps = (int)ceil_div(g.cig, 4 * ept);
     pl->steps_per_split = pl->ksteps;
     if (ceil_div(g.co * g.kh * g.kw / g.g, IG_TILE_C) > 65535 || g.g > 65535) return CONV_ERR_SHAPE;
@@ -412,7 +412,7 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
       if (!plan_depthwise(g, pl)) return CONV_ERR_SHAPE;
     } else {
       // implicit GEMM: k-blocks of 64 bytes; split only small grids with long k
-      const int ept = dtype == CONV_F16 ? 8 : 4;
+      const int ept = half16(dtype) ? 8 : 4;
       const int64_t kg = g.cig * g.kh * g.kw;
       const int64_t steps = ceil_div(kg, 4 * ept);
       const int64_t tiles = ceil_div(g.n * g.ho * g.wo, IG_TILE_P) * ceil_div(g.cog, IG_TILE_C) * g.g;
@@ -472,7 +472,7 @@ int check_call(const conv_problem* p, int dtype, bool transpose, const void* x, 
   if (p->has_bias && !bias) return CONV_ERR_ARG;
   if (p->has_residual && !residual) return CONV_ERR_ARG;
 
-  const size_t es = dtype == CONV_F16 ? 2 : 4;
+  const size_t es = (size_t)dtype_size(dtype);
   int64_t chunk = g.n;
   if (pl.scratch_per_image > 0) {
     if (!scratch) return CONV_ERR_SCRATCH;
@@ -585,7 +585,7 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
   Plan pl;
   st = make_plan(p, dtype, g, &pl);
   if (st) return st;
-  const char* dn = dtype == CONV_F16 ? "f16" : "f32";
+  const char* dn = dtype == CONV_F16 ? "f16" : dtype == CONV_BF16 ? "bf16" : "f32";
   char tmp[128];
   switch (pl.variant) {
     case CONV_VARIANT_IMPLICIT_GEMM:

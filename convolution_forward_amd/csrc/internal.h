@@ -10,7 +10,7 @@
 
 namespace convfwd {
 
-enum Dtype { F32 = 0, F16 = 1 };
+enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
 
 // Output modes of the matrix kernels.
 enum OutMode {
@@ -216,12 +216,12 @@ struct Col2imArgs {
 
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
-hipError_t launch_halo(const HaloArgs& a, hipStream_t s);
-hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s);
+hipError_t launch_halo(Dtype dt, const HaloArgs& a, hipStream_t s);
+hipError_t launch_pointwise(Dtype dt, const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s);
-hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s);
-hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s);
-hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s);
+hipError_t launch_rowband(Dtype dt, const RowbandArgs& a, hipStream_t s);
+hipError_t launch_grouped(Dtype dt, const GroupedArgs& a, hipStream_t s);
+hipError_t launch_rowshift(Dtype dt, const HaloArgs& a, hipStream_t s);
 hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s);
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
                                   hipStream_t s);

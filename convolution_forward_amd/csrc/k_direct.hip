@@ -68,6 +68,8 @@ hipError_t launch_depthwise(Dtype dt, const DepthwiseArgs& a, hipStream_t s) {
   const size_t lds = (size_t)a.tih * a.tiw * sizeof(float);
   if (dt == F16)
     hipLaunchKernelGGL(depthwise_kernel<_Float16>, grid, dim3(256), lds, s, a);
+  else if (dt == BF16)
+    hipLaunchKernelGGL(depthwise_kernel<__bf16>, grid, dim3(256), lds, s, a);
   else
     hipLaunchKernelGGL(depthwise_kernel<float>, grid, dim3(256), lds, s, a);
   return hipGetLastError();
@@ -106,13 +108,17 @@ template <>
 struct DwVec<_Float16> {
   typedef uint2 type;
 };
+template <>
+struct DwVec<__bf16> {
+  typedef uint2 type;
+};
 
 template <typename T>
 __device__ __forceinline__ void dw_unpack(const typename DwVec<T>::type& v, float (&f)[4]) {
   if constexpr (sizeof(T) == 4) {
     f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
   } else {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef T h4 __attribute__((ext_vector_type(4)));
     const h4 h = __builtin_bit_cast(h4, v);
 #pragma unroll
     for (int k = 0; k < 4; ++k) f[k] = (float)h[k];
@@ -124,10 +130,10 @@ __device__ __forceinline__ typename DwVec<T>::type dw_pack(const float (&f)[4]) 
   if constexpr (sizeof(T) == 4) {
     return float4{f[0], f[1], f[2], f[3]};
   } else {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    typedef T h4 __attribute__((ext_vector_type(4)));
     h4 h;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) h[k] = (_Float16)f[k];
+    for (int k = 0; k < 4; ++k) h[k] = (T)f[k];
     return __builtin_bit_cast(uint2, h);
   }
 }
@@ -617,8 +623,9 @@ static hipError_t launch_dw_wave_t(const DepthwiseArgs& a, long long planes, int
 
 hipError_t launch_depthwise_wave(Dtype dt, const DepthwiseArgs& a, long long planes, int cus,
                                  size_t lds, hipStream_t s) {
-  return dt == F16 ? launch_dw_wave_t<_Float16>(a, planes, cus, lds, s)
-                   : launch_dw_wave_t<float>(a, planes, cus, lds, s);
+  return dt == F16    ? launch_dw_wave_t<_Float16>(a, planes, cus, lds, s)
+         : dt == BF16 ? launch_dw_wave_t<__bf16>(a, planes, cus, lds, s)
+                      : launch_dw_wave_t<float>(a, planes, cus, lds, s);
 }
 
 template <typename T>
@@ -645,8 +652,9 @@ static hipError_t launch_dw_plane_t(const DepthwiseArgs& a, int grid, size_t lds
 
 hipError_t launch_depthwise_plane(Dtype dt, const DepthwiseArgs& a, int grid, size_t lds,
                                   hipStream_t s) {
-  return dt == F16 ? launch_dw_plane_t<_Float16>(a, grid, lds, s)
-                   : launch_dw_plane_t<float>(a, grid, lds, s);
+  return dt == F16    ? launch_dw_plane_t<_Float16>(a, grid, lds, s)
+         : dt == BF16 ? launch_dw_plane_t<__bf16>(a, grid, lds, s)
+                      : launch_dw_plane_t<float>(a, grid, lds, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -719,7 +727,9 @@ static hipError_t launch_reduce_t(const ReduceArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_reduce(Dtype dt, const ReduceArgs& a, hipStream_t s) {
-  return dt == F16 ? launch_reduce_t<_Float16>(a, s) : launch_reduce_t<float>(a, s);
+  return dt == F16    ? launch_reduce_t<_Float16>(a, s)
+         : dt == BF16 ? launch_reduce_t<__bf16>(a, s)
+                      : launch_reduce_t<float>(a, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -767,6 +777,8 @@ hipError_t launch_col2im(Dtype dt, const Col2imArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.total + 255) / 256));
   if (dt == F16)
     hipLaunchKernelGGL(col2im_kernel<_Float16>, grid, dim3(256), 0, s, a);
+  else if (dt == BF16)
+    hipLaunchKernelGGL(col2im_kernel<__bf16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(col2im_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

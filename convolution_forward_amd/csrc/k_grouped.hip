@@ -22,6 +22,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "mfma16.h"
 
 namespace convfwd {
 
@@ -40,8 +41,12 @@ constexpr int GC_NT = 1024;     // threads per workgroup: 16 waves, 4 per SIMD
 
 // KS: k-steps (taps <= 2 KS).  CB: 8-channel row groups of the output
 // channels (cog <= 8 CB).  VEC: x 8-byte aligned and h * w % 4 == 0.
-template <int KS, int CB, bool VEC, int AK = -1>
+template <typename E, int KS, int CB, bool VEC, int AK = -1>
 __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) {
+  typedef E half8_t __attribute__((ext_vector_type(8)));
+  typedef E half4_t __attribute__((ext_vector_type(4)));
+  typedef E half2_t __attribute__((ext_vector_type(2)));
+
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   u32x4_t* xs = reinterpret_cast<u32x4_t*>(smem);                      // [pos] octets
   u32x4_t* wl = reinterpret_cast<u32x4_t*>(smem + a.xs_bytes);          // [co][tap] octets
@@ -51,11 +56,11 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   const int n = blockIdx.x / a.groups, g = blockIdx.x - n * a.groups;
   const int hw = a.h * a.w, howo = a.ho * a.wo;
   const int taps = a.kh * a.kw;
-  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x) + ((long long)n * a.c_in + g * 8) * hw;
-  const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt) + (long long)g * a.cog * 8 * taps;
-  const _Float16* bias = static_cast<const _Float16*>(a.bias);
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
+  const E* __restrict__ x = static_cast<const E*>(a.x) + ((long long)n * a.c_in + g * 8) * hw;
+  const E* __restrict__ w = static_cast<const E*>(a.wt) + (long long)g * a.cog * 8 * taps;
+  const E* bias = static_cast<const E*>(a.bias);
+  const E* res = static_cast<const E*>(a.res);
+  E* y = static_cast<E*>(a.y);
   const long long obase = ((long long)n * a.c_out + g * a.cog) * howo;
 
   // ---- loads: 4 consecutive pixels of the 8 planes per item (items beyond the
@@ -81,10 +86,10 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   // weights (cog x 8 x taps halves, contiguous) and bias: one element per item
   const int nw = a.cog * 8 * taps;  // <= 32 x 8 x 10
   constexpr int WN = (32 * 8 * GC_MAXTAPS + GC_NT - 1) / GC_NT;
-  _Float16 wv[WN];
+  E wv[WN];
 #pragma unroll
   for (int i = 0; i < WN; ++i) wv[i] = w[min(tid + GC_NT * i, nw - 1)];
-  const _Float16 bv_in = *(bias ? bias + g * a.cog + min(tid, a.cog - 1) : x);
+  const E bv_in = *(bias ? bias + g * a.cog + min(tid, a.cog - 1) : x);
 
   // ---- zero the staged plane (padding positions stay zero) and the weight
   // octets (taps past the last and channels past cog stay zero) ----
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
     if (q < nw) {
       const int co = q / (8 * taps), r = q - co * 8 * taps;
       const int ci = r / taps, t = r - ci * taps;
-      reinterpret_cast<_Float16*>(wl + co * GC_MAXTAPS + t)[ci] = wv[i];
+      reinterpret_cast<E*>(wl + co * GC_MAXTAPS + t)[ci] = wv[i];
     }
   }
   if (tid < 32) bsm[tid] = (float)bv_in;
@@ -141,8 +146,8 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   // output channels, which need all 16 accumulator elements); wave w takes
   // passes w, w + 16, ...  Lane l: pixel l % 32 of each block, output channels
   // 8 (i / 4) + 4 (l / 32) + i % 4 for accumulator element i < 4 CB.
-  _Float16* __restrict__ yg = y + obase;
-  const _Float16* rg = res ? res + obase : nullptr;
+  E* __restrict__ yg = y + obase;
+  const E* rg = res ? res + obase : nullptr;
   const int nblk = (howo + 31) / 32;
   constexpr int NB = CB >= 4 ? 1 : 2;
   for (int b0 = NB * wave; b0 < nblk; b0 += NB * (GC_NT / 64)) {
@@ -162,8 +167,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
         const int oh = (int)mdiv((unsigned)p, a.mg_wo), ow = p - oh * a.wo;
         const u32x4_t v = xs[oh * a.sh * a.wp + ow * a.sw + tofs[ks]];
         const u32x4_t bf = tok[ks] ? v : u32x4_t{0, 0, 0, 0};
-        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, af[ks]),
-                                                        __builtin_bit_cast(half8_t, bf), acc[u], 0, 0, 0);
+        acc[u] = mfma_32x32x16<E>(af[ks], bf, acc[u]);
       }
     }
 #pragma unroll
@@ -187,14 +191,15 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
 #pragma unroll
         for (int i = 0; i < 4 * CB; ++i) {
           const int co = 8 * (i / 4) + 4 * hi + (i & 3);
-          if (co < a.cog) store_out(yg + co * howo + pix[u], (_Float16)v[i]);
+          if (co < a.cog) store_out(yg + co * howo + pix[u], (E)v[i]);
         }
       }
     }
   }
 }
 
-hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s) {
+template <typename E>
+static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n * a.groups));
   const size_t lds = (size_t)a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4;
   const int taps = a.kh * a.kw;
@@ -202,11 +207,11 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s) {
   // ReLU and sigmoid with the activation fixed at compile time on the vector path
 #define GC_CASE(KS_, CB_)                                                                      \
   if (a.vec && a.act == 1)                                                                     \
-    hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true, 1>), grid, dim3(GC_NT), lds, s, a);   \
+    hipLaunchKernelGGL((grouped_c8_kernel<E, KS_, CB_, true, 1>), grid, dim3(GC_NT), lds, s, a);   \
   else if (a.vec && a.act == 3)                                                                \
-    hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true, 3>), grid, dim3(GC_NT), lds, s, a);   \
-  else if (a.vec) hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, true>), grid, dim3(GC_NT), lds, s, a); \
-  else hipLaunchKernelGGL((grouped_c8_kernel<KS_, CB_, false>), grid, dim3(GC_NT), lds, s, a);
+    hipLaunchKernelGGL((grouped_c8_kernel<E, KS_, CB_, true, 3>), grid, dim3(GC_NT), lds, s, a);   \
+  else if (a.vec) hipLaunchKernelGGL((grouped_c8_kernel<E, KS_, CB_, true>), grid, dim3(GC_NT), lds, s, a); \
+  else hipLaunchKernelGGL((grouped_c8_kernel<E, KS_, CB_, false>), grid, dim3(GC_NT), lds, s, a);
 #define GC_KS(KS_)                          \
   if (a.cog <= 8) { GC_CASE(KS_, 1) }       \
   else if (a.cog <= 16) { GC_CASE(KS_, 2) } \
@@ -221,6 +226,10 @@ hipError_t launch_grouped(const GroupedArgs& a, hipStream_t s) {
 #undef GC_KS
 #undef GC_CASE
   return hipGetLastError();
+}
+
+hipError_t launch_grouped(Dtype dt, const GroupedArgs& a, hipStream_t s) {
+  return dt == BF16 ? launch_grouped_t<__bf16>(a, s) : launch_grouped_t<_Float16>(a, s);
 }
 
 }  // namespace convfwd

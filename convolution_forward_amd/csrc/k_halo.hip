@@ -25,6 +25,7 @@
 // for bit.  Epilogue: bias, residual, activation in float32, float16 store.
 #include "epilogue.h"
 #include "internal.h"
+#include "mfma16.h"
 
 namespace convfwd {
 
@@ -37,7 +38,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int MAXT = HALO_MAXT;
 constexpr int MAXI = HALO_MAXI;
 
-__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 
 // LDS slot of octet o at position p.  A fragment read has 16 lanes on 16
 // consecutive positions with the same octet; with positions OCT*16 bytes apart,
@@ -52,8 +52,12 @@ __device__ __forceinline__ int swz(int p, int o) {
 
 }  // namespace
 
-template <int KH, int KW, int OCT, int NT>
+template <typename E, int KH, int KW, int OCT, int NT>
 __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
+  typedef E half8_t __attribute__((ext_vector_type(8)));
+  typedef E half4_t __attribute__((ext_vector_type(4)));
+  typedef E half2_t __attribute__((ext_vector_type(2)));
+
   constexpr int KHW = KH * KW;
   constexpr int SLOTS = KHW * OCT;
   constexpr int NM = (SLOTS + 3) / 4;
@@ -83,8 +87,8 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   const int in_bytes = in_items * 16;
   const long long hw_in = (long long)a.h * a.w;
 
-  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x);
-  const _Float16* __restrict__ wt = static_cast<const _Float16*>(a.wt);
+  const E* __restrict__ x = static_cast<const E*>(a.x);
+  const E* __restrict__ wt = static_cast<const E*>(a.wt);
 
   // ---- per-thread staging descriptors (independent of the chunk) ----
   int in_off[MAXI];    // element offset of the octet's channel 0 at this position
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     const int pos = ii * a.tiw + jj;
     in_lds[i] = (pos * OCT + swz<OCT>(pos, o)) * 16;
   }
-  const _Float16* __restrict__ ximg = x + (long long)n * a.c_in * hw_in;
+  const E* __restrict__ ximg = x + (long long)n * a.c_in * hw_in;
 
   // weights: item = (co_l, octet) -> KHW contiguous 16-byte vectors
   const int w_item = tid;
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   const int w_co_l = w_live ? w_item / OCT : 0;
   const int w_o = w_live ? w_item - (w_item / OCT) * OCT : 0;
   const bool w_ok = w_live && (co0 + w_co_l) < a.cog;
-  const _Float16* __restrict__ wrow =
+  const E* __restrict__ wrow =
       wt + ((long long)(g * a.cog + (w_ok ? co0 + w_co_l : 0)) * a.cig + 8 * w_o) * KHW;
 
   // Staging registers.  Loads are unconditional (padding items read a valid
@@ -130,12 +134,12 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
       if (i < ni) {
-        const _Float16* p = ximg + coff + in_off[i];
+        const E* p = ximg + coff + in_off[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) rin[i][e] = p[e * hw_in];
       }
     }
-    const _Float16* pw = wrow + (long long)c * CH * KHW;
+    const E* pw = wrow + (long long)c * CH * KHW;
     if (a.wvec) {
       const u32x4_t* p = reinterpret_cast<const u32x4_t*>(pw);
 #pragma unroll
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     for (int i = 0; i < MAXI; ++i) {
       half8_t v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = in_ok[i] ? rin[i][e] : _Float16(0);
+      for (int e = 0; e < 8; ++e) v[e] = in_ok[i] ? rin[i][e] : E(0);
       if (i < ni && in_live[i]) *reinterpret_cast<half8_t*>(base + in_lds[i]) = v;
     }
     if (w_live) {
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           v[e] = w_ok ? __builtin_bit_cast(half8_t, rw[(e * KHW + t) / 8])[(e * KHW + t) % 8]
-                      : _Float16(0);
+                      : E(0);
         const int pos = t * TN + w_co_l;
         *reinterpret_cast<half8_t*>(wb + (pos * OCT + swz<OCT>(pos, w_o)) * 16) = v;
       }
@@ -223,8 +227,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[i]), as_half8(bf), acc[i],
-                                                        0, 0, 0);
+        acc[i] = mfma_16x16x32<E>(af[i], bf, acc[i]);
     }
   };
 
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   const int tile_px = rows * a.wo;
   float* outt = reinterpret_cast<float*>(smem);  // [TNc][rows * wo]; the loop ended on a barrier
   float* bsm = reinterpret_cast<float*>(smem + 2 * HALO_BUF_BYTES) - 32;
-  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  const E* __restrict__ bias = static_cast<const E*>(a.bias);
   if (tid < TNc) bsm[tid] = (bias && co0 + tid < a.cog) ? (float)bias[g * a.cog + co0 + tid] : 0.f;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
@@ -264,8 +267,8 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
     }
   }
   __syncthreads();
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
+  const E* res = static_cast<const E*>(a.res);
+  E* y = static_cast<E*>(a.y);
   const int cvalid = min(TNc, a.cog - co0);
   const int total = cvalid * tile_px;
   const long long hw_out = (long long)a.ho * a.wo;
@@ -298,39 +301,44 @@ __global__ __launch_bounds__(256, 2) void halo_kernel(const HaloArgs a) {
   act_array(v, a.act, a.alpha, a.beta);
 #pragma unroll
   for (int k2 = 0; k2 < EPT; ++k2)
-    if (tid + 256 * k2 < total) y[oidx[k2]] = (_Float16)v[k2];
+    if (tid + 256 * k2 < total) y[oidx[k2]] = (E)v[k2];
 }
 
-template <int KH, int KW, int OCT>
+template <typename E, int KH, int KW, int OCT>
 static hipError_t launch_halo_o(const HaloArgs& a, hipStream_t s, dim3 grid) {
   const int rb = a.tr * a.tcb;
   const int per_wave = a.cb == 2 ? (rb + 1) / 2 : (rb + 3) / 4;
   if (per_wave <= 4)
-    hipLaunchKernelGGL((halo_kernel<KH, KW, OCT, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((halo_kernel<E, KH, KW, OCT, 4>), grid, dim3(256), 0, s, a);
   else if (per_wave == 7)
-    hipLaunchKernelGGL((halo_kernel<KH, KW, OCT, 7>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((halo_kernel<E, KH, KW, OCT, 7>), grid, dim3(256), 0, s, a);
   else if (per_wave <= 8)
-    hipLaunchKernelGGL((halo_kernel<KH, KW, OCT, 8>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((halo_kernel<E, KH, KW, OCT, 8>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template <int KH, int KW>
+template <typename E, int KH, int KW>
 static hipError_t launch_halo_k(const HaloArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n_rt * a.n * a.groups));
   switch (a.oct) {
-    case 4: return launch_halo_o<KH, KW, 4>(a, s, grid);
-    case 2: return launch_halo_o<KH, KW, 2>(a, s, grid);
-    case 1: return launch_halo_o<KH, KW, 1>(a, s, grid);
+    case 4: return launch_halo_o<E, KH, KW, 4>(a, s, grid);
+    case 2: return launch_halo_o<E, KH, KW, 2>(a, s, grid);
+    case 1: return launch_halo_o<E, KH, KW, 1>(a, s, grid);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_halo(const HaloArgs& a, hipStream_t s) {
-  if (a.kh == 3 && a.kw == 3) return launch_halo_k<3, 3>(a, s);
-  if (a.kh == 1 && a.kw == 1) return launch_halo_k<1, 1>(a, s);
+template <typename E>
+static hipError_t launch_halo_t(const HaloArgs& a, hipStream_t s) {
+  if (a.kh == 3 && a.kw == 3) return launch_halo_k<E, 3, 3>(a, s);
+  if (a.kh == 1 && a.kw == 1) return launch_halo_k<E, 1, 1>(a, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_halo(Dtype dt, const HaloArgs& a, hipStream_t s) {
+  return dt == BF16 ? launch_halo_t<__bf16>(a, s) : launch_halo_t<_Float16>(a, s);
 }
 
 }  // namespace convfwd

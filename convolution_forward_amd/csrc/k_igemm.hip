@@ -1,5 +1,5 @@
 // Generic implicit-GEMM convolution for gfx950 (any stride, dilation, pads,
-// groups, kernel size; f16 or f32 operands, f32 accumulation).
+// groups, kernel size; f16, bf16 or f32 operands, f32 accumulation).
 //
 // Per group g the layer is the product Y_g[p, co] = sum_k A[p, k] * B[k, co]
 // with p = (n, oh, ow) the output pixel, k = (ci', kh, kw) in the order of the
@@ -12,7 +12,8 @@
 // Each k-block (64 bytes of k: 32 halves or 16 floats) is gathered from global
 // memory straight into LDS rows, k contiguous, double-buffered through
 // registers.  Each wave multiplies a 32 x 32 sub-tile with MFMA:
-//   f16: v_mfma_f32_16x16x32_f16, one lane feeds 8 consecutive k of one row;
+//   f16 / bf16: v_mfma_f32_16x16x32_{f16,bf16}, one lane feeds 8 consecutive k
+//   of one row;
 //   f32: v_mfma_f32_16x16x4_f32, one lane feeds 4 consecutive k over 4 steps.
 // Lane l always feeds k-slot (l / 16) of row (l % 16) of both operands with the
 // same k values, so the product is exact regardless of the hardware's internal
@@ -29,6 +30,7 @@
 namespace convfwd {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -37,6 +39,11 @@ template <>
 struct IgVec<_Float16> {
   static constexpr int EPT = 8;
   typedef half8_t vec;
+};
+template <>
+struct IgVec<__bf16> {
+  static constexpr int EPT = 8;
+  typedef bf16x8_t vec;
 };
 template <>
 struct IgVec<float> {
@@ -54,6 +61,12 @@ template <>
 __device__ __forceinline__ void mfma_step<_Float16>(const half8_t& a, const half8_t& b,
                                                      floatx4_t& acc) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mfma_step<__bf16>(const bf16x8_t& a, const bf16x8_t& b,
+                                                   floatx4_t& acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
 template <>
@@ -275,6 +288,8 @@ hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s) {
             a.groups * a.splits);
   if (dt == F16)
     hipLaunchKernelGGL(igemm_kernel<_Float16>, grid, dim3(256), 0, s, a);
+  else if (dt == BF16)
+    hipLaunchKernelGGL(igemm_kernel<__bf16>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(igemm_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

@@ -40,6 +40,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "mfma16.h"
 
 namespace convfwd {
 
@@ -68,9 +69,13 @@ __device__ __forceinline__ int pw_slot(int p, int o) { return o ^ ((p >> 1) & 7)
 // straddles two tiles.
 // AK: the activation fixed at compile time (the ONNX code), or -1 for the
 // launch's code chosen at run time.
-template <int PW_TC, bool CT, int PF, bool VEC, int AK = -1>
+template <typename E, int PW_TC, bool CT, int PF, bool VEC, int AK = -1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF > 2 ? 2 : PW_TC == 128 || PF > 1 ? 3 : 4)))
 void pointwise_f16_kernel(const PwArgs a) {
+  typedef E half8_t __attribute__((ext_vector_type(8)));
+  typedef E half4_t __attribute__((ext_vector_type(4)));
+  typedef E half2_t __attribute__((ext_vector_type(2)));
+
   constexpr int PW_WBYTES = PW_TC * PW_WROW;
   constexpr int PW_NW = PW_TC * (PW_KC / 8) / 256;  // 16-byte weight vectors per thread
   static_assert(PW_TC * PW_OROW <= PW_XBYTES + PW_WBYTES, "output tile reuses the staging area");
@@ -85,11 +90,11 @@ void pointwise_f16_kernel(const PwArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hw = a.hw;
-  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x);
-  const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt);
-  const _Float16* bias = static_cast<const _Float16*>(a.bias);
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
+  const E* __restrict__ x = static_cast<const E*>(a.x);
+  const E* __restrict__ w = static_cast<const E*>(a.wt);
+  const E* bias = static_cast<const E*>(a.bias);
+  const E* res = static_cast<const E*>(a.res);
+  E* y = static_cast<E*>(a.y);
 
   // staging item of this thread: channel octet so, 4-pixel group sg of the tile
   const int so = tid >> 5, sg = tid & 31;
@@ -102,7 +107,7 @@ void pointwise_f16_kernel(const PwArgs a) {
   u32x2_t xr[PF][8];       // 8 channels x 4 pixels
   u32x4_t wr[PF][PW_NW];   // weight vectors
   u32x2_t wt[PF][KG];      // ConvTranspose weights: KG input channels x 4 GEMM rows
-  _Float16 br[PF];         // bias of tile row tid (tid < TC), converted when staged
+  E br[PF];         // bias of tile row tid (tid < TC), converted when staged
   float* bsm = reinterpret_cast<float*>(smem + PW_XBYTES + PW_WBYTES);
 
   // work item = tile * nchunks + chunk; tile = (image, pixel tile, row tile),
@@ -126,7 +131,7 @@ void pointwise_f16_kernel(const PwArgs a) {
     // x: channels c0 + 8 so + e, pixels p0 + 4 sg .. + 3 (clamped into the plane
     // and the channel range; out-of-range values are zeroed when staged)
     const int px = min(p0 + 4 * sg, hw - 4);
-    const _Float16* xb = x + ((long long)n * a.c_in) * hw + px;
+    const E* xb = x + ((long long)n * a.c_in) * hw + px;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ci = min(c0 + 8 * so + e, a.c_in - 1);
@@ -141,7 +146,7 @@ void pointwise_f16_kernel(const PwArgs a) {
     }
     {  // bias of tile row tid (any valid address without bias)
       const int m = min(co0 + (tid % PW_TC), a.c_out - 1);
-      const _Float16* bp = bias ? bias + (CT ? m / 4 : m) : x;
+      const E* bp = bias ? bias + (CT ? m / 4 : m) : x;
       br[S] = *bp;
     }
     if constexpr (CT) {
@@ -151,7 +156,7 @@ void pointwise_f16_kernel(const PwArgs a) {
 #pragma unroll
       for (int e = 0; e < KG; ++e) {
         const int ci = min(c0 + KG * kg + e, a.c_in - 1);
-        const _Float16* src = w + (long long)ci * a.c_out + m;
+        const E* src = w + (long long)ci * a.c_out + m;
         if constexpr (VEC) {
           wt[S][e] = *reinterpret_cast<const u32x2_t*>(src);
         } else {
@@ -168,7 +173,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const int q = tid + 256 * i;
         const int co = min(co0 + (q >> 3), a.c_out - 1);
         const int ci = min(c0 + 8 * (q & 7), a.c_in - 8);  // c_in % 8 == 0
-        const _Float16* src = w + (long long)co * a.c_in + ci;
+        const E* src = w + (long long)co * a.c_in + ci;
         if constexpr (VEC) {
           wr[S][i] = *reinterpret_cast<const u32x4_t*>(src);
         } else {
@@ -199,7 +204,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         half8_t v;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          v[e] = e < cvalid ? __builtin_bit_cast(half4_t, xr[S][e])[j] : (_Float16)0.0f;
+          v[e] = e < cvalid ? __builtin_bit_cast(half4_t, xr[S][e])[j] : (E)0.0f;
         const int p = 4 * sg + j;
         *reinterpret_cast<half8_t*>(xs + p * 128 + 16 * pw_slot(p, so)) = v;
       }
@@ -209,10 +214,10 @@ void pointwise_f16_kernel(const PwArgs a) {
       const int kvalid = a.c_in - (c0 + KG * kg);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        _Float16 v __attribute__((ext_vector_type(KG)));
+        E v __attribute__((ext_vector_type(KG)));
 #pragma unroll
         for (int e = 0; e < KG; ++e)
-          v[e] = e < kvalid ? __builtin_bit_cast(half4_t, wt[S][e])[j] : (_Float16)0.0f;
+          v[e] = e < kvalid ? __builtin_bit_cast(half4_t, wt[S][e])[j] : (E)0.0f;
         *reinterpret_cast<decltype(v)*>(ws + (4 * mq + j) * PW_WROW + 2 * KG * kg) = v;
       }
     } else {
@@ -252,7 +257,7 @@ void pointwise_f16_kernel(const PwArgs a) {
       for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
-          acc[pb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[pb], bf[cb], acc[pb][cb], 0, 0, 0);
+          acc[pb][cb] = mfma_16x16x32<E>(af[pb], bf[cb], acc[pb][cb]);
     }
   };
 
@@ -284,7 +289,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         for (int cb = 0; cb < 4; ++cb) {
           const int p = min(p0 + pl0 + 16 * pb, hw - 4);
           const int co = min(co0 + cl0 + 16 * cb, a.c_out - 1);
-          const _Float16* src = res + ((long long)n * a.c_out + co) * hw + p;
+          const E* src = res + ((long long)n * a.c_out + co) * hw + p;
           half4_t h;
           if constexpr (VEC) {
             h = __builtin_bit_cast(half4_t, *reinterpret_cast<const u32x2_t*>(src));
@@ -306,7 +311,7 @@ void pointwise_f16_kernel(const PwArgs a) {
       for (int cb = 0; cb < 4; ++cb) {
         half4_t h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[4 * cb + i];
+        for (int i = 0; i < 4; ++i) h[i] = (E)v[4 * cb + i];
         *reinterpret_cast<half4_t*>(smem + (cl0 + 16 * cb) * PW_OROW + 2 * (pl0 + 16 * pb)) = h;
       }
     }
@@ -342,7 +347,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const half4_t e0 = *reinterpret_cast<const half4_t*>(rp);
         const half4_t e1 = *reinterpret_cast<const half4_t*>(rp + PW_OROW);
         const half8_t hv = {e0[0], e1[0], e0[1], e1[1], e0[2], e1[2], e0[3], e1[3]};
-        _Float16* dst = y + (((long long)n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v;
+        E* dst = y + (((long long)n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v;
         if constexpr (VEC) {
           store_out(reinterpret_cast<half8_t*>(dst), hv);
         } else {
@@ -370,7 +375,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const int co = co0 + row;
         if (co < a.c_out && px < pvalid) {
           const half8_t h = *reinterpret_cast<const half8_t*>(smem + row * PW_OROW + 2 * px);
-          _Float16* dst = y + ((long long)n * a.c_out + co) * hw + p0 + px;
+          E* dst = y + ((long long)n * a.c_out + co) * hw + p0 + px;
           const int cnt = min(8, pvalid - px);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -426,37 +431,42 @@ void pointwise_f16_kernel(const PwArgs a) {
   group(std::false_type{}, k);  // cnt is a multiple of PF
 }
 
-template <int TC, bool CT, int PF, bool VEC, int AK = -1>
+template <typename E, int TC, bool CT, int PF, bool VEC, int AK = -1>
 static hipError_t launch_pw_t(const PwArgs& a, int cus, hipStream_t s) {
   // persistent: one workgroup per resident slot (an uneven last round measured
   // faster than fewer workgroups with equal shares)
   static std::atomic<int> per_cu{0};
   int r = per_cu.load(std::memory_order_relaxed);
   if (r == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<TC, CT, PF, VEC, AK>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, pointwise_f16_kernel<E, TC, CT, PF, VEC, AK>, 256, 0) !=
             hipSuccess || r < 1)
       r = 1;
     per_cu.store(r, std::memory_order_relaxed);
   }
   long long grid = std::min<long long>((long long)r * cus, a.ntiles);
   if (grid < a.ntiles) grid = std::max<long long>(8, grid & ~7LL);  // whole XCD rounds
-  hipLaunchKernelGGL((pointwise_f16_kernel<TC, CT, PF, VEC, AK>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((pointwise_f16_kernel<E, TC, CT, PF, VEC, AK>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int TC, bool CT, int PF>
+template <typename E, int TC, bool CT, int PF>
 static hipError_t launch_pw_v(const PwArgs& a, int cus, hipStream_t s) {
   // ReLU and identity, the common cases, with the activation fixed at compile time
-  if (a.vec && a.act == 1) return launch_pw_t<TC, CT, PF, true, 1>(a, cus, s);
-  if (a.vec && a.act == 0) return launch_pw_t<TC, CT, PF, true, 0>(a, cus, s);
-  return a.vec ? launch_pw_t<TC, CT, PF, true>(a, cus, s) : launch_pw_t<TC, CT, PF, false>(a, cus, s);
+  if (a.vec && a.act == 1) return launch_pw_t<E, TC, CT, PF, true, 1>(a, cus, s);
+  if (a.vec && a.act == 0) return launch_pw_t<E, TC, CT, PF, true, 0>(a, cus, s);
+  return a.vec ? launch_pw_t<E, TC, CT, PF, true>(a, cus, s) : launch_pw_t<E, TC, CT, PF, false>(a, cus, s);
 }
 
-hipError_t launch_pointwise(const PwArgs& a, int cus, hipStream_t s) {
+template <typename E>
+static hipError_t launch_pointwise_t(const PwArgs& a, int cus, hipStream_t s) {
   // One work item in flight: deeper prefetch (2 or 4 items, fewer resident
   // workgroups) measured slower on the 1x1 and ConvTranspose workload shapes.
-  if (a.ct) return a.tc == 64 ? launch_pw_v<64, true, 1>(a, cus, s) : launch_pw_v<128, true, 1>(a, cus, s);
-  return a.tc == 64 ? launch_pw_v<64, false, 1>(a, cus, s) : launch_pw_v<128, false, 1>(a, cus, s);
+  if (a.ct) return a.tc == 64 ? launch_pw_v<E, 64, true, 1>(a, cus, s) : launch_pw_v<E, 128, true, 1>(a, cus, s);
+  return a.tc == 64 ? launch_pw_v<E, 64, false, 1>(a, cus, s) : launch_pw_v<E, 128, false, 1>(a, cus, s);
+}
+
+hipError_t launch_pointwise(Dtype dt, const PwArgs& a, int cus, hipStream_t s) {
+  return dt == BF16 ? launch_pointwise_t<__bf16>(a, cus, s) : launch_pointwise_t<_Float16>(a, cus, s);
 }
 
 }  // namespace convfwd

@@ -29,6 +29,7 @@
 
 #include "epilogue.h"
 #include "internal.h"
+#include "mfma16.h"
 
 namespace convfwd {
 
@@ -50,14 +51,18 @@ constexpr int RB_FILLI = 1024;     // items of the first KH rows at most
 // NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; WV: waves (8: two
 // 32-channel blocks x four 32-pixel blocks; 4: one channel block); VEC: whole
 // 16-byte input and output vectors.
-template <int NST, int WV, bool VEC, int AK = -1>
+template <typename E, int NST, int WV, bool VEC, int AK = -1>
 __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
+  typedef E half8_t __attribute__((ext_vector_type(8)));
+  typedef E half4_t __attribute__((ext_vector_type(4)));
+  typedef E half2_t __attribute__((ext_vector_type(2)));
+
   constexpr int NT = 64 * WV;
   constexpr int RB_FILL = (RB_FILLI + NT - 1) / NT;  // items per thread for the first KH rows
   constexpr int RB_NSTV = 64 * 16 / NT;              // output vectors per thread and row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_rb[];
   // ring: [ci][slot][rp halves]; output tile [64][RB_OPITCH bytes]; bias [64]
-  _Float16* ring = reinterpret_cast<_Float16*>(smem_rb);
+  E* ring = reinterpret_cast<E*>(smem_rb);
   unsigned char* otile = smem_rb + a.ring_bytes;
   float* bsm = reinterpret_cast<float*>(otile + 64 * RB_OPITCH);
 
@@ -76,8 +81,8 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   const int r0 = band * a.band_rows;
   const int r1 = min(r0 + a.band_rows, a.ho);
 
-  const _Float16* __restrict__ x = static_cast<const _Float16*>(a.x) + (long long)n * a.c_in * a.h * a.w;
-  const _Float16* __restrict__ w = static_cast<const _Float16*>(a.wt);
+  const E* __restrict__ x = static_cast<const E*>(a.x) + (long long)n * a.c_in * a.h * a.w;
+  const E* __restrict__ w = static_cast<const E*>(a.wt);
   static_assert(64 * 2 * RB_MAXST * 8 <= 64 * 1024, "weights staging");
 
   // ---- wave roles: channel block cbw, pixel block pb0 of 32 ----
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   auto load_item = [&](int ir0, const Item& it) __attribute__((always_inline)) {
     const int v = it.v, ci = it.ci;
     const int ir = ir0 + it.r;
-    const _Float16* src = x + ((long long)ci * a.h + min(max(ir, 0), a.h - 1)) * a.w + 8 * v;
+    const E* src = x + ((long long)ci * a.h + min(max(ir, 0), a.h - 1)) * a.w + 8 * v;
     u32x4_t d;
     if constexpr (VEC) {  // w % 8 == 0, 16-byte aligned rows
       d = *reinterpret_cast<const u32x4_t*>(src);
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     if (it.live) {
       const int v = it.v, ci = it.ci;
       const int slot = (ir0 + it.r) & (RB_RING - 1);
-      _Float16* dst = ring + (ci * RB_RING + slot) * rp + a.pl + 8 * v;
+      E* dst = ring + (ci * RB_RING + slot) * rp + a.pl + 8 * v;
       const half8_t h = __builtin_bit_cast(half8_t, d);
       if constexpr (VEC) {  // w % 8 == 0: whole vectors (the ring column offset is odd-aligned)
 #pragma unroll
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   // when aligned (at most RB_WV per thread), element reads otherwise
   const int per_co = groups * a.kw;
   const int wtotal = min(64, a.c_out - co0) * per_co;  // halves
-  const _Float16* wsrc = w + (long long)co0 * per_co;
+  const E* wsrc = w + (long long)co0 * per_co;
   constexpr int RB_WV = (64 * 2 * RB_MAXST * 8 / 8 + NT - 1) / NT;
   u32x4_t wv[RB_WV];
   if (a.wvec) {  // uniform: w 16-byte aligned and the tile's run a whole number of vectors
@@ -178,9 +183,9 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   // without a bias the slot holds -0.0, whose addition is exact for every
   // value (a zero keeps its sign), so the epilogue adds it unconditionally
   const float bv_in = (a.bias && co0 + (tid & 63) < a.c_out)
-                          ? (float)static_cast<const _Float16*>(a.bias)[co0 + (tid & 63)] : -0.0f;
+                          ? (float)static_cast<const E*>(a.bias)[co0 + (tid & 63)] : -0.0f;
   {
-    _Float16* wl = ring;
+    E* wl = ring;
     if (a.wvec) {
 #pragma unroll
       for (int k = 0; k < RB_WV; ++k) {
@@ -254,8 +259,8 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   int pxo[CB];  // ring column offset of this lane's output column in each pixel block
 #pragma unroll
   for (int j = 0; j < CB; ++j) pxo[j] = 2 * min(32 * (pb0 + j) + (lane & 31), a.wo - 1);
-  const _Float16* __restrict__ res = static_cast<const _Float16*>(a.res);
-  _Float16* y = static_cast<_Float16*>(a.y);
+  const E* __restrict__ res = static_cast<const E*>(a.res);
+  E* y = static_cast<E*>(a.y);
   const long long ybase = ((long long)n * a.c_out + co0) * a.ho * a.wo;
 
   // one output row; J = (oh - r0) % 3 at compile time picks the prefetch registers
@@ -284,9 +289,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
         u32x4_t f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = src[e];
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, f),
-                                                        __builtin_bit_cast(half8_t, wf[st]),
-                                                        acc[j], 0, 0, 0);
+        acc[j] = mfma_32x32x16<E>(f, wf[st], acc[j]);
       }
     }
 
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
       for (int q = 0; q < 4; ++q) {
         half4_t h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = (_Float16)v[4 * q + i];
+        for (int i = 0; i < 4; ++i) h[i] = (E)v[4 * q + i];
         *reinterpret_cast<half4_t*>(otile + c * RB_OPITCH + 2 * (pxb + 8 * q + 4 * half)) = h;
       }
     }
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
         const int c = (int)mdiv((unsigned)q, a.mg_vpr), v = q - c * vpr;
         const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4_t*>(
                                                           otile + c * RB_OPITCH + 16 * v));
-        _Float16* dst = y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v;
+        E* dst = y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v;
         const int cnt = min(8, a.wo - 8 * v);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -354,30 +357,35 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   }
 }
 
-template <int NST>
+template <typename E, int NST>
 static void launch_rb_nst(const RowbandArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const bool two = a.c_out > 32;
   if (a.vec && a.act == 1) {  // ReLU, the common case, fixed at compile time
-    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, true, 1>), grid, dim3(512), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<NST, 4, true, 1>), grid, dim3(256), lds, s, a);
+    if (two) hipLaunchKernelGGL((rowband_kernel<E, NST, 8, true, 1>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<E, NST, 4, true, 1>), grid, dim3(256), lds, s, a);
   } else if (a.vec) {
-    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, true>), grid, dim3(512), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<NST, 4, true>), grid, dim3(256), lds, s, a);
+    if (two) hipLaunchKernelGGL((rowband_kernel<E, NST, 8, true>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<E, NST, 4, true>), grid, dim3(256), lds, s, a);
   } else {
-    if (two) hipLaunchKernelGGL((rowband_kernel<NST, 8, false>), grid, dim3(512), lds, s, a);
-    else hipLaunchKernelGGL((rowband_kernel<NST, 4, false>), grid, dim3(256), lds, s, a);
+    if (two) hipLaunchKernelGGL((rowband_kernel<E, NST, 8, false>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<E, NST, 4, false>), grid, dim3(256), lds, s, a);
   }
 }
 
-hipError_t launch_rowband(const RowbandArgs& a, hipStream_t s) {
+hipError_t launch_rowband(Dtype dt, const RowbandArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n * a.n_ct * a.n_band));
   const size_t lds = (size_t)a.ring_bytes + 64 * RB_OPITCH + 64 * 4;
   // k-steps: exact for the 3-channel 7x7 stem, else the maximum (padded steps
   // multiply zero weights)
   const int nst = (a.c_in * a.kh + 1) / 2;
   if (nst > RB_MAXST) return hipErrorInvalidValue;
-  if (nst == 11) launch_rb_nst<11>(a, grid, lds, s);
-  else launch_rb_nst<RB_MAXST>(a, grid, lds, s);
+  if (dt == BF16) {
+    if (nst == 11) launch_rb_nst<__bf16, 11>(a, grid, lds, s);
+    else launch_rb_nst<__bf16, RB_MAXST>(a, grid, lds, s);
+  } else {
+    if (nst == 11) launch_rb_nst<_Float16, 11>(a, grid, lds, s);
+    else launch_rb_nst<_Float16, RB_MAXST>(a, grid, lds, s);
+  }
   return hipGetLastError();
 }
 

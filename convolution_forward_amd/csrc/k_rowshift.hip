@@ -100,15 +100,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, in
                                            (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// v_mfma_f32_32x32x16_f16 or _bf16: the operands are the same 16 bytes.
+template <typename E>
 __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  typedef E e8 __attribute__((ext_vector_type(8)));
+  if constexpr (std::is_same_v<E, __bf16>)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(e8, a),
+                                                   __builtin_bit_cast(e8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8, a),
+                                                  __builtin_bit_cast(e8, b), c, 0, 0, 0);
 }
 
 }  // namespace
 
-template <int R, bool XV, bool WV, int AK = -1>
+template <typename E, int R, bool XV, bool WV, int AK = -1>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
+  typedef E half8_t __attribute__((ext_vector_type(8)));
+  typedef E half4_t __attribute__((ext_vector_type(4)));
+  typedef E half2_t __attribute__((ext_vector_type(2)));
+
   typedef RsLayout<R> L;
   constexpr int NP = L::NP;
   // the epilogue's partial sums (4 waves x NP row pairs x 16 floats x 64 lanes)
@@ -132,10 +143,10 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int co0 = ct * 32;
   const int hw = a.h * a.w;
 
-  const _Float16* __restrict__ ximg =
-      static_cast<const _Float16*>(a.x) + ((long long)n * a.c_in + (long long)g * a.cig) * hw;
-  const _Float16* __restrict__ wg =
-      static_cast<const _Float16*>(a.wt) + (long long)g * a.cog * a.cig * 9;
+  const E* __restrict__ ximg =
+      static_cast<const E*>(a.x) + ((long long)n * a.c_in + (long long)g * a.cig) * hw;
+  const E* __restrict__ wg =
+      static_cast<const E*>(a.wt) + (long long)g * a.cog * a.cig * 9;
 
   // ---- each wave stages only its own 16 channels of every stage (octets
   // 2 wave, 2 wave + 1) and its own 16-channel slice of the weights, which are
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     } else {  // input not 8-byte aligned or planes not a multiple of 4: element loads
 #pragma unroll
       for (int i = i0; i < i1; ++i) {
-        const _Float16* src = ximg + xoff + in_off[i];
+        const E* src = ximg + xoff + in_off[i];
         const int left = hw - 1 - (in_off[i] % hw);  // last valid pixel of this group
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
           const u32x4_t f = kw == 0 ? fr[q] : kw == 1 ? row_shift<1>(fr[q]) : row_shift<2>(fr[q]);
-          acc[q] = mfma32(f, bf[kh * 3 + kw], acc[q]);
+          acc[q] = mfma32<E>(f, bf[kh * 3 + kw], acc[q]);
         }
       // the loads go out between the multiplications: a load whose issue
       // stalls (memory pipeline full) then leaves the matrix unit busy
@@ -347,8 +358,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   constexpr int KI = R / 2;  // 32 x R x 4 items over 256 threads
   const int howo = a.ho * a.wo;
   const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
-  const _Float16* res = static_cast<const _Float16*>(a.res);
-  const _Float16* __restrict__ bias = static_cast<const _Float16*>(a.bias);
+  const E* res = static_cast<const E*>(a.res);
+  const E* __restrict__ bias = static_cast<const E*>(a.bias);
   float* bsm = reinterpret_cast<float*>(smem + L::BIAS);  // the tile's 32 biases
   const bool pairs = a.o2;  // y / residual 4-byte aligned, wo even (uniform)
   auto it_co = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) / R; };
@@ -419,7 +430,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef std::integral_constant<int, 2> LAST;
   // the tile's biases, loaded first (any valid address without bias) and kept
   // in LDS for the epilogue
-  const _Float16 b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
+  const E b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
   // only stage 0 is loaded before the first multiplications: stages 1 and 2
   // are issued with stage 0's multiplications, so that the multiplications
   // start as soon as the first stage has arrived
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           *reinterpret_cast<floatx2_t*>(dst) = floatx2_t{acc[q][4 * i4 + 2 * j2], acc[q][4 * i4 + 2 * j2 + 1]};
         }
     __syncthreads();
-    _Float16* yt = static_cast<_Float16*>(a.y) + obase;
+    E* yt = static_cast<E*>(a.y) + obase;
     const float rhowo = 1.0f / (float)howo;
 #pragma unroll
     for (int k = 0; k < KV; ++k) {
@@ -527,7 +538,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
       act_apply<AK>(v, a.act, a.alpha, a.beta);
       half8_t h;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) h[j] = (_Float16)v[j];
+      for (int j = 0; j < 8; ++j) h[j] = (E)v[j];
       *reinterpret_cast<half8_t*>(yt + e0) = h;
     }
     return;
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           floatx4_t{acc[q][4 * i4], acc[q][4 * i4 + 1], acc[q][4 * i4 + 2], acc[q][4 * i4 + 3]};
   __syncthreads();
 
-  _Float16* y = static_cast<_Float16*>(a.y);
+  E* y = static_cast<E*>(a.y);
   float v[KI * 4];
 #pragma unroll
   for (int k = 0; k < KI; ++k) {
@@ -602,27 +613,28 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2)
         if (e_valid(k, 2 * j2)) {  // wo even: both of the pair exist
-          const half2_t h = {(_Float16)v[4 * k + 2 * j2], (_Float16)v[4 * k + 2 * j2 + 1]};
+          const half2_t h = {(E)v[4 * k + 2 * j2], (E)v[4 * k + 2 * j2 + 1]};
           *reinterpret_cast<half2_t*>(y + obase + e_index(k, 2 * j2)) = h;
         }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (e_valid(k, j)) y[obase + e_index(k, j)] = (_Float16)v[4 * k + j];
+        if (e_valid(k, j)) y[obase + e_index(k, j)] = (E)v[4 * k + j];
     }
   }
 }
 
-hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s) {
+template <typename E>
+static hipError_t launch_rowshift_t(const HaloArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups));
 #define RS_LAUNCH(R_)                                                                        \
   {                                                                                          \
     if (a.xvec && a.wvec && a.act == 1) /* ReLU fixed at compile time */                   \
-      hipLaunchKernelGGL((rowshift_kernel<R_, true, true, 1>), grid, dim3(256), 0, s, a);     \
-    else if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, true>), grid, dim3(256), 0, s, a); \
-    else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<R_, true, false>), grid, dim3(256), 0, s, a); \
-    else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<R_, false, true>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((rowshift_kernel<R_, false, false>), grid, dim3(256), 0, s, a);           \
+      hipLaunchKernelGGL((rowshift_kernel<E, R_, true, true, 1>), grid, dim3(256), 0, s, a);     \
+    else if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, true, true>), grid, dim3(256), 0, s, a); \
+    else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, true, false>), grid, dim3(256), 0, s, a); \
+    else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, false, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((rowshift_kernel<E, R_, false, false>), grid, dim3(256), 0, s, a);           \
   }
   if (a.ho <= 8)
     RS_LAUNCH(8)
@@ -632,6 +644,10 @@ hipError_t launch_rowshift(const HaloArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 #undef RS_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_rowshift(Dtype dt, const HaloArgs& a, hipStream_t s) {
+  return dt == BF16 ? launch_rowshift_t<__bf16>(a, s) : launch_rowshift_t<_Float16>(a, s);
 }
 
 }  // namespace convfwd

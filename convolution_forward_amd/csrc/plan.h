@@ -73,4 +73,8 @@ int check_call(const conv_problem* p, int dtype, bool transpose, const void* x, 
 // Bytes per element of a conv_dtype.
 inline int64_t dtype_size(int dtype) { return dtype == CONV_F32 ? 4 : 2; }
 
+// A 16-bit floating operand type (float16 or bfloat16): the matrix kernels
+// that move 16-bit elements serve both, with the MFMA of that type.
+inline bool half16(int dtype) { return dtype == CONV_F16 || dtype == CONV_BF16; }
+
 }  // namespace convfwd

@@ -27,8 +27,8 @@
  *   bias     [c_out]                    (optional)
  *   residual same shape as y            (optional; may alias y exactly)
  *   y        NCHW  [n, c_out, Ho, Wo]
- * Element types: CONV_F32 (float32 everywhere) or CONV_F16 (float16 operands and
- * output, float32 accumulation).  Every operand pointer is a base device pointer;
+ * Element types: CONV_F32 (float32 everywhere), CONV_F16 or CONV_BF16 (16-bit
+ * operands and output, float32 accumulation).  Every operand pointer is a base device pointer;
  * the element offsets in conv_problem are added to it (arena-style placement).
  *
  * Ownership and execution: device buffers belong to the caller.  conv_forward and
@@ -66,8 +66,12 @@ enum {
     CONV_ERR_DEVICE = 5   /* the HIP runtime refused a launch */
 };
 
-/* Element type of x, w, bias, residual and y. */
-typedef enum { CONV_F32 = 0, CONV_F16 = 1 } conv_dtype;
+/* Element type of x, w, bias, residual and y ("Convolution, pooling and resize",
+ * "Layout and operands": float, and half in and out with float32 accumulation).
+ * CONV_BF16 is bfloat16 in and out with float32 accumulation, the same kernels
+ * as float16 with the bfloat16 MFMA instructions (no page fixes a bfloat16
+ * tolerance; the library's tests hold it to 1.6e-2 * sum|w*x|). */
+typedef enum { CONV_F32 = 0, CONV_F16 = 1, CONV_BF16 = 2 } conv_dtype;
 
 /* Fused activations (the list of "Layout and operands"), ONNX definitions:
  * relu max(0,v); tanh; sigmoid 1/(1+e^-v); silu v*sigmoid(v);

@@ -19,10 +19,28 @@ import torch
 
 import convolution_forward_amd as cf
 import oracle
+import workloads
 
-TOL = {"f32": 1e-5, "f16": 2e-3}
-NP = {"f32": np.float32, "f16": np.float16}
-TORCH = {"f32": torch.float32, "f16": torch.float16}
+# bfloat16 (no page fixes its tolerance): fp16's 2e-3 is 4 units of fp16
+# roundoff (2^-11); the same 4 units of bfloat16 roundoff (2^-8) give 1.6e-2.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2}
+NP = {"f32": np.float32, "f16": np.float16, "bf16": np.int16}  # device storage
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_storage(a, dtype):
+    """Host array of operand values -> the array whose bytes the device gets
+    (bfloat16: the 16-bit patterns of bfloat16-exact values)."""
+    if dtype == "bf16":
+        return workloads.bf16_bits(a).view(np.int16)
+    return np.asarray(a).astype(NP[dtype])
+
+
+def from_storage(a, dtype):
+    """Device bytes back to operand values (bfloat16 -> exact float32)."""
+    if dtype == "bf16":
+        return workloads.bf16_from_bits(np.asarray(a).view(np.uint16))
+    return a
 
 
 def dev(a):
@@ -67,11 +85,11 @@ def run_gpu(geom, dtype, x, w, b=None, r=None, transpose=False, variant="auto", 
     ho, wo = cf.conv_output_extent(p)
     yshape = (geom.n, geom.c_out, ho, wo)
 
-    def place(a, off):
+    def place(a, off, raw=False):
         if a is None:
             return None
         flat = np.zeros(off + a.size, npdt)
-        flat[off:] = a.astype(npdt).ravel()
+        flat[off:] = (a if raw else to_storage(a, dtype)).ravel()
         return dev(flat)
 
     xd, wd, bd = place(x, offs[0]), place(w, offs[1]), place(b, offs[2])
@@ -82,8 +100,13 @@ def run_gpu(geom, dtype, x, w, b=None, r=None, transpose=False, variant="auto", 
         rd = yd
     else:
         rd = place(r, offs[3])
-        init = np.full(ysize, np.nan, npdt) if y_init is None else y_init.astype(npdt).ravel()
-        yd = place(init, offs[4])
+        if y_init is not None:
+            init = to_storage(y_init, dtype).ravel()
+        elif dtype == "bf16":
+            init = np.full(ysize, 0x7FC0, np.int16)  # quiet NaN
+        else:
+            init = np.full(ysize, np.nan, npdt)
+        yd = place(init, offs[4], raw=True)
     whole, per = cf.conv_scratch_size(p, dtype)
     sbytes = whole if scratch_images is None else per * scratch_images
     scratch = torch.empty(max(sbytes, 16) // 4 + 4, dtype=torch.float32, device="cuda") \
@@ -92,7 +115,7 @@ def run_gpu(geom, dtype, x, w, b=None, r=None, transpose=False, variant="auto", 
     fn(p, dtype, xd, wd, bd, rd, yd, scratch, sbytes if scratch is not None else 0, stream())
     torch.cuda.synchronize()
     out = yd.cpu().numpy()[offs[4]:].reshape(yshape)
-    return out
+    return from_storage(out, dtype)
 
 
 def oracle_ref(geom, x, w, b=None, r=None, transpose=False):
@@ -112,8 +135,12 @@ def bound(dtype, y_ref, s_ref, b=None, r=None, c_axis=1, act="identity"):
         sp = sp + np.abs(np.asarray(b, np.float64)).reshape(shp)
     if r is not None:
         sp = sp + np.abs(np.asarray(r, np.float64))
-    mag = np.abs(y_ref).astype(NP[dtype])
-    half_ulp = np.spacing(mag).astype(np.float64) / 2
+    if dtype == "bf16":  # half an ulp of bfloat16 (8 significant bits) at |y|
+        _, e = np.frexp(np.abs(np.asarray(y_ref, np.float64)))
+        half_ulp = np.ldexp(1.0, e - 9)
+    else:
+        mag = np.abs(y_ref).astype(NP[dtype])
+        half_ulp = np.spacing(mag).astype(np.float64) / 2
     if act in TRANSCENDENTAL:
         half_ulp = half_ulp + 4 * np.spacing(np.abs(y_ref).astype(np.float32)).astype(np.float64)
     return TOL[dtype] * sp + half_ulp

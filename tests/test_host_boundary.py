@@ -168,7 +168,8 @@ def test_validation_errors(mut, status):
 
 def test_bad_enums_and_pointers():
     p = _good()
-    assert _fwd(p, dtype=2) == cf.CONV_ERR_ARG
+    assert _fwd(p, dtype=3) == cf.CONV_ERR_ARG
+    assert _fwd(p, dtype=-1) == cf.CONV_ERR_ARG
     p.activation = 9
     assert _fwd(p) == cf.CONV_ERR_ARG
     p = _good()
@@ -332,3 +333,45 @@ def test_status_strings():
     for s in range(6):
         assert cf.status_string(s) and cf.status_string(s) != "unknown status"
     assert cf.status_string(42) == "unknown status"
+
+
+def test_bf16_plans_mirror_f16():
+    """bfloat16 takes every kernel float16 takes (same 16-bit data movement,
+    the bfloat16 MFMA): the plan names differ only in the type."""
+    for l in workloads.LAYERS + workloads.EXTRA_LAYERS:
+        if l.dtype != "f16":
+            continue
+        q = cf.make_problem(l.n, l.c_in, l.h, l.w, l.c_out, l.kh, l.kw, groups=l.groups,
+                            stride=l.stride, dilation=l.dilation, pads=l.pads,
+                            transpose=l.transpose, residual=l.residual)
+        a = cf.conv_describe_variant(q, "f16")
+        b = cf.conv_describe_variant(q, "bf16")
+        assert b == a.replace(".f16", ".bf16"), (a, b)
+        assert cf.conv_scratch_size(q, "f16") == cf.conv_scratch_size(q, "bf16")
+    p = cf.make_problem(1, 3, 8, 8, 4, 3, 3)
+    with pytest.raises(cf.ConvError):
+        cf.conv_describe_variant(p, 3)
+
+
+def test_bf16_input_rounding_is_nearest_even_once():
+    """The inputs' bfloat16 rounding (float64 -> 8 significant bits, ties to
+    even, no double rounding through float32) against a brute-force nearest
+    search over the two bfloat16 neighbours."""
+    rng = np.random.default_rng(3)
+    a = np.concatenate([rng.standard_normal(20000) * 4, rng.uniform(-1, 1, 20000)])
+    # exact ties and near-ties: midpoints of adjacent bfloat16 values, and the
+    # float32 neighbours of a midpoint
+    lo = workloads.bf16_round(rng.uniform(0.5, 2, 2000)).astype(np.float64)
+    step = np.ldexp(1.0, np.frexp(lo)[1] - 8)
+    mid = lo + step / 2
+    a = np.concatenate([a, mid, np.nextafter(mid, 0), np.nextafter(mid, 10)])
+    r = workloads.bf16_round(a).astype(np.float64)
+    m, e = np.frexp(a)
+    down = np.ldexp(np.floor(np.ldexp(m, 8)), e - 8)
+    up = np.ldexp(np.floor(np.ldexp(m, 8)) + 1, e - 8)
+    dd, du = np.abs(a - down), np.abs(up - a)
+    even_down = (np.floor(np.ldexp(m, 8)) % 2) == 0
+    want = np.where(dd < du, down, np.where(du < dd, up, np.where(even_down, down, up)))
+    assert np.array_equal(r, want)
+    bits = workloads.bf16_bits(r)
+    assert np.array_equal(workloads.bf16_from_bits(bits).astype(np.float64), r)

@@ -38,7 +38,7 @@ class Layer:
     name: str
     workload: int
     index: int
-    dtype: str  # "f32" or "f16"
+    dtype: str  # "f32", "f16" or "bf16"
     n: int
     c_in: int
     h: int
@@ -62,6 +62,8 @@ class Layer:
 
     @property
     def np_dtype(self):
+        """numpy type holding the operand values (bfloat16 values are held
+        exactly in float32; numpy has no bfloat16 type)."""
         return np.float16 if self.dtype == "f16" else np.float32
 
     @property
@@ -106,6 +108,9 @@ LAYERS = [
 EXTRA_LAYERS = [
     Layer("x1_late3x3_512_7x7_f16", 6, 0, "f16", 1, 512, 7, 7, 512, 3, 3, (1, 512, 7, 7),
           pads=(1, 1, 1, 1), act="relu"),
+    # the bottleneck layer of workload 2 with bfloat16 operands
+    Layer("x2_bottleneck3x3_bf16", 7, 0, "bf16", 32, 256, 14, 14, 256, 3, 3,
+          (32, 256, 14, 14), pads=(1, 1, 1, 1), act="relu", residual=True),
 ]
 
 BY_NAME = {l.name: l for l in LAYERS + EXTRA_LAYERS}
@@ -133,19 +138,48 @@ class Inputs:
     extra: dict = field(default_factory=dict)
 
 
+def bf16_round(a) -> np.ndarray:
+    """Round float64 values once, to nearest with ties to even, to bfloat16
+    (8 significant bits), returned exactly as float32.  Done from float64
+    directly (frexp / rint / ldexp are exact), not through float32, so there is
+    no double rounding.  Finite values in the normal range only."""
+    m, e = np.frexp(np.asarray(a, np.float64))
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8).astype(np.float32)
+
+
+def bf16_bits(a) -> np.ndarray:
+    """The 16-bit patterns of bfloat16-exact float32 values (the upper halves)."""
+    f = np.ascontiguousarray(a, np.float32)
+    bits = f.view(np.uint32)
+    assert not np.any(bits & 0xFFFF), "value not exact in bfloat16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def bf16_from_bits(bits) -> np.ndarray:
+    """float32 values of bfloat16 bit patterns."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize(a, dtype: str) -> np.ndarray:
+    """Round float64 values once to the operand type ("f32", "f16", "bf16")."""
+    if dtype == "bf16":
+        return bf16_round(a)
+    return np.asarray(a, np.float64).astype(np.float16 if dtype == "f16" else np.float32)
+
+
 def make_inputs(layer: Layer, seeds: tuple | None = None) -> Inputs:
     """The layer's seeded inputs, drawn in float64 and rounded once to its dtype.
 
     Draws fill arrays in C order, so a smaller batch is a prefix of the full
     batch's x and residual."""
-    dt = layer.np_dtype
+    q = lambda a: quantize(a, layer.dtype)
     s = seeds or tuple(seed(layer, t) for t in range(4))
-    x = np.random.default_rng(s[0]).uniform(-1.0, 1.0, layer.x_shape).astype(dt)
+    x = q(np.random.default_rng(s[0]).uniform(-1.0, 1.0, layer.x_shape))
     std = math.sqrt(2.0 / fan_in(layer))
-    w = (np.random.default_rng(s[1]).standard_normal(layer.w_shape) * std).astype(dt)
-    b = (np.random.default_rng(s[2]).uniform(-0.1, 0.1, (layer.c_out,)).astype(dt)
+    w = q(np.random.default_rng(s[1]).standard_normal(layer.w_shape) * std)
+    b = (q(np.random.default_rng(s[2]).uniform(-0.1, 0.1, (layer.c_out,)))
          if layer.bias else None)
-    r = (np.random.default_rng(s[3]).uniform(-1.0, 1.0, layer.out_shape).astype(dt)
+    r = (q(np.random.default_rng(s[3]).uniform(-1.0, 1.0, layer.out_shape))
          if layer.residual else None)
     return Inputs(x, w, b, r)
 
