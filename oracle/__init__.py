@@ -63,6 +63,13 @@ class _Geom(ctypes.Structure):
         ("alpha", ctypes.c_double), ("beta", ctypes.c_double)]
 
 
+class _PoolGeom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n", "c", "h", "w", "kh", "kw", "sh", "sw", "dh", "dw", "pt", "pl", "pb", "pr")] + [
+        ("kind", ctypes.c_int32), ("ceil_mode", ctypes.c_int32),
+        ("count_include_pad", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -86,6 +93,9 @@ def _load():
         lib.oracle_conv2d_im2col.argtypes = [g, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.oracle_conv_transpose2d.argtypes = [g, dp, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.oracle_conv_transpose2d_gather.argtypes = [g, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.oracle_pool_extent.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, i64p]
+        lib.oracle_pool2d.argtypes = [ctypes.POINTER(_PoolGeom), dp, ctypes.c_double, dp, dp]
+        lib.oracle_global_pool.argtypes = [ctypes.c_int, i64, i64, dp, dp, dp]
         _lib = lib
     return _lib
 
@@ -267,3 +277,85 @@ def conv_transpose2d_gather(g: Geom, x, w, b=None, r=None, threads=0):
 
 def max_threads() -> int:
     return _load().oracle_max_threads()
+
+
+# ------------------------------------------------------------------ pooling
+
+# Lowest finite value of each element type (an empty max window's result,
+# "Convolution, pooling and resize", "Pooling and resize").
+LOWEST = {"f32": -3.4028234663852886e38, "f16": -65504.0, "bf16": -3.3895313892515355e38}
+
+
+@dataclass
+class PoolGeom:
+    """A pooling problem: window, stride, dilation, explicit pads, ceil mode,
+    count_include_pad; kind "max" or "average"."""
+
+    n: int
+    c: int
+    h: int
+    w: int
+    kh: int = 1
+    kw: int = 1
+    sh: int = 1
+    sw: int = 1
+    dh: int = 1
+    dw: int = 1
+    pt: int = 0
+    pl: int = 0
+    pb: int = 0
+    pr: int = 0
+    kind: str = "max"
+    ceil_mode: bool = False
+    count_include_pad: bool = False
+
+    def _c(self) -> _PoolGeom:
+        return _PoolGeom(self.n, self.c, self.h, self.w, self.kh, self.kw, self.sh, self.sw,
+                         self.dh, self.dw, self.pt, self.pl, self.pb, self.pr,
+                         {"max": 0, "average": 1}[self.kind], int(self.ceil_mode),
+                         int(self.count_include_pad), 0)
+
+
+def pool_extent(n_in, k, s, d, pad_begin, pad_end, ceil_mode):
+    """Pooling output size along one axis (floor or ceil mode); None if no window fits."""
+    out = ctypes.c_int64(0)
+    rc = _load().oracle_pool_extent(n_in, k, s, d, pad_begin, pad_end, int(ceil_mode),
+                                    ctypes.byref(out))
+    return None if rc else out.value
+
+
+def pool_out_shape(g: PoolGeom):
+    ho = pool_extent(g.h, g.kh, g.sh, g.dh, g.pt, g.pb, g.ceil_mode)
+    wo = pool_extent(g.w, g.kw, g.sw, g.dw, g.pl, g.pr, g.ceil_mode)
+    if ho is None or wo is None:
+        raise ValueError("no pooling window fits")
+    return (g.n, g.c, ho, wo)
+
+
+def pool2d(g: PoolGeom, x, dtype="f32"):
+    """MaxPool / AveragePool by their definitions in fp64 ("Pooling and resize":
+    NaN, empty-window, ceil_mode and count_include_pad rules).  Returns
+    (y, scale) with scale = sum|x| / divisor for the average (zeros for max)."""
+    x = _f64(x)
+    assert x.shape == (g.n, g.c, g.h, g.w), x.shape
+    shp = pool_out_shape(g)
+    y = np.empty(shp, np.float64)
+    s = np.empty(shp, np.float64)
+    rc = _load().oracle_pool2d(ctypes.byref(g._c()), _p(x), LOWEST[dtype], _p(y), _p(s))
+    if rc:
+        raise ValueError("oracle_pool2d rejected the problem")
+    return y, s
+
+
+def global_pool(kind, x):
+    """GlobalMaxPool / GlobalAveragePool over each (n, c) plane of x [n, c, h, w].
+    Returns (y [n, c, 1, 1], scale) with scale the mean |x| (zeros for max)."""
+    x = _f64(x)
+    n, c, h, w = x.shape
+    y = np.empty((n, c, 1, 1), np.float64)
+    s = np.empty((n, c, 1, 1), np.float64)
+    rc = _load().oracle_global_pool({"max": 0, "average": 1}[kind], n * c, h * w, _p(x),
+                                    _p(y), _p(s))
+    if rc:
+        raise ValueError("oracle_global_pool rejected the problem")
+    return y, s

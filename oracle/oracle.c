@@ -22,8 +22,11 @@
  *  - "Convolution, pooling and resize" (OneGpu docs), section "Layout and
  *    operands" (NCHW / OIHW, ConvTranspose weight [Cin, Cout/groups, KH, KW],
  *    explicit pads, dilation, groups, fused epilogue order: sum, bias,
- *    residual, activation; the nine fused activations) and section
- *    "ConvInteger" (asymmetric padding is part of the problem geometry).
+ *    residual, activation; the nine fused activations), section
+ *    "ConvInteger" (asymmetric padding is part of the problem geometry) and
+ *    section "Pooling and resize" (MaxPool / AveragePool with padding,
+ *    dilation, ceil_mode and count_include_pad; the NaN and empty-window
+ *    rules; global pools over a plane).
  *
  * Readings where the pages are silent:
  *  - padding is zero padding (ONNX Conv semantics), begin and end pads are
@@ -459,4 +462,128 @@ int oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ---------------------------------------------------------------------- */
+/* Pooling ("Convolution, pooling and resize", section "Pooling and        */
+/* resize"; ONNX MaxPool / AveragePool / GlobalMaxPool /                   */
+/* GlobalAveragePool)                                                      */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    int64_t n, c, h, w, kh, kw, sh, sw, dh, dw, pt, pl, pb, pr;
+    int32_t kind;              /* 0 max, 1 average */
+    int32_t ceil_mode;         /* 1: the output size rounds up */
+    int32_t count_include_pad; /* average: padding taps count in the divisor */
+    int32_t pad_;
+} oracle_pool_geom;
+
+/* Output size along one axis.  Floor mode is the convolution's equation.
+ * Ceil mode rounds the division up, and then drops a last window that starts
+ * inside the end padding (its first tap at or beyond the input's end).
+ * Returns 0 and writes *out, or -1 when no window fits. */
+int oracle_pool_extent(int64_t in, int64_t k, int64_t s, int64_t d, int64_t pb,
+                       int64_t pe, int ceil_mode, int64_t* out)
+{
+    if (in < 1 || k < 1 || s < 1 || d < 1 || pb < 0 || pe < 0) return -1;
+    int64_t span = in + pb + pe - d * (k - 1) - 1;
+    if (span < 0) return -1;
+    int64_t o = ceil_mode ? (span + s - 1) / s + 1 : span / s + 1;
+    if (ceil_mode && (o - 1) * s - pb >= in) o -= 1;
+    if (o < 1) return -1;
+    *out = o;
+    return 0;
+}
+
+/* Windowed pooling over each (n, c) plane.  The window of output (oh, ow)
+ * holds the taps ih = oh*sh - pt + kh*dh, iw = ow*sw - pl + kw*dw.  A tap is
+ * real when it lies inside the input, padding when it lies inside the pads,
+ * and beyond the padding otherwise (only in ceil mode).
+ *  - max: the largest real tap.  NaN taps are skipped unless every real tap is
+ *    NaN (then NaN); +0 counts as larger than -0; a window with no real tap
+ *    gives `lowest` (the lowest finite value of the element type).
+ *  - average: the sum of the real taps over the divisor, which counts the
+ *    real taps, plus the padding taps when count_include_pad is set (taps
+ *    beyond the padding never count); 0/0 is NaN.  scale (may be NULL)
+ *    receives sum |x| over the same divisor, the magnitude the tolerance
+ *    scales with.
+ * y is [n, c, ho, wo]. */
+int oracle_pool2d(const oracle_pool_geom* g, const double* x, double lowest, double* y,
+                  double* scale)
+{
+    int64_t ho, wo;
+    if (g->n < 1 || g->c < 1) return -1;
+    if (oracle_pool_extent(g->h, g->kh, g->sh, g->dh, g->pt, g->pb, g->ceil_mode, &ho) ||
+        oracle_pool_extent(g->w, g->kw, g->sw, g->dw, g->pl, g->pr, g->ceil_mode, &wo))
+        return -1;
+    if (g->kind != 0 && g->kind != 1) return -1;
+    for (int64_t p = 0; p < g->n * g->c; ++p) {
+        const double* xp = x + p * g->h * g->w;
+        for (int64_t oh = 0; oh < ho; ++oh)
+            for (int64_t ow = 0; ow < wo; ++ow) {
+                double best = 0.0, sum = 0.0, mag = 0.0;
+                int64_t real = 0, counted = 0, finite_seen = 0, nan_seen = 0;
+                for (int64_t kh = 0; kh < g->kh; ++kh)
+                    for (int64_t kw = 0; kw < g->kw; ++kw) {
+                        int64_t ih = oh * g->sh - g->pt + kh * g->dh;
+                        int64_t iw = ow * g->sw - g->pl + kw * g->dw;
+                        int in_h = ih >= 0 && ih < g->h, in_w = iw >= 0 && iw < g->w;
+                        int pad_h = ih >= -g->pt && ih < g->h + g->pb;
+                        int pad_w = iw >= -g->pl && iw < g->w + g->pr;
+                        if (in_h && in_w) {
+                            double v = xp[ih * g->w + iw];
+                            ++real;
+                            ++counted;
+                            sum += v;
+                            mag += fabs(v);
+                            if (isnan(v)) {
+                                nan_seen = 1;
+                            } else if (!finite_seen || v > best ||
+                                       (v == best && signbit(best) && !signbit(v))) {
+                                best = v;
+                                finite_seen = 1;
+                            }
+                        } else if (pad_h && pad_w) {
+                            ++counted; /* a padding tap */
+                        }
+                    }
+                int64_t oi = (p * ho + oh) * wo + ow;
+                if (g->kind == 0) {
+                    y[oi] = finite_seen ? best : (nan_seen ? NAN : lowest);
+                    if (scale) scale[oi] = 0.0;
+                } else {
+                    int64_t div = g->count_include_pad ? counted : real;
+                    y[oi] = sum / (double)div;
+                    if (scale) scale[oi] = mag / (double)div;
+                }
+            }
+    }
+    return 0;
+}
+
+/* Global pooling: one value per (n, c) plane of hw elements.  kind 0: the
+ * largest element under the same rules as oracle_pool2d's max (the plane is
+ * never empty); kind 1: the mean.  scale receives the mean of |x|. */
+int oracle_global_pool(int kind, int64_t planes, int64_t hw, const double* x, double* y,
+                       double* scale)
+{
+    if (planes < 1 || hw < 1 || (kind != 0 && kind != 1)) return -1;
+    for (int64_t p = 0; p < planes; ++p) {
+        const double* xp = x + p * hw;
+        double best = 0.0, sum = 0.0, mag = 0.0;
+        int finite_seen = 0, nan_seen = 0;
+        for (int64_t i = 0; i < hw; ++i) {
+            double v = xp[i];
+            sum += v;
+            mag += fabs(v);
+            if (isnan(v)) nan_seen = 1;
+            else if (!finite_seen || v > best || (v == best && signbit(best) && !signbit(v))) {
+                best = v;
+                finite_seen = 1;
+            }
+        }
+        y[p] = kind == 0 ? (finite_seen ? best : (nan_seen ? NAN : 0.0)) : sum / (double)hw;
+        if (scale) scale[p] = kind == 0 ? 0.0 : mag / (double)hw;
+    }
+    return 0;
 }
