@@ -175,6 +175,88 @@ def time_layer(cf, torch, layer, steps, warmup, loops):
     }
 
 
+def time_pool(cf, torch, layer, steps, warmup, loops):
+    """The pooling layers, timed like the convolutions (rotating operand sets,
+    median of event-timed loops); bound by HBM: bytes = x + y once each."""
+    p = cf.make_pool_problem(layer.n, layer.c, layer.h, layer.w, layer.kind,
+                             kernel=layer.kernel, stride=layer.stride, dilation=layer.dilation,
+                             pads=layer.pads, ceil_mode=layer.ceil_mode,
+                             count_include_pad=layer.count_include_pad)
+    variant = cf.pool_describe_variant(p, layer.dtype)
+    ho, wo = cf.pool_output_extent(p)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[layer.dtype]
+    x0 = torch.from_numpy(np.ascontiguousarray(workloads.make_pool_input(layer))).cuda().to(tdt)
+    es = esize(layer.dtype)
+    nbytes = (x0.numel() + layer.n * layer.c * ho * wo) * es
+    nsets = max(1, min(256, math.ceil(ROTATE_BYTES / nbytes)))
+    sets = [(x0 if i == 0 else x0.clone(),
+             torch.empty((layer.n, layer.c, ho, wo), dtype=tdt, device="cuda"))
+            for i in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fn = cf.lib().pool_forward
+    pref = ctypes.byref(p)
+    dt = cf.DTYPES[layer.dtype]
+    args = [(x.data_ptr(), y.data_ptr()) for x, y in sets]
+    counter = [0]
+
+    def call():
+        x, y = args[counter[0] % nsets]
+        counter[0] += 1
+        st = fn(pref, dt, x, y, sh)
+        if st:
+            raise cf.ConvError(st, "pool_forward")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    torch.cuda.synchronize()
+    loop_s = []
+    for _ in range(loops):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(sleep_cycles(torch, host_us * steps * 1.5 + 2000.0))
+        ev0.record(stream)
+        for _ in range(steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        loop_s.append(ev0.elapsed_time(ev1) * 1e-3)
+    del sets
+    torch.cuda.empty_cache()
+    avg = float(np.median(loop_s)) / steps
+    roof_s = nbytes / (PEAK["hbm_gbs"] * 1e9)
+    return {"name": layer.name, "variant": variant, "dtype": layer.dtype, "rotating_sets": nsets,
+            "us_avg": avg * 1e6, "us_loops": [round(t / steps * 1e6, 3) for t in loop_s],
+            "gbs": nbytes / avg / 1e9, "alg_bytes": nbytes, "bound": "hbm",
+            "roof_us": roof_s * 1e6, "roof_frac": roof_s / avg}
+
+
+def oracle_pool(layer, budget_s):
+    """The pooling oracle on the host cores over the whole layer (single thread:
+    the pooling definitions are plain loops)."""
+    import oracle
+
+    x = workloads.make_pool_input(layer)
+    runs, spent = 0, 0.0
+    while runs == 0 or (spent < budget_s and runs < 50):
+        t0 = time.perf_counter()
+        if layer.kind.startswith("global"):
+            oracle.global_pool(layer.kind.split("_")[1], x)
+        else:
+            g = oracle.PoolGeom(layer.n, layer.c, layer.h, layer.w, *layer.kernel, *layer.stride,
+                                *layer.dilation, *layer.pads, kind=layer.kind,
+                                ceil_mode=layer.ceil_mode,
+                                count_include_pad=layer.count_include_pad)
+            oracle.pool2d(g, x, dtype=layer.dtype)
+        spent += time.perf_counter() - t0
+        runs += 1
+    return {"s_per_run": spent / runs, "runs": runs, "threads": 1}
+
+
 _SLEEP_RATE = None
 
 
@@ -353,7 +435,17 @@ def main():
     macs, nbytes = layer_stats(layer)
     value = 2 * macs / (h["total_s"] / args.steps) / 1e12
     traffic = traffic_from_profiles(kernel_source_hash())
+    pools = []
+    if not args.headline_only and not args.layers:
+        for pl in workloads.POOL_LAYERS:
+            r = time_pool(cf, torch, pl, args.steps, args.warmup, args.loops)
+            print(f"# {pl.name}: {r['variant']} {r['us_avg']:.2f} us {r['gbs']:.0f} GB/s "
+                  f"{100 * r['roof_frac']:.1f}% of hbm roof", file=sys.stderr, flush=True)
+            pools.append(r)
     cpu = None if args.no_cpu_baseline else cpu_baseline(results, args.oracle_budget)
+    if cpu is not None:
+        for r in pools:
+            r["oracle"] = oracle_pool(workloads.POOL_BY_NAME[r["name"]], args.oracle_budget)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -384,6 +476,8 @@ def main():
         },
         "cpu_baseline": cpu,
         "configs": config_sums(results),
+        "pools": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                  for r in pools],
         "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                     if k not in ("total_s", "wall_s")} for r in results.values()],
     }

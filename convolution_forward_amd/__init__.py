@@ -39,6 +39,8 @@ EXPORTS = (
     "conv_output_extent", "conv_resolve_auto_pad", "conv_scratch_size",
     "conv_describe_variant", "conv_forward", "conv_transpose_forward",
     "conv_check", "conv_status_string", "conv_forward_noalloc",
+    "pool_output_extent", "pool_resolve_auto_pad", "pool_describe_variant", "pool_check",
+    "pool_forward",
 )
 
 
@@ -62,6 +64,18 @@ class conv_problem(ctypes.Structure):
         ("has_bias", ctypes.c_int32), ("has_residual", ctypes.c_int32),
         ("variant_override", ctypes.c_int32), ("split_override", ctypes.c_int32)]
 
+
+class pool_problem(ctypes.Structure):
+    """Mirror of struct pool_problem in include/pool.h (same field order)."""
+
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n", "c", "h", "w", "kh", "kw", "stride_h", "stride_w", "dil_h", "dil_w",
+        "pad_top", "pad_left", "pad_bottom", "pad_right", "x_off", "y_off")] + [
+        ("kind", ctypes.c_int32), ("ceil_mode", ctypes.c_int32),
+        ("count_include_pad", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+POOL_KINDS = {"max": 0, "average": 1, "global_max": 2, "global_average": 3}
 
 _lib = None
 
@@ -87,6 +101,12 @@ def lib():
         L.conv_transpose_forward.argtypes = fwd
         L.conv_check.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, ctypes.c_uint64]
         L.conv_forward_noalloc.argtypes = [P, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+        PP = ctypes.POINTER(pool_problem)
+        L.pool_output_extent.argtypes = [PP, i64p, i64p]
+        L.pool_resolve_auto_pad.argtypes = [PP, ctypes.c_int]
+        L.pool_describe_variant.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_uint64]
+        L.pool_check.argtypes = [PP, ctypes.c_int, vp, vp]
+        L.pool_forward.argtypes = [PP, ctypes.c_int, vp, vp, vp]
         L.conv_status_string.argtypes = [ctypes.c_int]
         L.conv_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -206,4 +226,52 @@ def conv_forward_noalloc(p, dtype, x, w, bias, residual, y, stream=None, check=T
                                     _ptr(residual), _ptr(y), stream or None)
     if check and st:
         raise ConvError(st, "conv_forward_noalloc")
+    return st
+
+
+# ------------------------------------------------------------------ pooling
+
+def make_pool_problem(n, c, h, w, kind="max", kernel=(1, 1), stride=(1, 1), dilation=(1, 1),
+                      pads=(0, 0, 0, 0), ceil_mode=False, count_include_pad=False,
+                      offsets=(0, 0)) -> pool_problem:
+    """A pool_problem; pads are (top, left, bottom, right)."""
+    return pool_problem(n, c, h, w, kernel[0], kernel[1], stride[0], stride[1], dilation[0],
+                        dilation[1], pads[0], pads[1], pads[2], pads[3], offsets[0], offsets[1],
+                        POOL_KINDS[kind] if isinstance(kind, str) else int(kind), int(ceil_mode),
+                        int(count_include_pad), 0)
+
+
+def pool_output_extent(p: pool_problem):
+    ho, wo = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().pool_output_extent(ctypes.byref(p), ctypes.byref(ho), ctypes.byref(wo))
+    if st:
+        raise ConvError(st, "pool_output_extent")
+    return ho.value, wo.value
+
+
+def pool_resolve_auto_pad(p: pool_problem, auto_pad) -> pool_problem:
+    mode = AUTO_PAD[auto_pad] if isinstance(auto_pad, str) else int(auto_pad)
+    st = lib().pool_resolve_auto_pad(ctypes.byref(p), mode)
+    if st:
+        raise ConvError(st, "pool_resolve_auto_pad")
+    return p
+
+
+def pool_describe_variant(p: pool_problem, dtype) -> str:
+    buf = ctypes.create_string_buffer(128)
+    st = lib().pool_describe_variant(ctypes.byref(p), _dt(dtype), buf, len(buf))
+    if st:
+        raise ConvError(st, "pool_describe_variant")
+    return buf.value.decode()
+
+
+def pool_check(p: pool_problem, dtype, x, y) -> int:
+    return lib().pool_check(ctypes.byref(p), _dt(dtype), _ptr(x), _ptr(y))
+
+
+def pool_forward(p: pool_problem, dtype, x, y, stream=None, check=True) -> int:
+    """Enqueue the pooling forward on `stream`."""
+    st = lib().pool_forward(ctypes.byref(p), _dt(dtype), _ptr(x), _ptr(y), stream or None)
+    if check and st:
+        raise ConvError(st, "pool_forward")
     return st

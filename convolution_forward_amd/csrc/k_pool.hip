@@ -1,0 +1,315 @@
+// Pooling forward for gfx950 ("Convolution, pooling and resize", section
+// "Pooling and resize"; include/pool.h states the operations):
+//
+//  * Windowed MaxPool / AveragePool, band kernel: one workgroup per (plane,
+//    band of output rows).  The band's input rows (its windows' reach, clipped
+//    to the input) are staged in LDS as float32 with coalesced loads (16-byte
+//    vectors when rows allow), then consecutive threads take consecutive
+//    outputs of a row, read their taps from LDS and store coalesced.  Rows
+//    outside the input are never touched: a tap is tested against the input
+//    (real), the pads (padding) or neither (beyond the padding, ceil mode).
+//  * Direct kernel: the same per-output arithmetic with the taps read from
+//    global memory, for rows too wide to stage.
+//  * Global pools: a workgroup loads the values of up to 4096 elements (whole
+//    planes, or a 4096-element chunk of a larger plane) into LDS and reduces
+//    each plane with a fixed halving tree (pairs i and i + ceil(m/2) while
+//    m > 1); larger planes reduce their chunk results the same way.  The order
+//    depends on the plane size only.
+//
+// Max is taken over integer keys of the float32 bits (the sign-magnitude
+// order turned into two's complement order), which orders -0 below +0 and
+// makes the result independent of the order; NaN taps get the lowest key so
+// that they are skipped, and a result still at that key is NaN if the window
+// had a real tap, else the element type's lowest finite value.  Every value
+// of the three element types is exact in float32, so the max is bit-exact.
+// The average sums the real taps in float32 in (kh, kw) order and divides by
+// the count the geometry gives (real taps, plus padding taps with
+// count_include_pad).
+#include <climits>
+#include <type_traits>
+
+#include "conv.h"
+#include "epilogue.h"
+#include "internal.h"
+#include "plan.h"
+#include "pool.h"
+#include "pool_plan.h"
+
+namespace convfwd {
+
+namespace {
+
+__device__ __forceinline__ int max_key(float v) {
+  const int s = __float_as_int(v);
+  return v != v ? INT_MIN : (s >= 0 ? s : s ^ 0x7FFFFFFF);
+}
+
+__device__ __forceinline__ float key_value(int k) {
+  return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF);
+}
+
+template <typename T>
+__device__ __forceinline__ float lowest_finite() {
+  if constexpr (std::is_same_v<T, float>) return -3.4028234663852886e38f;
+  else if constexpr (std::is_same_v<T, _Float16>) return -65504.0f;
+  else return -3.3895313892515355e38f;  // bfloat16 0xff7f
+}
+
+struct PoolArgs {
+  const void* x;
+  void* y;
+  int planes, h, w, ho, wo;
+  int kh, kw, sh, sw, dh, dw, pt, pl, pb, pr;
+  int cip;
+  int band_rows, in_rows, n_band;
+  int planes_wg, chunks;
+  int vec;      // x 16-byte aligned and w % (16 / sizeof(T)) == 0: rows in 16-byte items
+  Magic mg_wo, mg_w;
+};
+
+// Taps of one window along an axis: [k0, k1) real, count_pad = taps inside
+// the padded axis.  o*s - p + k*d in [0, n) for real taps, [-p, n + pe) for
+// padding ones.
+__device__ __forceinline__ void axis_taps(int o, int s, int p, int pe, int d, int k, int n,
+                                          int& real, int& padded) {
+  real = 0;
+  padded = 0;
+  const int st = o * s - p;
+  for (int t = 0; t < k; ++t) {
+    const int i = st + t * d;
+    real += (i >= 0 && i < n);
+    padded += (i >= -p && i < n + pe);
+  }
+}
+
+// One output: LOAD(ih, iw) returns the float value of a real tap.
+template <typename T, bool AVG, typename Load>
+__device__ __forceinline__ T pool_one(const PoolArgs& a, int oh, int ow, Load load) {
+  const int ih0 = oh * a.sh - a.pt, iw0 = ow * a.sw - a.pl;
+  int rh, ph, rw, pw;
+  axis_taps(oh, a.sh, a.pt, a.pb, a.dh, a.kh, a.h, rh, ph);
+  axis_taps(ow, a.sw, a.pl, a.pr, a.dw, a.kw, a.w, rw, pw);
+  if constexpr (AVG) {
+    float sum = 0.0f;
+    for (int kh = 0; kh < a.kh; ++kh) {
+      const int ih = ih0 + kh * a.dh;
+      if ((unsigned)ih >= (unsigned)a.h) continue;
+      for (int kw = 0; kw < a.kw; ++kw) {
+        const int iw = iw0 + kw * a.dw;
+        if ((unsigned)iw < (unsigned)a.w) sum += load(ih, iw);
+      }
+    }
+    const int cnt = a.cip ? ph * pw : rh * rw;
+    return from_f32<T>(sum / (float)cnt);
+  } else {
+    int m = INT_MIN;
+    for (int kh = 0; kh < a.kh; ++kh) {
+      const int ih = ih0 + kh * a.dh;
+      if ((unsigned)ih >= (unsigned)a.h) continue;
+      for (int kw = 0; kw < a.kw; ++kw) {
+        const int iw = iw0 + kw * a.dw;
+        if ((unsigned)iw < (unsigned)a.w) m = max(m, max_key(load(ih, iw)));
+      }
+    }
+    float v;
+    if (m != INT_MIN) v = key_value(m);
+    else v = rh * rw > 0 ? __int_as_float(0x7FC00000) : lowest_finite<T>();
+    return from_f32<T>(v);
+  }
+}
+
+template <typename T, bool AVG>
+__global__ __launch_bounds__(256) void pool_band_kernel(const PoolArgs a) {
+  extern __shared__ float rows[];  // in_rows x w
+  const int plane = blockIdx.x / a.n_band;
+  const int band = blockIdx.x - plane * a.n_band;
+  const int oh0 = band * a.band_rows;
+  const int nrow = min(a.band_rows, a.ho - oh0);
+  const int ih_lo = oh0 * a.sh - a.pt;  // input row of LDS row 0 (may be < 0)
+  const long long hw = (long long)a.h * a.w;
+  const T* __restrict__ xp = static_cast<const T*>(a.x) + (long long)plane * hw;
+  // stage the input rows of the band that exist
+  const int r0 = max(0, -ih_lo), r1 = min(a.in_rows, a.h - ih_lo);
+  if (r1 > r0) {
+    const int n_el = (r1 - r0) * a.w;
+    const T* src = xp + (long long)(ih_lo + r0) * a.w;
+    float* dst = rows + r0 * a.w;
+    constexpr int V = 16 / sizeof(T);
+    if (a.vec) {  // rows start on 16-byte boundaries: whole-vector items
+      typedef T tv __attribute__((ext_vector_type(V)));
+      for (int i = threadIdx.x; i < n_el / V; i += 256) {
+        const tv v = *reinterpret_cast<const tv*>(src + (long long)i * V);
+#pragma unroll
+        for (int e = 0; e < V; ++e) dst[i * V + e] = to_f32(v[e]);
+      }
+    } else {
+      for (int i = threadIdx.x; i < n_el; i += 256) dst[i] = to_f32(src[i]);
+    }
+  }
+  __syncthreads();
+  T* __restrict__ yp = static_cast<T*>(a.y) + (long long)plane * a.ho * a.wo + (long long)oh0 * a.wo;
+  const int n_out = nrow * a.wo;
+  for (int i = threadIdx.x; i < n_out; i += 256) {
+    const int r = (int)mdiv((unsigned)i, a.mg_wo);
+    const int ow = i - r * a.wo;
+    yp[i] = pool_one<T, AVG>(a, oh0 + r, ow, [&](int ih, int iw) {
+      return rows[(ih - ih_lo) * a.w + iw];
+    });
+  }
+}
+
+template <typename T, bool AVG>
+__global__ __launch_bounds__(256) void pool_direct_kernel(const PoolArgs a) {
+  const long long total = (long long)a.planes * a.ho * a.wo;
+  const long long o = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (o >= total) return;
+  const long long plane = o / ((long long)a.ho * a.wo);
+  const int rem = (int)(o - plane * a.ho * a.wo);
+  const int oh = (int)mdiv((unsigned)rem, a.mg_wo);
+  const int ow = rem - oh * a.wo;
+  const T* __restrict__ xp = static_cast<const T*>(a.x) + plane * a.h * a.w;
+  static_cast<T*>(a.y)[o] = pool_one<T, AVG>(a, oh, ow, [&](int ih, int iw) {
+    return to_f32(xp[(long long)ih * a.w + iw]);
+  });
+}
+
+// Halving tree over `planes` runs of m 32-bit words each, in LDS: float32
+// sums (AVG) or max keys.
+template <bool AVG>
+__device__ __forceinline__ void tree(unsigned* v, int planes, int stride, int m) {
+  while (m > 1) {
+    const int half = (m + 1) >> 1, pairs = m - half;
+    for (int i = threadIdx.x; i < planes * pairs; i += 256) {
+      const int q = i / pairs, j = i - q * pairs;
+      unsigned* p = v + q * stride + j;
+      if constexpr (AVG)
+        p[0] = __float_as_uint(__uint_as_float(p[0]) + __uint_as_float(p[half]));
+      else
+        p[0] = (unsigned)max((int)p[0], (int)p[half]);
+    }
+    __syncthreads();
+    m = half;
+  }
+}
+
+// Loads n values at src into LDS words: float32 bits (AVG) or max keys.
+template <typename T, bool AVG>
+__device__ __forceinline__ void load_run(const T* __restrict__ src, unsigned* dst, int n) {
+  constexpr int V = 16 / sizeof(T);
+  const bool vec = (reinterpret_cast<uintptr_t>(src) % 16) == 0;  // uniform
+  auto put = [&](int i, float f) {
+    if constexpr (AVG) dst[i] = __float_as_uint(f);
+    else dst[i] = (unsigned)max_key(f);
+  };
+  if (vec) {
+    typedef T tv __attribute__((ext_vector_type(V)));
+    for (int i = threadIdx.x; i < n / V; i += 256) {
+      const tv v = *reinterpret_cast<const tv*>(src + (long long)i * V);
+#pragma unroll
+      for (int e = 0; e < V; ++e) put(i * V + e, to_f32(v[e]));
+    }
+    for (int i = n / V * V + threadIdx.x; i < n; i += 256) put(i, to_f32(src[i]));
+  } else {
+    for (int i = threadIdx.x; i < n; i += 256) put(i, to_f32(src[i]));
+  }
+}
+
+template <typename T, bool AVG>
+__device__ __forceinline__ T global_result(unsigned v, float inv_hw) {
+  if constexpr (AVG) {
+    return from_f32<T>(__uint_as_float(v) * inv_hw);
+  } else {
+    const int k = (int)v;
+    return from_f32<T>(k == INT_MIN ? __int_as_float(0x7FC00000) : key_value(k));
+  }
+}
+
+template <typename T, bool AVG>
+__global__ __launch_bounds__(256) void pool_global_kernel(const PoolArgs a) {
+  __shared__ unsigned vals[kPoolChunk];
+  __shared__ unsigned part[kPoolChunk];
+  const int hw = a.h * a.w;
+  const float inv_hw = 1.0f / (float)hw;
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  T* __restrict__ y = static_cast<T*>(a.y);
+  if (a.chunks == 1) {
+    const int p0 = blockIdx.x * a.planes_wg;
+    const int np = min(a.planes_wg, a.planes - p0);
+    load_run<T, AVG>(x + (long long)p0 * hw, vals, np * hw);
+    __syncthreads();
+    tree<AVG>(vals, np, hw, hw);
+    if ((int)threadIdx.x < np) y[p0 + threadIdx.x] = global_result<T, AVG>(vals[threadIdx.x * hw], inv_hw);
+    return;
+  }
+  const long long plane = blockIdx.x;
+  for (int c = 0; c < a.chunks; ++c) {
+    const int first = c * (int)kPoolChunk;
+    const int n = min((int)kPoolChunk, hw - first);
+    load_run<T, AVG>(x + plane * hw + first, vals, n);
+    __syncthreads();
+    tree<AVG>(vals, 1, n, n);
+    if (threadIdx.x == 0) part[c] = vals[0];
+    __syncthreads();
+  }
+  tree<AVG>(part, 1, a.chunks, a.chunks);
+  if (threadIdx.x == 0) y[plane] = global_result<T, AVG>(part[0], inv_hw);
+}
+
+template <typename T>
+hipError_t launch_pool_t(const PoolGeo& g, const PoolPlan& pl, const PoolArgs& a, hipStream_t s) {
+  const bool avg = g.kind == POOL_AVERAGE || g.kind == POOL_GLOBAL_AVERAGE;
+  if (pl.variant == POOLV_GLOBAL) {
+    const unsigned grid = pl.chunks > 1 ? (unsigned)a.planes
+                                        : (unsigned)((a.planes + a.planes_wg - 1) / a.planes_wg);
+    if (avg) hipLaunchKernelGGL((pool_global_kernel<T, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((pool_global_kernel<T, false>), dim3(grid), dim3(256), 0, s, a);
+  } else if (pl.variant == POOLV_BAND) {
+    const unsigned grid = (unsigned)((long long)a.planes * a.n_band);
+    const size_t lds = (size_t)a.in_rows * a.w * sizeof(float);
+    if (avg) hipLaunchKernelGGL((pool_band_kernel<T, true>), dim3(grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((pool_band_kernel<T, false>), dim3(grid), dim3(256), lds, s, a);
+  } else {
+    const long long total = (long long)a.planes * a.ho * a.wo;
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    if (avg) hipLaunchKernelGGL((pool_direct_kernel<T, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((pool_direct_kernel<T, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+}  // namespace convfwd
+
+using namespace convfwd;
+
+extern "C" int pool_forward(const pool_problem* p, int dtype, const void* x, void* y,
+                            void* stream) {
+  int st = pool_check(p, dtype, x, y);
+  if (st) return st;
+  PoolGeo g;
+  pool_validate(p, dtype, &g);
+  PoolPlan pl;
+  pool_make_plan(g, &pl);
+  const int64_t es = dtype_size(dtype);
+  PoolArgs a{};
+  a.x = static_cast<const char*>(x) + p->x_off * es;
+  a.y = static_cast<char*>(y) + p->y_off * es;
+  a.planes = (int)(g.n * g.c);
+  a.h = (int)g.h; a.w = (int)g.w; a.ho = (int)g.ho; a.wo = (int)g.wo;
+  a.kh = (int)g.kh; a.kw = (int)g.kw; a.sh = (int)g.sh; a.sw = (int)g.sw;
+  a.dh = (int)g.dh; a.dw = (int)g.dw;
+  a.pt = (int)g.pt; a.pl = (int)g.pl; a.pb = (int)g.pb; a.pr = (int)g.pr;
+  a.cip = g.cip;
+  a.band_rows = pl.band_rows; a.in_rows = pl.in_rows; a.n_band = pl.n_band;
+  a.planes_wg = pl.planes_wg; a.chunks = pl.chunks;
+  a.vec = reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && (g.w * es) % 16 == 0;
+  a.mg_wo = make_magic((unsigned)g.wo);
+  a.mg_w = make_magic((unsigned)g.w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == CONV_F16) e = launch_pool_t<_Float16>(g, pl, a, s);
+  else if (dtype == CONV_BF16) e = launch_pool_t<__bf16>(g, pl, a, s);
+  else e = launch_pool_t<float>(g, pl, a, s);
+  return e == hipSuccess ? CONV_OK : CONV_ERR_DEVICE;
+}

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "conv.h"
+#include "pool.h"
 
 extern "C" {
 typedef struct {
@@ -42,6 +43,8 @@ int oracle_conv2d_im2col(const oracle_geom* g, const double* x, const double* w,
 int oracle_conv_transpose2d(const oracle_geom* g, const double* x, const double* w,
                             const double* b, const double* r, double* y, double* s,
                             int threads);
+int oracle_pool_extent(int64_t in, int64_t k, int64_t s, int64_t d, int64_t pb, int64_t pe,
+                       int ceil_mode, int64_t* out);
 int oracle_conv_transpose2d_gather(const oracle_geom* g, const double* x, const double* w,
                                    const double* b, const double* r, double* y, int threads);
 }
@@ -252,8 +255,46 @@ static void check_edges() {
   }
 }
 
+// Pooling problems, random and at the limits, through extent / auto_pad /
+// describe / check, the extents compared with the oracle's.
+static void check_pool(int iters) {
+  char buf[256];
+  for (int it = 0; it < iters; ++it) {
+    pool_problem p;
+    memset(&p, 0, sizeof p);
+    p.n = dim(3); p.c = dim(8); p.h = dim(30); p.w = dim(30);
+    p.kh = dim(5); p.kw = dim(5); p.stride_h = dim(3); p.stride_w = dim(3);
+    p.dil_h = dim(2); p.dil_w = dim(2);
+    p.pad_top = pick(-1, 4); p.pad_left = pick(0, 4); p.pad_bottom = pick(0, 4);
+    p.pad_right = next_u64() % 20 == 0 ? INT64_MAX : pick(0, 4);
+    p.kind = (int)pick(-1, 4); p.ceil_mode = (int)pick(0, 2); p.count_include_pad = (int)pick(0, 1);
+    p.reserved = next_u64() % 20 == 0;
+    p.x_off = next_u64() % 10 == 0 ? ((int64_t)1 << pick(40, 62)) : pick(0, 9);
+    p.y_off = pick(0, 9);
+    const int dtype = (int)pick(-1, 3);
+    int64_t ho = 0, wo = 0;
+    const int st = pool_output_extent(&p, &ho, &wo);
+    if (st == CONV_OK && p.kind < 2 && p.h < 1000 && p.w < 1000 && p.kh < 100 && p.kw < 100 &&
+        p.pad_right < 100 && p.stride_h < 100 && p.stride_w < 100 && p.dil_h < 100 && p.dil_w < 100) {
+      int64_t oh, ow;
+      const int a = oracle_pool_extent(p.h, p.kh, p.stride_h, p.dil_h, p.pad_top, p.pad_bottom,
+                                       p.ceil_mode, &oh);
+      const int b = oracle_pool_extent(p.w, p.kw, p.stride_w, p.dil_w, p.pad_left, p.pad_right,
+                                       p.ceil_mode, &ow);
+      EXPECT(a == 0 && b == 0 && oh == ho && ow == wo, "pool extent %" PRId64 " vs %" PRId64, ho, oh);
+    }
+    (void)pool_describe_variant(&p, dtype, buf, sizeof buf);
+    const uintptr_t base = (uintptr_t)1 << 44;
+    const int c = pool_check(&p, dtype, (const void*)base, (const void*)(base + ((uintptr_t)1 << 42)));
+    EXPECT(c >= CONV_OK && c <= CONV_ERR_DEVICE, "pool check status %d", c);
+    pool_problem q = p;
+    (void)pool_resolve_auto_pad(&q, (int)pick(-1, 4));
+  }
+}
+
 int main(int argc, char** argv) {
   check_edges();
+  check_pool(argc > 1 ? atoi(argv[1]) : 20000);
   const int iters = argc > 1 ? atoi(argv[1]) : 20000;
   check_planner(iters);
   check_oracle(iters / 20);

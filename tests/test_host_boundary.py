@@ -22,9 +22,14 @@ FAKE = 1 << 40  # never dereferenced: every call below fails validation first
 
 
 def _header_functions():
-    src = open(os.path.join(ROOT, "include", "conv.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv_\w+)\s*\(", src, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():

@@ -191,3 +191,53 @@ def random_tensor(rng: np.random.Generator, shape, dtype, lo=-1.0, hi=1.0):
 def integer_tensor(rng: np.random.Generator, shape, dtype, lo=-2, hi=2):
     """Small integers: exact in fp16 and fp32, so sums are exact in any order."""
     return rng.integers(lo, hi + 1, shape).astype(dtype)
+
+
+# ------------------------------------------------------------------ pooling
+
+@dataclass(frozen=True)
+class PoolLayer:
+    """A pooling step of the same models ("Convolution, pooling and resize",
+    "Pooling and resize"); x ~ U[-1,1] rounded once to the dtype."""
+
+    name: str
+    workload: int
+    index: int
+    dtype: str
+    n: int
+    c: int
+    h: int
+    w: int
+    kind: str  # "max", "average", "global_max", "global_average"
+    kernel: tuple = (1, 1)
+    stride: tuple = (1, 1)
+    dilation: tuple = (1, 1)
+    pads: tuple = (0, 0, 0, 0)
+    ceil_mode: bool = False
+    count_include_pad: bool = False
+
+    @property
+    def x_shape(self):
+        return (self.n, self.c, self.h, self.w)
+
+
+POOL_LAYERS = [
+    # the ResNet stem's max pool, on the stem convolution's output shape
+    PoolLayer("p1_maxpool3x3s2_f16", 8, 0, "f16", 32, 64, 112, 112, "max", (3, 3), (2, 2),
+              pads=(1, 1, 1, 1)),
+    # an average pool in ceil mode without padding counted, on the depthwise
+    # block's shape
+    PoolLayer("p2_avgpool3x3s2_ceil_f32", 8, 1, "f32", 64, 240, 28, 28, "average", (3, 3),
+              (2, 2), ceil_mode=True),
+    # the classifier head: global average over 2048 planes of 7x7
+    PoolLayer("p3_globalavg_f16", 8, 2, "f16", 32, 2048, 7, 7, "global_average"),
+    # global max over the pointwise layer's output
+    PoolLayer("p4_globalmax_f32", 8, 3, "f32", 64, 80, 14, 14, "global_max"),
+]
+
+POOL_BY_NAME = {l.name: l for l in POOL_LAYERS}
+
+
+def make_pool_input(layer: PoolLayer) -> np.ndarray:
+    rng = np.random.default_rng(SEED_BASE + 1000 * layer.workload + 10 * layer.index)
+    return quantize(rng.uniform(-1.0, 1.0, layer.x_shape), layer.dtype)
