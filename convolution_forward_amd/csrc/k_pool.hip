@@ -65,6 +65,7 @@ struct PoolArgs {
   int planes_wg, chunks;
   int vec;      // x 16-byte aligned and w % (16 / sizeof(T)) == 0: rows in 16-byte items
   Magic mg_wo, mg_w;
+  Magic mg_pairs[14];  // global tree: division by each level's pair count
 };
 
 // Taps of one window along an axis: [k0, k1) real, count_pad = taps inside
@@ -118,7 +119,60 @@ __device__ __forceinline__ T pool_one(const PoolArgs& a, int oh, int ow, Load lo
   }
 }
 
-template <typename T, bool AVG>
+// One output of a KH x KW window read from the staged rows: every tap's LDS
+// address is clamped into the staged block, so all reads can issue at once,
+// and a tap outside the input is masked out (max: the NaN key; sum: 0).
+template <typename T, bool AVG, int KH, int KW>
+__device__ __forceinline__ T pool_one_fixed(const PoolArgs& a, const float* rows, int ih_lo,
+                                            int oh, int ow) {
+  const int ih0 = oh * a.sh - a.pt, iw0 = ow * a.sw - a.pl;
+  bool vh[KH], vw[KW];
+  int ro[KH], co[KW];
+  int rh = 0, rw = 0, ph = 0, pw = 0;
+#pragma unroll
+  for (int k = 0; k < KH; ++k) {
+    const int ih = ih0 + k * a.dh;
+    vh[k] = (unsigned)ih < (unsigned)a.h;
+    rh += vh[k];
+    ph += (ih >= -a.pt && ih < a.h + a.pb);
+    ro[k] = (min(max(ih, ih_lo), ih_lo + a.in_rows - 1) - ih_lo) * a.w;
+  }
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int iw = iw0 + k * a.dw;
+    vw[k] = (unsigned)iw < (unsigned)a.w;
+    rw += vw[k];
+    pw += (iw >= -a.pl && iw < a.w + a.pr);
+    co[k] = min(max(iw, 0), a.w - 1);
+  }
+  float v[KH * KW];
+#pragma unroll
+  for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+    for (int kw = 0; kw < KW; ++kw) v[kh * KW + kw] = rows[ro[kh] + co[kw]];
+  if constexpr (AVG) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) sum += (vh[kh] && vw[kw]) ? v[kh * KW + kw] : 0.0f;
+    const int cnt = a.cip ? ph * pw : rh * rw;
+    return from_f32<T>(sum / (float)cnt);
+  } else {
+    int m = INT_MIN;
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw)
+        m = max(m, (vh[kh] && vw[kw]) ? max_key(v[kh * KW + kw]) : INT_MIN);
+    float r;
+    if (m != INT_MIN) r = key_value(m);
+    else r = rh * rw > 0 ? __int_as_float(0x7FC00000) : lowest_finite<T>();
+    return from_f32<T>(r);
+  }
+}
+
+template <typename T, bool AVG, int KF>
 __global__ __launch_bounds__(256) void pool_band_kernel(const PoolArgs a) {
   extern __shared__ float rows[];  // in_rows x w
   const int plane = blockIdx.x / a.n_band;
@@ -140,7 +194,9 @@ __global__ __launch_bounds__(256) void pool_band_kernel(const PoolArgs a) {
       for (int i = threadIdx.x; i < n_el / V; i += 256) {
         const tv v = *reinterpret_cast<const tv*>(src + (long long)i * V);
 #pragma unroll
-        for (int e = 0; e < V; ++e) dst[i * V + e] = to_f32(v[e]);
+        for (int e = 0; e < V; e += 4)
+          *reinterpret_cast<float4*>(dst + i * V + e) =
+              float4{to_f32(v[e]), to_f32(v[e + 1]), to_f32(v[e + 2]), to_f32(v[e + 3])};
       }
     } else {
       for (int i = threadIdx.x; i < n_el; i += 256) dst[i] = to_f32(src[i]);
@@ -152,9 +208,12 @@ __global__ __launch_bounds__(256) void pool_band_kernel(const PoolArgs a) {
   for (int i = threadIdx.x; i < n_out; i += 256) {
     const int r = (int)mdiv((unsigned)i, a.mg_wo);
     const int ow = i - r * a.wo;
-    yp[i] = pool_one<T, AVG>(a, oh0 + r, ow, [&](int ih, int iw) {
-      return rows[(ih - ih_lo) * a.w + iw];
-    });
+    if constexpr (KF > 0)
+      yp[i] = pool_one_fixed<T, AVG, KF, KF>(a, rows, ih_lo, oh0 + r, ow);
+    else
+      yp[i] = pool_one<T, AVG>(a, oh0 + r, ow, [&](int ih, int iw) {
+        return rows[(ih - ih_lo) * a.w + iw];
+      });
   }
 }
 
@@ -174,22 +233,36 @@ __global__ __launch_bounds__(256) void pool_direct_kernel(const PoolArgs a) {
 }
 
 // Halving tree over `planes` runs of m 32-bit words each, in LDS: float32
-// sums (AVG) or max keys.
+// sums (AVG) or max keys.  Level l's pair count divides by mg[l].
 template <bool AVG>
-__device__ __forceinline__ void tree(unsigned* v, int planes, int stride, int m) {
-  while (m > 1) {
+__device__ __forceinline__ unsigned tree_op(unsigned x, unsigned y) {
+  if constexpr (AVG) return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  else return (unsigned)max((int)x, (int)y);
+}
+
+template <bool AVG>
+__device__ __forceinline__ void tree(unsigned* v, int planes, int stride, int m, const Magic* mg) {
+  for (int l = 0; m > 1; ++l) {
     const int half = (m + 1) >> 1, pairs = m - half;
     for (int i = threadIdx.x; i < planes * pairs; i += 256) {
-      const int q = i / pairs, j = i - q * pairs;
+      const int q = (int)mdiv((unsigned)i, mg[l]), j = i - q * pairs;
       unsigned* p = v + q * stride + j;
-      if constexpr (AVG)
-        p[0] = __float_as_uint(__uint_as_float(p[0]) + __uint_as_float(p[half]));
-      else
-        p[0] = (unsigned)max((int)p[0], (int)p[half]);
+      p[0] = tree_op<AVG>(p[0], p[half]);
     }
     __syncthreads();
     m = half;
   }
+}
+
+// The same tree over one run, by one thread.
+template <bool AVG>
+__device__ __forceinline__ unsigned tree_serial(unsigned* v, int m) {
+  while (m > 1) {
+    const int half = (m + 1) >> 1, pairs = m - half;
+    for (int j = 0; j < pairs; ++j) v[j] = tree_op<AVG>(v[j], v[j + half]);
+    m = half;
+  }
+  return v[0];
 }
 
 // Loads n values at src into LDS words: float32 bits (AVG) or max keys.
@@ -226,8 +299,7 @@ __device__ __forceinline__ T global_result(unsigned v, float inv_hw) {
 
 template <typename T, bool AVG>
 __global__ __launch_bounds__(256) void pool_global_kernel(const PoolArgs a) {
-  __shared__ unsigned vals[kPoolChunk];
-  __shared__ unsigned part[kPoolChunk];
+  extern __shared__ unsigned gsm[];  // planes_wg * hw words (small planes) or 2 chunks
   const int hw = a.h * a.w;
   const float inv_hw = 1.0f / (float)hw;
   const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -235,24 +307,45 @@ __global__ __launch_bounds__(256) void pool_global_kernel(const PoolArgs a) {
   if (a.chunks == 1) {
     const int p0 = blockIdx.x * a.planes_wg;
     const int np = min(a.planes_wg, a.planes - p0);
-    load_run<T, AVG>(x + (long long)p0 * hw, vals, np * hw);
+    load_run<T, AVG>(x + (long long)p0 * hw, gsm, np * hw);
     __syncthreads();
-    tree<AVG>(vals, np, hw, hw);
-    if ((int)threadIdx.x < np) y[p0 + threadIdx.x] = global_result<T, AVG>(vals[threadIdx.x * hw], inv_hw);
+    if (a.planes_wg == 256) {  // small planes: one thread per plane, no barrier
+      if ((int)threadIdx.x < np)
+        y[p0 + threadIdx.x] = global_result<T, AVG>(tree_serial<AVG>(gsm + threadIdx.x * hw, hw), inv_hw);
+      return;
+    }
+    tree<AVG>(gsm, np, hw, hw, a.mg_pairs);
+    if ((int)threadIdx.x < np) y[p0 + threadIdx.x] = global_result<T, AVG>(gsm[threadIdx.x * hw], inv_hw);
     return;
   }
+  unsigned* vals = gsm;
+  unsigned* part = gsm + kPoolChunk;
   const long long plane = blockIdx.x;
   for (int c = 0; c < a.chunks; ++c) {
     const int first = c * (int)kPoolChunk;
     const int n = min((int)kPoolChunk, hw - first);
     load_run<T, AVG>(x + plane * hw + first, vals, n);
     __syncthreads();
-    tree<AVG>(vals, 1, n, n);
+    if (n == (int)kPoolChunk) {
+      tree<AVG>(vals, 1, n, n, a.mg_pairs);
+    } else {  // the last, shorter chunk: its own levels
+      if (threadIdx.x == 0) tree_serial<AVG>(vals, n);
+      __syncthreads();
+    }
     if (threadIdx.x == 0) part[c] = vals[0];
     __syncthreads();
   }
-  tree<AVG>(part, 1, a.chunks, a.chunks);
-  if (threadIdx.x == 0) y[plane] = global_result<T, AVG>(part[0], inv_hw);
+  if (threadIdx.x == 0) y[plane] = global_result<T, AVG>(tree_serial<AVG>(part, a.chunks), inv_hw);
+}
+
+template <typename T, bool AVG>
+void launch_band(const PoolArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  if (a.kh == 3 && a.kw == 3)
+    hipLaunchKernelGGL((pool_band_kernel<T, AVG, 3>), grid, dim3(256), lds, s, a);
+  else if (a.kh == 2 && a.kw == 2)
+    hipLaunchKernelGGL((pool_band_kernel<T, AVG, 2>), grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((pool_band_kernel<T, AVG, 0>), grid, dim3(256), lds, s, a);
 }
 
 template <typename T>
@@ -261,13 +354,14 @@ hipError_t launch_pool_t(const PoolGeo& g, const PoolPlan& pl, const PoolArgs& a
   if (pl.variant == POOLV_GLOBAL) {
     const unsigned grid = pl.chunks > 1 ? (unsigned)a.planes
                                         : (unsigned)((a.planes + a.planes_wg - 1) / a.planes_wg);
-    if (avg) hipLaunchKernelGGL((pool_global_kernel<T, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((pool_global_kernel<T, false>), dim3(grid), dim3(256), 0, s, a);
+    const size_t lds = pl.chunks > 1 ? 2 * kPoolChunk * 4 : (size_t)a.planes_wg * g.h * g.w * 4;
+    if (avg) hipLaunchKernelGGL((pool_global_kernel<T, true>), dim3(grid), dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((pool_global_kernel<T, false>), dim3(grid), dim3(256), lds, s, a);
   } else if (pl.variant == POOLV_BAND) {
-    const unsigned grid = (unsigned)((long long)a.planes * a.n_band);
+    const dim3 grid((unsigned)((long long)a.planes * a.n_band));
     const size_t lds = (size_t)a.in_rows * a.w * sizeof(float);
-    if (avg) hipLaunchKernelGGL((pool_band_kernel<T, true>), dim3(grid), dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((pool_band_kernel<T, false>), dim3(grid), dim3(256), lds, s, a);
+    if (avg) launch_band<T, true>(a, grid, lds, s);
+    else launch_band<T, false>(a, grid, lds, s);
   } else {
     const long long total = (long long)a.planes * a.ho * a.wo;
     const unsigned grid = (unsigned)((total + 255) / 256);
@@ -306,6 +400,14 @@ extern "C" int pool_forward(const pool_problem* p, int dtype, const void* x, voi
   a.vec = reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && (g.w * es) % 16 == 0;
   a.mg_wo = make_magic((unsigned)g.wo);
   a.mg_w = make_magic((unsigned)g.w);
+  {  // the tree's levels over a full run (a plane, or a 4096-element chunk)
+    int m = (int)(pl.chunks > 1 ? kPoolChunk : g.h * g.w), l = 0;
+    while (m > 1 && l < 14) {
+      const int half = (m + 1) >> 1;
+      a.mg_pairs[l++] = make_magic((unsigned)(m - half));
+      m = half;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == CONV_F16) e = launch_pool_t<_Float16>(g, pl, a, s);

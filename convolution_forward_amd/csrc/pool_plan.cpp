@@ -95,8 +95,11 @@ int pool_make_plan(const PoolGeo& g, PoolPlan* pl) {
   if (g.kind == POOL_GLOBAL_MAX || g.kind == POOL_GLOBAL_AVERAGE) {
     pl->variant = POOLV_GLOBAL;
     const int64_t hw = g.h * g.w;
-    if (hw <= kPoolChunk) {
-      pl->planes_wg = (int)std::min<int64_t>(kPoolChunk / hw, 256);
+    if (hw <= 64) {  // one thread per plane, 256 planes (at most 64 KiB of LDS)
+      pl->planes_wg = 256;
+      pl->chunks = 1;
+    } else if (hw <= kPoolChunk) {
+      pl->planes_wg = (int)std::min<int64_t>(kPoolChunk / hw, 255);
       pl->chunks = 1;
     } else {
       pl->planes_wg = 1;

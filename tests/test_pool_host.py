@@ -101,6 +101,6 @@ def test_variant_names():
     p = cf.make_pool_problem(1, 1, 4, 6000, "average", kernel=(3, 3))
     assert cf.pool_describe_variant(p, "f32") == "pool.average.f32.direct"
     p = cf.make_pool_problem(32, 2048, 7, 7, "global_average")
-    assert cf.pool_describe_variant(p, "bf16") == "pool.global_average.bf16.tree.planes83"
+    assert cf.pool_describe_variant(p, "bf16") == "pool.global_average.bf16.tree.planes256"
     p = cf.make_pool_problem(2, 3, 100, 100, "global_max")
     assert cf.pool_describe_variant(p, "f32") == "pool.global_max.f32.tree.chunks3"
