@@ -96,6 +96,8 @@ def _load():
         lib.oracle_pool_extent.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, i64p]
         lib.oracle_pool2d.argtypes = [ctypes.POINTER(_PoolGeom), dp, ctypes.c_double, dp, dp]
         lib.oracle_global_pool.argtypes = [ctypes.c_int, i64, i64, dp, dp, dp]
+        lib.oracle_conv_integer.argtypes = [ctypes.POINTER(_Geom), dp, dp, ctypes.c_int32, dp, dp,
+                                            ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -359,3 +361,23 @@ def global_pool(kind, x):
     if rc:
         raise ValueError("oracle_global_pool rejected the problem")
     return y, s
+
+
+# -------------------------------------------------------------- ConvInteger
+
+def conv_integer(g: Geom, x, w, x_zero=0, w_zero=0, threads=0):
+    """ONNX ConvInteger ("Convolution, pooling and resize", "ConvInteger"):
+    sum of (x - x_zero) * (w - w_zero[co]) over the real taps, exact, then
+    wrapped to int32.  x and w are integer arrays of uint8 or int8 values;
+    w_zero is a scalar or one value per output channel."""
+    x = np.ascontiguousarray(np.asarray(x, np.int32))
+    w = np.ascontiguousarray(np.asarray(w, np.int32))
+    assert x.shape == (g.n, g.c_in, g.h, g.w), x.shape
+    assert w.shape == (g.c_out, g.c_in // g.groups, g.kh, g.kw), w.shape
+    wz = np.ascontiguousarray(np.broadcast_to(np.asarray(w_zero, np.int32), (g.c_out,)))
+    y = np.empty(out_shape(g), np.int32)
+    rc = _load().oracle_conv_integer(ctypes.byref(g._c()), _p(x), _p(w), int(x_zero), _p(wz),
+                                     _p(y), threads)
+    if rc:
+        raise ValueError("oracle_conv_integer rejected the problem")
+    return y

@@ -24,6 +24,8 @@
  *    explicit pads, dilation, groups, fused epilogue order: sum, bias,
  *    residual, activation; the nine fused activations), section
  *    "ConvInteger" (asymmetric padding is part of the problem geometry) and
+ *    section "ConvInteger" (the integer convolution with zero points, int32
+ *    with wrap-around, padding as the zero point), and
  *    section "Pooling and resize" (MaxPool / AveragePool with padding,
  *    dilation, ceil_mode and count_include_pad; the NaN and empty-window
  *    rules; global pools over a plane).
@@ -585,5 +587,52 @@ int oracle_global_pool(int kind, int64_t planes, int64_t hw, const double* x, do
         y[p] = kind == 0 ? (finite_seen ? best : (nan_seen ? NAN : 0.0)) : sum / (double)hw;
         if (scale) scale[p] = kind == 0 ? 0.0 : mag / (double)hw;
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* ConvInteger ("Convolution, pooling and resize", section "ConvInteger";  */
+/* ONNX ConvInteger)                                                        */
+/* ---------------------------------------------------------------------- */
+
+/* y[n,co,oh,ow] = sum over the real taps of (x - x_zero) * (w[co,...] - w_zero[co]),
+ * exactly in 64-bit integers, then reduced to int32 with wrap-around (the value
+ * modulo 2^32 in two's complement).  x and w hold the integer values of their
+ * uint8 or int8 elements; w_zero has c_out entries (a per-tensor zero point is
+ * passed repeated).  A padded tap is the real value zero, i.e. the quantized
+ * value x_zero, so it adds nothing: it is skipped.  Geometry as oracle_conv2d
+ * (the activation, bias and residual fields are not used). */
+int oracle_conv_integer(const oracle_geom* g, const int32_t* x, const int32_t* w,
+                        int32_t x_zero, const int32_t* w_zero, int32_t* y, int threads)
+{
+    int64_t ho, wo;
+    if (!geom_ok(g)) return -1;
+    if (oracle_conv_extent(g->h, g->kh, g->sh, g->dh, g->pt, g->pb, &ho) ||
+        oracle_conv_extent(g->w, g->kw, g->sw, g->dw, g->pl, g->pr, &wo))
+        return -1;
+    const int64_t cig = g->c_in / g->groups, cog = g->c_out / g->groups;
+    set_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < g->n; ++n)
+        for (int64_t co = 0; co < g->c_out; ++co) {
+            const int64_t grp = co / cog;
+            for (int64_t oh = 0; oh < ho; ++oh)
+                for (int64_t ow = 0; ow < wo; ++ow) {
+                    int64_t acc = 0;
+                    for (int64_t ci = 0; ci < cig; ++ci)
+                        for (int64_t kh = 0; kh < g->kh; ++kh)
+                            for (int64_t kw = 0; kw < g->kw; ++kw) {
+                                int64_t ih = oh * g->sh - g->pt + kh * g->dh;
+                                int64_t iw = ow * g->sw - g->pl + kw * g->dw;
+                                if (ih < 0 || ih >= g->h || iw < 0 || iw >= g->w) continue;
+                                int64_t xv = x[((n * g->c_in + grp * cig + ci) * g->h + ih) * g->w + iw];
+                                int64_t wv = w[((co * cig + ci) * g->kh + kh) * g->kw + kw];
+                                acc += (xv - x_zero) * (wv - w_zero[co]);
+                            }
+                    uint32_t low = (uint32_t)(uint64_t)acc;
+                    y[((n * g->c_out + co) * ho + oh) * wo + ow] =
+                        (int32_t)(low >= 0x80000000u ? (int64_t)low - 0x100000000LL : (int64_t)low);
+                }
+        }
     return 0;
 }
