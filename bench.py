@@ -44,6 +44,7 @@ PEAK = {  # MI355X published peaks
     "f16_mfma_tflops": 2500.0,
     "f32_tflops": 157.3,
     "hbm_gbs": 8000.0,
+    "i8_mfma_tops": 5000.0,
 }
 ROTATE_BYTES = 1 << 30
 
@@ -233,6 +234,90 @@ def time_pool(cf, torch, layer, steps, warmup, loops):
             "us_avg": avg * 1e6, "us_loops": [round(t / steps * 1e6, 3) for t in loop_s],
             "gbs": nbytes / avg / 1e9, "alg_bytes": nbytes, "bound": "hbm",
             "roof_us": roof_s * 1e6, "roof_frac": roof_s / avg}
+
+
+def time_int(cf, torch, layer, steps, warmup, loops):
+    """The quantized layers (ConvInteger): int8 operands, int32 output; bound by
+    the int8 MFMA peak or HBM (bytes = x + w + y once each)."""
+    p = cf.make_problem(layer.n, layer.c_in, layer.h, layer.w, layer.c_out, layer.kh, layer.kw,
+                        groups=layer.groups, stride=layer.stride, dilation=layer.dilation,
+                        pads=layer.pads)
+    variant = cf.conv_integer_describe_variant(p, layer.x_type, layer.w_type)
+    x, w, xz, wz = workloads.make_int_inputs(layer)
+    npt = {"u8": np.uint8, "i8": np.int8}
+    x0 = torch.from_numpy(np.ascontiguousarray(x.astype(npt[layer.x_type]).view(np.uint8))).cuda()
+    w0 = torch.from_numpy(np.ascontiguousarray(w.astype(npt[layer.w_type]).view(np.uint8))).cuda()
+    xzd = torch.from_numpy(np.array([xz]).astype(npt[layer.x_type]).view(np.uint8)).cuda()
+    wzd = torch.from_numpy(wz.astype(npt[layer.w_type]).view(np.uint8)).cuda()
+    N, C, H, W = layer.out_shape
+    macs = N * C * H * W * (layer.c_in // layer.groups) * layer.kh * layer.kw
+    nbytes = x0.numel() + w0.numel() + N * C * H * W * 4
+    nsets = max(1, min(256, math.ceil(ROTATE_BYTES / nbytes)))
+    sets = [(x0 if i == 0 else x0.clone(), w0 if i == 0 else w0.clone(),
+             torch.empty(layer.out_shape, dtype=torch.int32, device="cuda")) for i in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fn = cf.lib().conv_integer_forward
+    pref = ctypes.byref(p)
+    xt, wt = cf.CONVI_TYPES[layer.x_type], cf.CONVI_TYPES[layer.w_type]
+    args = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in sets]
+    counter = [0]
+
+    def call():
+        xa, wa, ya = args[counter[0] % nsets]
+        counter[0] += 1
+        st = fn(pref, xt, wt, xa, wa, xzd.data_ptr(), wzd.data_ptr(), 1, ya, sh)
+        if st:
+            raise cf.ConvError(st, "conv_integer_forward")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    torch.cuda.synchronize()
+    loop_s = []
+    for _ in range(loops):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(sleep_cycles(torch, host_us * steps * 1.5 + 2000.0))
+        ev0.record(stream)
+        for _ in range(steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        loop_s.append(ev0.elapsed_time(ev1) * 1e-3)
+    del sets
+    torch.cuda.empty_cache()
+    avg = float(np.median(loop_s)) / steps
+    t_c = 2 * macs / (PEAK["i8_mfma_tops"] * 1e12)
+    t_m = nbytes / (PEAK["hbm_gbs"] * 1e9)
+    return {"name": layer.name, "variant": variant, "dtype": f"{layer.x_type}{layer.w_type}->i32",
+            "rotating_sets": nsets, "us_avg": avg * 1e6,
+            "us_loops": [round(t / steps * 1e6, 3) for t in loop_s],
+            "tops": 2 * macs / avg / 1e12, "gbs": nbytes / avg / 1e9, "macs": macs,
+            "alg_bytes": nbytes, "bound": "mfma" if t_c >= t_m else "hbm",
+            "roof_us": max(t_c, t_m) * 1e6, "roof_frac": max(t_c, t_m) / avg}
+
+
+def oracle_int(layer, budget_s):
+    import oracle
+
+    x, w, xz, wz = workloads.make_int_inputs(layer)
+    g = oracle.Geom(layer.n, layer.c_in, layer.h, layer.w, layer.c_out, layer.kh, layer.kw,
+                    groups=layer.groups, sh=layer.stride[0], sw=layer.stride[1],
+                    dh=layer.dilation[0], dw=layer.dilation[1], pt=layer.pads[0],
+                    pl=layer.pads[1], pb=layer.pads[2], pr=layer.pads[3])
+    runs, spent = 0, 0.0
+    while runs == 0 or (spent < budget_s and runs < 50):
+        t0 = time.perf_counter()
+        oracle.conv_integer(g, x, w, xz, wz)
+        spent += time.perf_counter() - t0
+        runs += 1
+    N, C, H, W = layer.out_shape
+    macs = N * C * H * W * (layer.c_in // layer.groups) * layer.kh * layer.kw
+    return {"s_per_run": spent / runs, "runs": runs, "gops": 2 * macs * runs / spent / 1e9}
 
 
 def oracle_pool(layer, budget_s):
@@ -442,10 +527,19 @@ def main():
             print(f"# {pl.name}: {r['variant']} {r['us_avg']:.2f} us {r['gbs']:.0f} GB/s "
                   f"{100 * r['roof_frac']:.1f}% of hbm roof", file=sys.stderr, flush=True)
             pools.append(r)
+    ints = []
+    if not args.headline_only and not args.layers:
+        for il in workloads.INT_LAYERS:
+            r = time_int(cf, torch, il, args.steps, args.warmup, args.loops)
+            print(f"# {il.name}: {r['variant']} {r['us_avg']:.2f} us {r['tops']:.1f} TOP/s "
+                  f"{100 * r['roof_frac']:.1f}% of {r['bound']} roof", file=sys.stderr, flush=True)
+            ints.append(r)
     cpu = None if args.no_cpu_baseline else cpu_baseline(results, args.oracle_budget)
     if cpu is not None:
         for r in pools:
             r["oracle"] = oracle_pool(workloads.POOL_BY_NAME[r["name"]], args.oracle_budget)
+        for r in ints:
+            r["oracle"] = oracle_int(workloads.INT_BY_NAME[r["name"]], args.oracle_budget)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -478,6 +572,8 @@ def main():
         "configs": config_sums(results),
         "pools": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in pools],
+        "conv_integer": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                         for r in ints],
         "layers": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                     if k not in ("total_s", "wall_s")} for r in results.values()],
     }

@@ -40,7 +40,7 @@ EXPORTS = (
     "conv_describe_variant", "conv_forward", "conv_transpose_forward",
     "conv_check", "conv_status_string", "conv_forward_noalloc",
     "pool_output_extent", "pool_resolve_auto_pad", "pool_describe_variant", "pool_check",
-    "pool_forward",
+    "pool_forward", "conv_integer_describe_variant", "conv_integer_check", "conv_integer_forward",
 )
 
 
@@ -107,6 +107,12 @@ def lib():
         L.pool_describe_variant.argtypes = [PP, ctypes.c_int, ctypes.c_char_p, ctypes.c_uint64]
         L.pool_check.argtypes = [PP, ctypes.c_int, vp, vp]
         L.pool_forward.argtypes = [PP, ctypes.c_int, vp, vp, vp]
+        L.conv_integer_describe_variant.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_char_p,
+                                                    ctypes.c_uint64]
+        L.conv_integer_check.argtypes = [P, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                         ctypes.c_int, vp]
+        L.conv_integer_forward.argtypes = [P, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                           ctypes.c_int, vp, vp]
         L.conv_status_string.argtypes = [ctypes.c_int]
         L.conv_status_string.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -274,4 +280,38 @@ def pool_forward(p: pool_problem, dtype, x, y, stream=None, check=True) -> int:
     st = lib().pool_forward(ctypes.byref(p), _dt(dtype), _ptr(x), _ptr(y), stream or None)
     if check and st:
         raise ConvError(st, "pool_forward")
+    return st
+
+
+# -------------------------------------------------------------- ConvInteger
+
+CONVI_TYPES = {"u8": 0, "i8": 1}
+
+
+def _it(t):
+    return CONVI_TYPES[t] if isinstance(t, str) else int(t)
+
+
+def conv_integer_describe_variant(p: conv_problem, x_type, w_type) -> str:
+    buf = ctypes.create_string_buffer(128)
+    st = lib().conv_integer_describe_variant(ctypes.byref(p), _it(x_type), _it(w_type), buf,
+                                             len(buf))
+    if st:
+        raise ConvError(st, "conv_integer_describe_variant")
+    return buf.value.decode()
+
+
+def conv_integer_check(p, x_type, w_type, x, w, x_zero, w_zero, w_zero_per_channel, y) -> int:
+    return lib().conv_integer_check(ctypes.byref(p), _it(x_type), _it(w_type), _ptr(x), _ptr(w),
+                                    _ptr(x_zero), _ptr(w_zero), int(w_zero_per_channel), _ptr(y))
+
+
+def conv_integer_forward(p, x_type, w_type, x, w, x_zero, w_zero, w_zero_per_channel, y,
+                         stream=None, check=True) -> int:
+    """Enqueue ConvInteger (int32 output with wrap-around) on `stream`."""
+    st = lib().conv_integer_forward(ctypes.byref(p), _it(x_type), _it(w_type), _ptr(x), _ptr(w),
+                                    _ptr(x_zero), _ptr(w_zero), int(w_zero_per_channel), _ptr(y),
+                                    stream or None)
+    if check and st:
+        raise ConvError(st, "conv_integer_forward")
     return st

@@ -241,3 +241,55 @@ POOL_BY_NAME = {l.name: l for l in POOL_LAYERS}
 def make_pool_input(layer: PoolLayer) -> np.ndarray:
     rng = np.random.default_rng(SEED_BASE + 1000 * layer.workload + 10 * layer.index)
     return quantize(rng.uniform(-1.0, 1.0, layer.x_shape), layer.dtype)
+
+
+# -------------------------------------------------------------- ConvInteger
+
+@dataclass(frozen=True)
+class IntLayer:
+    """A quantized convolution ("Convolution, pooling and resize", "ConvInteger"):
+    x and w uniform over their type's range, one x zero point, per-channel w
+    zero points."""
+
+    name: str
+    workload: int
+    index: int
+    x_type: str  # "u8" or "i8"
+    w_type: str
+    n: int
+    c_in: int
+    h: int
+    w: int
+    c_out: int
+    kh: int
+    kw: int
+    out_shape: tuple
+    groups: int = 1
+    stride: tuple = (1, 1)
+    dilation: tuple = (1, 1)
+    pads: tuple = (0, 0, 0, 0)
+
+
+INT_LAYERS = [
+    # the bottleneck 3x3 layer of workload 2, quantized: uint8 activations with a
+    # zero point, int8 weights with one zero point per output channel
+    IntLayer("q1_bottleneck3x3_u8i8", 9, 0, "u8", "i8", 32, 256, 14, 14, 256, 3, 3,
+             (32, 256, 14, 14), pads=(1, 1, 1, 1)),
+]
+
+INT_BY_NAME = {l.name: l for l in INT_LAYERS}
+
+
+def make_int_inputs(layer: IntLayer):
+    """(x, w, x_zero, w_zero) as int64 arrays / ints of the operands' values."""
+    lo = {"u8": 0, "i8": -128}
+    s = [SEED_BASE + 1000 * layer.workload + 10 * layer.index + t for t in range(4)]
+    x = np.random.default_rng(s[0]).integers(lo[layer.x_type], lo[layer.x_type] + 256,
+                                             (layer.n, layer.c_in, layer.h, layer.w))
+    w = np.random.default_rng(s[1]).integers(
+        lo[layer.w_type], lo[layer.w_type] + 256,
+        (layer.c_out, layer.c_in // layer.groups, layer.kh, layer.kw))
+    xz = int(np.random.default_rng(s[2]).integers(lo[layer.x_type], lo[layer.x_type] + 256))
+    wz = np.random.default_rng(s[3]).integers(lo[layer.w_type], lo[layer.w_type] + 256,
+                                              layer.c_out)
+    return x, w, xz, wz
