@@ -98,6 +98,7 @@ def _load():
         lib.oracle_global_pool.argtypes = [ctypes.c_int, i64, i64, dp, dp, dp]
         lib.oracle_conv_integer.argtypes = [ctypes.POINTER(_Geom), dp, dp, ctypes.c_int32, dp, dp,
                                             ctypes.c_int]
+        lib.oracle_conv2d_winograd.argtypes = [g, dp, dp, dp, dp, dp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -380,4 +381,22 @@ def conv_integer(g: Geom, x, w, x_zero=0, w_zero=0, threads=0):
                                      _p(y), threads)
     if rc:
         raise ValueError("oracle_conv_integer rejected the problem")
+    return y
+
+
+# ------------------------------------------------------------ Winograd F(2x2,3x3)
+
+def conv2d_winograd(g: Geom, x, w, b=None, r=None, threads=0):
+    """Winograd F(2x2, 3x3) in fp64 by the minimal filtering algorithm's steps
+    ("Convolutions", section 2.6; Lavin and Gray 2016): weight and input-tile
+    transforms, the sixteen products summed over input channels, the output
+    transform, then the epilogue.  3x3, stride 1, dilation 1 only."""
+    x, w, b, r = _f64(x), _f64(w), _f64(b), _f64(r)
+    shp = out_shape(g)
+    _check_shapes(g, x, w, b, r, shp, False)
+    y = np.empty(shp, np.float64)
+    rc = _load().oracle_conv2d_winograd(ctypes.byref(g._c()), _p(x), _p(w), _p(b), _p(r), _p(y),
+                                        threads)
+    if rc:
+        raise ValueError("oracle_conv2d_winograd rejected the problem")
     return y

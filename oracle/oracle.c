@@ -16,7 +16,8 @@
  *  - "Convolutions" (ml-interview-book, part 4, ch. 2), section 1
  *    "Intuition first" (worked 4x4 * 3x3 example, im2col), section 2.1
  *    (boxed output-size equation), 2.3 (MACs and params), 2.4 (convolution
- *    as a matrix multiply; col2im is the adjoint scatter-add), 2.5
+ *    as a matrix multiply; col2im is the adjoint scatter-add), 2.6
+ *    (Winograd's minimal filtering: F(2x2, 3x3) with 16 multiplies), 2.5
  *    (transposed convolution), section 6 (output_padding), exercise 3
  *    (checkerboard counts).
  *  - "Convolution, pooling and resize" (OneGpu docs), section "Layout and
@@ -632,6 +633,93 @@ int oracle_conv_integer(const oracle_geom* g, const int32_t* x, const int32_t* w
                     uint32_t low = (uint32_t)(uint64_t)acc;
                     y[((n * g->c_out + co) * ho + oh) * wo + ow] =
                         (int32_t)(low >= 0x80000000u ? (int64_t)low - 0x100000000LL : (int64_t)low);
+                }
+        }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Winograd F(2x2, 3x3) ("Convolutions", section 2.6: F(m, r) computes m   */
+/* outputs of an r-tap filter with m + r - 1 multiplies, 16 against 36 in  */
+/* 2-D, at the cost of transforms of the input tiles and the weights;      */
+/* "Convolution, pooling and resize", "Not built, with the numbers":       */
+/* sixteen batched products between the transforms)                       */
+/* ---------------------------------------------------------------------- */
+
+/* The minimal filtering algorithm of Lavin and Gray (2016) for a 3x3
+ * cross-correlation with stride 1 and dilation 1, in double:
+ *   U = G g G^T    (4x4, per output channel and input channel)
+ *   V = B^T d B    (4x4, per input channel and 4x4 input tile d, the tiles
+ *                   taken every 2 outputs; taps outside the input are 0)
+ *   M = sum over input channels of U (.) V  (the sixteen products)
+ *   Y = A^T M A    (the 2x2 outputs of the tile)
+ * with B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1],
+ *      G   = [1 0 0; 1/2 1/2 1/2; 1/2 -1/2 1/2; 0 0 1],
+ *      A^T = [1 1 1 0; 0 1 -1 -1],
+ * then bias, residual and activation as oracle_conv2d.  Groups are contiguous
+ * channel blocks.  Outputs of a tile beyond Ho or Wo are dropped.  Returns -1
+ * unless the kernel is 3x3 with stride 1 and dilation 1. */
+int oracle_conv2d_winograd(const oracle_geom* g, const double* x, const double* w,
+                           const double* b, const double* r, double* y, int threads)
+{
+    static const double BT[4][4] = {{1, 0, -1, 0}, {0, 1, 1, 0}, {0, -1, 1, 0}, {0, 1, 0, -1}};
+    static const double GM[4][3] = {{1, 0, 0}, {0.5, 0.5, 0.5}, {0.5, -0.5, 0.5}, {0, 0, 1}};
+    static const double AT[2][4] = {{1, 1, 1, 0}, {0, 1, -1, -1}};
+    int64_t ho, wo;
+    if (!geom_ok(g)) return -1;
+    if (g->kh != 3 || g->kw != 3 || g->sh != 1 || g->sw != 1 || g->dh != 1 || g->dw != 1) return -1;
+    if (oracle_conv_extent(g->h, 3, 1, 1, g->pt, g->pb, &ho) ||
+        oracle_conv_extent(g->w, 3, 1, 1, g->pl, g->pr, &wo))
+        return -1;
+    const int64_t cig = g->c_in / g->groups, cog = g->c_out / g->groups;
+    const int64_t th_n = (ho + 1) / 2, tw_n = (wo + 1) / 2;
+    set_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < g->n; ++n)
+        for (int64_t co = 0; co < g->c_out; ++co) {
+            const int64_t grp = co / cog;
+            for (int64_t th = 0; th < th_n; ++th)
+                for (int64_t tw = 0; tw < tw_n; ++tw) {
+                    double m[4][4] = {{0}};
+                    for (int64_t ci = 0; ci < cig; ++ci) {
+                        const double* gw = w + (co * cig + ci) * 9;
+                        double gg[4][3], u[4][4], d[4][4], bd[4][4], v[4][4];
+                        for (int i = 0; i < 4; ++i)      /* G g */
+                            for (int j = 0; j < 3; ++j)
+                                gg[i][j] = GM[i][0] * gw[j] + GM[i][1] * gw[3 + j] + GM[i][2] * gw[6 + j];
+                        for (int i = 0; i < 4; ++i)      /* (G g) G^T */
+                            for (int j = 0; j < 4; ++j)
+                                u[i][j] = gg[i][0] * GM[j][0] + gg[i][1] * GM[j][1] + gg[i][2] * GM[j][2];
+                        for (int i = 0; i < 4; ++i)      /* the input tile */
+                            for (int j = 0; j < 4; ++j) {
+                                int64_t ih = 2 * th - g->pt + i, iw = 2 * tw - g->pl + j;
+                                d[i][j] = (ih >= 0 && ih < g->h && iw >= 0 && iw < g->w)
+                                              ? x[((n * g->c_in + grp * cig + ci) * g->h + ih) * g->w + iw]
+                                              : 0.0;
+                            }
+                        for (int i = 0; i < 4; ++i)      /* B^T d */
+                            for (int j = 0; j < 4; ++j)
+                                bd[i][j] = BT[i][0] * d[0][j] + BT[i][1] * d[1][j] + BT[i][2] * d[2][j] + BT[i][3] * d[3][j];
+                        for (int i = 0; i < 4; ++i)      /* (B^T d) B */
+                            for (int j = 0; j < 4; ++j)
+                                v[i][j] = bd[i][0] * BT[j][0] + bd[i][1] * BT[j][1] + bd[i][2] * BT[j][2] + bd[i][3] * BT[j][3];
+                        for (int i = 0; i < 4; ++i)
+                            for (int j = 0; j < 4; ++j) m[i][j] += u[i][j] * v[i][j];
+                    }
+                    double am[2][4];
+                    for (int i = 0; i < 2; ++i)          /* A^T M */
+                        for (int j = 0; j < 4; ++j)
+                            am[i][j] = AT[i][0] * m[0][j] + AT[i][1] * m[1][j] + AT[i][2] * m[2][j] + AT[i][3] * m[3][j];
+                    for (int i = 0; i < 2; ++i)          /* (A^T M) A, then the epilogue */
+                        for (int j = 0; j < 2; ++j) {
+                            int64_t oh = 2 * th + i, ow = 2 * tw + j;
+                            if (oh >= ho || ow >= wo) continue;
+                            double acc = am[i][0] * AT[j][0] + am[i][1] * AT[j][1] + am[i][2] * AT[j][2] + am[i][3] * AT[j][3];
+                            int64_t oi = ((n * g->c_out + co) * ho + oh) * wo + ow;
+                            if (b) acc += b[co];
+                            if (r) acc += r[oi];
+                            y[oi] = oracle_activation(g->act, acc, g->alpha, g->beta);
+                        }
                 }
         }
     return 0;
