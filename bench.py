@@ -91,7 +91,7 @@ def build_problem(cf, layer):
                            layer.kw, groups=layer.groups, stride=layer.stride,
                            dilation=layer.dilation, pads=layer.pads, out_pad=layer.out_pad,
                            transpose=layer.transpose, act=layer.act, bias=layer.bias,
-                           residual=layer.residual)
+                           residual=layer.residual, variant=layer.variant)
 
 
 def time_layer(cf, torch, layer, steps, warmup, loops):

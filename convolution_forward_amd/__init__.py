@@ -30,7 +30,7 @@ AUTO_PAD = {"NOTSET": 0, "SAME_UPPER": 1, "SAME_LOWER": 2, "VALID": 3}
 VARIANTS = {
     "auto": 0, "implicit_gemm": 1, "pointwise_gemm": 2, "depthwise_direct": 3,
     "transpose_gemm_col2im": 4, "implicit_gemm_halo": 5, "implicit_gemm_rowband": 6,
-    "implicit_gemm_grouped": 7,
+    "implicit_gemm_grouped": 7, "winograd": 8,
 }
 # default activation parameters (ONNX): hard_sigmoid alpha/beta, leaky alpha
 ACT_DEFAULTS = {"hard_sigmoid": (0.2, 0.5), "leaky_relu": (0.01, 0.0)}

@@ -238,6 +238,19 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
         r.act = p->activation; r.alpha = p->act_alpha; r.beta = p->act_beta;
         e = launch_reduce(dt, r, s);
       }
+    } else if (pl.variant == CONV_VARIANT_WINOGRAD) {
+      WinoArgs a{};
+      a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc; a.u = scratch;
+      a.n = cn; a.c_in = (int)g.ci; a.h = (int)g.h; a.w = (int)g.w; a.c_out = (int)g.co;
+      a.groups = (int)g.g; a.cig = (int)g.cig; a.cog = (int)g.cog;
+      a.pt = (int)g.pt; a.pl = (int)g.pl; a.ho = (int)g.ho; a.wo = (int)g.wo;
+      a.th = (int)ceil_div(g.ho, 2); a.tw = (int)ceil_div(g.wo, 2);
+      a.tiles = cn * a.th * a.tw;
+      a.cb = pl.wino_cb;
+      a.mg_tpi = make_magic((unsigned)(a.th * a.tw));
+      a.mg_tw = make_magic((unsigned)a.tw);
+      a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      e = launch_winograd(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_GROUPED) {
       GroupedArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;

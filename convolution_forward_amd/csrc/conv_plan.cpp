@@ -55,7 +55,7 @@ int validate(const conv_problem* p, int dtype, Geo* g) {
     return CONV_ERR_ARG;
   if ((p->has_bias != 0 && p->has_bias != 1) || (p->has_residual != 0 && p->has_residual != 1))
     return CONV_ERR_ARG;
-  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_IMPLICIT_GEMM_GROUPED)
+  if (p->variant_override < CONV_VARIANT_AUTO || p->variant_override > CONV_VARIANT_WINOGRAD)
     return CONV_ERR_ARG;
   if (p->split_override < 0 || p->split_override > kMaxSplits) return CONV_ERR_ARG;
   if (p->x_off < 0 || p->w_off < 0 || p->b_off < 0 || p->r_off < 0 || p->y_off < 0)
@@ -184,6 +184,20 @@ bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
          g.sw == 2 && g.dh == 1 && g.dw == 1 && g.pt == 0 && g.pl == 0 && g.pb == 0 &&
          g.pr == 0 && g.oph == 0 && g.opw == 0 && !residual && g.w % 4 == 0 && g.w <= 128 &&
          pw_items(g.n, ceil_div(g.h * g.w, (128 / g.w) * g.w), ceil_div(4 * g.co, 128), g.ci) < (1LL << 30);
+}
+
+// Winograd F(2x2, 3x3): 16-bit operands, 3x3, stride 1, dilation 1, input
+// channels per group in whole steps of 16 (16-byte weight fragments), tile and
+// channel-tile counts inside the grid limits.
+bool winograd_applicable(const Geo& g, int dtype) {
+  if (g.transpose || !half16(dtype) || g.kh != 3 || g.kw != 3 || g.sh != 1 || g.sw != 1 ||
+      g.dh != 1 || g.dw != 1 || g.cig % 16)
+    return false;
+  int64_t tiles, t;
+  if (!mul_ok(g.n, ceil_div(g.ho, 2), &tiles) || !mul_ok(tiles, ceil_div(g.wo, 2), &tiles))
+    return false;
+  return tiles < (1LL << 31) - 64 && ceil_div(g.cog, 32) <= 65535 && g.g <= 65535 &&
+         mul_ok(16 * g.co, g.cig, &t);
 }
 
 // Depthwise output tile: whole plane when the staged input fits, else smaller
@@ -360,6 +374,16 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (ceil_div(g.co * g.kh * g.kw / g.g, IG_TILE_C) > 65535 || g.g > 65535) return CONV_ERR_SHAPE;
   } else {
     if (v == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM) return CONV_ERR_ARG;
+    if (v == CONV_VARIANT_WINOGRAD) {  // only when asked for (see conv.h)
+      if (!winograd_applicable(g, dtype) || p->split_override > 1) return CONV_ERR_ARG;
+      pl->variant = v;
+      const int64_t tiles = g.n * ceil_div(g.ho, 2) * ceil_div(g.wo, 2);
+      pl->wino_cb = ceil_div(tiles, 32) * ceil_div(g.cog, 64) * g.g >= kPlanCUs ? 2 : 1;
+      pl->scratch_per_image = (uint64_t)(16 * g.co * g.cig) * 2u;
+      pl->scratch_whole = pl->scratch_per_image;
+      pl->scratch_fixed = 1;
+      return CONV_OK;
+    }
     const bool pw_ok = pointwise_applicable(g, dtype);
     if (v == CONV_VARIANT_POINTWISE_GEMM && !pw_ok) return CONV_ERR_ARG;
     if (v == CONV_VARIANT_AUTO && pw_ok && p->split_override <= 1) v = CONV_VARIANT_POINTWISE_GEMM;
@@ -446,6 +470,7 @@ const char* variant_name(int v) {
     case CONV_VARIANT_IMPLICIT_GEMM_HALO: return "implicit_gemm_halo";
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND: return "implicit_gemm_rowband";
     case CONV_VARIANT_IMPLICIT_GEMM_GROUPED: return "implicit_gemm_grouped";
+    case CONV_VARIANT_WINOGRAD: return "winograd_f2x2_3x3";
     default: return "unknown";
   }
 }
@@ -478,7 +503,8 @@ int check_call(const conv_problem* p, int dtype, bool transpose, const void* x, 
     if (!scratch) return CONV_ERR_SCRATCH;
     if (reinterpret_cast<uintptr_t>(scratch) % 16) return CONV_ERR_ARG;
     if (scratch_bytes < pl.scratch_per_image) return CONV_ERR_SCRATCH;
-    chunk = std::min<int64_t>(g.n, (int64_t)(scratch_bytes / pl.scratch_per_image));
+    if (!pl.scratch_fixed)
+      chunk = std::min<int64_t>(g.n, (int64_t)(scratch_bytes / pl.scratch_per_image));
   }
 
   const char* xb = static_cast<const char*>(x) + p->x_off * es;
@@ -497,7 +523,8 @@ int check_call(const conv_problem* p, int dtype, bool transpose, const void* x, 
   if (overlaps(ry, rx) || overlaps(ry, rw) || (bb && overlaps(ry, rbias))) return CONV_ERR_OVERLAP;
   if (rb && overlaps(ry, rr) && !(ry.lo == rr.lo && ry.hi == rr.hi)) return CONV_ERR_OVERLAP;
   if (pl.scratch_per_image > 0) {
-    Range rs{(uintptr_t)scratch, (uintptr_t)scratch + (uint64_t)chunk * pl.scratch_per_image};
+    const uint64_t used = pl.scratch_fixed ? pl.scratch_whole : (uint64_t)chunk * pl.scratch_per_image;
+    Range rs{(uintptr_t)scratch, (uintptr_t)scratch + used};
     if (overlaps(rs, rx) || overlaps(rs, rw) || (bb && overlaps(rs, rbias)) ||
         (rb && overlaps(rs, rr)) || overlaps(rs, ry))
       return CONV_ERR_OVERLAP;
@@ -615,6 +642,9 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                  pl.dw_bh);
       else
         snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
+      break;
+    case CONV_VARIANT_WINOGRAD:
+      snprintf(tmp, sizeof tmp, "winograd_f2x2_3x3.%s.t32x%d", dn, 32 * pl.wino_cb);
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_HALO:
       if (pl.halo.rowshift)

@@ -215,7 +215,24 @@ struct Col2imArgs {
 };
 
 
+// Winograd F(2x2, 3x3): 16-bit operands, 3x3, stride 1, dilation 1.
+struct WinoArgs {
+  const void* x;
+  const void* wt;
+  const void* bias;
+  const void* res;
+  void* y;
+  void* u;               // scratch: transformed weights [16][c_out][cig], 16-bit
+  int n, c_in, h, w, c_out, groups, cig, cog, pt, pl, ho, wo;
+  int th, tw, tiles;     // 2x2 output tiles per column / row of an image, in the chunk
+  int cb;                // 32-channel blocks per workgroup (1 or 2)
+  Magic mg_tpi, mg_tw;   // divisions by th * tw and by tw
+  int act;
+  float alpha, beta;
+};
+
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
+hipError_t launch_winograd(Dtype dt, const WinoArgs& a, hipStream_t s);
 hipError_t launch_halo(Dtype dt, const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(Dtype dt, const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s);

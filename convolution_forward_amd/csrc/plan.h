@@ -51,6 +51,8 @@ struct Plan {
   int pw_tc;      // pointwise: output channels per tile
   int rb_band_rows;  // row band: output rows per workgroup
   int ct_fused;      // transpose: kernel = stride = 2 taps gathered by the GEMM epilogue
+  int scratch_fixed; // scratch does not grow with the batch (Winograd weights): no chunks
+  int wino_cb;       // Winograd: 32-channel blocks per workgroup
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -110,9 +110,20 @@ typedef enum {
     CONV_VARIANT_IMPLICIT_GEMM_ROWBAND = 6, /* stride 2, few input channels (image stems):
                                               a ring of staged input rows per output-row
                                               band, kw taps read as consecutive halves */
-    CONV_VARIANT_IMPLICIT_GEMM_GROUPED = 7 /* 8 input channels per group: the group's
+    CONV_VARIANT_IMPLICIT_GEMM_GROUPED = 7, /* 8 input channels per group: the group's
                                               padded planes staged whole, one workgroup
                                               per (image, group) */
+    CONV_VARIANT_WINOGRAD = 8  /* Winograd F(2x2, 3x3) ("Convolutions", section 2.6):
+                                  3x3, stride 1, dilation 1, 16-bit operands, input
+                                  channels per group a multiple of 16.  Never chosen by
+                                  AUTO: its transformed operands are rounded to 16 bits,
+                                  which adds rounding of cross terms that the direct sum
+                                  does not have, so its error is not bounded by
+                                  tol * sum|w*x| for every input (it meets the bound on
+                                  the tests' distributions).  Needs scratch for the
+                                  transformed weights, 16 * c_out * c_in/groups * 2 bytes,
+                                  whatever the batch (conv_scratch_size reports it as
+                                  both figures; no image chunking). */
 } conv_variant;
 
 /* The problem: shape, explicit pads, stride, dilation, groups, fused activation
@@ -131,7 +142,8 @@ typedef struct conv_problem {
     int32_t activation;             /* conv_activation */
     float act_alpha, act_beta;      /* hard_sigmoid alpha/beta; clip lo/hi; leaky alpha */
     int32_t has_bias, has_residual; /* 0/1: whether bias / residual are applied */
-    int32_t variant_override;       /* conv_variant; 0 = AUTO (tests force variants) */
+    int32_t variant_override;       /* conv_variant; 0 = AUTO; others force a variant
+                                       (CONV_ERR_ARG if it cannot run the shape) */
     int32_t split_override;         /* split-k ranges; 0 = AUTO, 1 = whole k, R > 1 forces R */
 } conv_problem;
 

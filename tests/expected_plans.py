@@ -14,6 +14,7 @@ EXPECTED_PLANS = {
     "w5b_convtranspose2x2s2_f16": "transpose_gemm_col2im.f16.fused_k2s2.t128x64",
     "x1_late3x3_512_7x7_f16": "implicit_gemm.f16.t64x64.split16",
     "x2_bottleneck3x3_bf16": "implicit_gemm_halo.bf16.rowshift.r14.n32",
+    "x3_bottleneck3x3_f16_winograd": "winograd_f2x2_3x3.f16.t32x32",
 }
 
 
@@ -22,4 +23,4 @@ def layer_problem(cf, layer):
                            layer.kw, groups=layer.groups, stride=layer.stride,
                            dilation=layer.dilation, pads=layer.pads, out_pad=layer.out_pad,
                            transpose=layer.transpose, act=layer.act, bias=layer.bias,
-                           residual=layer.residual)
+                           residual=layer.residual, variant=layer.variant)

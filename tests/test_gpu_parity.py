@@ -75,7 +75,8 @@ def test_workload_layer_full_size(name):
     _say(f"[parity-full] {name} n={layer.n} {variant}")
     inp = workloads.make_inputs(layer)
     g = geom_from_layer(layer)
-    y = run_gpu(g, layer.dtype, inp.x, inp.w, inp.b, inp.r, transpose=layer.transpose)
+    y = run_gpu(g, layer.dtype, inp.x, inp.w, inp.b, inp.r, transpose=layer.transpose,
+                variant=layer.variant)
     assert y.shape == layer.out_shape
     yr, sr = oracle_ref(g, inp.x, inp.w, inp.b, inp.r, transpose=layer.transpose)
     q = assert_parity(layer.dtype, y, yr, sr, inp.b, inp.r, what=name, act=layer.act)

@@ -58,6 +58,7 @@ class Layer:
     beta: float = 0.0
     bias: bool = True
     residual: bool = False
+    variant: str = "auto"  # a variant the caller asks for (the plan's own choice by default)
     note: str = ""
 
     @property
@@ -111,6 +112,10 @@ EXTRA_LAYERS = [
     # the bottleneck layer of workload 2 with bfloat16 operands
     Layer("x2_bottleneck3x3_bf16", 7, 0, "bf16", 32, 256, 14, 14, 256, 3, 3,
           (32, 256, 14, 14), pads=(1, 1, 1, 1), act="relu", residual=True),
+    # the same layer (same seeded inputs as workload 2) through Winograd
+    # F(2x2, 3x3), which the caller must ask for
+    Layer("x3_bottleneck3x3_f16_winograd", 2, 0, "f16", 32, 256, 14, 14, 256, 3, 3,
+          (32, 256, 14, 14), pads=(1, 1, 1, 1), act="relu", residual=True, variant="winograd"),
 ]
 
 BY_NAME = {l.name: l for l in LAYERS + EXTRA_LAYERS}
