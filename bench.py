@@ -469,6 +469,55 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def ceilings(torch):
+    """Measured ceilings of this GPU: a streaming copy (1 GiB read + 1 GiB written,
+    16-byte vectors) and register-only MFMA loops, from libconvprobe.so."""
+    path = os.path.join(ROOT, "convolution_forward_amd", "libconvprobe.so")
+    L = ctypes.CDLL(path)
+    L.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                             ctypes.c_void_p]
+    L.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                             ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e-3 / reps
+
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best_copy = 0.0
+    for per_cu in (4, 8, 16):
+        t = timed(lambda: L.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, cus * per_cu, sh), 5)
+        best_copy = max(best_copy, 2 * nbytes / t / 1e9)
+    del src, dst
+    out = torch.empty(cus * 4 * 256, dtype=torch.float32, device="cuda")
+    macs_per_iter = {0: 4 * 32 * 32 * 16, 1: 8 * 16 * 16 * 32, 2: 8 * 16 * 16 * 64}
+    names = {0: "mfma_f32_32x32x16_f16_tflops", 1: "mfma_f32_16x16x32_f16_tflops",
+             2: "mfma_i32_16x16x64_i8_tops"}
+    res = {"copy_gbs": round(best_copy, 1), "copy_bytes": 2 * nbytes}
+    iters = 4000
+    for kind in (0, 1, 2):
+        best = 0.0
+        for per_cu in (1, 2, 4):
+            blocks = cus * per_cu
+            t = timed(lambda: L.probe_mfma(kind, iters, blocks, out.data_ptr(), sh), 3)
+            best = max(best, 2 * blocks * 4 * iters * macs_per_iter[kind] / t / 1e12)
+        res[names[kind]] = round(best, 1)
+    res["compute_units"] = cus
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -481,6 +530,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure the streaming-copy and register-only MFMA ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -502,6 +553,7 @@ def main():
         return
 
     cf.lib()  # fail loudly if the native library is missing
+    ceil = ceilings(torch) if args.ceilings else None
     default = [l.name for l in workloads.LAYERS] + [l.name for l in workloads.EXTRA_LAYERS]
     names = [HEADLINE] if args.headline_only else (
         args.layers.split(",") if args.layers else default)
@@ -570,6 +622,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "configs": config_sums(results),
+        "ceilings": ceil,
         "pools": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                   for r in pools],
         "conv_integer": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}

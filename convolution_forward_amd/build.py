@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libconvfwd.so")
+# measurement probes for the benchmark (measured ceilings), a library of their own
+PROBE_SRC = "probe_ceilings.hip"
+PROBE_LIB = os.path.join(PKG, "libconvprobe.so")
 
 SOURCES = ["conv_plan.cpp", "pool_plan.cpp", "conv_host.cpp", "k_pool.hip", "k_convint.hip", "k_winograd.hip", "k_igemm.hip", "k_direct.hip", "k_halo.hip", "k_rowshift.hip", "k_pointwise.hip", "k_rowband.hip", "k_grouped.hip", "k_pointwise32.hip"]
 
@@ -46,8 +49,16 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc link failed")
     os.replace(tmp, LIB)
+    probe_obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc link failed (probe library)")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
