@@ -8,13 +8,23 @@
 //    outputs of a row, read their taps from LDS and store coalesced.  Rows
 //    outside the input are never touched: a tap is tested against the input
 //    (real), the pads (padding) or neither (beyond the padding, ceil mode).
+//  * Row-vector kernel (windows of 2 or 3 taps per axis, horizontal stride 1
+//    or 2, rows of whole 16-byte vectors): a thread owns one 16-byte vector
+//    of each input row its output row reads and the outputs whose windows
+//    start in it; the one or two elements a window reaches into the vectors
+//    beside it come from the neighbouring lanes (which own those vectors)
+//    through a lane shuffle, or from memory at the wave's two ends.  Every
+//    load of a thread is issued before any arithmetic, so a wave keeps its
+//    whole input in flight, and the outputs leave as one 8- or 16-byte
+//    nontemporal store per thread.
 //  * Direct kernel: the same per-output arithmetic with the taps read from
 //    global memory, for rows too wide to stage.
 //  * Global pools: a workgroup loads the values of up to 4096 elements (whole
 //    planes, or a 4096-element chunk of a larger plane) into LDS and reduces
 //    each plane with a fixed halving tree (pairs i and i + ceil(m/2) while
 //    m > 1); larger planes reduce their chunk results the same way.  The order
-//    depends on the plane size only.
+//    depends on the plane size only: the planes per workgroup (chosen for
+//    about 1024 workgroups) change which thread adds a pair, not the pairs.
 //
 // Max is taken over integer keys of the float32 bits (the sign-magnitude
 // order turned into two's complement order), which orders -0 below +0 and
@@ -64,7 +74,9 @@ struct PoolArgs {
   int band_rows, in_rows, n_band;
   int planes_wg, chunks;
   int vec;      // x 16-byte aligned and w % (16 / sizeof(T)) == 0: rows in 16-byte items
-  Magic mg_wo, mg_w;
+  int yvec;     // row vector: y aligned to a thread's outputs and wo a multiple of them
+  int tpr, threads;
+  Magic mg_wo, mg_w, mg_tpr, mg_ho;
   Magic mg_pairs[14];  // global tree: division by each level's pair count
 };
 
@@ -217,6 +229,216 @@ __global__ __launch_bounds__(256) void pool_band_kernel(const PoolArgs a) {
   }
 }
 
+// Row-vector kernel helpers.  Bits of element i of a thread's stretch of one
+// input row, i in [-WE, V + WE): the last word of the left neighbour's
+// vector, the thread's own four words, the first word of the right
+// neighbour's.
+template <typename T>
+__device__ __forceinline__ unsigned stretch_bits(const unsigned (&d)[4], unsigned lw, unsigned rw,
+                                                 int i) {
+  constexpr int V = 16 / sizeof(T), WE = 4 / sizeof(T);
+  unsigned w;
+  int k;
+  if (i < 0) { w = lw; k = i + WE; }
+  else if (i < V) { w = d[i / WE]; k = i % WE; }
+  else { w = rw; k = i - V; }
+  return sizeof(T) == 4 ? w : (w >> (16 * k)) & 0xFFFFu;
+}
+
+// Max key of an element's bits: the sign-magnitude order as two's complement
+// (-0 below +0); NaN, like a tap outside the input, gets INT_MIN.
+template <typename T>
+__device__ __forceinline__ int bits_key(unsigned b, bool ok) {
+  if constexpr (sizeof(T) == 4) {
+    const int s = (int)b;
+    const bool nan = (b & 0x7FFFFFFFu) > 0x7F800000u;
+    return ok && !nan ? s ^ ((s >> 31) & 0x7FFFFFFF) : INT_MIN;
+  } else {
+    constexpr unsigned kInf = std::is_same_v<T, _Float16> ? 0x7C00u : 0x7F80u;
+    const int s = (int)(short)b;
+    const bool nan = (b & 0x7FFFu) > kInf;
+    return ok && !nan ? s ^ ((s >> 31) & 0x7FFF) : INT_MIN;
+  }
+}
+
+// Bits of the max from its key; m == INT_MIN: NaN if the window had a real
+// tap (all of them NaN), else the type's lowest finite value.
+template <typename T>
+__device__ __forceinline__ unsigned key_bits(int m, bool real) {
+  if constexpr (sizeof(T) == 4) {
+    return m != INT_MIN ? (unsigned)(m ^ ((m >> 31) & 0x7FFFFFFF))
+                        : (real ? 0x7FC00000u : 0xFF7FFFFFu);
+  } else {
+    constexpr bool F16 = std::is_same_v<T, _Float16>;
+    return m != INT_MIN ? (unsigned)(m ^ ((m >> 31) & 0x7FFF)) & 0xFFFFu
+                        : (real ? (F16 ? 0x7E00u : 0x7FC0u) : (F16 ? 0xFBFFu : 0xFF7Fu));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float bits_f32(unsigned b) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float(b);
+  else return to_f32(__builtin_bit_cast(T, (unsigned short)b));
+}
+
+// PL: the left pad (the window of output o starts at element o * SW - PL of
+// the thread's stretch).  Branch-free apart from the loads at the wave's ends:
+// every load reads a clamped, valid address and taps outside the input are
+// masked when the keys or terms are formed.
+template <typename T, bool AVG, int KH, int KW, int SW, int PL>
+__global__ __launch_bounds__(256) void pool_rowvec_kernel(const PoolArgs a) {
+  constexpr int V = 16 / sizeof(T);   // elements per vector
+  constexpr int WE = 4 / sizeof(T);   // elements per 32-bit word
+  constexpr int OPT = V / SW;         // outputs per thread
+  constexpr int NC = (OPT - 1) * SW + KW;  // columns the thread's windows cover
+  static_assert(PL <= WE && NC - PL <= V + WE, "window reach beyond the neighbour words");
+  const int lane = threadIdx.x & 63;
+  const int t_raw = blockIdx.x * 256 + threadIdx.x;
+  const bool live = t_raw < a.threads;
+  const int t = live ? t_raw : a.threads - 1;  // dead lanes repeat the last thread
+  const int row = (int)mdiv((unsigned)t, a.mg_tpr);
+  const int j = t - row * a.tpr;
+  const int plane = (int)mdiv((unsigned)row, a.mg_ho);
+  const int oh = row - plane * a.ho;
+  const int col0 = j * V;
+  const int colc = min(col0, a.w - V);  // clamped: a valid vector of the row
+  const int ih0 = oh * a.sh - a.pt;
+  const T* __restrict__ xp = static_cast<const T*>(a.x) + (long long)plane * a.h * a.w;
+
+  unsigned d[KH][4], lw[KH], rw[KH];
+  bool rok[KH];
+#pragma unroll
+  for (int kh = 0; kh < KH; ++kh) rok[kh] = (unsigned)(ih0 + kh) < (unsigned)a.h;
+  if (a.vec) {
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      const int ihc = min(max(ih0 + kh, 0), a.h - 1);
+      const u4 v = *reinterpret_cast<const u4*>(xp + (long long)ihc * a.w + colc);
+      d[kh][0] = v[0]; d[kh][1] = v[1]; d[kh][2] = v[2]; d[kh][3] = v[3];
+    }
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      lw[kh] = __shfl_up(d[kh][3], 1);
+      rw[kh] = __shfl_down(d[kh][0], 1);
+    }
+    // at the wave's two ends the neighbouring vector of the row is another
+    // wave's: its word comes from memory (a clamped address; columns outside
+    // the row are masked below)
+    if (lane == 0 || lane == 63) {
+      const int cw = min(max(lane == 0 ? col0 - WE : col0 + V, 0), a.w - WE);
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) {
+        const int ihc = min(max(ih0 + kh, 0), a.h - 1);
+        const unsigned v = *reinterpret_cast<const unsigned*>(xp + (long long)ihc * a.w + cw);
+        if (lane == 0) lw[kh] = v;
+        else rw[kh] = v;
+      }
+    }
+  } else {  // rows not 16-byte aligned: element loads at clamped addresses
+    typedef std::conditional_t<sizeof(T) == 4, unsigned, unsigned short> bits_t;
+    const bits_t* xb = reinterpret_cast<const bits_t*>(xp);
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      const long long rb = (long long)min(max(ih0 + kh, 0), a.h - 1) * a.w;
+      unsigned e[V + 2 * WE];
+#pragma unroll
+      for (int i = 0; i < V + 2 * WE; ++i)
+        e[i] = xb[rb + min(max(col0 - WE + i, 0), a.w - 1)];
+      if constexpr (WE == 1) {
+        lw[kh] = e[0];
+        for (int k = 0; k < 4; ++k) d[kh][k] = e[1 + k];
+        rw[kh] = e[V + 1];
+      } else {
+        lw[kh] = e[0] | (e[1] << 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d[kh][k] = e[2 + 2 * k] | (e[3 + 2 * k] << 16);
+        rw[kh] = e[V + 2] | (e[V + 3] << 16);
+      }
+    }
+  }
+
+  // columns: real (inside the row) and inside the padded extent
+  bool vc[NC], pc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int iw = col0 + c - PL;
+    vc[c] = (unsigned)iw < (unsigned)a.w;
+    pc[c] = iw >= -a.pl && iw < a.w + a.pr;
+  }
+  int rh = 0, ph = 0;
+#pragma unroll
+  for (int kh = 0; kh < KH; ++kh) {
+    rh += rok[kh];
+    ph += (ih0 + kh >= -a.pt && ih0 + kh < a.h + a.pb);
+  }
+  unsigned ob[OPT];  // output bits
+  if constexpr (AVG) {
+    float cs[NC];  // column sums over the window's rows, in row order
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      cs[c] = 0.0f;
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) {
+        const float v = bits_f32<T>(stretch_bits<T>(d[kh], lw[kh], rw[kh], c - PL));
+        cs[c] += rok[kh] & vc[c] ? v : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int o = 0; o < OPT; ++o) {
+      float sum = 0.0f;
+      int rwn = 0, pwn = 0;
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) {
+        sum += cs[o * SW + kw];
+        rwn += vc[o * SW + kw];
+        pwn += pc[o * SW + kw];
+      }
+      const int cnt = a.cip ? ph * pwn : rh * rwn;
+      const T r = from_f32<T>(sum / (float)cnt);
+      if constexpr (sizeof(T) == 4) ob[o] = __float_as_uint(r);
+      else ob[o] = __builtin_bit_cast(unsigned short, r);
+    }
+  } else {
+    int cm[NC];  // column maxima over the window's rows
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      cm[c] = INT_MIN;
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh)
+        cm[c] = max(cm[c], bits_key<T>(stretch_bits<T>(d[kh], lw[kh], rw[kh], c - PL),
+                                       rok[kh] & vc[c]));
+    }
+#pragma unroll
+    for (int o = 0; o < OPT; ++o) {
+      int m = INT_MIN, rwn = 0;
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) {
+        m = max(m, cm[o * SW + kw]);
+        rwn += vc[o * SW + kw];
+      }
+      ob[o] = key_bits<T>(m, rh * rwn > 0);
+    }
+  }
+  if (!live) return;
+  T* __restrict__ yp = static_cast<T*>(a.y) + (long long)row * a.wo + j * OPT;
+  if (a.yvec) {  // wo a multiple of OPT and y aligned: one store of OPT outputs
+    constexpr int NW = OPT * sizeof(T) / 4;
+    typedef unsigned uw __attribute__((ext_vector_type(NW)));
+    uw v;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) v[k] = sizeof(T) == 4 ? ob[k] : ob[2 * k] | (ob[2 * k + 1] << 16);
+    __builtin_nontemporal_store(v, reinterpret_cast<uw*>(yp));
+  } else {
+#pragma unroll
+    for (int o = 0; o < OPT; ++o)
+      if (j * OPT + o < a.wo) {
+        if constexpr (sizeof(T) == 4) yp[o] = __uint_as_float(ob[o]);
+        else yp[o] = __builtin_bit_cast(T, (unsigned short)ob[o]);
+      }
+  }
+}
+
 template <typename T, bool AVG>
 __global__ __launch_bounds__(256) void pool_direct_kernel(const PoolArgs a) {
   const long long total = (long long)a.planes * a.ho * a.wo;
@@ -309,11 +531,6 @@ __global__ __launch_bounds__(256) void pool_global_kernel(const PoolArgs a) {
     const int np = min(a.planes_wg, a.planes - p0);
     load_run<T, AVG>(x + (long long)p0 * hw, gsm, np * hw);
     __syncthreads();
-    if (a.planes_wg == 256) {  // small planes: one thread per plane, no barrier
-      if ((int)threadIdx.x < np)
-        y[p0 + threadIdx.x] = global_result<T, AVG>(tree_serial<AVG>(gsm + threadIdx.x * hw, hw), inv_hw);
-      return;
-    }
     tree<AVG>(gsm, np, hw, hw, a.mg_pairs);
     if ((int)threadIdx.x < np) y[p0 + threadIdx.x] = global_result<T, AVG>(gsm[threadIdx.x * hw], inv_hw);
     return;
@@ -348,6 +565,48 @@ void launch_band(const PoolArgs& a, dim3 grid, size_t lds, hipStream_t s) {
     hipLaunchKernelGGL((pool_band_kernel<T, AVG, 0>), grid, dim3(256), lds, s, a);
 }
 
+// The planner takes the row-vector kernel only where the window's reach
+// beyond the thread's vector is at most one word on each side, which is
+// exactly the set of instantiations below; anything else is refused.
+template <typename T, int KW, int SW, int PL>
+constexpr bool rowvec_fits() {
+  constexpr int V = 16 / sizeof(T), WE = 4 / sizeof(T);
+  return PL <= WE && KW - SW - PL <= WE && V % SW == 0;
+}
+
+template <typename T, bool AVG, int KH, int KW, int SW, int PL>
+bool launch_rowvec_p(const PoolArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (rowvec_fits<T, KW, SW, PL>()) {
+    hipLaunchKernelGGL((pool_rowvec_kernel<T, AVG, KH, KW, SW, PL>), grid, dim3(256), 0, s, a);
+    return true;
+  }
+  return false;
+}
+
+template <typename T, bool AVG, int KH, int KW, int SW>
+bool launch_rowvec_s(const PoolArgs& a, dim3 grid, hipStream_t s) {
+  if (a.pl == 0) return launch_rowvec_p<T, AVG, KH, KW, SW, 0>(a, grid, s);
+  if (a.pl == 1) return launch_rowvec_p<T, AVG, KH, KW, SW, 1>(a, grid, s);
+  if (a.pl == 2) return launch_rowvec_p<T, AVG, KH, KW, SW, 2>(a, grid, s);
+  return false;
+}
+
+template <typename T, bool AVG, int KH, int KW>
+bool launch_rowvec_k(const PoolArgs& a, dim3 grid, hipStream_t s) {
+  if (a.sw == 1) return launch_rowvec_s<T, AVG, KH, KW, 1>(a, grid, s);
+  if (a.sw == 2) return launch_rowvec_s<T, AVG, KH, KW, 2>(a, grid, s);
+  return false;
+}
+
+template <typename T, bool AVG>
+bool launch_rowvec(const PoolArgs& a, dim3 grid, hipStream_t s) {
+  if (a.kh == 3 && a.kw == 3) return launch_rowvec_k<T, AVG, 3, 3>(a, grid, s);
+  if (a.kh == 2 && a.kw == 2) return launch_rowvec_k<T, AVG, 2, 2>(a, grid, s);
+  if (a.kh == 3 && a.kw == 2) return launch_rowvec_k<T, AVG, 3, 2>(a, grid, s);
+  if (a.kh == 2 && a.kw == 3) return launch_rowvec_k<T, AVG, 2, 3>(a, grid, s);
+  return false;
+}
+
 template <typename T>
 hipError_t launch_pool_t(const PoolGeo& g, const PoolPlan& pl, const PoolArgs& a, hipStream_t s) {
   const bool avg = g.kind == POOL_AVERAGE || g.kind == POOL_GLOBAL_AVERAGE;
@@ -357,6 +616,10 @@ hipError_t launch_pool_t(const PoolGeo& g, const PoolPlan& pl, const PoolArgs& a
     const size_t lds = pl.chunks > 1 ? 2 * kPoolChunk * 4 : (size_t)a.planes_wg * g.h * g.w * 4;
     if (avg) hipLaunchKernelGGL((pool_global_kernel<T, true>), dim3(grid), dim3(256), lds, s, a);
     else hipLaunchKernelGGL((pool_global_kernel<T, false>), dim3(grid), dim3(256), lds, s, a);
+  } else if (pl.variant == POOLV_ROWVEC) {
+    const dim3 grid((unsigned)((a.threads + 255) / 256));
+    const bool ok = avg ? launch_rowvec<T, true>(a, grid, s) : launch_rowvec<T, false>(a, grid, s);
+    if (!ok) return hipErrorInvalidValue;
   } else if (pl.variant == POOLV_BAND) {
     const dim3 grid((unsigned)((long long)a.planes * a.n_band));
     const size_t lds = (size_t)a.in_rows * a.w * sizeof(float);
@@ -400,6 +663,14 @@ extern "C" int pool_forward(const pool_problem* p, int dtype, const void* x, voi
   a.vec = reinterpret_cast<uintptr_t>(a.x) % 16 == 0 && (g.w * es) % 16 == 0;
   a.mg_wo = make_magic((unsigned)g.wo);
   a.mg_w = make_magic((unsigned)g.w);
+  if (pl.variant == POOLV_ROWVEC) {
+    const int64_t opt = 16 / es / g.sw;
+    a.tpr = pl.tpr;
+    a.threads = (int)pl.threads;
+    a.mg_tpr = make_magic((unsigned)pl.tpr);
+    a.mg_ho = make_magic((unsigned)g.ho);
+    a.yvec = reinterpret_cast<uintptr_t>(a.y) % (uintptr_t)(opt * es) == 0 && g.wo % opt == 0;
+  }
   {  // the tree's levels over a full run (a plane, or a 4096-element chunk)
     int m = (int)(pl.chunks > 1 ? kPoolChunk : g.h * g.w), l = 0;
     while (m > 1 && l < 14) {

@@ -51,6 +51,7 @@ int pool_validate(const pool_problem* p, int dtype, PoolGeo* out) {
   PoolGeo g{};
   g.n = p->n; g.c = p->c; g.h = p->h; g.w = p->w;
   g.kind = p->kind; g.ceil_mode = p->ceil_mode; g.cip = p->count_include_pad;
+  g.es = (int)dtype_size(dtype);
   if (g.n < 1 || g.c < 1 || g.h < 1 || g.w < 1) return CONV_ERR_SHAPE;
   if (g.n > kLim || g.c > kLim || g.h > kLim || g.w > kLim) return CONV_ERR_SHAPE;
   const bool global = g.kind == POOL_GLOBAL_MAX || g.kind == POOL_GLOBAL_AVERAGE;
@@ -90,16 +91,33 @@ int pool_validate(const pool_problem* p, int dtype, PoolGeo* out) {
   return CONV_OK;
 }
 
+bool pool_rowvec_applies(const PoolGeo& g) {
+  if (g.kind != POOL_MAX && g.kind != POOL_AVERAGE) return false;
+  if (g.kh < 2 || g.kh > 3 || g.kw < 2 || g.kw > 3 || g.sw < 1 || g.sw > 2) return false;
+  if (g.dh != 1 || g.dw != 1) return false;
+  const int64_t v = 16 / g.es, word = 4 / g.es;  // elements per vector and per 32-bit word
+  if (g.w % v != 0) return false;
+  // left reach pl, right reach kw - sw - pl beyond the thread's vector
+  if (g.pl > word || g.kw - g.sw - g.pl > word) return false;
+  const int64_t opt = v / g.sw, tpr = ceil_div(g.wo, opt);
+  return tpr * v >= g.w;  // every real column belongs to some thread of the row
+}
+
 int pool_make_plan(const PoolGeo& g, PoolPlan* pl) {
   memset(pl, 0, sizeof *pl);
   if (g.kind == POOL_GLOBAL_MAX || g.kind == POOL_GLOBAL_AVERAGE) {
     pl->variant = POOLV_GLOBAL;
-    const int64_t hw = g.h * g.w;
-    if (hw <= 64) {  // one thread per plane, 256 planes (at most 64 KiB of LDS)
-      pl->planes_wg = 256;
-      pl->chunks = 1;
-    } else if (hw <= kPoolChunk) {
-      pl->planes_wg = (int)std::min<int64_t>(kPoolChunk / hw, 255);
+    const int64_t hw = g.h * g.w, planes = g.n * g.c;
+    if (hw <= kPoolChunk) {
+      // 256 / P lanes per plane (a power of two, at most 64): about 32 pairs
+      // per lane on the first level, then fewer planes per workgroup until
+      // the grid has about 1024 workgroups; the LDS holds P planes
+      int64_t lanes = 1;
+      while (lanes < 64 && lanes * 32 < hw) lanes *= 2;
+      while (lanes < 64 && ceil_div(planes, 256 / lanes) < 1024) lanes *= 2;
+      int64_t P = 256 / lanes;
+      while (P > 1 && P * hw > kPoolChunk) P /= 2;
+      pl->planes_wg = (int)P;
       pl->chunks = 1;
     } else {
       pl->planes_wg = 1;
@@ -108,6 +126,16 @@ int pool_make_plan(const PoolGeo& g, PoolPlan* pl) {
       pl->chunks = (int)ch;
     }
     return CONV_OK;
+  }
+  if (pool_rowvec_applies(g)) {
+    const int64_t opt = 16 / g.es / g.sw;
+    int64_t t;
+    if (mulok(g.n * g.c, g.ho, &t) && mulok(t, ceil_div(g.wo, opt), &t) && t <= kLim) {
+      pl->variant = POOLV_ROWVEC;
+      pl->tpr = (int)ceil_div(g.wo, opt);
+      pl->threads = t;
+      return CONV_OK;
+    }
   }
   // band: output rows per workgroup such that the staged input rows fit the
   // LDS budget as float32 and each workgroup has a few hundred outputs
@@ -188,6 +216,8 @@ int pool_describe_variant(const pool_problem* p, int dtype, char* buf, uint64_t 
   char tmp[96];
   if (pl.variant == POOLV_BAND)
     snprintf(tmp, sizeof tmp, "pool.%s.%s.band%d", kinds[g.kind], dn, pl.band_rows);
+  else if (pl.variant == POOLV_ROWVEC)
+    snprintf(tmp, sizeof tmp, "pool.%s.%s.rowvec%d", kinds[g.kind], dn, (int)(16 / g.es / g.sw));
   else if (pl.variant == POOLV_DIRECT)
     snprintf(tmp, sizeof tmp, "pool.%s.%s.direct", kinds[g.kind], dn);
   else if (pl.chunks > 1)

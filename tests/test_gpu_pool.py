@@ -148,6 +148,46 @@ def test_pool_random_geometries(seed):
     check(g, kind, dtype, x)
 
 
+def _sweep_rowvec(seed):
+    """A random geometry the row-vector kernel takes: windows of 2 or 3 taps,
+    horizontal stride 1 or 2, rows of whole 16-byte vectors, a left pad and a
+    right reach of at most one 32-bit word."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = ("f32", "f16", "bf16")[seed % 3]
+    v, we = (4, 1) if dtype == "f32" else (8, 2)
+    while True:
+        kh, kw, sw = int(rng.integers(2, 4)), int(rng.integers(2, 4)), int(rng.integers(1, 3))
+        pl = int(rng.integers(0, we + 1))
+        if kw - sw - pl > we:
+            continue
+        g = oracle.PoolGeom(int(rng.integers(1, 4)), int(rng.integers(1, 6)),
+                            int(rng.integers(1, 21)), v * int(rng.integers(1, 9)), kh, kw,
+                            int(rng.integers(1, 4)), sw, 1, 1, int(rng.integers(0, 3)), pl,
+                            int(rng.integers(0, 3)), int(rng.integers(0, 3)),
+                            ceil_mode=bool(rng.integers(0, 2)),
+                            count_include_pad=bool(rng.integers(0, 2)))
+        try:
+            _, _, _, wo = oracle.pool_out_shape(g)
+        except ValueError:
+            continue
+        if -(-wo // (v // sw)) * v >= g.w:
+            return g, dtype, ("max", "average")[(seed // 3) % 2]
+
+
+@pytest.mark.parametrize("seed", range(36))
+def test_pool_rowvec_geometries(seed):
+    """The row-vector kernel over random geometries (several waves per row
+    block, so that neighbour columns cross wave ends), with x and y at element
+    offsets that break the vector alignment on every third case."""
+    g, dtype, kind = _sweep_rowvec(seed)
+    p = _problem(g, kind)
+    assert ".rowvec" in cf.pool_describe_variant(p, dtype), cf.pool_describe_variant(p, dtype)
+    offsets = ((0, 0), (1, 0), (0, 3))[seed % 3]
+    _say(f"[pool rowvec {seed}] {kind} {dtype} {offsets} {g}")
+    x = _q(np.random.default_rng(seed + 11).uniform(-2, 2, (g.n, g.c, g.h, g.w)), dtype)
+    check(g, kind, dtype, x, offsets=offsets)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_pool_special_values(dtype):
     """NaN taps skipped unless all are NaN, -0 below +0, infinities, and windows
@@ -185,10 +225,12 @@ def test_pool_special_values(dtype):
 
 def test_pool_direct_kernel_wide_rows():
     for kind in ("max", "average"):
-        g = oracle.PoolGeom(1, 2, 5, 6000, 3, 3, 1, 2, pt=1, pl=1, pb=1, pr=1)
+        # 6001 columns: not whole vectors (no row-vector kernel), and three
+        # rows of them do not fit the band kernel's LDS
+        g = oracle.PoolGeom(1, 2, 5, 6001, 3, 3, 1, 2, pt=1, pl=1, pb=1, pr=1)
         p = _problem(g, kind)
         assert cf.pool_describe_variant(p, "f32").endswith(".direct")
-        x = np.random.default_rng(1).uniform(-1, 1, (1, 2, 5, 6000)).astype(np.float32)
+        x = np.random.default_rng(1).uniform(-1, 1, (1, 2, 5, 6001)).astype(np.float32)
         check(g, kind, "f32", x)
 
 

@@ -96,11 +96,26 @@ def test_bad_enums_pointers_and_overlap():
 def test_variant_names():
     p = cf.make_pool_problem(32, 64, 112, 112, "max", kernel=(3, 3), stride=(2, 2),
                              pads=(1, 1, 1, 1))
-    assert cf.pool_describe_variant(p, "f16").startswith("pool.max.f16.band")
+    assert cf.pool_describe_variant(p, "f16") == "pool.max.f16.rowvec4"
+    # 3x3 stride 1 on rows of whole vectors: 8 (f16) or 4 (f32) outputs a thread
+    p = cf.make_pool_problem(2, 3, 16, 16, "average", kernel=(3, 3), pads=(1, 1, 1, 1))
+    assert cf.pool_describe_variant(p, "f16") == "pool.average.f16.rowvec8"
+    assert cf.pool_describe_variant(p, "f32") == "pool.average.f32.rowvec4"
+    # rows that are not whole 16-byte vectors, dilation, a wide left pad or a
+    # large window: the band kernel
+    for kw in ({"kernel": (3, 3), "stride": (2, 2), "w": 113},
+               {"kernel": (3, 3), "dilation": (2, 2)},
+               {"kernel": (3, 3), "pads": (2, 2, 2, 2)},
+               {"kernel": (5, 5)}):
+        w = kw.pop("w", 112)
+        p = cf.make_pool_problem(32, 64, 112, w, "max", **kw)
+        assert cf.pool_describe_variant(p, "f32").startswith("pool.max.f32.band"), kw
     # a row too wide to stage three input rows in 64 KiB: the direct kernel
     p = cf.make_pool_problem(1, 1, 4, 6000, "average", kernel=(3, 3))
     assert cf.pool_describe_variant(p, "f32") == "pool.average.f32.direct"
     p = cf.make_pool_problem(32, 2048, 7, 7, "global_average")
-    assert cf.pool_describe_variant(p, "bf16") == "pool.global_average.bf16.tree.planes256"
+    assert cf.pool_describe_variant(p, "bf16") == "pool.global_average.bf16.tree.planes64"
+    p = cf.make_pool_problem(64, 80, 14, 14, "global_max")
+    assert cf.pool_describe_variant(p, "f32") == "pool.global_max.f32.tree.planes4"
     p = cf.make_pool_problem(2, 3, 100, 100, "global_max")
     assert cf.pool_describe_variant(p, "f32") == "pool.global_max.f32.tree.chunks3"
