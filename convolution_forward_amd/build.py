@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libconvfwd.so")
 PROBE_SRC = "probe_ceilings.hip"
 PROBE_LIB = os.path.join(PKG, "libconvprobe.so")
 
-SOURCES = ["conv_plan.cpp", "pool_plan.cpp", "conv_host.cpp", "k_pool.hip", "k_convint.hip", "k_winograd.hip", "k_igemm.hip", "k_direct.hip", "k_halo.hip", "k_rowshift.hip", "k_pointwise.hip", "k_rowband.hip", "k_grouped.hip", "k_pointwise32.hip"]
+SOURCES = ["conv_plan.cpp", "pool_plan.cpp", "conv_host.cpp", "k_pool.hip", "k_convint.hip", "k_convint_rs.hip", "k_winograd.hip", "k_igemm.hip", "k_direct.hip", "k_halo.hip", "k_rowshift.hip", "k_pointwise.hip", "k_rowband.hip", "k_grouped.hip", "k_pointwise32.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

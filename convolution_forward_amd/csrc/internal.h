@@ -233,6 +233,23 @@ struct WinoArgs {
 
 hipError_t launch_igemm(Dtype dt, const IgemmArgs& a, hipStream_t s);
 hipError_t launch_winograd(Dtype dt, const WinoArgs& a, hipStream_t s);
+
+// ConvInteger on the row-shift kernel (3x3, stride 1, rows of at most 14
+// outputs, channels per group a multiple of 128).  Pointers include the
+// problem's offsets; xzp / wzp may be null (zero).
+struct ConvIntRsArgs {
+  const unsigned char* x;
+  const unsigned char* wt;
+  const unsigned char* xzp;
+  const unsigned char* wzp;
+  int wz_per_channel;
+  int* y;
+  int n, c_in, h, w, c_out, groups, cig, cog, pt, pl, ho, wo;
+  int n_ct;              // 32-channel tiles per group
+  int xvec, wvec, yvec;  // x planes of whole 4-byte groups; weights 16-byte aligned; y tiles of whole 16-byte vectors
+  Magic mg_nct, mg_n, mg_g4, mg_w, mg_howo, mg_wo;
+};
+hipError_t launch_convint_rowshift(const ConvIntRsArgs& a, bool xu, bool wu, hipStream_t s);
 hipError_t launch_halo(Dtype dt, const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(Dtype dt, const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s);

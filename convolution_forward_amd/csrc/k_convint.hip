@@ -22,6 +22,8 @@
 //
 // Tile: 64 pixels x 64 output channels, 4 waves of 32 x 32 (2 x 2 blocks of
 // 16 x 16), k-blocks of 64 taps double-buffered through registers and LDS.
+// 3x3 stride-1 layers on narrow images take the row-shift kernel instead
+// (k_convint_rs.hip).
 #include <stdio.h>
 #include <string.h>
 
@@ -262,6 +264,15 @@ int convint_validate(const conv_problem* p, int x_type, int w_type, Geo* g) {
   return CONV_OK;
 }
 
+// The row-shift kernel: 3x3, stride 1, no dilation, output rows and columns
+// at most 14, channels per group a multiple of 128 (one stage: 4 waves x 32)
+// and at most 14563 (the MFMA sums stay inside int32: 9 * 14563 * 2^14 < 2^31).
+bool convint_rowshift_applies(const Geo& g) {
+  return g.kh == 3 && g.kw == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 &&
+         g.cig % 128 == 0 && g.cig <= 14563 && g.ho <= 14 && g.wo <= 14 &&
+         ceil_div(g.cog, 32) * g.n * g.g <= 2147483647LL;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,8 +284,12 @@ int conv_integer_describe_variant(const conv_problem* p, int x_type, int w_type,
   const int st = convint_validate(p, x_type, w_type, &g);
   if (st) return st;
   char tmp[64];
-  snprintf(tmp, sizeof tmp, "conv_integer.%s%s.implicit_gemm.i8mfma.t64x64",
-           x_type == CONVI_U8 ? "u8" : "i8", w_type == CONVI_U8 ? "u8" : "i8");
+  if (convint_rowshift_applies(g))
+    snprintf(tmp, sizeof tmp, "conv_integer.%s%s.rowshift.r%d.i8mfma32",
+             x_type == CONVI_U8 ? "u8" : "i8", w_type == CONVI_U8 ? "u8" : "i8", g.ho <= 8 ? 8 : 14);
+  else
+    snprintf(tmp, sizeof tmp, "conv_integer.%s%s.implicit_gemm.i8mfma.t64x64",
+             x_type == CONVI_U8 ? "u8" : "i8", w_type == CONVI_U8 ? "u8" : "i8");
   const size_t need = strlen(tmp) + 1;
   if (len < need) return CONV_ERR_ARG;
   memcpy(buf, tmp, need);
@@ -307,6 +322,35 @@ int conv_integer_forward(const conv_problem* p, int x_type, int w_type, const vo
   if (st) return st;
   Geo g;
   convint_validate(p, x_type, w_type, &g);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool xu = x_type == CONVI_U8, wu = w_type == CONVI_U8;
+  if (convint_rowshift_applies(g)) {
+    ConvIntRsArgs r{};
+    r.x = static_cast<const unsigned char*>(x) + p->x_off;
+    r.wt = static_cast<const unsigned char*>(w) + p->w_off;
+    r.xzp = static_cast<const unsigned char*>(x_zero);
+    r.wzp = static_cast<const unsigned char*>(w_zero);
+    r.wz_per_channel = w_zero_per_channel;
+    r.y = static_cast<int*>(y) + p->y_off;
+    r.n = (int)g.n; r.c_in = (int)g.ci; r.h = (int)g.h; r.w = (int)g.w; r.c_out = (int)g.co;
+    r.groups = (int)g.g; r.cig = (int)g.cig; r.cog = (int)g.cog;
+    r.pt = (int)g.pt; r.pl = (int)g.pl; r.ho = (int)g.ho; r.wo = (int)g.wo;
+    r.n_ct = (int)ceil_div(g.cog, 32);
+    const int64_t hw = g.h * g.w, howo = g.ho * g.wo;
+    // 4-byte loads of whole 4-pixel groups: every plane starts 4-byte aligned
+    r.xvec = reinterpret_cast<uintptr_t>(r.x) % 4 == 0 && hw % 4 == 0;
+    r.wvec = reinterpret_cast<uintptr_t>(r.wt) % 16 == 0;  // rows of cig * 9, a multiple of 16
+    // every tile starts 16-byte aligned and holds whole 4-int vectors
+    r.yvec = reinterpret_cast<uintptr_t>(r.y) % 16 == 0 &&
+             (howo % 4 == 0 || (g.cog % 4 == 0 && g.co % 4 == 0));
+    r.mg_nct = make_magic((unsigned)r.n_ct);
+    r.mg_n = make_magic((unsigned)g.n);
+    r.mg_g4 = make_magic((unsigned)((hw + 3) / 4));
+    r.mg_w = make_magic((unsigned)g.w);
+    r.mg_howo = make_magic((unsigned)howo);
+    r.mg_wo = make_magic((unsigned)g.wo);
+    return launch_convint_rowshift(r, xu, wu, s) == hipSuccess ? CONV_OK : CONV_ERR_DEVICE;
+  }
   ConvIntArgs a{};
   a.x = static_cast<const unsigned char*>(x) + p->x_off;
   a.w = static_cast<const unsigned char*>(w) + p->w_off;
@@ -324,8 +368,6 @@ int conv_integer_forward(const conv_problem* p, int x_type, int w_type, const vo
   a.wvec = reinterpret_cast<uintptr_t>(a.w) % 16 == 0 && a.kg % 16 == 0;
   const dim3 grid((unsigned)ceil_div(a.pix, CI_TILE), (unsigned)ceil_div(a.cog, CI_TILE),
                   (unsigned)a.groups);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool xu = x_type == CONVI_U8, wu = w_type == CONVI_U8;
   if (xu && wu) hipLaunchKernelGGL((convint_kernel<true, true>), grid, dim3(256), 0, s, a);
   else if (xu) hipLaunchKernelGGL((convint_kernel<true, false>), grid, dim3(256), 0, s, a);
   else if (wu) hipLaunchKernelGGL((convint_kernel<false, true>), grid, dim3(256), 0, s, a);

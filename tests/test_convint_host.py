@@ -23,6 +23,17 @@ def test_good_and_names():
         for wt in ("u8", "i8"):
             assert cf.conv_integer_describe_variant(_p(), xt, wt) == \
                 f"conv_integer.{xt}{wt}.implicit_gemm.i8mfma.t64x64"
+    # 3x3 stride 1, rows of at most 14 outputs, 128k channels per group: row shift
+    p = cf.make_problem(32, 256, 14, 14, 256, 3, 3, pads=(1, 1, 1, 1))
+    assert cf.conv_integer_describe_variant(p, "u8", "i8") == "conv_integer.u8i8.rowshift.r14.i8mfma32"
+    p = cf.make_problem(2, 512, 7, 7, 64, 3, 3, pads=(1, 1, 1, 1), groups=2)
+    assert cf.conv_integer_describe_variant(p, "i8", "i8") == "conv_integer.i8i8.rowshift.r8.i8mfma32"
+    for kw in (dict(c_in=192), dict(h=15, w=15), dict(stride=(2, 2)), dict(dilation=(2, 2))):
+        a = dict(c_in=256, h=14, w=14, stride=(1, 1), dilation=(1, 1))
+        a.update(kw)
+        p = cf.make_problem(2, a["c_in"], a["h"], a["w"], 64, 3, 3, pads=(1, 1, 1, 1),
+                            stride=a["stride"], dilation=a["dilation"])
+        assert cf.conv_integer_describe_variant(p, "u8", "u8").endswith("implicit_gemm.i8mfma.t64x64"), kw
 
 
 @pytest.mark.parametrize("kw", [dict(act="relu"), dict(bias=True), dict(residual=True),

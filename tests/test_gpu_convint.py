@@ -123,6 +123,40 @@ def test_long_reduction_flushes_accumulator():
     check(g, "u8", "i8", x, w, 0, np.array([127, 0, -3]), 1)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_rowshift_geometries(seed):
+    """The row-shift kernel (3x3 stride 1, rows of at most 14 outputs, 128k
+    channels per group) over random pads, extents (both row counts, planes
+    of pixel counts not a multiple of 4), groups, channel counts that leave a
+    partial 32-channel tile, all type mixes and zero-point forms, and element
+    offsets that break the x, w and y alignments."""
+    rng = np.random.default_rng(900 + seed)
+    xt, wt = ("u8", "i8")[seed % 2], ("u8", "i8")[(seed // 2) % 2]
+    G = int(rng.choice([1, 2]))
+    while True:
+        g = oracle.Geom(int(rng.integers(1, 4)), G * 128 * int(rng.integers(1, 3)),
+                        int(rng.integers(1, 15)), int(rng.integers(1, 15)),
+                        G * int(rng.choice([8, 32, 40, 64])), 3, 3, groups=G,
+                        pt=int(rng.integers(0, 3)), pl=int(rng.integers(0, 3)),
+                        pb=int(rng.integers(0, 3)), pr=int(rng.integers(0, 3)))
+        try:
+            _, _, ho, wo = oracle.out_shape(g)
+        except ValueError:
+            continue
+        if ho <= 14 and wo <= 14:
+            break
+    p = problem_from(g)
+    assert ".rowshift." in cf.conv_integer_describe_variant(p, xt, wt)
+    per_channel = seed % 3 != 2
+    x = _rand(rng, xt, (g.n, g.c_in, g.h, g.w))
+    w = _rand(rng, wt, (g.c_out, g.c_in // G, 3, 3))
+    xz = None if seed % 5 == 4 else int(_rand(rng, xt, ()))
+    wz = _rand(rng, wt, (g.c_out,)) if per_channel else (None if seed % 4 == 3 else int(_rand(rng, wt, ())))
+    offsets = ((0, 0, 0), (1, 0, 0), (0, 3, 0), (0, 0, 1))[seed % 4]
+    print(f"[convint rowshift {seed}] {xt}{wt} pc={per_channel} off={offsets} {g}", flush=True)
+    check(g, xt, wt, x, w, xz, wz, per_channel, offsets=offsets)
+
+
 @pytest.mark.parametrize("name", [l.name for l in workloads.INT_LAYERS])
 def test_workload_layer_full_size(name):
     l = workloads.INT_BY_NAME[name]
