@@ -207,7 +207,31 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_nct = make_magic((unsigned)a.n_ct);
       a.mg_n = make_magic((unsigned)cn);
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+      a.splits = 1;
+      a.sps = (int)(g.cig / 64);
+      if (pl.splits > 1) {  // row-shift split k: raw planes, then the ordered reduce
+        a.splits = pl.splits;
+        a.sps = pl.steps_per_split;
+        a.planes = static_cast<float*>(scratch);
+        a.plane_stride = (long long)cn * y_img;
+        a.mg_ng = make_magic((unsigned)(cn * g.g));
+        a.bias = nullptr; a.res = nullptr;
+        a.oflat = 0; a.o2 = 0;
+        a.act = CONV_ACT_IDENTITY;
+      }
       e = pl.halo.rowshift ? launch_rowshift(dt, a, s) : launch_halo(dt, a, s);
+      if (e == hipSuccess && pl.splits > 1) {
+        ReduceArgs r{};
+        r.planes = static_cast<const float*>(scratch);
+        r.plane_stride = (long long)cn * y_img;
+        r.splits = pl.splits;
+        r.bias = bb; r.res = rc; r.y = yc;
+        r.total = (long long)cn * y_img;
+        r.hw = (int)(g.ho * g.wo); r.c_out = (int)g.co;
+        r.vec = r.total % 4 == 0 && r.plane_stride % 4 == 0;
+        r.act = p->activation; r.alpha = p->act_alpha; r.beta = p->act_beta;
+        e = launch_reduce(dt, r, s);
+      }
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM) {
       IgemmArgs a{};
       a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;

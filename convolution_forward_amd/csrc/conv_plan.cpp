@@ -420,16 +420,40 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     HaloShape hs{};
     const bool halo_ok = plan_halo(g, dtype, &hs);
     if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO && !halo_ok) return CONV_ERR_ARG;
+    // row-shift split k: the largest count of equal ranges of 64-channel
+    // stages that keeps the grid at most one workgroup per CU
+    const int64_t rs_grid = (int64_t)hs.n_ct * g.n * g.g;
+    const int64_t rs_stages = g.cig / 64;
+    int64_t rs_split = 1;
+    if (halo_ok && hs.rowshift) {
+      if (p->split_override >= 1) {
+        rs_split = p->split_override;
+      } else if (rs_grid < 32) {
+        for (int64_t r = std::min<int64_t>(rs_stages, kMaxSplits); r >= 2; --r)
+          if (rs_stages % r == 0 && rs_grid * r <= kPlanCUs) { rs_split = r; break; }
+      }
+    }
     if (v == CONV_VARIANT_AUTO) {
       if (depthwise_applicable(g)) v = CONV_VARIANT_DEPTHWISE_DIRECT;
       else if (halo_ok && p->split_override <= 1 &&
                (int64_t)hs.n_ct * hs.n_rt * g.n * g.g >= (hs.rowshift ? 32 : 128))
         v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
+      else if (halo_ok && hs.rowshift && rs_split > 1 && rs_stages % rs_split == 0)
+        v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
       else v = CONV_VARIANT_IMPLICIT_GEMM;
     }
     if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO) {
-      if (p->split_override > 1) return CONV_ERR_ARG;
+      if (p->split_override > 1 && !hs.rowshift) return CONV_ERR_ARG;
       pl->halo = hs;
+      if (rs_split > 1) {
+        // ranges of whole stages only; the row-shift kernel alone splits
+        if (!hs.rowshift || rs_stages % rs_split != 0 || rs_grid * rs_split > 2147483647LL)
+          return CONV_ERR_ARG;
+        pl->splits = (int)rs_split;
+        pl->ksteps = (int)rs_stages;
+        pl->steps_per_split = (int)(rs_stages / rs_split);
+        pl->scratch_per_image = (uint64_t)(rs_split * g.co * g.ho * g.wo) * 4u;
+      }
     } else if (v == CONV_VARIANT_DEPTHWISE_DIRECT) {
       if (!depthwise_applicable(g)) return CONV_ERR_ARG;
       if (p->split_override > 1) return CONV_ERR_ARG;
@@ -647,7 +671,10 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
       snprintf(tmp, sizeof tmp, "winograd_f2x2_3x3.%s.t32x%d", dn, 32 * pl.wino_cb);
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_HALO:
-      if (pl.halo.rowshift)
+      if (pl.halo.rowshift && pl.splits > 1)
+        snprintf(tmp, sizeof tmp, "implicit_gemm_halo.%s.rowshift.r%d.n32.split%d", dn, pl.halo.tr,
+                 pl.splits);
+      else if (pl.halo.rowshift)
         snprintf(tmp, sizeof tmp, "implicit_gemm_halo.%s.rowshift.r%d.n32", dn, pl.halo.tr);
       else
         snprintf(tmp, sizeof tmp, "implicit_gemm_halo.%s.r%dx%d.n%d.c%d", dn, pl.halo.tr,

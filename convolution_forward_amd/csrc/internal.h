@@ -89,6 +89,12 @@ struct HaloArgs {
   Magic mg_nct, mg_n;    // row-shift kernel: divisors n_ct and n
   int act;
   float alpha, beta;
+  // row-shift split k: `splits` ranges of `sps` 64-channel stages, range r
+  // writing float32 plane r at planes + r * plane_stride
+  int splits, sps;
+  float* planes;
+  long long plane_stride;
+  Magic mg_ng;           // divisor n * groups
 };
 
 // Grouped convolution, 8 input channels per group: one workgroup per (image,

@@ -114,7 +114,10 @@ __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c)
 
 }  // namespace
 
-template <typename E, int R, bool XV, bool WV, int AK = -1>
+// RAW: split k.  Workgroup range r multiplies stages [r sps, (r + 1) sps) and
+// writes its float32 sums (no bias, residual or activation) to plane r of the
+// scratch; the reduce kernel adds the planes in range order and finishes.
+template <typename E, int R, bool XV, bool WV, int AK = -1, bool RAW = false>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef E half8_t __attribute__((ext_vector_type(8)));
   typedef E half4_t __attribute__((ext_vector_type(4)));
@@ -136,17 +139,23 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // (divisions by the host's multiply-shift constants: the tile's first loads
   // wait on this index arithmetic)
   const int bid = xcd_logical(blockIdx.x, gridDim.x);
-  const int bq = (int)mdiv((unsigned)bid, a.mg_nct);
-  const int ct = bid - bq * a.n_ct;
+  const int bq2 = (int)mdiv((unsigned)bid, a.mg_nct);
+  const int ct = bid - bq2 * a.n_ct;
+  int r = 0, bq = bq2;  // split range (slowest), then (group, image)
+  if constexpr (RAW) {
+    r = (int)mdiv((unsigned)bq2, a.mg_ng);
+    bq = bq2 - r * a.n * a.groups;
+  }
   const int g = (int)mdiv((unsigned)bq, a.mg_n);
   const int n = bq - g * a.n;
   const int co0 = ct * 32;
   const int hw = a.h * a.w;
+  const int ch0 = RAW ? r * a.sps * RS_CH : 0;  // first input channel of the range
 
   const E* __restrict__ ximg =
-      static_cast<const E*>(a.x) + ((long long)n * a.c_in + (long long)g * a.cig) * hw;
+      static_cast<const E*>(a.x) + ((long long)n * a.c_in + (long long)g * a.cig + ch0) * hw;
   const E* __restrict__ wg =
-      static_cast<const E*>(a.wt) + (long long)g * a.cog * a.cig * 9;
+      static_cast<const E*>(a.wt) + (long long)g * a.cog * a.cig * 9 + (long long)ch0 * 9;
 
   // ---- each wave stages only its own 16 channels of every stage (octets
   // 2 wave, 2 wave + 1) and its own 16-channel slice of the weights, which are
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
 
   u32x2_t rin[2][L::NI][8];  // two staged stages in flight: [set][item][channel], 4 pixels
   u32x4_t rwv[2][L::NW];
-  const int nstages = a.cig / RS_CH;
+  const int nstages = RAW ? a.sps : a.cig / RS_CH;
 
   // the loads of one stage in three parts (part 0 and 1: the two halves of the
   // input items, part 2: the weights), so that each tap row's multiplications
@@ -203,8 +212,8 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // weights: the per-lane part of every address is a 32-bit item offset and the
   // stage and plane parts are scalar offsets, so the loads need no vector
   // address arithmetic between the multiplications they are issued with
-  const __amdgpu_buffer_rsrc_t x_rsrc = uniform_rsrc(ximg, a.cig * hw * 2);
-  const __amdgpu_buffer_rsrc_t w_rsrc = uniform_rsrc(wg, a.cog * a.cig * 9 * 2);
+  const __amdgpu_buffer_rsrc_t x_rsrc = uniform_rsrc(ximg, nstages * RS_CH * hw * 2);
+  const __amdgpu_buffer_rsrc_t w_rsrc = uniform_rsrc(wg, (a.cog * a.cig - ch0) * 9 * 2);
   auto load_part = [&](int s, int set, int part) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const E* res = static_cast<const E*>(a.res);
   const E* __restrict__ bias = static_cast<const E*>(a.bias);
   float* bsm = reinterpret_cast<float*>(smem + L::BIAS);  // the tile's 32 biases
-  const bool pairs = a.o2;  // y / residual 4-byte aligned, wo even (uniform)
+  const bool pairs = !RAW && a.o2;  // y / residual 4-byte aligned, wo even (uniform)
   auto it_co = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) / R; };
   auto it_oh = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) % R; };
   const int it_ow = 4 * (tid & 3);  // 256 k % 4 == 0: the same quad for every k
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // flat path: the tile's outputs (its channels' planes, contiguous in y) as
   // vectors of 8; thread t takes vectors t + 256 k, k < KV, clamped to the last
   constexpr int KV = (32 * R * (RS_COLS - 2) / 8 + 255) / 256;
-  const bool flat = a.oflat;  // uniform
+  const bool flat = !RAW && a.oflat;  // uniform
   const int ftot = min(32, a.cog - co0) * howo;  // a multiple of 8 on the flat path
   const int nvec = ftot >> 3;
   u32x4_t rv[KV];  // the residual (flat path), prefetched during the last step
@@ -616,6 +625,11 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           const half2_t h = {(E)v[4 * k + 2 * j2], (E)v[4 * k + 2 * j2 + 1]};
           *reinterpret_cast<half2_t*>(y + obase + e_index(k, 2 * j2)) = h;
         }
+    } else if constexpr (RAW) {
+      float* pl = a.planes + r * a.plane_stride + obase;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (e_valid(k, j)) pl[e_index(k, j)] = v[4 * k + j];
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -624,9 +638,23 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   }
 }
 
+template <typename E, int R>
+static void launch_rowshift_raw(const HaloArgs& a, dim3 grid, hipStream_t s) {
+  if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, -1, true>), grid, dim3(256), 0, s, a);
+  else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<E, R, true, false, -1, true>), grid, dim3(256), 0, s, a);
+  else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R, false, true, -1, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((rowshift_kernel<E, R, false, false, -1, true>), grid, dim3(256), 0, s, a);
+}
+
 template <typename E>
 static hipError_t launch_rowshift_t(const HaloArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups));
+  const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups * a.splits));
+  if (a.splits > 1) {
+    if (a.ho <= 8) launch_rowshift_raw<E, 8>(a, grid, s);
+    else if (a.ho <= 14) launch_rowshift_raw<E, 14>(a, grid, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
 #define RS_LAUNCH(R_)                                                                        \
   {                                                                                          \
     if (a.xvec && a.wvec && a.act == 1) /* ReLU fixed at compile time */                   \

@@ -653,6 +653,15 @@ def test_random_sweep(kind, seed):
     yr, sr = oracle.conv2d(g, x, w, b, r)
     y = run_gpu(g, "f16", x, w, b, r, variant=v)
     assert_parity("f16", y, yr, sr, b, r, what=f"sweep {kind}", act=g.act)
+    if kind == "rowshift":
+        # whole k in one workgroup, and (when the planner splits this small
+        # grid) the split through a one-image scratch: the same bits as the
+        # whole-batch split
+        y1 = run_gpu(g, "f16", x, w, b, r, variant=v, splits=1)
+        assert_parity("f16", y1, yr, sr, b, r, what="sweep rowshift whole k", act=g.act)
+        if ".split" in name:
+            yc = run_gpu(g, "f16", x, w, b, r, variant=v, scratch_images=1)
+            assert np.array_equal(_bits(y), _bits(yc))
 
 
 DEPTHWISE_CASES = [

@@ -252,10 +252,41 @@ def test_scratch_rules():
 
 def test_split_cut_is_shape_only_and_deterministic():
     """The cut depends on the full-batch shape only, never on the scratch size."""
-    p = cf.make_problem(4, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
-    a = cf.conv_describe_variant(p, "f16")
-    assert a == cf.conv_describe_variant(p, "f16")
-    assert cf.conv_scratch_size(p, "f16")[1] * 4 == cf.conv_scratch_size(p, "f16")[0]
+    for dt, n in (("f32", 4), ("f16", 1), ("bf16", 1)):
+        p = cf.make_problem(n, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
+        a = cf.conv_describe_variant(p, dt)
+        assert a == cf.conv_describe_variant(p, dt)
+        assert ".split" in a and not a.endswith("split1"), a
+        whole, per = cf.conv_scratch_size(p, dt)
+        R = int(re.search(r"split(\d+)", a).group(1))
+        assert per == R * 512 * 49 * 4 and whole == n * per, (a, whole, per)
+
+
+def test_rowshift_split_plans():
+    """A 16-bit row-shift layer with a small grid splits k into equal ranges of
+    whole 64-channel stages, the largest count that keeps the grid at one
+    workgroup per CU; a forced count must divide the stages."""
+    p = cf.make_problem(1, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
+    assert cf.conv_describe_variant(p, "f16") == "implicit_gemm_halo.f16.rowshift.r8.n32.split8"
+    assert cf.conv_describe_variant(p, "bf16") == "implicit_gemm_halo.bf16.rowshift.r8.n32.split8"
+    p = cf.make_problem(3, 128, 7, 7, 96, 3, 3, pads=(1, 1, 1, 1))  # 9 tiles, 2 stages
+    assert cf.conv_describe_variant(p, "f16").endswith("rowshift.r8.n32.split2")
+    # 32 tiles or more: whole k
+    p = cf.make_problem(2, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
+    assert cf.conv_describe_variant(p, "f16") == "implicit_gemm_halo.f16.rowshift.r8.n32"
+    for s, want in ((4, "rowshift.r14.n32.split4"), (1, "rowshift.r14.n32")):
+        p = cf.make_problem(1, 256, 14, 14, 64, 3, 3, pads=(1, 1, 1, 1), splits=s,
+                            variant="implicit_gemm_halo")
+        assert cf.conv_describe_variant(p, "f16").endswith(want)
+    for s in (3, 5):  # not a divisor of the 4 stages
+        p = cf.make_problem(1, 256, 14, 14, 64, 3, 3, pads=(1, 1, 1, 1), splits=s,
+                            variant="implicit_gemm_halo")
+        with pytest.raises(cf.ConvError):
+            cf.conv_describe_variant(p, "f16")
+    # a forced count the stages do not divide, variant left to the planner:
+    # the generic implicit GEMM splits instead
+    p = cf.make_problem(1, 256, 14, 14, 64, 3, 3, pads=(1, 1, 1, 1), splits=3)
+    assert cf.conv_describe_variant(p, "f16") == "implicit_gemm.f16.t64x64.split3"
 
 
 def test_variant_names_for_workloads():
