@@ -420,25 +420,26 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     HaloShape hs{};
     const bool halo_ok = plan_halo(g, dtype, &hs);
     if (v == CONV_VARIANT_IMPLICIT_GEMM_HALO && !halo_ok) return CONV_ERR_ARG;
-    // row-shift split k: the largest count of equal ranges of 64-channel
-    // stages that keeps the grid at most one workgroup per CU
+    // row-shift split k (grids that fill at most half the CUs): the largest
+    // count of equal ranges of 64-channel stages that keeps the grid at most
+    // one workgroup per CU
     const int64_t rs_grid = (int64_t)hs.n_ct * g.n * g.g;
     const int64_t rs_stages = g.cig / 64;
     int64_t rs_split = 1;
     if (halo_ok && hs.rowshift) {
       if (p->split_override >= 1) {
         rs_split = p->split_override;
-      } else if (rs_grid < 32) {
+      } else if (rs_grid * 2 <= kPlanCUs) {
         for (int64_t r = std::min<int64_t>(rs_stages, kMaxSplits); r >= 2; --r)
           if (rs_stages % r == 0 && rs_grid * r <= kPlanCUs) { rs_split = r; break; }
       }
     }
     if (v == CONV_VARIANT_AUTO) {
       if (depthwise_applicable(g)) v = CONV_VARIANT_DEPTHWISE_DIRECT;
+      else if (halo_ok && hs.rowshift && rs_split > 1 && rs_stages % rs_split == 0)
+        v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
       else if (halo_ok && p->split_override <= 1 &&
                (int64_t)hs.n_ct * hs.n_rt * g.n * g.g >= (hs.rowshift ? 32 : 128))
-        v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
-      else if (halo_ok && hs.rowshift && rs_split > 1 && rs_stages % rs_split == 0)
         v = CONV_VARIANT_IMPLICIT_GEMM_HALO;
       else v = CONV_VARIANT_IMPLICIT_GEMM;
     }

@@ -463,13 +463,17 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   if (tid < 32) bsm[tid] = bias ? (float)b_in : -0.0f;
   __syncthreads();
   // step 0: stage 1 into set 1 with the multiplications, then stage 2 into
-  // set 0 (stage indexes clamped: with fewer stages the extra loads repeat the
-  // last stage and are unused), then stage 1 into buffer 1
-  if (nstages == 1) load_epilogue_operands();
+  // set 0, then stage 1 into buffer 1; stages that do not exist are not
+  // loaded (the kernel cannot end before every load it issued has returned)
   __builtin_amdgcn_sched_barrier(0);
-  compute(0, [&](int kh) __attribute__((always_inline)) { load_part(min(1, nstages - 1), 1, kh); });
+  if (nstages == 1) {  // uniform
+    load_epilogue_operands();
+    compute(0, no_hook);
+  } else {
+    compute(0, [&](int kh) __attribute__((always_inline)) { load_part(1, 1, kh); });
+  }
   __builtin_amdgcn_sched_barrier(0);
-  load_stage(min(2, nstages - 1), 0);
+  if (nstages > 2) load_stage(2, 0);
   if (nstages > 1) store_stage(1, 1);
   int s = 1;
   for (; s + 3 < nstages; s += 2) {  // both steps prefetch a stage

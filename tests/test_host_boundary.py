@@ -263,16 +263,18 @@ def test_split_cut_is_shape_only_and_deterministic():
 
 
 def test_rowshift_split_plans():
-    """A 16-bit row-shift layer with a small grid splits k into equal ranges of
-    whole 64-channel stages, the largest count that keeps the grid at one
-    workgroup per CU; a forced count must divide the stages."""
+    """A 16-bit row-shift layer whose grid fills at most half the CUs splits k
+    into equal ranges of whole 64-channel stages, the largest count that keeps
+    the grid at one workgroup per CU; a forced count must divide the stages."""
     p = cf.make_problem(1, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
     assert cf.conv_describe_variant(p, "f16") == "implicit_gemm_halo.f16.rowshift.r8.n32.split8"
     assert cf.conv_describe_variant(p, "bf16") == "implicit_gemm_halo.bf16.rowshift.r8.n32.split8"
     p = cf.make_problem(3, 128, 7, 7, 96, 3, 3, pads=(1, 1, 1, 1))  # 9 tiles, 2 stages
     assert cf.conv_describe_variant(p, "f16").endswith("rowshift.r8.n32.split2")
-    # 32 tiles or more: whole k
-    p = cf.make_problem(2, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
+    p = cf.make_problem(8, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))  # 128 tiles
+    assert cf.conv_describe_variant(p, "f16") == "implicit_gemm_halo.f16.rowshift.r8.n32.split2"
+    # more than half the CUs' worth of tiles: whole k
+    p = cf.make_problem(16, 512, 7, 7, 512, 3, 3, pads=(1, 1, 1, 1))
     assert cf.conv_describe_variant(p, "f16") == "implicit_gemm_halo.f16.rowshift.r8.n32"
     for s, want in ((4, "rowshift.r14.n32.split4"), (1, "rowshift.r14.n32")):
         p = cf.make_problem(1, 256, 14, 14, 64, 3, 3, pads=(1, 1, 1, 1), splits=s,
