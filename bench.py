@@ -454,10 +454,12 @@ def traffic_from_profiles(kernel_src_hash):
     m = re.search(r"^traffic: (.*)$", txt, re.M)
     if not m:
         return None
-    kv = dict(item.split("=", 1) for item in m.group(1).split())
-    if kv.get("source_sha") != kernel_src_hash:
+    # only the two fields used; the kernel name that follows may hold spaces
+    sha = re.search(r"\bsource_sha=(\S+)", m.group(1))
+    nbytes = re.search(r"\bbytes_per_launch=([0-9.]+)", m.group(1))
+    if not sha or not nbytes or sha.group(1) != kernel_src_hash:
         return None
-    return float(kv["bytes_per_launch"])
+    return float(nbytes.group(1))
 
 
 def kernel_source_hash():
