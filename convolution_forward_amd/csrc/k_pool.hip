@@ -399,6 +399,65 @@ __global__ __launch_bounds__(256) void pool_rowvec_kernel(const PoolArgs a) {
       if constexpr (sizeof(T) == 4) ob[o] = __float_as_uint(r);
       else ob[o] = __builtin_bit_cast(unsigned short, r);
     }
+  } else if constexpr (sizeof(T) == 2) {
+    // 16-bit max, two keys per 32-bit word.  A window with a real tap keeps
+    // its max when its taps outside the input repeat one of its real taps:
+    // rows outside the input were loaded as the nearest edge row (which the
+    // window then contains), and the words past the row's ends are made
+    // copies of its edge columns here (the element path loaded them so).
+    // Keys are formed without the NaN test: a NaN tap shows in the result as
+    // a key above +inf or below -inf, and only then is the output recomputed
+    // with NaN taps skipped (the exact rule, rarely taken).
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    constexpr int NWD = V / 2 + 2;  // words: left, home 0..3, right
+    constexpr int KINF = std::is_same_v<T, _Float16> ? 0x7C00 : 0x7F80;
+    const bool left_out = j == 0;                 // columns col0 - 2, col0 - 1
+    const bool home_out = col0 >= a.w;            // the whole vector past the row
+    const bool right_out = col0 + V >= a.w;       // columns col0 + V, col0 + V + 1
+    s2 cm[NWD];  // per word, the column maxima over the window's rows (keys)
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      unsigned wd[NWD] = {lw[kh], d[kh][0], d[kh][1], d[kh][2], d[kh][3], rw[kh]};
+      if (a.vec) {  // uniform
+        const unsigned first = (wd[1] & 0xFFFFu) * 0x10001u;
+        const unsigned last = (home_out ? wd[0] >> 16 : wd[4] >> 16) * 0x10001u;
+        wd[0] = left_out ? first : wd[0];
+#pragma unroll
+        for (int q = 1; q < NWD - 1; ++q) wd[q] = home_out ? last : wd[q];
+        wd[NWD - 1] = right_out ? last : wd[NWD - 1];
+      }
+#pragma unroll
+      for (int q = 0; q < NWD; ++q) {
+        const s2 x = __builtin_bit_cast(s2, wd[q]);
+        const s2 k = x ^ ((x >> (short)15) & (short)0x7FFF);
+        cm[q] = kh == 0 ? k : (cm[q] > k ? cm[q] : k);
+      }
+    }
+#pragma unroll
+    for (int o = 0; o < OPT; ++o) {
+      int m = INT_MIN, rwn = 0;
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) {
+        const int e = o * SW + kw - PL + 2;  // element of the stretch, from -2
+        m = max(m, (int)cm[e >> 1][e & 1]);
+        rwn += vc[o * SW + kw];
+      }
+      const bool real = rh * rwn > 0;
+      if (__builtin_expect(real && (m > KINF || m < -KINF - 1), 0)) {
+        // a NaN tap: the exact rule over this output's taps
+        m = INT_MIN;
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+          for (int kw = 0; kw < KW; ++kw) {
+            const int c = o * SW + kw;
+            m = max(m, bits_key<T>(stretch_bits<T>(d[kh], lw[kh], rw[kh], c - PL), rok[kh] & vc[c]));
+          }
+        ob[o] = key_bits<T>(m, true);
+      } else {
+        ob[o] = real ? (unsigned)(m ^ ((m >> 31) & 0x7FFF)) & 0xFFFFu : key_bits<T>(INT_MIN, false);
+      }
+    }
   } else {
     int cm[NC];  // column maxima over the window's rows
 #pragma unroll

@@ -223,6 +223,46 @@ def test_pool_special_values(dtype):
         check(g, kind, dtype, xx)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_pool_rowvec_special_values(dtype):
+    """NaN, +-0 and infinities on rows of whole 16-byte vectors (the row-vector
+    kernel), x aligned and at an element offset: an all-NaN window, NaN among
+    numbers at the row ends and in the middle, -0 beside +0, rows of -inf
+    only, +inf; windows that reach past both row ends and past the last row."""
+    v = 4 if dtype == "f32" else 8
+    w = 3 * v
+    rng = np.random.default_rng(31)
+    x = _q(rng.uniform(-1, 1, (2, 3, 9, w)), dtype).astype(np.float32)
+    x[0, 0, :2, :2] = np.nan                  # an all-NaN window (top-left corner)
+    x[0, 1, ::2, ::3] = np.nan                # NaN among numbers
+    x[0, 1, 4, w - 1] = np.nan                # NaN at a row's last column
+    x[0, 2, :, 0] = np.nan                    # NaN down the first column
+    x[1, 0] = -0.0
+    x[1, 0, 4, 4] = 0.0                       # +0 among -0
+    x[1, 1, 2, :] = -np.inf
+    x[1, 2, :, :] = -np.inf                   # only -inf: the max is -inf
+    x[0, 2, 5, 5] = np.inf
+    for kind in ("max", "average"):
+        for (k, s_, p, cm) in (((3, 3), 2, (1, 1, 1, 1), True), ((2, 2), 2, (0, 0, 1, 1), True),
+                               ((3, 3), 1, (1, 1, 1, 1), False), ((3, 2), 2, (2, 0, 2, 0), True)):
+            g = oracle.PoolGeom(2, 3, 9, w, k[0], k[1], s_, s_, 1, 1, *p, ceil_mode=cm,
+                                count_include_pad=False)
+            pp = _problem(g, kind)
+            assert ".rowvec" in cf.pool_describe_variant(pp, dtype), cf.pool_describe_variant(pp, dtype)
+            g.kind = kind
+            yr, sr = oracle.pool2d(g, x, dtype=dtype)
+            for off in ((0, 0), (1, 0)):
+                _say(f"[pool rowvec special] {dtype} {kind} {k} s{s_} {p} ceil={cm} off={off}")
+                y = run_pool(g, kind, dtype, x, offsets=off)
+                if kind == "max":
+                    assert_max_exact(y, yr, dtype, "rowvec special max")
+                else:
+                    fin = np.isfinite(yr)
+                    assert np.array_equal(np.isnan(y), np.isnan(yr))
+                    assert np.array_equal(y[~fin & ~np.isnan(yr)], yr[~fin & ~np.isnan(yr)])
+                    assert_avg(np.where(fin, y, 0), np.where(fin, yr, 0), np.where(fin, sr, 0), dtype)
+
+
 def test_pool_direct_kernel_wide_rows():
     for kind in ("max", "average"):
         # 6001 columns: not whole vectors (no row-vector kernel), and three
