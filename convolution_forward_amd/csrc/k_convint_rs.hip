@@ -31,8 +31,9 @@
 //    channels (v_dot4 against ones) and keeps the totals over the stages; the
 //    positions' totals meet in LDS (integer adds), the padding positions hold
 //    cin/groups copies of the staged pad byte, and Sx of an output is the sum
-//    of its 3 x 3 window of positions.  Sw: the weight bytes of each staged
-//    16-byte piece, added the same way per output channel.
+//    of its 3 x 3 window of positions.  Sw: each lane adds the bytes of its B
+//    data (one output channel's weights of its channels) over the stages; the
+//    lanes' sums meet per channel in LDS.
 //  * The MFMA sums stay inside int32 (|xs ws| <= 2^14 and K <= 14563 * 9 is
 //    checked by the host), the corrections are uint32 arithmetic, which wraps
 //    as the int32 result must.
@@ -112,9 +113,20 @@ __device__ __forceinline__ int dot_ones(unsigned v, int acc) {
   return __builtin_amdgcn_sdot4((int)v, 0x01010101, acc, false);
 }
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform so that it lives in scalar registers: a load's
+// per-lane part is a 32-bit offset, the stage and plane parts scalar offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 }  // namespace
 
-template <bool XU, bool WU, int R, bool XV>
+template <bool XU, bool WU, int R, bool XV, bool WV>
 __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsArgs a) {
   typedef CrLayout<R> L;
   constexpr int NP = L::NP;
@@ -153,8 +165,7 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   const int groups4 = (hw + 3) / 4;
   const int in_items = 2 * groups4;
   int in_off[L::NI];
-  int in_lds[L::NI][4];
-  int in_pos[L::NI][4];
+  int in_lds[L::NI][4];  // LDS byte address (position p: (8 p + slot) 16), -1 for none
   bool in_live[L::NI];
 #pragma unroll
   for (int i = 0; i < L::NI; ++i) {
@@ -171,7 +182,6 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
       const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
       const int pos = (ih + a.pt) * CR_COLS + iw + a.pl;
       const bool ok = in_live[i] && f < hw;
-      in_pos[i][k4] = ok ? pos : -1;
       in_lds[i][k4] = ok ? (pos * 8 + slot8(pos, o)) * 16 : -1;
     }
   }
@@ -179,14 +189,12 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   // 9 taps, 288 contiguous bytes of the channel's 1152 in the stage)
   int w_off[L::NW];
   int w_lds[L::NW];
-  int w_col[L::NW];
   bool w_ok[L::NW];
   static_assert(L::NW * 64 == 32 * 18, "one piece per lane and vector");
 #pragma unroll
   for (int i = 0; i < L::NW; ++i) {
     const int q = lane + i * 64;
     const int col = q / 18, piece = q - (q / 18) * 18;
-    w_col[i] = col;
     w_ok[i] = co0 + col < a.cog;
     w_off[i] = w_ok[i] ? (int)((long long)(co0 + col) * a.cig * 9 + 288 * wave + piece * 16) : 0;
     w_lds[i] = L::IN_BYTES + col * CR_WROW + 288 * wave + piece * 16;
@@ -195,22 +203,23 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   unsigned rin[L::NI][16];  // the next stage's input bytes: [item][plane], 4 pixels
   u32x4_t rwv[L::NW];
   int pacc[L::NI][4];       // byte sums of the item's positions over its channels
-  int sacc[L::NW];          // byte sums of the weight pieces
+  int sacc = 0;             // byte sum of this lane's B data (its channel's weights)
 #pragma unroll
   for (int i = 0; i < L::NI; ++i)
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) pacc[i][k4] = 0;
-#pragma unroll
-  for (int i = 0; i < L::NW; ++i) sacc[i] = 0;
   const int nstages = a.cig / CR_CH;
+  const __amdgpu_buffer_rsrc_t x_rsrc = uniform_rsrc(ximg, nstages * CR_CH * hw);
+  const __amdgpu_buffer_rsrc_t w_rsrc = uniform_rsrc(wg, a.cog * a.cig * 9);
 
   auto load_stage = [&](int s) __attribute__((always_inline)) {
     const long long xoff = (long long)s * CR_CH * hw;
     const long long woff = (long long)s * CR_CH * 9;
-    if (a.wvec) {  // 16-byte aligned weights
+    if constexpr (WV) {  // 16-byte aligned weights
 #pragma unroll
       for (int i = 0; i < L::NW; ++i)
-        rwv[i] = *reinterpret_cast<const u32x4_t*>(wg + woff + w_off[i]);
+        rwv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 w_rsrc, w_off[i], (int)woff, 0));
     } else {
 #pragma unroll
       for (int i = 0; i < L::NW; ++i) {
@@ -223,12 +232,14 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
     }
 #pragma unroll
     for (int i = 0; i < L::NI; ++i) {
-      const unsigned char* src = ximg + xoff + (in_live[i] ? in_off[i] : 0);
+      // a dead item's offset is item 0's (valid), so every load is unconditional
+      const unsigned char* src = ximg + xoff + in_off[i];
       if constexpr (XV) {  // 4-byte aligned planes of whole 4-pixel groups
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rin[i][e] = *reinterpret_cast<const unsigned*>(src + (long long)e * hw);
+        for (int e = 0; e < 16; ++e)
+          rin[i][e] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, in_off[i], (int)xoff + e * hw, 0);
       } else {  // byte loads, clamped to the group's last pixel in the plane
-        const int left = in_live[i] ? hw - 1 - (in_off[i] % hw) : 0;
+        const int left = hw - 1 - (in_off[i] % hw);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           unsigned v = 0;
@@ -267,10 +278,7 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
     for (int i = 0; i < L::NW; ++i) {
       u32x4_t v = rwv[i];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = w_ok[i] ? v[q] ^ wflip : 0u;
-        sacc[i] = dot_ones(v[q], sacc[i]);
-      }
+      for (int q = 0; q < 4; ++q) v[q] = w_ok[i] ? v[q] ^ wflip : 0u;
       *reinterpret_cast<u32x4_t*>(base + w_lds[i]) = v;
     }
   };
@@ -296,15 +304,21 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
       const u32x4_t t = *reinterpret_cast<const u32x4_t*>(wb + 16 * v);
       raw[4 * v] = t[0]; raw[4 * v + 1] = t[1]; raw[4 * v + 2] = t[2]; raw[4 * v + 3] = t[3];
     }
-    u32x4_t bf[9];
+    // Sw: each (channel, input channel, tap) of the stage is in exactly one
+    // lane's B data, so the lanes' sums add up to the channels' byte sums
 #pragma unroll
-    for (int t = 0; t < 9; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)  // channels 4q..4q+3 of the run at tap t: bytes c * 9 + t
-        bf[t][q] = byte_of(raw, (4 * q) * 9 + t) | (byte_of(raw, (4 * q + 1) * 9 + t) << 8) |
-                   (byte_of(raw, (4 * q + 2) * 9 + t) << 16) | (byte_of(raw, (4 * q + 3) * 9 + t) << 24);
+    for (int v = 0; v < 36; ++v) sacc = dot_ones(raw[v], sacc);
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh) {
+      u32x4_t bf[3];  // the tap row's three B fragments, regrouped from the raw bytes
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // channels 4q..4q+3 of the run at tap t: bytes c * 9 + t
+          const int t = kh * 3 + kw;
+          bf[kw][q] = byte_of(raw, (4 * q) * 9 + t) | (byte_of(raw, (4 * q + 1) * 9 + t) << 8) |
+                      (byte_of(raw, (4 * q + 2) * 9 + t) << 16) | (byte_of(raw, (4 * q + 3) * 9 + t) << 24);
+        }
       u32x4_t fr[NP];  // row pair 2q + kh of every output row pair q
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
         for (int q = 0; q < NP; ++q) {
           const u32x4_t f = kw == 0 ? fr[q] : kw == 1 ? row_shift<1>(fr[q]) : row_shift<2>(fr[q]);
           acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, f),
-                                                         __builtin_bit_cast(i32x4_t, bf[kh * 3 + kw]),
+                                                         __builtin_bit_cast(i32x4_t, bf[kw]),
                                                          acc[q], 0, 0, 0);
         }
     }
@@ -360,9 +374,8 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   for (int i = 0; i < L::NI; ++i)
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4)
-      if (in_pos[i][k4] >= 0) atomicAdd(&psum[in_pos[i][k4]], pacc[i][k4]);
-#pragma unroll
-  for (int i = 0; i < L::NW; ++i) atomicAdd(&sws[w_col[i]], sacc[i]);
+      if (in_lds[i][k4] >= 0) atomicAdd(&psum[in_lds[i][k4] >> 7], pacc[i][k4]);
+  atomicAdd(&sws[lane & 31], sacc);
   // each wave's partial sums as a copy [channel][row][16 columns]: accumulator
   // elements 4 i4 .. 4 i4 + 3 of row pair q are pixels 8 i4 + 4 (l / 32) + 0..3
   // of the pair, 4 consecutive columns of one row
@@ -432,10 +445,16 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
 
 hipError_t launch_convint_rowshift(const ConvIntRsArgs& a, bool xu, bool wu, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups));
-#define CR_LAUNCH(XU_, WU_, R_)                                                                   \
-  {                                                                                               \
-    if (a.xvec) hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, true>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, false>), grid, dim3(256), 0, s, a);       \
+#define CR_LAUNCH(XU_, WU_, R_)                                                                          \
+  {                                                                                                      \
+    if (a.xvec && a.wvec)                                                                                \
+      hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, true, true>), grid, dim3(256), 0, s, a);   \
+    else if (a.xvec)                                                                                     \
+      hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, true, false>), grid, dim3(256), 0, s, a);  \
+    else if (a.wvec)                                                                                     \
+      hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, false, true>), grid, dim3(256), 0, s, a);  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((convint_rowshift_kernel<XU_, WU_, R_, false, false>), grid, dim3(256), 0, s, a); \
   }
 #define CR_R(XU_, WU_)        \
   {                           \
