@@ -106,7 +106,9 @@ typedef enum {
     CONV_VARIANT_DEPTHWISE_DIRECT = 3,  /* one input channel per group, direct, no MFMA */
     CONV_VARIANT_TRANSPOSE_GEMM_COL2IM = 4, /* ConvTranspose: GEMM + gathering col2im */
     CONV_VARIANT_IMPLICIT_GEMM_HALO = 5, /* implicit GEMM with the input halo tile staged
-                                            once per channel chunk and reused for all taps */
+                                            once per channel chunk and reused for all taps;
+                                            its row-shift path splits k itself when its
+                                            grid fills at most half the compute units */
     CONV_VARIANT_IMPLICIT_GEMM_ROWBAND = 6, /* stride 2, few input channels (image stems):
                                               a ring of staged input rows per output-row
                                               band, kw taps read as consecutive halves */
@@ -144,7 +146,13 @@ typedef struct conv_problem {
     int32_t has_bias, has_residual; /* 0/1: whether bias / residual are applied */
     int32_t variant_override;       /* conv_variant; 0 = AUTO; others force a variant
                                        (CONV_ERR_ARG if it cannot run the shape) */
-    int32_t split_override;         /* split-k ranges; 0 = AUTO, 1 = whole k, R > 1 forces R */
+    int32_t split_override;         /* split-k ranges; 0 = AUTO, 1 = whole k, R > 1 forces R.
+                                       The halo variant splits only on its row-shift
+                                       path (3x3 stride 1, rows of at most 14 outputs)
+                                       and only into R equal ranges of whole 64-channel
+                                       stages (CONV_ERR_ARG otherwise); under AUTO a
+                                       forced R that no row-shift split allows goes to
+                                       the generic implicit GEMM. */
 } conv_problem;
 
 /* Output extent (the OutputExtent / TransposeOutputExtent analog): writes Ho, Wo.
