@@ -117,7 +117,12 @@ __device__ __forceinline__ floatx16_t mfma32(u32x4_t a, u32x4_t b, floatx16_t c)
 // RAW: split k.  Workgroup range r multiplies stages [r sps, (r + 1) sps) and
 // writes its float32 sums (no bias, residual or activation) to plane r of the
 // scratch; the reduce kernel adds the planes in range order and finishes.
-template <typename E, int R, bool XV, bool WV, int AK = -1, bool RAW = false>
+// NS: the number of 64-channel stages when it is 1..4, at least 5 when NS = 5,
+// any (read from the arguments) when NS = -1.  With the count known the
+// prologue and the last steps have no branches on it, so the wait before each
+// LDS store counts exactly the loads issued after its data (a branch around a
+// group of loads makes the compiler wait for every load at the join).
+template <typename E, int R, bool XV, bool WV, int AK = -1, bool RAW = false, int NS = -1>
 __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef E half8_t __attribute__((ext_vector_type(8)));
   typedef E half4_t __attribute__((ext_vector_type(4)));
@@ -160,12 +165,15 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // ---- each wave stages only its own 16 channels of every stage (octets
   // 2 wave, 2 wave + 1) and its own 16-channel slice of the weights, which are
   // all its multiplications read: the waves need no barrier between stages and
-  // drift freely, one's loads overlapping another's multiplications ----
+  // drift freely, one's loads overlapping another's multiplications.  Only the
+  // global offsets are computed before the first stage's loads go out; the LDS
+  // positions follow while those loads fly (at one wave per SIMD every
+  // instruction ahead of the first load delays the whole tile). ----
   // input staging items: (one of the wave's two octets, 4-pixel group)
   const int groups4 = (hw + 3) / 4;
   const int in_items = 2 * groups4;
   int in_off[L::NI];
-  int in_lds[L::NI][4];
+  int in_grp4[L::NI], in_oct[L::NI];
   bool in_live[L::NI];
 #pragma unroll
   for (int i = 0; i < L::NI; ++i) {
@@ -174,35 +182,28 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     const int qq = in_live[i] ? q : 0;
     const int qd = (int)mdiv((unsigned)qq, a.mg_g4);
     const int o = 2 * wave + qd;
-    const int grp4 = qq - qd * groups4;
-    in_off[i] = 8 * o * hw + 4 * grp4;
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int f = 4 * grp4 + k4;  // pixels past the plane's end (hw % 4 != 0) are skipped
-      const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
-      const int pos = (ih + a.pt) * RS_COLS + iw + a.pl;
-      in_lds[i][k4] = f < hw ? (pos * 8 + slot8(pos, o)) * 16 : -1;
-    }
+    in_grp4[i] = qq - qd * groups4;
+    in_oct[i] = o;
+    in_off[i] = 8 * o * hw + 4 * in_grp4[i];
   }
   // weight staging vectors: (output channel, 16-byte piece of the wave's 16
-  // channels x 9 taps, 288 contiguous bytes of the channel's 1152)
+  // channels x 9 taps, 288 contiguous bytes of the channel's 1152).  Channels
+  // past the group's last read its last one: their sums feed only output
+  // channels that are never stored.
   int w_off[L::NW];
-  int w_lds[L::NW];
-  bool w_ok[L::NW], w_live[L::NW];
   static_assert(L::NW * 64 == 32 * 18, "one weight vector per lane and step");
 #pragma unroll
   for (int i = 0; i < L::NW; ++i) {
-    const int q = lane + i * 64;
-    w_live[i] = true;
-    const int col = q / 18, piece = q - (q / 18) * 18;
-    w_ok[i] = co0 + col < a.cog;
-    w_off[i] = w_ok[i] ? (int)((long long)(co0 + col) * a.cig * 9 + 144 * wave + piece * 8) : 0;
-    w_lds[i] = L::IN_BYTES + col * RS_WROW + 288 * wave + piece * 16;
+    const unsigned q = (unsigned)(lane + i * 64);
+    const unsigned col = __umul24(q, 3641u) >> 16;  // q / 18, exact for q < 576
+    w_off[i] = (int)__umul24((unsigned)min(co0 + (int)col, a.cog - 1), (unsigned)(a.cig * 9)) +
+               144 * wave + 8 * ((int)q - 18 * (int)col);
   }
 
   u32x2_t rin[2][L::NI][8];  // two staged stages in flight: [set][item][channel], 4 pixels
   u32x4_t rwv[2][L::NW];
-  const int nstages = RAW ? a.sps : a.cig / RS_CH;
+  const int nstages = NS >= 1 && NS <= 4 ? NS : RAW ? a.sps : a.cig / RS_CH;
+  if constexpr (NS == 5) __builtin_assume(nstages >= 5);
 
   // the loads of one stage in three parts (part 0 and 1: the two halves of the
   // input items, part 2: the weights), so that each tap row's multiplications
@@ -261,6 +262,36 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     load_part(s, set, 1);
     load_part(s, set, 2);
   };
+  // only stage 0 is loaded before the first multiplications: stages 1 and 2
+  // are issued with stage 0's multiplications, so that the multiplications
+  // start as soon as the first stage has arrived
+  load_stage(0, 0);
+  // the tile's biases (any valid address without bias), kept in LDS for the
+  // epilogue
+  const E* __restrict__ bias = static_cast<const E*>(a.bias);
+  const E b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // LDS positions of the staging items: input octets channel-innermost at
+  // their padded tile position (pixels past the plane's end, hw % 4 != 0, go
+  // nowhere), weight vectors into the output channel's padded row
+  int in_lds[L::NI][4];
+#pragma unroll
+  for (int i = 0; i < L::NI; ++i)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int f = 4 * in_grp4[i] + k4;
+      const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
+      const int pos = (ih + a.pt) * RS_COLS + iw + a.pl;
+      in_lds[i][k4] = f < hw ? (pos * 8 + slot8(pos, in_oct[i])) * 16 : -1;
+    }
+  int w_lds[L::NW];
+#pragma unroll
+  for (int i = 0; i < L::NW; ++i) {
+    const unsigned q = (unsigned)(lane + i * 64);
+    const unsigned col = __umul24(q, 3641u) >> 16;
+    w_lds[i] = L::IN_BYTES + (int)col * RS_WROW + 288 * wave + 16 * ((int)q - 18 * (int)col);
+  }
 
   // Branch-free: dead items and pixels past the plane write the sink, so no
   // store sits behind a branch (which would make the compiler wait for every
@@ -283,9 +314,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
     if (part == 2) {
 #pragma unroll
       for (int i = 0; i < L::NW; ++i) {
-        const u32x4_t v = w_ok[i] ? rwv[set][i] : u32x4_t{0, 0, 0, 0};
-        unsigned char* dst = w_live[i] ? base + w_lds[i] : smem + L::SINK;
-        *reinterpret_cast<u32x4_t*>(dst) = v;
+        *reinterpret_cast<u32x4_t*>(base + w_lds[i]) = rwv[set][i];
       }
     }
   };
@@ -368,7 +397,6 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   const int howo = a.ho * a.wo;
   const long long obase = ((long long)n * a.c_out + g * a.cog + co0) * howo;
   const E* res = static_cast<const E*>(a.res);
-  const E* __restrict__ bias = static_cast<const E*>(a.bias);
   float* bsm = reinterpret_cast<float*>(smem + L::BIAS);  // the tile's 32 biases
   const bool pairs = !RAW && a.o2;  // y / residual 4-byte aligned, wo even (uniform)
   auto it_co = [&](int k) __attribute__((always_inline)) { return ((tid + 256 * k) >> 2) / R; };
@@ -437,13 +465,6 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   typedef std::integral_constant<int, 0> LOAD;
   typedef std::integral_constant<int, 1> STORE_ONLY;
   typedef std::integral_constant<int, 2> LAST;
-  // the tile's biases, loaded first (any valid address without bias) and kept
-  // in LDS for the epilogue
-  const E b_in = *(bias ? bias + g * a.cog + min(co0 + (tid & 31), a.cog - 1) : ximg);
-  // only stage 0 is loaded before the first multiplications: stages 1 and 2
-  // are issued with stage 0's multiplications, so that the multiplications
-  // start as soon as the first stage has arrived
-  load_stage(0, 0);
   // zero the padding positions of both stages' input regions (rows and
   // columns outside the image) while the first loads fly: staging writes only
   // image positions, so these stay zero
@@ -469,11 +490,17 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   if (nstages == 1) {  // uniform
     load_epilogue_operands();
     compute(0, no_hook);
+  } else if constexpr (NS >= 3) {
+    compute(0, [&](int kh) __attribute__((always_inline)) {
+      if (kh == 0) { load_part(1, 1, 0); load_part(1, 1, 1); }
+      else if (kh == 1) { load_part(1, 1, 2); load_part(2, 0, 0); }
+      else { load_part(2, 0, 1); load_part(2, 0, 2); }
+    });
   } else {
     compute(0, [&](int kh) __attribute__((always_inline)) { load_part(1, 1, kh); });
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (nstages > 2) load_stage(2, 0);
+  if (NS < 3 && nstages > 2) load_stage(2, 0);
   if (nstages > 1) store_stage(1, 1);
   int s = 1;
   for (; s + 3 < nstages; s += 2) {  // both steps prefetch a stage
@@ -642,39 +669,45 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   }
 }
 
+// Launches one instance; the aligned paths take the instance of their stage
+// count (1..4, or 5 for five and more), the others the run-time count.
+template <typename E, int R, bool XV, bool WV, int AK, bool RAW>
+static void launch_rs(const HaloArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (XV && WV) {
+    const int ns = RAW ? a.sps : a.cig / RS_CH;
+    switch (ns < 5 ? ns : 5) {
+      case 1: hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, AK, RAW, 1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, AK, RAW, 2>), grid, dim3(256), 0, s, a); break;
+      case 3: hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, AK, RAW, 3>), grid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, AK, RAW, 4>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, AK, RAW, 5>), grid, dim3(256), 0, s, a); break;
+    }
+  } else {
+    hipLaunchKernelGGL((rowshift_kernel<E, R, XV, WV, AK, RAW>), grid, dim3(256), 0, s, a);
+  }
+}
+
+template <typename E, int R, int AK, bool RAW>
+static void launch_rs_aligned(const HaloArgs& a, dim3 grid, hipStream_t s) {
+  if (a.xvec && a.wvec) launch_rs<E, R, true, true, AK, RAW>(a, grid, s);
+  else if (a.xvec) launch_rs<E, R, true, false, -1, RAW>(a, grid, s);
+  else if (a.wvec) launch_rs<E, R, false, true, -1, RAW>(a, grid, s);
+  else launch_rs<E, R, false, false, -1, RAW>(a, grid, s);
+}
+
 template <typename E, int R>
-static void launch_rowshift_raw(const HaloArgs& a, dim3 grid, hipStream_t s) {
-  if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R, true, true, -1, true>), grid, dim3(256), 0, s, a);
-  else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<E, R, true, false, -1, true>), grid, dim3(256), 0, s, a);
-  else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R, false, true, -1, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((rowshift_kernel<E, R, false, false, -1, true>), grid, dim3(256), 0, s, a);
+static void launch_rs_r(const HaloArgs& a, dim3 grid, hipStream_t s) {
+  if (a.splits > 1) launch_rs_aligned<E, R, -1, true>(a, grid, s);
+  else if (a.act == 1) launch_rs_aligned<E, R, 1, false>(a, grid, s);  // ReLU fixed at compile time
+  else launch_rs_aligned<E, R, -1, false>(a, grid, s);
 }
 
 template <typename E>
 static hipError_t launch_rowshift_t(const HaloArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n_ct * a.n * a.groups * a.splits));
-  if (a.splits > 1) {
-    if (a.ho <= 8) launch_rowshift_raw<E, 8>(a, grid, s);
-    else if (a.ho <= 14) launch_rowshift_raw<E, 14>(a, grid, s);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
-  }
-#define RS_LAUNCH(R_)                                                                        \
-  {                                                                                          \
-    if (a.xvec && a.wvec && a.act == 1) /* ReLU fixed at compile time */                   \
-      hipLaunchKernelGGL((rowshift_kernel<E, R_, true, true, 1>), grid, dim3(256), 0, s, a);     \
-    else if (a.xvec && a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, true, true>), grid, dim3(256), 0, s, a); \
-    else if (a.xvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, true, false>), grid, dim3(256), 0, s, a); \
-    else if (a.wvec) hipLaunchKernelGGL((rowshift_kernel<E, R_, false, true>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((rowshift_kernel<E, R_, false, false>), grid, dim3(256), 0, s, a);           \
-  }
-  if (a.ho <= 8)
-    RS_LAUNCH(8)
-  else if (a.ho <= 14)
-    RS_LAUNCH(14)
-  else
-    return hipErrorInvalidValue;
-#undef RS_LAUNCH
+  if (a.ho <= 8) launch_rs_r<E, 8>(a, grid, s);
+  else if (a.ho <= 14) launch_rs_r<E, 14>(a, grid, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
