@@ -192,7 +192,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.oct = pl.halo.oct; a.tr = pl.halo.tr; a.tcb = pl.halo.tcb; a.cb = pl.halo.cb;
       a.tih = pl.halo.tih; a.tiw = pl.halo.tiw; a.n_ct = pl.halo.n_ct; a.n_rt = pl.halo.n_rt;
       a.wvec = reinterpret_cast<uintptr_t>(wb) % 16 == 0;
-      a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0;
+      a.xvec = reinterpret_cast<uintptr_t>(xc) % 8 == 0 && (g.h * g.w) % 4 == 0 && g.h * g.w >= 8;
       a.ovec = reinterpret_cast<uintptr_t>(yc) % 8 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 8 == 0) &&
                (g.ho * g.wo) % 4 == 0;
       a.o2 = reinterpret_cast<uintptr_t>(yc) % 4 == 0 && (!rc || reinterpret_cast<uintptr_t>(rc) % 4 == 0) &&

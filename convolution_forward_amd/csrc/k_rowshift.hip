@@ -72,8 +72,8 @@ struct RsLayout {
   static constexpr int SINK = 2 * STAGE;             // 16 bytes that dead staging writes hit
   static constexpr int BIAS = 2 * STAGE + 16;        // 32 bias floats
   static constexpr int TOTAL = BIAS + 32 * 4;         // double buffer + sink + bias
-  static constexpr int MAX_GROUPS = 16 * 16 / 4;     // 4-pixel groups of an input plane
-  static constexpr int NI = (8 * MAX_GROUPS + 255) / 256;
+  static constexpr int MAX_GROUPS = 16 * 16 / 8;     // 8-pixel groups of an input plane
+  static constexpr int NI = (2 * MAX_GROUPS + 63) / 64;  // input items per lane (two octets per wave)
   static constexpr int NW = (32 * 72 + 255) / 256;   // 16-byte weight vectors per thread
 };
 
@@ -169,23 +169,16 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // global offsets are computed before the first stage's loads go out; the LDS
   // positions follow while those loads fly (at one wave per SIMD every
   // instruction ahead of the first load delays the whole tile). ----
-  // input staging items: (one of the wave's two octets, 4-pixel group)
-  const int groups4 = (hw + 3) / 4;
-  const int in_items = 2 * groups4;
-  int in_off[L::NI];
-  int in_grp4[L::NI], in_oct[L::NI];
-  bool in_live[L::NI];
-#pragma unroll
-  for (int i = 0; i < L::NI; ++i) {
-    const int q = lane + i * 64;
-    in_live[i] = q < in_items;
-    const int qq = in_live[i] ? q : 0;
-    const int qd = (int)mdiv((unsigned)qq, a.mg_g4);
-    const int o = 2 * wave + qd;
-    in_grp4[i] = qq - qd * groups4;
-    in_oct[i] = o;
-    in_off[i] = 8 * o * hw + 4 * in_grp4[i];
-  }
+  // input staging items: (one of the wave's two octets, 8-pixel group); a
+  // group's first pixel is clamped so that its 8 pixels stay inside the plane
+  // (the last group of a plane whose size is not a multiple of 8 overlaps the
+  // one before and stores the same values again)
+  static_assert(L::NI == 1, "one input item per lane");
+  const int groups8 = (hw + 7) / 8;
+  const bool in_live = lane < 2 * groups8;
+  const int in_oct = 2 * wave + (lane >= groups8 ? 1 : 0);
+  const int in_f0 = max(0, min(8 * (lane - (lane >= groups8 ? groups8 : 0)), hw - 8));
+  const int in_off = 8 * in_oct * hw + in_f0;
   // weight staging vectors: (output channel, 16-byte piece of the wave's 16
   // channels x 9 taps, 288 contiguous bytes of the channel's 1152).  Channels
   // past the group's last read its last one: their sums feed only output
@@ -200,15 +193,14 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
                144 * wave + 8 * ((int)q - 18 * (int)col);
   }
 
-  u32x2_t rin[2][L::NI][8];  // two staged stages in flight: [set][item][channel], 4 pixels
+  u32x4_t rin[2][8];  // two staged stages in flight: [set][channel], 8 pixels
   u32x4_t rwv[2][L::NW];
   const int nstages = NS >= 1 && NS <= 4 ? NS : RAW ? a.sps : a.cig / RS_CH;
   if constexpr (NS == 5) __builtin_assume(nstages >= 5);
 
-  // the loads of one stage in three parts (part 0 and 1: the two halves of the
-  // input items, part 2: the weights), so that each tap row's multiplications
-  // can carry one part
-  static_assert(L::NI % 2 == 0, "input items split in two halves");
+  // the loads of one stage in three parts (part 0 and 1: the input's channels
+  // 0-3 and 4-7 of the octet, part 2: the weights), so that each tap row's
+  // multiplications can carry one part
   // buffer descriptors over the image's group of planes and the group's
   // weights: the per-lane part of every address is a 32-bit item offset and the
   // stage and plane parts are scalar offsets, so the loads need no vector
@@ -218,7 +210,7 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   auto load_part = [&](int s, int set, int part) __attribute__((always_inline)) {
     const long long xoff = (long long)s * RS_CH * hw;
     const long long woff = (long long)s * RS_CH * 9;
-    const int i0 = part == 1 ? L::NI / 2 : 0, i1 = part == 0 ? L::NI / 2 : part == 1 ? L::NI : 0;
+    const int e0 = part == 1 ? 4 : 0;
     if (part == 2) {
       if constexpr (WV) {  // 16-byte aligned weights
 #pragma unroll
@@ -234,26 +226,20 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
           rwv[set][i] = __builtin_bit_cast(u32x4_t, h);
         }
       }
-    } else if constexpr (XV) {  // 8-byte aligned planes of whole 4-pixel groups
+    } else if constexpr (XV) {  // 8-byte aligned planes of at least 8 pixels, a multiple of 4
 #pragma unroll
-      for (int i = i0; i < i1; ++i) {
+      for (int e = e0; e < e0 + 4; ++e)
+        rin[set][e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      x_rsrc, 2 * in_off, 2 * (int)(xoff + e * hw), 0));
+    } else {  // input not 8-byte aligned, or planes not a multiple of 4 or below 8: element loads
+      const E* src = ximg + xoff + in_off;
+      const int left = hw - 1 - in_f0;  // last valid pixel of this group
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          rin[set][i][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                           x_rsrc, 2 * in_off[i], 2 * (int)(xoff + e * hw), 0));
-      }
-    } else {  // input not 8-byte aligned or planes not a multiple of 4: element loads
+      for (int e = e0; e < e0 + 4; ++e) {
+        half8_t h;
 #pragma unroll
-      for (int i = i0; i < i1; ++i) {
-        const E* src = ximg + xoff + in_off[i];
-        const int left = hw - 1 - (in_off[i] % hw);  // last valid pixel of this group
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          half4_t h;
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) h[k4] = src[(long long)e * hw + min(k4, left)];
-          rin[set][i][e] = __builtin_bit_cast(u32x2_t, h);
-        }
+        for (int k8 = 0; k8 < 8; ++k8) h[k8] = src[(long long)e * hw + min(k8, left)];
+        rin[set][e] = __builtin_bit_cast(u32x4_t, h);
       }
     }
   };
@@ -275,16 +261,14 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // LDS positions of the staging items: input octets channel-innermost at
   // their padded tile position (pixels past the plane's end, hw % 4 != 0, go
   // nowhere), weight vectors into the output channel's padded row
-  int in_lds[L::NI][4];
+  int in_lds[8];
 #pragma unroll
-  for (int i = 0; i < L::NI; ++i)
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int f = 4 * in_grp4[i] + k4;
-      const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
-      const int pos = (ih + a.pt) * RS_COLS + iw + a.pl;
-      in_lds[i][k4] = f < hw ? (pos * 8 + slot8(pos, in_oct[i])) * 16 : -1;
-    }
+  for (int k8 = 0; k8 < 8; ++k8) {
+    const int f = in_f0 + k8;
+    const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
+    const int pos = (ih + a.pt) * RS_COLS + iw + a.pl;
+    in_lds[k8] = f < hw ? (pos * 8 + slot8(pos, in_oct)) * 16 : -1;
+  }
   int w_lds[L::NW];
 #pragma unroll
   for (int i = 0; i < L::NW; ++i) {
@@ -298,16 +282,15 @@ __global__ __launch_bounds__(256) void rowshift_kernel(const HaloArgs a) {
   // outstanding load there, including the stage just prefetched).
   auto store_part = [&](int buf, int set, int part) __attribute__((always_inline)) {
     unsigned char* base = smem + buf * L::STAGE;
-    const int i0 = part == 1 ? L::NI / 2 : 0, i1 = part == 0 ? L::NI / 2 : part == 1 ? L::NI : 0;
+    if (part < 2) {  // pixels 0-3 or 4-7 of the group: all 8 channels of the octet
+      const int k0 = part == 1 ? 4 : 0;
 #pragma unroll
-    for (int i = i0; i < i1; ++i) {
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
+      for (int k8 = k0; k8 < k0 + 4; ++k8) {
         half8_t v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, rin[set][i][e])[k4];
-        const bool live = in_live[i] && in_lds[i][k4] >= 0;
-        unsigned char* dst = live ? base + in_lds[i][k4] : smem + L::SINK;
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half8_t, rin[set][e])[k8];
+        const bool live = in_live && in_lds[k8] >= 0;
+        unsigned char* dst = live ? base + in_lds[k8] : smem + L::SINK;
         *reinterpret_cast<half8_t*>(dst) = v;
       }
     }
