@@ -337,8 +337,9 @@ int conv_integer_forward(const conv_problem* p, int x_type, int w_type, const vo
     r.pt = (int)g.pt; r.pl = (int)g.pl; r.ho = (int)g.ho; r.wo = (int)g.wo;
     r.n_ct = (int)ceil_div(g.cog, 32);
     const int64_t hw = g.h * g.w, howo = g.ho * g.wo;
-    // 4-byte loads of whole 4-pixel groups: every plane starts 4-byte aligned
-    r.xvec = reinterpret_cast<uintptr_t>(r.x) % 4 == 0 && hw % 4 == 0;
+    // 8-byte loads of 8-pixel groups at 4-byte aligned plane offsets, planes of
+    // at least 8 pixels
+    r.xvec = reinterpret_cast<uintptr_t>(r.x) % 4 == 0 && hw % 4 == 0 && hw >= 8;
     r.wvec = reinterpret_cast<uintptr_t>(r.wt) % 16 == 0;  // rows of cig * 9, a multiple of 16
     // every tile starts 16-byte aligned and holds whole 4-int vectors
     r.yvec = reinterpret_cast<uintptr_t>(r.y) % 16 == 0 &&

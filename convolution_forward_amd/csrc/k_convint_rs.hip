@@ -47,6 +47,8 @@ namespace convfwd {
 namespace {
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -71,8 +73,8 @@ struct CrLayout {
   static constexpr int TOTAL = BASE + 32 * 4;
   static constexpr int PITCH = R * CR_COLS + 4;      // ints per channel in a partial-sum copy
   static constexpr int COPY = 32 * PITCH;            // ints per wave's copy
-  static constexpr int MAX_GROUPS = 16 * 16 / 4;     // 4-pixel groups of a plane
-  static constexpr int NI = (2 * MAX_GROUPS + 63) / 64;
+  static constexpr int MAX_GROUPS = 16 * 16 / 8;     // 8-pixel groups of a plane
+  static constexpr int NI = (2 * MAX_GROUPS + 63) / 64;  // input items per lane (two runs per wave)
   static constexpr int NW = (32 * 18 + 63) / 64;     // 16-byte weight pieces per lane
   static_assert(4 * COPY * 4 <= SINK, "partial sums do not fit the stage buffers");
   static_assert(TOTAL <= 160 * 1024, "LDS");
@@ -160,54 +162,39 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   const int ka = XU ? 128 - xz : -xz;
   const unsigned xflip = XU ? 0x80808080u : 0u, wflip = WU ? 0x80808080u : 0u;
 
-  // ---- staging items of this wave: (one of its two 16-channel runs, 4-pixel
-  // group); each covers 16 channel planes x 4 pixels ----
-  const int groups4 = (hw + 3) / 4;
-  const int in_items = 2 * groups4;
-  int in_off[L::NI];
-  int in_lds[L::NI][4];  // LDS byte address (position p: (8 p + slot) 16), -1 for none
-  bool in_live[L::NI];
-#pragma unroll
-  for (int i = 0; i < L::NI; ++i) {
-    const int q = lane + i * 64;
-    in_live[i] = q < in_items;
-    const int qq = in_live[i] ? q : 0;
-    const int qd = (int)mdiv((unsigned)qq, a.mg_g4);
-    const int o = 2 * wave + qd;
-    const int grp4 = qq - qd * groups4;
-    in_off[i] = 16 * o * hw + 4 * grp4;
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int f = 4 * grp4 + k4;  // pixels past the plane's end are skipped
-      const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
-      const int pos = (ih + a.pt) * CR_COLS + iw + a.pl;
-      const bool ok = in_live[i] && f < hw;
-      in_lds[i][k4] = ok ? (pos * 8 + slot8(pos, o)) * 16 : -1;
-    }
-  }
+  // ---- staging items of this wave: (one of its two 16-channel runs, 8-pixel
+  // group); each covers 16 channel planes x 8 pixels.  A group's first pixel is
+  // clamped so that its 8 pixels stay inside the plane (the last group of a
+  // plane whose size is not a multiple of 8 overlaps the one before and stores
+  // the same bytes again; its byte sums count only the pixels it owns). ----
+  static_assert(L::NI == 1, "one input item per lane");
+  const int groups8 = (hw + 7) / 8;
+  const bool in_live = lane < 2 * groups8;
+  const int in_run = 2 * wave + (lane >= groups8 ? 1 : 0);
+  const int in_grp = lane - (lane >= groups8 ? groups8 : 0);
+  const int in_f0 = max(0, min(8 * in_grp, hw - 8));
+  const int in_own = 8 * in_grp;  // first pixel this item owns (sums)
+  const int in_off = 16 * in_run * hw + in_f0;
   // weight pieces: (output channel, 16-byte piece of the wave's 32 channels x
-  // 9 taps, 288 contiguous bytes of the channel's 1152 in the stage)
+  // 9 taps, 288 contiguous bytes of the channel's 1152 in the stage).  Channels
+  // past the group's last read its last one: they feed only output channels
+  // (and weight sums) that are never used.
   int w_off[L::NW];
-  int w_lds[L::NW];
-  bool w_ok[L::NW];
   static_assert(L::NW * 64 == 32 * 18, "one piece per lane and vector");
 #pragma unroll
   for (int i = 0; i < L::NW; ++i) {
-    const int q = lane + i * 64;
-    const int col = q / 18, piece = q - (q / 18) * 18;
-    w_ok[i] = co0 + col < a.cog;
-    w_off[i] = w_ok[i] ? (int)((long long)(co0 + col) * a.cig * 9 + 288 * wave + piece * 16) : 0;
-    w_lds[i] = L::IN_BYTES + col * CR_WROW + 288 * wave + piece * 16;
+    const unsigned q = (unsigned)(lane + i * 64);
+    const unsigned col = __umul24(q, 3641u) >> 16;  // q / 18, exact for q < 576
+    w_off[i] = (int)__umul24((unsigned)min(co0 + (int)col, a.cog - 1), (unsigned)(a.cig * 9)) +
+               288 * wave + 16 * ((int)q - 18 * (int)col);
   }
 
-  unsigned rin[L::NI][16];  // the next stage's input bytes: [item][plane], 4 pixels
+  u32x2_t rin[16];          // the next stage's input bytes: [plane], 8 pixels
   u32x4_t rwv[L::NW];
-  int pacc[L::NI][4];       // byte sums of the item's positions over its channels
+  int pacc[8];              // byte sums of the item's positions over its channels
   int sacc = 0;             // byte sum of this lane's B data (its channel's weights)
 #pragma unroll
-  for (int i = 0; i < L::NI; ++i)
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) pacc[i][k4] = 0;
+  for (int k8 = 0; k8 < 8; ++k8) pacc[k8] = 0;
   const int nstages = a.cig / CR_CH;
   const __amdgpu_buffer_rsrc_t x_rsrc = uniform_rsrc(ximg, nstages * CR_CH * hw);
   const __amdgpu_buffer_rsrc_t w_rsrc = uniform_rsrc(wg, a.cog * a.cig * 9);
@@ -230,37 +217,57 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
                       ((unsigned)src[4 * q + 2] << 16) | ((unsigned)src[4 * q + 3] << 24);
       }
     }
+    // a dead item's offset is a valid one, so every load is unconditional
+    if constexpr (XV) {  // 4-byte aligned planes of at least 8 pixels, a multiple of 4
 #pragma unroll
-    for (int i = 0; i < L::NI; ++i) {
-      // a dead item's offset is item 0's (valid), so every load is unconditional
-      const unsigned char* src = ximg + xoff + in_off[i];
-      if constexpr (XV) {  // 4-byte aligned planes of whole 4-pixel groups
+      for (int e = 0; e < 16; ++e)
+        rin[e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 x_rsrc, in_off, (int)xoff + e * hw, 0));
+    } else {  // byte loads, clamped to the plane's last pixel
+      const unsigned char* src = ximg + xoff + in_off;
+      const int left = hw - 1 - in_f0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          rin[i][e] = __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, in_off[i], (int)xoff + e * hw, 0);
-      } else {  // byte loads, clamped to the group's last pixel in the plane
-        const int left = hw - 1 - (in_off[i] % hw);
+      for (int e = 0; e < 16; ++e) {
+        unsigned v[2] = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          unsigned v = 0;
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) v |= (unsigned)src[(long long)e * hw + min(k4, left)] << (8 * k4);
-          rin[i][e] = v;
-        }
+        for (int k8 = 0; k8 < 8; ++k8)
+          v[k8 >> 2] |= (unsigned)src[(long long)e * hw + min(k8, left)] << (8 * (k8 & 3));
+        rin[e] = u32x2_t{v[0], v[1]};
       }
     }
   };
+  // only the first stage is loaded before anything else is computed
+  load_stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+  // LDS byte address of the item's pixels (position p: (8 p + slot) 16), -1 for
+  // none; weight pieces into the output channel's padded row
+  int in_lds[8];
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) {
+    const int f = in_f0 + k8;
+    const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
+    const int pos = (ih + a.pt) * CR_COLS + iw + a.pl;
+    const bool ok = in_live && f < hw;
+    in_lds[k8] = ok ? (pos * 8 + slot8(pos, in_run)) * 16 : -1;
+  }
+  int w_lds[L::NW];
+#pragma unroll
+  for (int i = 0; i < L::NW; ++i) {
+    const unsigned q = (unsigned)(lane + i * 64);
+    const unsigned col = __umul24(q, 3641u) >> 16;
+    w_lds[i] = L::IN_BYTES + (int)col * CR_WROW + 288 * wave + 16 * ((int)q - 18 * (int)col);
+  }
 
   // Branch-free: dead items and pixels past the plane write the sink.
   auto store_stage = [&](int buf) __attribute__((always_inline)) {
     unsigned char* base = smem + buf * L::STAGE;
 #pragma unroll
-    for (int i = 0; i < L::NI; ++i) {
+    for (int h = 0; h < 2; ++h) {  // pixels 4h .. 4h + 3
       unsigned px[4][4];  // [pixel][word]: 16 channels of each of the 4 pixels
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const unsigned in4[4] = {rin[i][4 * q] ^ xflip, rin[i][4 * q + 1] ^ xflip,
-                                 rin[i][4 * q + 2] ^ xflip, rin[i][4 * q + 3] ^ xflip};
+        const unsigned in4[4] = {rin[4 * q][h] ^ xflip, rin[4 * q + 1][h] ^ xflip,
+                                 rin[4 * q + 2][h] ^ xflip, rin[4 * q + 3][h] ^ xflip};
         unsigned t4[4];
         transpose4(in4, t4);
 #pragma unroll
@@ -268,9 +275,10 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
       }
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
+        const int k8 = 4 * h + k4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) pacc[i][k4] = dot_ones(px[k4][q], pacc[i][k4]);
-        unsigned char* dst = in_lds[i][k4] >= 0 ? base + in_lds[i][k4] : smem + L::SINK;
+        for (int q = 0; q < 4; ++q) pacc[k8] = dot_ones(px[k4][q], pacc[k8]);
+        unsigned char* dst = in_lds[k8] >= 0 ? base + in_lds[k8] : smem + L::SINK;
         *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{px[k4][0], px[k4][1], px[k4][2], px[k4][3]};
       }
     }
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
     for (int i = 0; i < L::NW; ++i) {
       u32x4_t v = rwv[i];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = w_ok[i] ? v[q] ^ wflip : 0u;
+      for (int q = 0; q < 4; ++q) v[q] = v[q] ^ wflip;
       *reinterpret_cast<u32x4_t*>(base + w_lds[i]) = v;
     }
   };
@@ -337,9 +345,8 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
     }
   };
 
-  // ---- prologue: the first stage's loads, the padding positions of both
-  // buffers (the pad byte, never rewritten), the sums' initial values ----
-  load_stage(0);
+  // ---- prologue: (the first stage's loads are out) the padding positions of
+  // both buffers (the pad byte, never rewritten), the sums' initial values ----
   const unsigned pad4 = xpad * 0x01010101u;
   for (int q = tid; q < 2 * L::NPOS; q += 256) {
     const int st = q / L::NPOS, pos = q - st * L::NPOS;
@@ -371,10 +378,8 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   __syncthreads();  // every wave is done with the stage buffers the copies overwrite
   // the byte sums meet in LDS (integer adds: any order)
 #pragma unroll
-  for (int i = 0; i < L::NI; ++i)
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-      if (in_lds[i][k4] >= 0) atomicAdd(&psum[in_lds[i][k4] >> 7], pacc[i][k4]);
+  for (int k8 = 0; k8 < 8; ++k8)
+    if (in_lds[k8] >= 0 && in_f0 + k8 >= in_own) atomicAdd(&psum[in_lds[k8] >> 7], pacc[k8]);
   atomicAdd(&sws[lane & 31], sacc);
   // each wave's partial sums as a copy [channel][row][16 columns]: accumulator
   // elements 4 i4 .. 4 i4 + 3 of row pair q are pixels 8 i4 + 4 (l / 32) + 0..3
@@ -418,28 +423,43 @@ __global__ __launch_bounds__(256) void convint_rowshift_kernel(const ConvIntRsAr
   }
   __syncthreads();
 
-  // ---- outputs: the tile's channel planes are contiguous in y; item e is
-  // flat output e of the tile ----
+  // ---- outputs: item (channel co, output row oh, column quad), quad fastest,
+  // then the row, then the channel; thread t takes items t + 256 k.  An item's
+  // four partial-sum vectors and Sx are 16-byte LDS reads at the copy layout's
+  // (channel, row, 4 columns); its outputs are 4 consecutive columns of one row
+  // of y, stored as int pairs when wo is even (8-byte aligned), else singly. ----
+  static_assert(R % 2 == 0, "items per thread");
+  constexpr int KI = R / 2;  // 32 x R x 4 items over 256 threads
   const int howo = a.ho * a.wo;
-  const int ftot = min(32, a.cog - co0) * howo;
   int* yt = a.y + ((long long)n * a.c_out + (long long)g * a.cog + co0) * howo;
-  auto value = [&](int e) __attribute__((always_inline)) {
-    const int c = (int)mdiv((unsigned)e, a.mg_howo);
-    const int rem = e - c * howo;
-    const int oh = (int)mdiv((unsigned)rem, a.mg_wo);
-    const int ow = rem - oh * a.wo;
-    const int li = c * L::PITCH + oh * CR_COLS + ow;
-    const unsigned v = (unsigned)cp[li] + (unsigned)cp[L::COPY + li] + (unsigned)cp[2 * L::COPY + li] +
-                       (unsigned)cp[3 * L::COPY + li];
-    return (int)(v + (unsigned)kbs[c] * (unsigned)sxs[oh * CR_COLS + ow] + (unsigned)bases[c]);
-  };
-  if (a.yvec) {  // the tile starts 16-byte aligned and holds whole vectors of 4
-    for (int v = tid; 4 * v < ftot; v += 256) {
-      const i32x4_t r = {value(4 * v), value(4 * v + 1), value(4 * v + 2), value(4 * v + 3)};
-      __builtin_nontemporal_store(r, reinterpret_cast<i32x4_t*>(yt) + v);
+  const i32x4_t* cp4 = reinterpret_cast<const i32x4_t*>(cp);
+  const i32x4_t* sx4 = reinterpret_cast<const i32x4_t*>(sxs);
+  const bool even = (a.wo & 1) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0;  // uniform
+  const int quad = tid & 3;            // 256 k % 4 == 0: the same quad for every k
+#pragma unroll
+  for (int k = 0; k < KI; ++k) {
+    const int rest = (tid + 256 * k) >> 2;
+    const int co = rest / R, oh = rest - (rest / R) * R;
+    const int li = (co * L::PITCH + oh * CR_COLS + 4 * quad) >> 2;  // 16-byte aligned
+    const i32x4_t t = cp4[li] + cp4[L::COPY / 4 + li] + cp4[2 * L::COPY / 4 + li] + cp4[3 * L::COPY / 4 + li];
+    const i32x4_t sx = sx4[(oh * CR_COLS + 4 * quad) >> 2];
+    const unsigned kb = (unsigned)kbs[co], bs = (unsigned)bases[co];
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (int)((unsigned)t[j] + kb * (unsigned)sx[j] + bs);
+    if (co0 + co < a.cog && oh < a.ho) {
+      int* dst = yt + co * howo + oh * a.wo + 4 * quad;
+      if (even) {
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+          if (4 * quad + 2 * j2 < a.wo)
+            __builtin_nontemporal_store(i32x2_t{v[2 * j2], v[2 * j2 + 1]}, reinterpret_cast<i32x2_t*>(dst) + j2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * quad + j < a.wo) __builtin_nontemporal_store(v[j], dst + j);
+      }
     }
-  } else {
-    for (int e = tid; e < ftot; e += 256) yt[e] = value(e);
   }
 }
 
