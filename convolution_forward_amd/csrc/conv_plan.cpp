@@ -136,11 +136,13 @@ bool depthwise_applicable(const Geo& g) { return !g.transpose && g.cig == 1; }
 // kernel rows of at most 8 taps, at most 24 (ci, kh) groups, output rows of at
 // most 128; the new input rows of one output row fit one 16-byte item per
 // thread, the first KH rows four, and the ring holds KH rows plus three rows'
-// worth of prefetched ones.
+// worth of prefetched ones; an image's input planes and a 64-channel tile of
+// its output planes are below 2 GiB (32-bit byte offsets).
 bool rowband_applicable(const Geo& g, int dtype) {
   return !g.transpose && half16(dtype) && g.g == 1 && g.sh == 2 && g.sw == 2 && g.dh == 1 &&
          g.dw == 1 && g.kw <= 8 && g.ci * g.kh <= 24 && g.kh + 4 * g.sh <= 16 && g.wo <= 128 &&
-         g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024;
+         g.sh * g.ci * ceil_div(g.w, 8) <= 256 && g.kh * g.ci * ceil_div(g.w, 8) <= 1024 &&
+         g.ci * g.h * g.w * 2 < 2147483648LL && 64 * g.ho * g.wo * 2 < 2147483648LL;
 }
 
 // Grouped implicit GEMM: float16, 8 input channels per group, at most 32 output

@@ -46,6 +46,17 @@ constexpr int RB_MAXST = 12;       // MFMA k-steps (pairs of (ci, kh) groups) at
 constexpr int RB_OPITCH = 128 * 2 + 16;  // LDS bytes per output-tile row (float16)
 constexpr int RB_FILLI = 1024;     // items of the first KH rows at most
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform so that it lives in scalar registers: every access
+// is a 32-bit byte offset, with no 64-bit address arithmetic per load or store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rb_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 }  // namespace
 
 // NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; WV: waves (8: two
@@ -82,6 +93,7 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   const int r1 = min(r0 + a.band_rows, a.ho);
 
   const E* __restrict__ x = static_cast<const E*>(a.x) + (long long)n * a.c_in * a.h * a.w;
+  const __amdgpu_buffer_rsrc_t x_rsrc = rb_rsrc(x, a.c_in * a.h * a.w * 2);
   const E* __restrict__ w = static_cast<const E*>(a.wt);
   static_assert(64 * 2 * RB_MAXST * 8 <= 64 * 1024, "weights staging");
 
@@ -115,11 +127,14 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   auto load_item = [&](int ir0, const Item& it) __attribute__((always_inline)) {
     const int v = it.v, ci = it.ci;
     const int ir = ir0 + it.r;
-    const E* src = x + ((long long)ci * a.h + min(max(ir, 0), a.h - 1)) * a.w + 8 * v;
+    // element offset of the item's vector in the clamped row (32-bit: the
+    // image's planes are below 2 GiB)
+    const int off = (int)__umul24((unsigned)(ci * a.h + min(max(ir, 0), a.h - 1)), (unsigned)a.w) + 8 * v;
     u32x4_t d;
     if constexpr (VEC) {  // w % 8 == 0, 16-byte aligned rows
-      d = *reinterpret_cast<const u32x4_t*>(src);
+      d = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, 2 * off, 0, 0));
     } else {
+      const E* src = x + off;
       half8_t h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) h[e] = src[min(e, a.w - 1 - 8 * v)];
@@ -262,6 +277,24 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   const E* __restrict__ res = static_cast<const E*>(a.res);
   E* y = static_cast<E*>(a.y);
   const long long ybase = ((long long)n * a.c_out + co0) * a.ho * a.wo;
+  // the tile's output planes (and the residual's) from channel co0 on; the
+  // offsets below stay under 64 ho wo elements
+  const int howo = a.ho * a.wo;
+  const int tile_bytes = (int)min(2147483647LL, (long long)(a.c_out - co0) * howo * 2);
+  const __amdgpu_buffer_rsrc_t y_rsrc = rb_rsrc(y + ybase, tile_bytes);
+  const __amdgpu_buffer_rsrc_t r_rsrc = rb_rsrc(res ? res + ybase : x, res ? tile_bytes : 2);
+  const int cn = min(WV == 8 ? 64 : 32, a.c_out - co0);  // channels of the tile
+  const int vpr = (a.wo + 7) / 8;
+  // this thread's output vectors of a row (fixed count, past the end the last
+  // one repeats): tile element offset at output row 0
+  int so[RB_NSTV], sv[RB_NSTV], sc[RB_NSTV];
+#pragma unroll
+  for (int k = 0; k < RB_NSTV; ++k) {
+    const int q = min(tid + NT * k, cn * vpr - 1);
+    sc[k] = (int)mdiv((unsigned)q, a.mg_vpr);
+    sv[k] = q - sc[k] * vpr;
+    so[k] = (int)__umul24((unsigned)sc[k], (unsigned)howo) + 8 * sv[k];
+  }
 
   // one output row; J = (oh - r0) % 3 at compile time picks the prefetch registers
   auto row = [&](int oh, auto jc) __attribute__((always_inline)) {
@@ -306,10 +339,12 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = acc[j][i] + bv;
       if (res) {  // residual read in the fragment layout (clamped, before any store)
+        const int rrow = (int)__umul24((unsigned)min(c, a.c_out - co0 - 1), (unsigned)howo) + oh * a.wo;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int ow = min(pxb + 8 * (i / 4) + 4 * half + (i % 4), a.wo - 1);
-          v[i] = v[i] + (float)res[ybase + ((long long)min(c, a.c_out - co0 - 1) * a.ho + oh) * a.wo + ow];
+          const unsigned short r16 = __builtin_amdgcn_raw_buffer_load_b16(r_rsrc, 2 * (rrow + ow), 0, 0);
+          v[i] = v[i] + (float)__builtin_bit_cast(E, r16);
         }
       }
       act_apply<AK>(v, a.act, a.alpha, a.beta);
@@ -323,16 +358,14 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     }
     __syncthreads();
     // ---- whole rows of the tile: 16-byte vectors of 8 output columns ----
-    const int cn = min(WV == 8 ? 64 : 32, a.c_out - co0);  // channels of the tile
-    const int vpr = (a.wo + 7) / 8;
     if constexpr (VEC) {  // wo % 8 == 0: whole vectors; past the end the last one
       // repeats (same value, same address), so the store count is fixed
+      const int orow = oh * a.wo;
 #pragma unroll
       for (int k = 0; k < RB_NSTV; ++k) {
-        const int q = min(tid + NT * k, cn * vpr - 1);
-        const int c = (int)mdiv((unsigned)q, a.mg_vpr), v = q - c * vpr;
-        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + c * RB_OPITCH + 16 * v);
-        store_out(reinterpret_cast<u32x4_t*>(y + ybase + ((long long)c * a.ho + oh) * a.wo + 8 * v), d);
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + sc[k] * RB_OPITCH + 16 * sv[k]);
+        // nontemporal (the output is not read back)
+        __builtin_amdgcn_raw_buffer_store_b128(d, y_rsrc, 2 * (so[k] + orow), 0, 2);
       }
     } else {
       for (int q = tid; q < cn * vpr; q += NT) {
