@@ -142,6 +142,13 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.vec = reinterpret_cast<uintptr_t>(xc) % 16 == 0 && reinterpret_cast<uintptr_t>(yc) % 16 == 0 &&
               g.w % 8 == 0 && g.wo % 8 == 0;
       {
+        // two output rows per step: 64-channel tiles on the vector path, the new
+        // rows of two output rows one item per thread of 512, the first step's
+        // KH + SH rows at most the fill's item count
+        const int64_t nv = ceil_div(g.w, 8);
+        a.two_rows = a.vec && g.co > 32 && 2 * g.sh * g.ci * nv <= 512 && (g.kh + g.sh) * g.ci * nv <= 1024;
+      }
+      {
         const int64_t per_co = g.ci * g.kh * g.kw;
         // every tile's run starts at a multiple of 64 channels: whole vectors when
         // the base is aligned and each tile's length is a multiple of 8 halves

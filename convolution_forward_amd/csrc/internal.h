@@ -155,6 +155,7 @@ struct RowbandArgs {
   int ring_bytes;               // c_in * 16 rows * rpitch * 2
   int vec;                      // x, y 16-byte aligned, w % 8 == 0 and wo % 8 == 0
   int wvec;                     // weights 16-byte aligned, tile runs whole vectors
+  int two_rows;                 // two output rows per step (eight waves, whole vectors)
   Magic mg_nv;                  // division by the 8-half vectors per input row
   Magic mg_cin;                 // division by c_in
   Magic mg_vpr;                 // division by the 8-output vectors per output row

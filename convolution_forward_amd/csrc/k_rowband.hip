@@ -61,8 +61,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rb_rsrc(const void* p, int byt
 
 // NST: MFMA k-steps, ceil(Cin * KH / 2) <= RB_MAXST; WV: waves (8: two
 // 32-channel blocks x four 32-pixel blocks; 4: one channel block); VEC: whole
-// 16-byte input and output vectors.
-template <typename E, int NST, int WV, bool VEC, int AK = -1>
+// 16-byte input and output vectors; TWO: two output rows per step (one barrier
+// pair per two rows, two independent accumulator chains per wave; the output
+// tile holds two rows).
+template <typename E, int NST, int WV, bool VEC, int AK = -1, bool TWO = false>
 __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   typedef E half8_t __attribute__((ext_vector_type(8)));
   typedef E half4_t __attribute__((ext_vector_type(4)));
@@ -72,10 +74,10 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   constexpr int RB_FILL = (RB_FILLI + NT - 1) / NT;  // items per thread for the first KH rows
   constexpr int RB_NSTV = 64 * 16 / NT;              // output vectors per thread and row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_rb[];
-  // ring: [ci][slot][rp halves]; output tile [64][RB_OPITCH bytes]; bias [64]
+  // ring: [ci][slot][rp halves]; output tile [64 (two rows: 128)][RB_OPITCH bytes]; bias [64]
   E* ring = reinterpret_cast<E*>(smem_rb);
   unsigned char* otile = smem_rb + a.ring_bytes;
-  float* bsm = reinterpret_cast<float*>(otile + 64 * RB_OPITCH);
+  float* bsm = reinterpret_cast<float*>(otile + (TWO ? 128 : 64) * RB_OPITCH);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,7 +171,8 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
   // latencies overlap; then the weights pass through the ring area into
   // registers, the ring is zeroed and the first rows are stored ----
   const int first = r0 * a.sh - a.pt;
-  const int fill_items = a.kh * a.c_in * nv;
+  // the first step's rows: KH input rows, and SH more for a second output row
+  const int fill_items = (a.kh + (TWO ? a.sh : 0)) * a.c_in * nv;
   u32x4_t t[RB_FILL];
   Item fit[RB_FILL];
 #pragma unroll
@@ -178,11 +181,15 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     t[k] = load_item(first, fit[k]);
   }
   // prefetch ring of three: the new rows of output row o sit in lr[(o - r0) % 3]
-  const Item sit = decomp(tid, step_items);
+  const Item sit = decomp(tid, TWO ? 2 * step_items : step_items);
   u32x4_t lr[3];
-  lr[1] = load_item(new_rows(r0 + 1), sit);
-  lr[2] = load_item(new_rows(r0 + 2), sit);
-  lr[0] = load_item(new_rows(r0 + 3), sit);
+  if constexpr (TWO) {  // step k's new rows sit in lr[k % 2]; step 1's are loaded here
+    lr[1] = load_item(new_rows(r0 + 2), sit);
+  } else {
+    lr[1] = load_item(new_rows(r0 + 1), sit);
+    lr[2] = load_item(new_rows(r0 + 2), sit);
+    lr[0] = load_item(new_rows(r0 + 3), sit);
+  }
   // the tile's weights ([<= 64 channels][groups * kw] contiguous): 16-byte reads
   // when aligned (at most RB_WV per thread), element reads otherwise
   const int per_co = groups * a.kw;
@@ -381,19 +388,104 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     }
   };
 
-  for (int oh = r0; oh < r1; oh += 3) {  // unrolled by three: prefetch sets at compile time
-    row(oh, std::integral_constant<int, 0>{});
-    if (oh + 1 >= r1) break;
-    row(oh + 1, std::integral_constant<int, 1>{});
-    if (oh + 2 >= r1) break;
-    row(oh + 2, std::integral_constant<int, 2>{});
+  // two output rows oh, oh + 1 (the second is computed but not stored past the
+  // band); J = step % 2 at compile time picks the prefetch registers
+  auto row2 = [&](int oh, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    __syncthreads();  // rows of this step present; the previous step's tile has left
+    // the next step's new rows go to ring slots this step does not read (the
+    // ring spans KH + 3 SH rows from this step's first), then those registers
+    // take the rows of the step after
+    store_item(new_rows(oh + 2), sit, lr[(J + 1) % 2]);
+    lr[J] = load_item(new_rows(oh + 4), sit);
+
+    floatx16_t acc[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
+    const int ir_base = oh * a.sh - a.pt;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int slot = (ir_base + r * a.sh + gkh[st]) & (RB_RING - 1);
+        const unsigned int* src = reinterpret_cast<const unsigned int*>(ring + gbase[st] + slot * rp + pxo[0]);
+        u32x4_t f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = src[e];
+        acc[r] = mfma_32x32x16<E>(f, wf[st], acc[r]);
+      }
+    }
+    const int c = 32 * cbw + (lane & 31);
+    const int pxb = 32 * pb0;
+    const float bv = bsm[c];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = acc[r][i] + bv;
+      if (res) {  // residual read in the fragment layout (clamped, before any store)
+        const int rrow = (int)__umul24((unsigned)min(c, a.c_out - co0 - 1), (unsigned)howo) +
+                         min(oh + r, a.ho - 1) * a.wo;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ow = min(pxb + 8 * (i / 4) + 4 * half + (i % 4), a.wo - 1);
+          const unsigned short r16 = __builtin_amdgcn_raw_buffer_load_b16(r_rsrc, 2 * (rrow + ow), 0, 0);
+          v[i] = v[i] + (float)__builtin_bit_cast(E, r16);
+        }
+      }
+      act_apply<AK>(v, a.act, a.alpha, a.beta);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half4_t h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (E)v[4 * q + i];
+        *reinterpret_cast<half4_t*>(otile + (r * 64 + c) * RB_OPITCH + 2 * (pxb + 8 * q + 4 * half)) = h;
+      }
+    }
+    __syncthreads();
+    // ---- whole rows of the tile: 16-byte vectors of 8 output columns (the
+    // vector path: wo % 8 == 0) ----
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (oh + r < r1) {  // uniform
+        const int orow = (oh + r) * a.wo;
+#pragma unroll
+        for (int k = 0; k < RB_NSTV; ++k) {
+          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + (r * 64 + sc[k]) * RB_OPITCH + 16 * sv[k]);
+          __builtin_amdgcn_raw_buffer_store_b128(d, y_rsrc, 2 * (so[k] + orow), 0, 2);
+        }
+      }
+    }
+  };
+
+  if constexpr (TWO) {
+    static_assert(WV == 8 && VEC, "two-row steps: eight waves, whole vectors");
+    for (int oh = r0; oh < r1; oh += 4) {  // unrolled by two: prefetch sets at compile time
+      row2(oh, std::integral_constant<int, 0>{});
+      if (oh + 2 >= r1) break;
+      row2(oh + 2, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int oh = r0; oh < r1; oh += 3) {  // unrolled by three: prefetch sets at compile time
+      row(oh, std::integral_constant<int, 0>{});
+      if (oh + 1 >= r1) break;
+      row(oh + 1, std::integral_constant<int, 1>{});
+      if (oh + 2 >= r1) break;
+      row(oh + 2, std::integral_constant<int, 2>{});
+    }
   }
 }
 
 template <typename E, int NST>
 static void launch_rb_nst(const RowbandArgs& a, dim3 grid, size_t lds, hipStream_t s) {
   const bool two = a.c_out > 32;
-  if (a.vec && a.act == 1) {  // ReLU, the common case, fixed at compile time
+  if (a.two_rows) {  // eight waves, whole vectors: two output rows per step
+    lds += 64 * RB_OPITCH;
+    if (a.act == 1) hipLaunchKernelGGL((rowband_kernel<E, NST, 8, true, 1, true>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((rowband_kernel<E, NST, 8, true, -1, true>), grid, dim3(512), lds, s, a);
+  } else if (a.vec && a.act == 1) {  // ReLU, the common case, fixed at compile time
     if (two) hipLaunchKernelGGL((rowband_kernel<E, NST, 8, true, 1>), grid, dim3(512), lds, s, a);
     else hipLaunchKernelGGL((rowband_kernel<E, NST, 4, true, 1>), grid, dim3(256), lds, s, a);
   } else if (a.vec) {
