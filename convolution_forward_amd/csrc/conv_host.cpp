@@ -296,6 +296,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_w = make_magic((unsigned)g.w);
       a.mg_wo = make_magic((unsigned)g.wo);
       a.mg_kw = make_magic((unsigned)g.kw);
+      a.mg_taps = make_magic((unsigned)(g.kh * g.kw));
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_grouped(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_TRANSPOSE_GEMM_COL2IM && pl.ct_fused) {

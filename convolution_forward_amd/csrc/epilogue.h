@@ -38,10 +38,23 @@ __device__ __forceinline__ float apply_act(float v, int act, float alpha, float 
   }
 }
 
-template <int ACT>
+// Logistic function from the hardware base-2 exponential and reciprocal
+// (v_exp_f32 and v_rcp_f32, about 1 ulp each; scaling the argument by log2 e
+// adds |v| 2^-24 relative): within about |v| + 3 float32 ulps of 1 / (1 + e^-v),
+// inside a 16-bit output's rounding and the accumulation tolerance (which
+// grows with the sum's magnitude, itself at least |v|).  For kernels whose
+// outputs are stored in 16 bits; NaN propagates, +-inf give 1 and 0.
+__device__ __forceinline__ float logistic_fast(float v) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v));
+}
+
+// FX: sigmoid and SiLU through logistic_fast (16-bit outputs only).
+template <int ACT, bool FX = false>
 __device__ __forceinline__ float act_t(float v, float alpha, float beta) {
   if constexpr (ACT == 1) return v > 0.0f ? v : 0.0f;
   else if constexpr (ACT == 2) return tanhf(v);
+  else if constexpr (ACT == 3 && FX) return logistic_fast(v);
+  else if constexpr (ACT == 4 && FX) return v * logistic_fast(v);
   else if constexpr (ACT == 3) return 1.0f / (1.0f + expf(-v));
   else if constexpr (ACT == 4) return v / (1.0f + expf(-v));
   else if constexpr (ACT == 5) return fminf(fmaxf(alpha * v + beta, 0.0f), 1.0f);
@@ -54,12 +67,12 @@ __device__ __forceinline__ float act_t(float v, float alpha, float beta) {
 // Activation over a thread's whole batch of outputs: one uniform branch, then a
 // branch-free loop (an activation switch per element would multiply the code by
 // the batch size).
-template <int N>
+template <bool FX = false, int N>
 __device__ __forceinline__ void act_array(float (&v)[N], int act, float alpha, float beta) {
   switch (act) {
 #define CONVFWD_ACT_CASE(A)                                                   \
   case A:                                                                     \
-    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = act_t<A>(v[i], alpha, beta); \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = act_t<A, FX>(v[i], alpha, beta); \
     break;
     CONVFWD_ACT_CASE(1)
     CONVFWD_ACT_CASE(2)
@@ -101,14 +114,14 @@ __device__ __forceinline__ T epilogue_one(float v, const T* bias, const T* res, 
 
 // The activation fixed at compile time (AK = the ONNX code), or, for AK < 0,
 // the launch's code chosen at run time.  A fixed activation keeps the other
-// activations' code (and its registers) out of the kernel.
-template <int AK, int N>
+// activations' code (and its registers) out of the kernel.  FX: see act_t.
+template <int AK, bool FX = false, int N>
 __device__ __forceinline__ void act_apply(float (&v)[N], int act, float alpha, float beta) {
   if constexpr (AK < 0) {
-    act_array(v, act, alpha, beta);
+    act_array<FX>(v, act, alpha, beta);
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = act_t<AK>(v[i], alpha, beta);
+    for (int i = 0; i < N; ++i) v[i] = act_t<AK, FX>(v[i], alpha, beta);
   }
 }
 

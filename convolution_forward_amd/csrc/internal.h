@@ -112,6 +112,7 @@ struct GroupedArgs {
   int xs_bytes;          // LDS bytes of the staged plane (16 per position)
   int vec;               // x 8-byte aligned and h * w % 4 == 0
   Magic mg_w, mg_wo, mg_kw;  // divisors w, wo and kw
+  Magic mg_taps;             // divisor kh * kw
   int act;
   float alpha, beta;
 };

@@ -37,6 +37,18 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int GC_MAXTAPS = 10;  // k-steps of two taps: at most 5
 constexpr int GC_NT = 1024;     // threads per workgroup: 16 waves, 4 per SIMD
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform: accesses are 32-bit byte offsets, and an offset
+// past the range reads 0 and drops a store (so no access sits behind a branch).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gc_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+constexpr int GC_OOB = (int)0x80000000;  // a byte offset past every descriptor's range
+
 }  // namespace
 
 // KS: k-steps (taps <= 2 KS).  CB: 8-channel row groups of the output
@@ -51,6 +63,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   u32x4_t* xs = reinterpret_cast<u32x4_t*>(smem);                      // [pos] octets
   u32x4_t* wl = reinterpret_cast<u32x4_t*>(smem + a.xs_bytes);          // [co][tap] octets
   float* bsm = reinterpret_cast<float*>(smem + a.xs_bytes + 32 * GC_MAXTAPS * 16);
+  u32x4_t* sink = reinterpret_cast<u32x4_t*>(smem + a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = blockIdx.x / a.groups, g = blockIdx.x - n * a.groups;
@@ -83,12 +96,14 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
       }
     }
   }
-  // weights (cog x 8 x taps halves, contiguous) and bias: one element per item
-  const int nw = a.cog * 8 * taps;  // <= 32 x 8 x 10
-  constexpr int WN = (32 * 8 * GC_MAXTAPS + GC_NT - 1) / GC_NT;
-  E wv[WN];
+  // weights (cog x 8 x taps halves, contiguous): thread q < cog taps gathers
+  // the 8 input channels of (channel q / taps, tap q % taps), one octet
+  const int nwt = a.cog * taps;  // <= 32 x 10 < GC_NT
+  const int wq = min(tid, nwt - 1);
+  const int wco = (int)mdiv((unsigned)wq, a.mg_taps), wt = wq - wco * taps;
+  half8_t wv;
 #pragma unroll
-  for (int i = 0; i < WN; ++i) wv[i] = w[min(tid + GC_NT * i, nw - 1)];
+  for (int ci = 0; ci < 8; ++ci) wv[ci] = w[(wco * 8 + ci) * taps + wt];
   const E bv_in = *(bias ? bias + g * a.cog + min(tid, a.cog - 1) : x);
 
   // ---- zero the staged plane (padding positions stay zero) and the weight
@@ -97,33 +112,26 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   for (int q = tid; q < npos; q += GC_NT) xs[q] = u32x4_t{0, 0, 0, 0};
   for (int q = tid; q < 32 * GC_MAXTAPS; q += GC_NT) wl[q] = u32x4_t{0, 0, 0, 0};
   __syncthreads();
+  // branch-free: pixels past the plane and dead items write the sink
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = tid + GC_NT * i;
-    if (q < groups4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = 4 * q + j;
-        if (f < hw) {
-          half8_t v;
+    for (int j = 0; j < 4; ++j) {
+      const int f = 4 * q + j;
+      half8_t v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, xr[i][e])[j];
-          const int ih = (int)mdiv((unsigned)f, a.mg_w), iw = f - ih * a.w;
-          xs[(ih + a.pt) * a.wp + iw + a.pl] = __builtin_bit_cast(u32x4_t, v);
-        }
-      }
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(half4_t, xr[i][e])[j];
+      const int fc = min(f, hw - 1);
+      const int ih = (int)mdiv((unsigned)fc, a.mg_w), iw = fc - ih * a.w;
+      u32x4_t* dst = q < groups4 && f < hw ? xs + (ih + a.pt) * a.wp + iw + a.pl : sink;
+      *dst = __builtin_bit_cast(u32x4_t, v);
     }
   }
-#pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    const int q = tid + GC_NT * i;  // element (co, ci, tap) of the group's weights
-    if (q < nw) {
-      const int co = q / (8 * taps), r = q - co * 8 * taps;
-      const int ci = r / taps, t = r - ci * taps;
-      reinterpret_cast<E*>(wl + co * GC_MAXTAPS + t)[ci] = wv[i];
-    }
-  }
-  if (tid < 32) bsm[tid] = (float)bv_in;
+  *(tid < nwt ? wl + wco * GC_MAXTAPS + wt : sink) = __builtin_bit_cast(u32x4_t, wv);
+  // without a bias the slot holds -0.0, whose addition is exact for every
+  // value (a zero keeps its sign), so the epilogue adds it unconditionally
+  if (tid < 32) bsm[tid] = bias ? (float)bv_in : -0.0f;
   __syncthreads();
 
   // ---- A fragments: lane l holds output channel l % 32, taps 2 ks + l / 32 ----
@@ -146,16 +154,21 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   // output channels, which need all 16 accumulator elements); wave w takes
   // passes w, w + 16, ...  Lane l: pixel l % 32 of each block, output channels
   // 8 (i / 4) + 4 (l / 32) + i % 4 for accumulator element i < 4 CB.
-  E* __restrict__ yg = y + obase;
-  const E* rg = res ? res + obase : nullptr;
+  // the group's output (and residual) planes: cog x howo halves from obase
+  const int tile_bytes = a.cog * howo * 2;
+  const __amdgpu_buffer_rsrc_t y_rsrc = gc_rsrc(y + obase, tile_bytes);
+  const __amdgpu_buffer_rsrc_t r_rsrc = gc_rsrc(res ? res + obase : x, res ? tile_bytes : 2);
   const int nblk = (howo + 31) / 32;
   constexpr int NB = CB >= 4 ? 1 : 2;
   for (int b0 = NB * wave; b0 < nblk; b0 += NB * (GC_NT / 64)) {
     floatx16_t acc[NB];
-    int pix[NB];
+    int pix[NB], pbase[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       pix[u] = 32 * (b0 + u) + (lane & 31);
+      const int p = min(pix[u], howo - 1);
+      const int oh = (int)mdiv((unsigned)p, a.mg_wo), ow = p - oh * a.wo;
+      pbase[u] = oh * a.sh * a.wp + ow * a.sw;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
     }
@@ -163,36 +176,40 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        const int p = min(pix[u], howo - 1);
-        const int oh = (int)mdiv((unsigned)p, a.mg_wo), ow = p - oh * a.wo;
-        const u32x4_t v = xs[oh * a.sh * a.wp + ow * a.sw + tofs[ks]];
+        const u32x4_t v = xs[pbase[u] + tofs[ks]];
         const u32x4_t bf = tok[ks] ? v : u32x4_t{0, 0, 0, 0};
         acc[u] = mfma_32x32x16<E>(af[ks], bf, acc[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      float v[4 * CB];
+      // output (co, pix) at byte offset 2 (co howo + pix); outside the tile
+      // (co >= cog or pix >= howo) the offset lies past the descriptors' range
+      const int pofs = 2 * (4 * hi * howo + pix[u]);
+      const bool pok = pix[u] < howo;
+      auto off = [&](int i) __attribute__((always_inline)) {
+        const int c8 = 8 * (i / 4) + (i & 3);  // channel less 4 hi
+        return pok && c8 + 4 * hi < a.cog ? pofs + 2 * howo * c8 : GC_OOB;
+      };
+      // at most 8 values at a time (register pressure at four waves per SIMD)
+      constexpr int CH = 4 * CB > 8 ? 8 : 4 * CB;
 #pragma unroll
-      for (int i = 0; i < 4 * CB; ++i) {
-        const int co = 8 * (i / 4) + 4 * hi + (i & 3);
-        const float bv = bsm[co];  // read outside the condition: no branch per value
-        v[i] = bias ? acc[u][i] + bv : acc[u][i];
-      }
-      if (rg) {
+      for (int i0 = 0; i0 < 4 * CB; i0 += CH) {
+        float v[CH];
 #pragma unroll
-        for (int i = 0; i < 4 * CB; ++i) {
-          const int co = min(8 * (i / 4) + 4 * hi + (i & 3), a.cog - 1);
-          v[i] = v[i] + (float)rg[co * howo + min(pix[u], howo - 1)];
+        for (int j = 0; j < CH; ++j) {
+          const int i = i0 + j;
+          v[j] = acc[u][i] + bsm[8 * (i / 4) + 4 * hi + (i & 3)];
         }
-      }
-      act_apply<AK>(v, a.act, a.alpha, a.beta);
-      if (pix[u] < howo) {
+        if (res) {  // uniform
 #pragma unroll
-        for (int i = 0; i < 4 * CB; ++i) {
-          const int co = 8 * (i / 4) + 4 * hi + (i & 3);
-          if (co < a.cog) store_out(yg + co * howo + pix[u], (E)v[i]);
+          for (int j = 0; j < CH; ++j)
+            v[j] = v[j] + (float)__builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(r_rsrc, off(i0 + j), 0, 0));
         }
+        act_apply<AK, true>(v, a.act, a.alpha, a.beta);  // 16-bit outputs: fast logistic
+#pragma unroll
+        for (int j = 0; j < CH; ++j)  // nontemporal: the output is not read back
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (E)v[j]), y_rsrc, off(i0 + j), 0, 2);
       }
     }
   }
@@ -201,7 +218,7 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
 template <typename E>
 static hipError_t launch_grouped_t(const GroupedArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.n * a.groups));
-  const size_t lds = (size_t)a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4;
+  const size_t lds = (size_t)a.xs_bytes + 32 * GC_MAXTAPS * 16 + 32 * 4 + 16;  // + the sink
   const int taps = a.kh * a.kw;
   if (taps > GC_MAXTAPS) return hipErrorInvalidValue;
   // ReLU and sigmoid with the activation fixed at compile time on the vector path
