@@ -80,7 +80,11 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   // plane clamp to its last group; their LDS writes repeat that group's) ----
   const int groups4 = (hw + 3) / 4;
   constexpr int NI = 4096 / 4 / GC_NT;  // items per thread (planes up to 4096 pixels)
+  static_assert(NI == 1, "one item per thread");
+  // waves holding no item load and stage nothing (wave-uniform)
+  const bool xwave = 64 * __builtin_amdgcn_readfirstlane(wave) < groups4;
   u32x2_t xr[NI][8];
+  if (xwave) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = min(tid + GC_NT * i, groups4 - 1);
@@ -96,14 +100,18 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
       }
     }
   }
+  }
   // weights (cog x 8 x taps halves, contiguous): thread q < cog taps gathers
   // the 8 input channels of (channel q / taps, tap q % taps), one octet
   const int nwt = a.cog * taps;  // <= 32 x 10 < GC_NT
+  const bool wwave = 64 * __builtin_amdgcn_readfirstlane(wave) < nwt;  // uniform
   const int wq = min(tid, nwt - 1);
   const int wco = (int)mdiv((unsigned)wq, a.mg_taps), wt = wq - wco * taps;
   half8_t wv;
+  if (wwave) {
 #pragma unroll
-  for (int ci = 0; ci < 8; ++ci) wv[ci] = w[(wco * 8 + ci) * taps + wt];
+    for (int ci = 0; ci < 8; ++ci) wv[ci] = w[(wco * 8 + ci) * taps + wt];
+  }
   const E bv_in = *(bias ? bias + g * a.cog + min(tid, a.cog - 1) : x);
 
   // ---- zero the staged plane (padding positions stay zero) and the weight
@@ -112,7 +120,9 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
   for (int q = tid; q < npos; q += GC_NT) xs[q] = u32x4_t{0, 0, 0, 0};
   for (int q = tid; q < 32 * GC_MAXTAPS; q += GC_NT) wl[q] = u32x4_t{0, 0, 0, 0};
   __syncthreads();
-  // branch-free: pixels past the plane and dead items write the sink
+  // branch-free within a wave: pixels past the plane and dead items write
+  // the sink
+  if (xwave) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int q = tid + GC_NT * i;
@@ -128,7 +138,8 @@ __global__ __launch_bounds__(GC_NT) void grouped_c8_kernel(const GroupedArgs a) 
       *dst = __builtin_bit_cast(u32x4_t, v);
     }
   }
-  *(tid < nwt ? wl + wco * GC_MAXTAPS + wt : sink) = __builtin_bit_cast(u32x4_t, wv);
+  }
+  if (wwave) *(tid < nwt ? wl + wco * GC_MAXTAPS + wt : sink) = __builtin_bit_cast(u32x4_t, wv);
   // without a bias the slot holds -0.0, whose addition is exact for every
   // value (a zero keeps its sign), so the epilogue adds it unconditionally
   if (tid < 32) bsm[tid] = bias ? (float)bv_in : -0.0f;
