@@ -164,6 +164,13 @@ int64_t pw_items(int64_t n, int64_t pixel_tiles, int64_t channel_tiles, int64_t 
   return t;
 }
 
+// x, w and y (elements) of the float16 pointwise kernel below 2 GiB each: its
+// loads and stores take 32-bit byte offsets.
+bool pw_bytes_ok(int64_t x_elems, int64_t w_elems, int64_t y_elems) {
+  const int64_t lim = (1LL << 30) - 1024;  // elements of 2 bytes, with slack for a tile past the end
+  return x_elems < lim && w_elems < lim && y_elems < lim;
+}
+
 // Pointwise GEMM on x as it lies: 1x1, stride 1, no padding, one group, float16,
 // whole channel octets and planes of whole 4-pixel groups.
 bool pointwise_applicable(const Geo& g, int dtype) {
@@ -174,7 +181,8 @@ bool pointwise_applicable(const Geo& g, int dtype) {
   return !g.transpose && half16(dtype) && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
          g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
          (g.h * g.w) % 4 == 0 && g.h * g.w >= 4 &&
-         pw_items(g.n, ceil_div(g.h * g.w, 128), ceil_div(g.co, 64), g.ci) < (1LL << 30);
+         pw_items(g.n, ceil_div(g.h * g.w, 128), ceil_div(g.co, 64), g.ci) < (1LL << 30) &&
+         pw_bytes_ok(g.n * g.ci * g.h * g.w, g.co * g.ci, g.n * g.co * g.h * g.w);
 }
 
 // ConvTranspose whose kernel equals its stride of 2 with no padding: each output
@@ -185,7 +193,8 @@ bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
   return g.transpose && half16(dtype) && g.g == 1 && g.kh == 2 && g.kw == 2 && g.sh == 2 &&
          g.sw == 2 && g.dh == 1 && g.dw == 1 && g.pt == 0 && g.pl == 0 && g.pb == 0 &&
          g.pr == 0 && g.oph == 0 && g.opw == 0 && !residual && g.w % 4 == 0 && g.w <= 128 &&
-         pw_items(g.n, ceil_div(g.h * g.w, (128 / g.w) * g.w), ceil_div(4 * g.co, 128), g.ci) < (1LL << 30);
+         pw_items(g.n, ceil_div(g.h * g.w, (128 / g.w) * g.w), ceil_div(4 * g.co, 128), g.ci) < (1LL << 30) &&
+         pw_bytes_ok(g.n * g.ci * g.h * g.w, 4 * g.co * g.ci, 4 * g.n * g.co * g.h * g.w);
 }
 
 // Winograd F(2x2, 3x3): 16-bit operands, 3x3, stride 1, dilation 1, input

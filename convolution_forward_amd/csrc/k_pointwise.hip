@@ -61,6 +61,17 @@ constexpr int PW_OROW = PW_TP * 2 + 16;    // LDS bytes per output-tile row (flo
 // octet slot at pixel row p: the 16 rows of an MFMA block land on distinct banks
 __device__ __forceinline__ int pw_slot(int p, int o) { return o ^ ((p >> 1) & 7); }
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform.  Accesses take a per-lane 32-bit byte offset and a
+// uniform one; an access past the range reads 0 (a store is dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pw_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 }  // namespace
 
 // VEC: x 8-byte, w 16-byte (8-byte for ConvTranspose), y 16-byte and residual
@@ -103,6 +114,26 @@ void pointwise_f16_kernel(const PwArgs a) {
   constexpr int KG = PW_KC * PW_TC / 4 / 256;
   const int kg = tid % (PW_KC / KG), mq = tid / (PW_KC / KG);
 
+  // Vector path: every load is a per-thread byte offset fixed for the launch
+  // plus a uniform per-item one, through buffer descriptors (tensors below
+  // 2 GiB).  Nothing is clamped: channels past c_in are zeroed when staged,
+  // and pixels past the plane or rows past c_out only feed outputs that are
+  // never stored (reads past a tensor's end return 0).
+  const __amdgpu_buffer_rsrc_t x_rsrc = pw_rsrc(x, a.n * a.c_in * hw * 2);
+  const __amdgpu_buffer_rsrc_t w_rsrc = pw_rsrc(w, a.c_out * a.c_in * 2);
+  const __amdgpu_buffer_rsrc_t b_rsrc = pw_rsrc(bias ? bias : x, bias ? (CT ? a.c_out / 4 : a.c_out) * 2 : 0);
+  const __amdgpu_buffer_rsrc_t y_rsrc = pw_rsrc(y, a.n * a.c_out * hw * 2);
+  const __amdgpu_buffer_rsrc_t r_rsrc = pw_rsrc(res ? res : x, res ? a.n * a.c_out * hw * 2 : 0);
+  const int x_lane = 2 * (8 * so * hw + 4 * sg);
+  const int wt_lane = 2 * (KG * kg * a.c_out + 4 * mq);
+  const int b_lane = 2 * (CT ? (tid % PW_TC) / 4 : tid % PW_TC);
+  int w_lane[PW_NW];
+#pragma unroll
+  for (int i = 0; i < PW_NW; ++i) {
+    const int q = tid + 256 * i;
+    w_lane[i] = 2 * ((q >> 3) * a.c_in + 8 * (q & 7));
+  }
+
   // operand registers of PF work items in flight (slot = compile-time index)
   u32x2_t xr[PF][8];       // 8 channels x 4 pixels
   u32x4_t wr[PF][PW_NW];   // weight vectors
@@ -128,6 +159,25 @@ void pointwise_f16_kernel(const PwArgs a) {
   auto load = [&](auto S, int item) __attribute__((always_inline)) {
     int n, p0, co0, c0;
     decode(item, n, p0, co0, c0);
+    if constexpr (VEC) {
+      const int xoff = 2 * ((n * a.c_in + c0) * hw + p0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        xr[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, x_lane, xoff + 2 * e * hw, 0));
+      br[S] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, b_lane, 2 * (CT ? co0 / 4 : co0), 0));
+      if constexpr (CT) {  // weights lie [ci][m]: 4 rows m of KG input channels
+        const int woff = 2 * (c0 * a.c_out + co0);
+#pragma unroll
+        for (int e = 0; e < KG; ++e)
+          wt[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, wt_lane, woff + 2 * e * a.c_out, 0));
+      } else {  // w: row co0 + q / 8, 16-byte piece q % 8 of the chunk
+        const int woff = 2 * (co0 * a.c_in + c0);
+#pragma unroll
+        for (int i = 0; i < PW_NW; ++i)
+          wr[S][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane[i], woff, 0));
+      }
+      return;
+    }
     // x: channels c0 + 8 so + e, pixels p0 + 4 sg .. + 3 (clamped into the plane
     // and the channel range; out-of-range values are zeroed when staged)
     const int px = min(p0 + 4 * sg, hw - 4);
@@ -284,7 +334,15 @@ void pointwise_f16_kernel(const PwArgs a) {
           v[4 * cb + i] = t;
         }
       }
-      if (res) {  // never with CT
+      if (res && VEC) {  // never with CT; rows past c_out or pixels past the plane are never stored
+        const int roff = 2 * ((n * a.c_out + co0 + cl0) * hw + p0 + pl0 + 16 * pb);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const half4_t h = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, roff, 2 * 16 * cb * hw, 0));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * cb + i] = v[4 * cb + i] + (float)h[i];
+        }
+      } else if (res) {  // never with CT
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int p = min(p0 + pl0 + 16 * pb, hw - 4);
@@ -347,10 +405,11 @@ void pointwise_f16_kernel(const PwArgs a) {
         const half4_t e0 = *reinterpret_cast<const half4_t*>(rp);
         const half4_t e1 = *reinterpret_cast<const half4_t*>(rp + PW_OROW);
         const half8_t hv = {e0[0], e1[0], e0[1], e1[1], e0[2], e1[2], e0[3], e1[3]};
-        E* dst = y + (((long long)n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v;
-        if constexpr (VEC) {
-          store_out(reinterpret_cast<half8_t*>(dst), hv);
+        if constexpr (VEC) {  // nontemporal (the output is not read back)
+          const int off = 2 * (((n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, hv), y_rsrc, off, 0, 2);
         } else {
+          E* dst = y + (((long long)n * (a.c_out / 4) + cl0 + c) * ho + 2 * (h0 + hl) + kh) * wo + 8 * v;
 #pragma unroll
           for (int e = 0; e < 8; ++e) dst[e] = hv[e];
         }
@@ -365,7 +424,11 @@ void pointwise_f16_kernel(const PwArgs a) {
         const int q = tid + 256 * k;
         const int row = min(q >> 4, rlast), px = min(8 * (q & 15), pvalid - 8);
         const u32x4_t d = *reinterpret_cast<const u32x4_t*>(smem + row * PW_OROW + 2 * px);
-        store_out(reinterpret_cast<u32x4_t*>(y + ((long long)n * a.c_out + co0 + row) * hw + p0 + px), d);
+        // nontemporal (the output is not read back).  The whole offset is the
+        // per-lane one: with the tile's base in the scalar offset, stores of
+        // lanes repeating one vector lost their first 4 bytes now and then
+        // (the index probes caught it); loads take a scalar offset correctly.
+        __builtin_amdgcn_raw_buffer_store_b128(d, y_rsrc, 2 * ((n * a.c_out + co0 + row) * hw + p0 + px), 0, 2);
       }
     } else {
 #pragma unroll 1
