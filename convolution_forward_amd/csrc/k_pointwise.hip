@@ -114,11 +114,13 @@ void pointwise_f16_kernel(const PwArgs a) {
   constexpr int KG = PW_KC * PW_TC / 4 / 256;
   const int kg = tid % (PW_KC / KG), mq = tid / (PW_KC / KG);
 
-  // Vector path: every load is a per-thread byte offset fixed for the launch
-  // plus a uniform per-item one, through buffer descriptors (tensors below
-  // 2 GiB).  Nothing is clamped: channels past c_in are zeroed when staged,
-  // and pixels past the plane or rows past c_out only feed outputs that are
-  // never stored (reads past a tensor's end return 0).
+  // Vector path: every load's byte offset is a per-thread part fixed for the
+  // launch plus a uniform per-item part, added into the per-lane offset of a
+  // buffer access (tensors below 2 GiB).  Nothing is clamped: channels past
+  // c_in are zeroed when staged, pixels past the plane or rows past c_out only
+  // feed outputs that are never stored, and an offset past a tensor's end
+  // reads 0.  The range check covers the per-lane offset only, so no part of
+  // an offset goes in the scalar operand.
   const __amdgpu_buffer_rsrc_t x_rsrc = pw_rsrc(x, a.n * a.c_in * hw * 2);
   const __amdgpu_buffer_rsrc_t w_rsrc = pw_rsrc(w, a.c_out * a.c_in * 2);
   const __amdgpu_buffer_rsrc_t b_rsrc = pw_rsrc(bias ? bias : x, bias ? (CT ? a.c_out / 4 : a.c_out) * 2 : 0);
@@ -160,21 +162,21 @@ void pointwise_f16_kernel(const PwArgs a) {
     int n, p0, co0, c0;
     decode(item, n, p0, co0, c0);
     if constexpr (VEC) {
-      const int xoff = 2 * ((n * a.c_in + c0) * hw + p0);
+      const int xoff = x_lane + 2 * ((n * a.c_in + c0) * hw + p0);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        xr[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, x_lane, xoff + 2 * e * hw, 0));
-      br[S] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, b_lane, 2 * (CT ? co0 / 4 : co0), 0));
+        xr[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(x_rsrc, xoff + 2 * e * hw, 0, 0));
+      br[S] = __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, b_lane + 2 * (CT ? co0 / 4 : co0), 0, 0));
       if constexpr (CT) {  // weights lie [ci][m]: 4 rows m of KG input channels
-        const int woff = 2 * (c0 * a.c_out + co0);
+        const int woff = wt_lane + 2 * (c0 * a.c_out + co0);
 #pragma unroll
         for (int e = 0; e < KG; ++e)
-          wt[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, wt_lane, woff + 2 * e * a.c_out, 0));
+          wt[S][e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, woff + 2 * e * a.c_out, 0, 0));
       } else {  // w: row co0 + q / 8, 16-byte piece q % 8 of the chunk
         const int woff = 2 * (co0 * a.c_in + c0);
 #pragma unroll
         for (int i = 0; i < PW_NW; ++i)
-          wr[S][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane[i], woff, 0));
+          wr[S][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_lane[i] + woff, 0, 0));
       }
       return;
     }
@@ -338,7 +340,7 @@ void pointwise_f16_kernel(const PwArgs a) {
         const int roff = 2 * ((n * a.c_out + co0 + cl0) * hw + p0 + pl0 + 16 * pb);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const half4_t h = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, roff, 2 * 16 * cb * hw, 0));
+          const half4_t h = __builtin_bit_cast(half4_t, __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, roff + 2 * 16 * cb * hw, 0, 0));
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[4 * cb + i] = v[4 * cb + i] + (float)h[i];
         }
