@@ -177,7 +177,9 @@ bool pointwise_applicable(const Geo& g, int dtype) {
   if (dtype == CONV_F32)  // float32: planes and weight rows of whole float4 groups
     return !g.transpose && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 && g.pt == 0 &&
            g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 4 == 0 &&
-           (g.h * g.w) % 4 == 0 && ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) < (1LL << 31);
+           (g.h * g.w) % 4 == 0 && ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) < (1LL << 31) &&
+           g.n * g.ci * g.h * g.w < (1LL << 29) && g.co * g.ci < (1LL << 29) &&
+           g.n * g.co * g.h * g.w < (1LL << 29);  // 32-bit byte offsets
   return !g.transpose && half16(dtype) && g.kh == 1 && g.kw == 1 && g.sh == 1 && g.sw == 1 &&
          g.pt == 0 && g.pl == 0 && g.pb == 0 && g.pr == 0 && g.g == 1 && g.ci % 8 == 0 &&
          (g.h * g.w) % 4 == 0 && g.h * g.w >= 4 &&

@@ -48,6 +48,18 @@ constexpr int P32_NW = (P32_TC * P32_KC / 4 + P32_NT - 1) / P32_NT;  // w float4
 // against each other, so the groups' reads of one step hit different banks
 __device__ __forceinline__ int xcol(int k, int px) { return (px + 16 * ((k >> 3) & 3)) & 63; }
 
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform.  The per-lane offset is range checked: past the
+// range a load reads 0 and a store is dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t p32_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+constexpr int P32_OOB = (int)0x80000000;  // a byte offset past every descriptor's range
+
 }  // namespace
 
 // VEC: x and w 16-byte aligned (planes and weight rows of whole float4 groups
@@ -79,8 +91,30 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
     const long long img = mdiv((unsigned)P, a.mg_hw);  // P < 2^31
     xoff[i] = img * a.c_in * a.hw + (P - img * a.hw);
   }
+  // vector path: byte offsets through buffer descriptors (tensors below 2 GiB),
+  // a per-thread part computed once plus the chunk's; channels past c_in and
+  // rows past c_out read other data or 0 and are zeroed when staged
+  const __amdgpu_buffer_rsrc_t x_rsrc = p32_rsrc(x, (int)min(npix * a.c_in * 4, 2147483647LL));
+  const __amdgpu_buffer_rsrc_t w_rsrc = p32_rsrc(w, a.c_out * a.c_in * 4);
+  int xl[P32_NX], wl[P32_NW];
+#pragma unroll
+  for (int i = 0; i < P32_NX; ++i) xl[i] = 4 * (int)(xoff[i] + (long long)((tid + P32_NT * i) >> 4) * a.hw);
+#pragma unroll
+  for (int i = 0; i < P32_NW; ++i) {
+    const int q = min(tid + P32_NT * i, P32_TC * P32_KC / 4 - 1);
+    wl[i] = 4 * ((co0 + (q >> 4)) * a.c_in + 4 * (q & 15));
+  }
   floatx4_t xr[P32_NX], wr[P32_NW];
   auto load = [&](int c0) __attribute__((always_inline)) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < P32_NX; ++i)
+        xr[i] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xl[i] + 4 * c0 * a.hw, 0, 0));
+#pragma unroll
+      for (int i = 0; i < P32_NW; ++i)
+        wr[i] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, wl[i] + 4 * c0, 0, 0));
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < P32_NX; ++i) {
       const int q = tid + P32_NT * i;
@@ -153,7 +187,9 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
     }
   };
 
-  if (tid < P32_TC) bsm[tid] = bias ? bias[min(co0 + tid, a.c_out - 1)] : 0.f;
+  // without a bias the slot holds -0.0, whose addition is exact for every
+  // value (a zero keeps its sign)
+  if (tid < P32_TC) bsm[tid] = bias ? bias[min(co0 + tid, a.c_out - 1)] : -0.0f;
   const int nch = a.nchunks;
   load(0);
   stage(0, 0);
@@ -179,7 +215,35 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
 #pragma unroll
   for (int cb = 0; cb < 5; ++cb) acc[cb] = acc[cb] + part[(pb * 5 + cb) * 64 + lane];
   const long long P = P0 + 16 * pb + lc;
-  if (P < npix) {
+  if constexpr (VEC) {
+    // branch-free: outputs past the pixels or channels get an offset past the
+    // descriptors' range (their residual reads 0, their stores are dropped)
+    const __amdgpu_buffer_rsrc_t y_rsrc = p32_rsrc(y, (int)min(npix * a.c_out * 4, 2147483647LL));
+    const __amdgpu_buffer_rsrc_t r_rsrc = p32_rsrc(res ? res : x, res ? (int)min(npix * a.c_out * 4, 2147483647LL) : 0);
+    const int Pc = (int)min(P, npix - 1);
+    const int img = (int)mdiv((unsigned)Pc, a.mg_hw);
+    const int obase = img * a.c_out * a.hw + (Pc - img * a.hw);
+    auto off = [&](int m) __attribute__((always_inline)) {
+      return P < npix && co0 + m < a.c_out ? 4 * (obase + (co0 + m) * a.hw) : P32_OOB;
+    };
+    float v[20];
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * cb + 4 * lg + i;
+        float t = acc[cb][i] + bsm[m];  // the slot holds -0.0 without a bias
+        if (res) t = t + __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, off(m), 0, 0));
+        v[4 * cb + i] = t;
+      }
+    act_apply<AK>(v, a.act, a.alpha, a.beta);
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // nontemporal: the output is not read back
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[4 * cb + i]), y_rsrc,
+                                              off(16 * cb + 4 * lg + i), 0, 2);
+  } else if (P < npix) {
     const long long img = mdiv((unsigned)P, a.mg_hw), pp = P - img * a.hw;
     const long long obase = img * a.c_out * a.hw + pp;
     float v[20];
