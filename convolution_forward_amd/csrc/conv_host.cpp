@@ -158,7 +158,20 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_rowband(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_POINTWISE_GEMM) {
-      if (dt == F32) {
+      if (dt == F32 && pl.pw_strip) {
+        PwArgs a{};
+        a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
+        a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;
+        a.mg_hw = make_magic((unsigned)a.hw);
+        a.n_pt = (int)ceil_div((int64_t)cn * g.h * g.w, 256);
+        a.n_ct = (int)ceil_div(g.co, 16);
+        a.ntiles = a.n_pt * a.n_ct;
+        a.vec = reinterpret_cast<uintptr_t>(xc) % 16 == 0 && reinterpret_cast<uintptr_t>(wb) % 16 == 0 &&
+                reinterpret_cast<uintptr_t>(yc) % 16 == 0 &&
+                (rc == nullptr || reinterpret_cast<uintptr_t>(rc) % 16 == 0);
+        a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
+        e = launch_pointwise_f32_strip(a, s);
+      } else if (dt == F32) {
         PwArgs a{};
         a.x = xc; a.wt = wb; a.bias = bb; a.res = rc; a.y = yc;
         a.n = cn; a.c_in = (int)g.ci; a.hw = (int)(g.h * g.w); a.c_out = (int)g.co;

@@ -427,6 +427,12 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
       if (p->split_override > 1) return CONV_ERR_ARG;
       pl->variant = v;
       pl->pw_tc = dtype == CONV_F32 ? 80 : g.co > 64 ? 128 : 64;
+      // float32 with a short pixel axis: the 64 x 80 tiles would not fill two
+      // workgroups per CU, so each tile's loads would wait with nothing to hide
+      // them; strips of 16 channels x 256 pixels keep their loads in flight in
+      // registers instead (x is then read once per 16 channels: at most 8 times)
+      pl->pw_strip = dtype == CONV_F32 && g.ci % 16 == 0 && g.co <= 128 &&
+                     ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) <= 2 * kPlanCUs;
       pl->scratch_whole = 0;
       return CONV_OK;
     }
@@ -658,7 +664,10 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
                pl.splits);
       break;
     case CONV_VARIANT_POINTWISE_GEMM:
-      snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t%dx%d.k64", dn, dtype == CONV_F32 ? 64 : 128, pl.pw_tc);
+      if (pl.pw_strip)
+        snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t256x16.strip", dn);
+      else
+        snprintf(tmp, sizeof tmp, "pointwise_gemm.%s.t%dx%d.k64", dn, dtype == CONV_F32 ? 64 : 128, pl.pw_tc);
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_ROWBAND:
       snprintf(tmp, sizeof tmp, "implicit_gemm_rowband.%s.rows%d", dn, pl.rb_band_rows);

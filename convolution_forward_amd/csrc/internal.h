@@ -261,6 +261,7 @@ hipError_t launch_convint_rowshift(const ConvIntRsArgs& a, bool xu, bool wu, hip
 hipError_t launch_halo(Dtype dt, const HaloArgs& a, hipStream_t s);
 hipError_t launch_pointwise(Dtype dt, const PwArgs& a, int cus, hipStream_t s);
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s);
+hipError_t launch_pointwise_f32_strip(const PwArgs& a, hipStream_t s);
 hipError_t launch_rowband(Dtype dt, const RowbandArgs& a, hipStream_t s);
 hipError_t launch_grouped(Dtype dt, const GroupedArgs& a, hipStream_t s);
 hipError_t launch_rowshift(Dtype dt, const HaloArgs& a, hipStream_t s);

@@ -22,6 +22,7 @@
 // half adding channels 32h + s, 32h + 8 + s, 32h + 16 + s, 32h + 24 + s (MFMA
 // internal order); then first half + second half.
 #include <algorithm>
+#include <type_traits>
 
 #include "epilogue.h"
 #include "internal.h"
@@ -31,6 +32,7 @@ namespace convfwd {
 namespace {
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int P32_TP = 64;               // pixels per tile
 constexpr int P32_TC = 80;               // output channels per tile (5 blocks)
@@ -267,6 +269,184 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
         if (co0 + m < a.c_out) store_out(y + obase + (long long)(co0 + m) * a.hw, v[4 * cb + i]);
       }
   }
+}
+
+// Strip kernel for layers whose pixel axis is short (one round of the tiled
+// kernel above leaves CUs idle and each tile waits on its loads): a tile is 16
+// output channels x 256 consecutive pixels of the flattened axis, and the input
+// goes from memory straight into registers, D k-steps ahead, without LDS.
+//
+//  * Four waves, wave w owns pixels 64 w .. 64 w + 63 of the tile as 16 groups
+//    of 4 consecutive pixels (a group never straddles two images: h*w % 4 == 0).
+//  * v_mfma_f32_16x16x4_f32 with A = weights (16 output channels x 4 k) and
+//    B = x (4 k x 16 pixel groups).  Lane group g (lanes 16g .. 16g + 15) feeds
+//    channels g c_in/4 .. (g + 1) c_in/4 - 1 to the k-steps in turn, so step s
+//    multiplies channels s, c_in/4 + s, c_in/2 + s and 3 c_in/4 + s.  A lane loads
+//    the 4 pixels of its group as one 16-byte vector; element j of that vector
+//    is the B operand of accumulator set j (pixel 4 n + j), so the four sets
+//    share every A value and cover 64 pixels.
+//  * A lane's weights for 4 consecutive steps are one 16-byte load (w[co][ci]
+//    rows as they lie).  D steps of x and D/4 weight vectors are in flight per
+//    wave; each step refills the registers it has consumed with the step D
+//    later, and the last block of D steps issues no loads.
+//  * Epilogue: set j holds pixel 4 n + j of output channels 4 g + r, so a lane
+//    finishes 4 consecutive pixels per channel: one 16-byte residual load and
+//    one 16-byte store each.
+// Per output: the k-steps in order, each adding its 4 channels in the MFMA's
+// internal order.
+constexpr int PS_TP = 256;  // pixels per tile
+constexpr int PS_TC = 16;   // output channels per tile
+
+template <bool VEC, int D, int AK = -1>
+__global__ __launch_bounds__(256) void pointwise_f32_strip_kernel(const PwArgs a) {
+  static_assert(D % 4 == 0, "weights come 4 steps per load");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int L = xcd_logical(blockIdx.x, a.ntiles);  // channel tiles of a pixel range share an L2
+  const int pt = L / a.n_ct, ct = L - pt * a.n_ct;
+  const int co0 = ct * PS_TC;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int kq = a.c_in >> 2;  // k-steps (channels per lane group), a multiple of 4
+  const long long npix = (long long)a.n * a.hw;
+  const long long P = (long long)pt * PS_TP + 64 * wave + 4 * c16;  // the lane's first pixel
+  const int Pc = (int)min(P, npix - 4);                              // loads stay in x
+  const int img = (int)mdiv((unsigned)Pc, a.mg_hw);
+  const int hwo = Pc - img * a.hw;
+  const __amdgpu_buffer_rsrc_t x_rsrc = p32_rsrc(a.x, (int)(npix * a.c_in * 4));
+  const __amdgpu_buffer_rsrc_t w_rsrc = p32_rsrc(a.wt, a.c_out * a.c_in * 4);
+  const int xl = 4 * (img * a.c_in * a.hw + g * kq * a.hw + hwo);
+  const int wl = 4 * (min(co0 + c16, a.c_out - 1) * a.c_in + g * kq);
+  const int xstep = 4 * a.hw;  // bytes from one channel plane to the next
+
+  // step s of x (clamped to the last step: a refill past the end rereads it)
+  auto ldx = [&](int s) __attribute__((always_inline)) {
+    const int so = min(s, kq - 1) * xstep;
+    floatx4_t v;
+    if constexpr (VEC) {
+      v = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xl, so, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(x_rsrc, xl + 4 * j, so, 0));
+    }
+    return v;
+  };
+  // weights of steps s .. s + 3 (s a multiple of 4, clamped likewise)
+  auto ldw = [&](int s) __attribute__((always_inline)) {
+    const int so = 4 * min(s, kq - 4);
+    floatx4_t v;
+    if constexpr (VEC) {
+      v = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, wl, so, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(w_rsrc, wl + 4 * j, so, 0));
+    }
+    return v;
+  };
+
+  floatx4_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  floatx4_t bq[D], aq[D / 4];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {  // in the order they are consumed
+    if (i % 4 == 0) aq[i / 4] = ldw(i);
+    bq[i] = ldx(i);
+  }
+  // D steps from s0; REFILL: load step s + D into the registers step s frees.
+  // Steps at or past kq multiply a zero weight (their x is a clamped reread).
+  auto block = [&](int s0, auto refill) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int s = s0 + i;
+      const float av = s < kq ? aq[i / 4][i % 4] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bq[i][j], acc[j], 0, 0, 0);
+      if constexpr (decltype(refill)::value) {
+        bq[i] = ldx(s + D);
+        if (i % 4 == 3) aq[i / 4] = ldw(s - 3 + D);  // its four steps are done
+      }
+      // keep each step's loads among its own multiplies: the loads then leave in
+      // the order they are consumed, and each wait counts only the later ones
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const int nb = (kq + D - 1) / D;
+  for (int b = 0; b + 1 < nb; ++b) block(b * D, std::true_type{});
+
+  // outputs: channel co0 + 4 g + r, pixels P .. P + 3 (accumulator set j = pixel P + j);
+  // out-of-range ones get an offset past the descriptors (residual reads 0, store dropped)
+  const bool pv = P < npix;
+  const __amdgpu_buffer_rsrc_t y_rsrc = p32_rsrc(a.y, (int)(npix * a.c_out * 4));
+  const float* res = static_cast<const float*>(a.res);
+  const __amdgpu_buffer_rsrc_t r_rsrc = p32_rsrc(res ? a.res : a.y, res ? (int)(npix * a.c_out * 4) : 0);
+  const float* bias = static_cast<const float*>(a.bias);
+  int off[4];
+  float bv[4];
+  floatx4_t rv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int co = co0 + 4 * g + r;
+    off[r] = pv && co < a.c_out ? 4 * (img * a.c_out * a.hw + co * a.hw + hwo) : P32_OOB;
+    bv[r] = bias ? bias[min(co, a.c_out - 1)] : -0.0f;  // -0.0 adds exactly
+  }
+  // the residual is read during the last block's multiplications
+  if (res) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (VEC) {
+        rv[r] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, off[r], 0, 0));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rv[r][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, off[r] + 4 * j, 0, 0));
+      }
+    }
+  }
+  block((nb - 1) * D, std::false_type{});
+  float v[16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float t = acc[j][r] + bv[r];
+      if (res) t = t + rv[r][j];
+      v[4 * r + j] = t;
+    }
+  act_apply<AK>(v, a.act, a.alpha, a.beta);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (VEC) {
+      const floatx4_t o{v[4 * r], v[4 * r + 1], v[4 * r + 2], v[4 * r + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), y_rsrc, off[r], 0, 2);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[4 * r + j]), y_rsrc,
+                                              off[r] == P32_OOB ? P32_OOB : off[r] + 4 * j, 0, 2);
+    }
+  }
+}
+
+template <bool VEC, int D>
+static void launch_strip_act(const PwArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.ntiles);
+  if (a.act == 0) hipLaunchKernelGGL((pointwise_f32_strip_kernel<VEC, D, 0>), grid, dim3(256), 0, s, a);
+  else if (a.act == 1) hipLaunchKernelGGL((pointwise_f32_strip_kernel<VEC, D, 1>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((pointwise_f32_strip_kernel<VEC, D>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_pointwise_f32_strip(const PwArgs& a, hipStream_t s) {
+  // k-steps in flight: 20 when they divide the step count (no masked steps), else 16
+  const int kq = a.c_in / 4;
+  if (kq % 20 == 0) {
+    if (a.vec) launch_strip_act<true, 20>(a, s);
+    else launch_strip_act<false, 20>(a, s);
+  } else {
+    if (a.vec) launch_strip_act<true, 16>(a, s);
+    else launch_strip_act<false, 16>(a, s);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_pointwise_f32(const PwArgs& a, hipStream_t s) {

@@ -49,6 +49,7 @@ struct Plan {
   int dw_wave;    // whole-plane path: one wave per plane
   int dw_lm;      // one-wave path: LDS column of input column 0
   int pw_tc;      // pointwise: output channels per tile
+  int pw_strip;   // float32 pointwise: 16-channel x 256-pixel strips, x straight to registers
   int rb_band_rows;  // row band: output rows per workgroup
   int ct_fused;      // transpose: kernel = stride = 2 taps gathered by the GEMM epilogue
   int scratch_fixed; // scratch does not grow with the batch (Winograd weights): no chunks

@@ -9,7 +9,7 @@ EXPECTED_PLANS = {
     "w3b_pointwise_f16": "pointwise_gemm.f16.t128x128.k64",
     "w4a_depthwise5x5_f32": "depthwise_direct.f32.wave.col14",
     "w4b_depthwise3x3s2_f32": "depthwise_direct.f32.wave.col4",
-    "w4c_pointwise_f32": "pointwise_gemm.f32.t64x80.k64",
+    "w4c_pointwise_f32": "pointwise_gemm.f32.t256x16.strip",
     "w5a_dilated_grouped_f16": "implicit_gemm_grouped.f16.c8.n8",
     "w5b_convtranspose2x2s2_f16": "transpose_gemm_col2im.f16.fused_k2s2.t128x64",
     "x1_late3x3_512_7x7_f16": "implicit_gemm_halo.f16.rowshift.r8.n32.split8",
