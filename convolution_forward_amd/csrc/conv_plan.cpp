@@ -428,9 +428,10 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
       pl->variant = v;
       pl->pw_tc = dtype == CONV_F32 ? 80 : g.co > 64 ? 128 : 64;
       // float32 with a short pixel axis: the 64 x 80 tiles would not fill two
-      // workgroups per CU, so each tile's loads would wait with nothing to hide
-      // them; strips of 16 channels x 256 pixels keep their loads in flight in
-      // registers instead (x is then read once per 16 channels: at most 8 times)
+      // workgroups per CU, so each tile's chunked loads would wait with nothing
+      // to hide them; strips of 16 channels x 256 pixels keep a window of steps
+      // in flight in registers instead (x is read once per 16 channels: at most
+      // 8 times)
       pl->pw_strip = dtype == CONV_F32 && g.ci % 16 == 0 && g.co <= 128 &&
                      ceil_div(g.n * g.h * g.w, 64) * ceil_div(g.co, 80) <= 2 * kPlanCUs;
       pl->scratch_whole = 0;

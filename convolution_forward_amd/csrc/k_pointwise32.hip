@@ -437,15 +437,10 @@ static void launch_strip_act(const PwArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pointwise_f32_strip(const PwArgs& a, hipStream_t s) {
-  // k-steps in flight: 20 when they divide the step count (no masked steps), else 16
-  const int kq = a.c_in / 4;
-  if (kq % 20 == 0) {
-    if (a.vec) launch_strip_act<true, 20>(a, s);
-    else launch_strip_act<false, 20>(a, s);
-  } else {
-    if (a.vec) launch_strip_act<true, 16>(a, s);
-    else launch_strip_act<false, 16>(a, s);
-  }
+  // 12 k-steps in flight (deeper windows measured slower: the bytes a CU pulls
+  // from L2, not the latency, bound the strips)
+  if (a.vec) launch_strip_act<true, 12>(a, s);
+  else launch_strip_act<false, 12>(a, s);
   return hipGetLastError();
 }
 

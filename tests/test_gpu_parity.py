@@ -109,9 +109,9 @@ KERNELS = {
                                 "pointwise_gemm", "pointwise_gemm.f16"),
     "pointwise_f16": (oracle.Geom(3, 64, 12, 16, 200, 1, 1), "f16", False, "pointwise_gemm",
                       "pointwise_gemm.f16"),
-    "pointwise_f32": (oracle.Geom(3, 64, 10, 12, 200, 1, 1), "f32", False, "pointwise_gemm",
-                      "pointwise_gemm.f32.t64x80"),
-    "pointwise_f32_strip": (oracle.Geom(3, 144, 10, 12, 40, 1, 1), "f32", False, "pointwise_gemm",
+    "pointwise_f32": (oracle.Geom(3, 24, 10, 12, 200, 1, 1), "f32", False, "pointwise_gemm",
+                      "pointwise_gemm.f32.t64x80.k64"),
+    "pointwise_f32_strip": (oracle.Geom(3, 240, 10, 12, 100, 1, 1), "f32", False, "pointwise_gemm",
                             "pointwise_gemm.f32.t256x16.strip"),
     "transpose_fused": (oracle.Geom(4, 64, 10, 12, 32, 2, 2, sh=2, sw=2), "f16", True,
                         "transpose_gemm_col2im", "fused_k2s2"),
@@ -384,13 +384,16 @@ POINTWISE_F32_CASES = [
     (oracle.Geom(2, 36, 6, 10, 100, 1, 1, act="relu"), True, False),
     (oracle.Geom(1, 132, 5, 4, 17, 1, 1, act="silu"), False, True),
     (oracle.Geom(5, 8, 2, 2, 80, 1, 1, act="hard_swish"), True, True),
-    # strips of 16 channels x 256 pixels: 20-step blocks (c_in 240, 160), 16-step
-    # blocks with masked tail steps (c_in 144, 48, 16), ragged channel tiles,
-    # strips straddling images, a last strip with idle waves
+    # strips of 16 channels x 256 pixels: 12-step windows, whole (c_in 48, 144,
+    # 240, 288) or with masked tail steps (c_in 16, 160, 256, 320), ragged
+    # channel tiles, strips straddling images, a last strip with idle waves
+    (oracle.Geom(2, 256, 7, 8, 90, 1, 1, act="relu"), True, True),
     (oracle.Geom(3, 160, 14, 14, 80, 1, 1, act="relu"), True, True),
     (oracle.Geom(2, 144, 6, 10, 100, 1, 1), False, True),
     (oracle.Geom(5, 48, 7, 4, 40, 1, 1, act="sigmoid"), True, False),
     (oracle.Geom(1, 16, 2, 2, 5, 1, 1, act="relu"), True, True),
+    (oracle.Geom(2, 288, 6, 10, 40, 1, 1, act="relu"), True, True),
+    (oracle.Geom(1, 320, 4, 4, 100, 1, 1), False, True),
 ]
 
 
