@@ -480,6 +480,8 @@ def ceilings(torch):
                              ctypes.c_void_p]
     L.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                              ctypes.c_void_p]
+    L.probe_l2read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -503,11 +505,24 @@ def ceilings(torch):
         t = timed(lambda: L.probe_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, cus * per_cu, sh), 5)
         best_copy = max(best_copy, 2 * nbytes / t / 1e9)
     del src, dst
+    # L2 -> CU reads: a 2 MiB buffer (resident in every XCD's 4 MiB L2), each
+    # workgroup reading 2 MiB of it, 2 to 8 workgroups per CU
+    l2buf = torch.ones((2 << 20) // 4, dtype=torch.float32, device="cuda")
+    l2out = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda")
+    per_wg = 512
+    best_l2 = 0.0
+    for per_cu in (2, 4, 8):
+        blocks = cus * per_cu
+        t = timed(lambda: L.probe_l2read(l2buf.data_ptr(), (2 << 20) // 16, per_wg, blocks,
+                                         l2out.data_ptr(), sh), 5)
+        best_l2 = max(best_l2, blocks * per_wg * 4096 / t / 1e9)
+    del l2buf, l2out
     out = torch.empty(cus * 4 * 256, dtype=torch.float32, device="cuda")
     macs_per_iter = {0: 4 * 32 * 32 * 16, 1: 8 * 16 * 16 * 32, 2: 8 * 16 * 16 * 64}
     names = {0: "mfma_f32_32x32x16_f16_tflops", 1: "mfma_f32_16x16x32_f16_tflops",
              2: "mfma_i32_16x16x64_i8_tops"}
-    res = {"copy_gbs": round(best_copy, 1), "copy_bytes": 2 * nbytes}
+    res = {"copy_gbs": round(best_copy, 1), "copy_bytes": 2 * nbytes,
+           "l2_read_gbs": round(best_l2, 1), "l2_read_gbs_per_cu": round(best_l2 / cus, 2)}
     iters = 4000
     for kind in (0, 1, 2):
         best = 0.0

@@ -6,6 +6,11 @@
 //
 //  * probe_copy: a streaming copy, 16-byte vector loads and stores, every line
 //    touched once, as many workgroups as the chip holds, grid-stride.
+//  * probe_l2read: reads from the L2 into registers: every workgroup walks the
+//    same 2 MiB buffer (it stays in each XCD's L2 after the first touch) with
+//    16-byte loads, 8 per thread in flight, and folds what it read into one
+//    value per thread; the bytes a CU can pull from L2, which bounds the
+//    kernels that stage a tile per CU.
 //  * probe_mfma: register-only MFMA loops (independent accumulators, operands
 //    never reloaded): v_mfma_f32_32x32x16_f16 (kind 0), v_mfma_f32_16x16x32_f16
 //    (kind 1), v_mfma_i32_16x16x64_i8 (kind 2).  Each thread writes one value of
@@ -27,6 +32,22 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
                                                    u32x4* __restrict__ dst, long long n) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
     __builtin_nontemporal_store(src[i], dst + i);
+}
+
+__global__ __launch_bounds__(256) void l2read_kernel(const u32x4* __restrict__ src, int n16, int per_wg,
+                                                     unsigned* out) {
+  // workgroup b starts 4 KiB * b into the buffer (mod its size); thread t reads
+  // vectors start + t + 256 j, j < per_wg, eight loads in flight
+  const int start = (int)(((long long)blockIdx.x * 256) % n16);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < per_wg; j += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[(start + (int)threadIdx.x + 256 * (j + k)) % n16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k];
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 template <int KIND>
@@ -86,6 +107,18 @@ int probe_copy(const void* src, void* dst, long long n16, int blocks, void* stre
   if (!src || !dst || n16 < 1 || blocks < 1) return 1;
   hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// Each of blocks workgroups reads per_wg x 4 KiB (per_wg a multiple of 8) from
+// the n16 16-byte vectors at buf (a power of two, at most 2^27); out holds
+// blocks * 256 values.
+int probe_l2read(const void* buf, int n16, int per_wg, int blocks, void* out, void* stream) {
+  if (!buf || !out || n16 < 256 || (n16 & (n16 - 1)) || n16 > (1 << 27) || per_wg < 8 || per_wg % 8 ||
+      blocks < 1)
+    return 1;
+  hipLaunchKernelGGL(l2read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(buf), n16, per_wg, static_cast<unsigned*>(out));
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
