@@ -132,6 +132,7 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.mg_nv = make_magic((unsigned)((g.w + 7) / 8));
       a.mg_cin = make_magic((unsigned)g.ci);
       a.mg_vpr = make_magic((unsigned)((g.wo + 7) / 8));
+      a.mg_vpr2 = make_magic((unsigned)(2 * ((g.wo + 7) / 8)));
       a.band_rows = pl.rb_band_rows;
       a.n_band = (int)ceil_div(g.ho, a.band_rows);
       const int64_t need = std::max<int64_t>(g.pl + g.w, 2 * (g.wo - 1) + 8);

@@ -160,6 +160,7 @@ struct RowbandArgs {
   Magic mg_nv;                  // division by the 8-half vectors per input row
   Magic mg_cin;                 // division by c_in
   Magic mg_vpr;                 // division by the 8-output vectors per output row
+  Magic mg_vpr2;                // ... and by those of two output rows
   int act;
   float alpha, beta;
 };

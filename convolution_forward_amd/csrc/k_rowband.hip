@@ -303,6 +303,19 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
     so[k] = (int)__umul24((unsigned)sc[k], (unsigned)howo) + 8 * sv[k];
   }
 
+  // two-row steps: vector q of a channel's two output rows (2 vpr vectors,
+  // contiguous in y), channels in turn, so that the lanes of a store
+  // instruction cover whole runs of 2 wo outputs per channel (fixed count:
+  // past the end the last vector repeats)
+  constexpr int RB_NST2 = TWO ? (64 * 32 + NT - 1) / NT : 1;
+  int c2[RB_NST2], v2[RB_NST2];
+#pragma unroll
+  for (int k = 0; k < RB_NST2; ++k) {
+    const int q = min(tid + NT * k, cn * 2 * vpr - 1);
+    c2[k] = (int)mdiv((unsigned)q, a.mg_vpr2);
+    v2[k] = q - c2[k] * 2 * vpr;
+  }
+
   // one output row; J = (oh - r0) % 3 at compile time picks the prefetch registers
   auto row = [&](int oh, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
@@ -445,18 +458,20 @@ __global__ __launch_bounds__(64 * WV) void rowband_kernel(const RowbandArgs a) {
       }
     }
     __syncthreads();
-    // ---- whole rows of the tile: 16-byte vectors of 8 output columns (the
-    // vector path: wo % 8 == 0) ----
+    // ---- the tile's two rows per channel as one run of 16-byte vectors (the
+    // vector path: wo % 8 == 0, so row oh + 1 follows row oh in y); a row past
+    // the band gets the descriptor's size as its offset (store dropped).
+    // Whole runs per store instruction write faster than row-by-row stores
+    // (w3a 25.7 -> 23.6 us). ----
+    const int orow = oh * a.wo;
+    const int rows = min(2, r1 - oh);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if (oh + r < r1) {  // uniform
-        const int orow = (oh + r) * a.wo;
-#pragma unroll
-        for (int k = 0; k < RB_NSTV; ++k) {
-          const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + (r * 64 + sc[k]) * RB_OPITCH + 16 * sv[k]);
-          __builtin_amdgcn_raw_buffer_store_b128(d, y_rsrc, 2 * (so[k] + orow), 0, 2);
-        }
-      }
+    for (int k = 0; k < RB_NST2; ++k) {
+      const int r = v2[k] >= vpr ? 1 : 0, sv2 = v2[k] - r * vpr;
+      const u32x4_t d = *reinterpret_cast<const u32x4_t*>(otile + (r * 64 + c2[k]) * RB_OPITCH + 16 * sv2);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          d, y_rsrc, r < rows ? 2 * ((int)__umul24((unsigned)c2[k], (unsigned)howo) + orow + 8 * v2[k]) : tile_bytes,
+          0, 2);
     }
   };
 
