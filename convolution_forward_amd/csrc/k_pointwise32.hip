@@ -289,11 +289,16 @@ __global__ __launch_bounds__(P32_NT) void pointwise_f32_kernel(const PwArgs a) {
 //    rows as they lie).  D steps of x and D/4 weight vectors are in flight per
 //    wave; each step refills the registers it has consumed with the step D
 //    later, and the last block of D steps issues no loads.
+//  * The channel tiles of one pixel range read the same x and run side by side
+//    on one XCD.  Tile ct takes the k-steps in a rotated order, starting at step
+//    (D ct) mod (c_in / 4) and wrapping round, so a piece of x is fetched from
+//    HBM by one tile while the others find it in L2 later; taken in the same
+//    order, all of them waited on the same misses.
 //  * Epilogue: set j holds pixel 4 n + j of output channels 4 g + r, so a lane
 //    finishes 4 consecutive pixels per channel: one 16-byte residual load and
 //    one 16-byte store each.
-// Per output: the k-steps in order, each adding its 4 channels in the MFMA's
-// internal order.
+// Per output: the k-steps in the tile's rotated order, each adding its 4
+// channels in the MFMA's internal order.
 constexpr int PS_TP = 256;  // pixels per tile
 constexpr int PS_TC = 16;   // output channels per tile
 
@@ -317,9 +322,16 @@ __global__ __launch_bounds__(256) void pointwise_f32_strip_kernel(const PwArgs a
   const int wl = 4 * (min(co0 + c16, a.c_out - 1) * a.c_in + g * kq);
   const int xstep = 4 * a.hw;  // bytes from one channel plane to the next
 
-  // step s of x (clamped to the last step: a refill past the end rereads it)
+  // k-step s of x, taken at rotated position rotk(s) (clamped to the last step
+  // first: a refill past the end rereads it)
+  // the channel tiles of one pixel range start their k-steps D apart (mod kq)
+  const int rot = (ct * D) % kq;
+  auto rotk = [&](int s) __attribute__((always_inline)) {
+    const int r = s + rot;
+    return r >= kq ? r - kq : r;
+  };
   auto ldx = [&](int s) __attribute__((always_inline)) {
-    const int so = min(s, kq - 1) * xstep;
+    const int so = rotk(min(s, kq - 1)) * xstep;
     floatx4_t v;
     if constexpr (VEC) {
       v = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xl, so, 0));
@@ -330,9 +342,10 @@ __global__ __launch_bounds__(256) void pointwise_f32_strip_kernel(const PwArgs a
     }
     return v;
   };
-  // weights of steps s .. s + 3 (s a multiple of 4, clamped likewise)
+  // weights of steps s .. s + 3 (s a multiple of 4, clamped likewise; rot and
+  // kq are multiples of 4, so the four stay consecutive after the rotation)
   auto ldw = [&](int s) __attribute__((always_inline)) {
-    const int so = 4 * min(s, kq - 4);
+    const int so = 4 * rotk(min(s, kq - 4));
     floatx4_t v;
     if constexpr (VEC) {
       v = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, wl, so, 0));
