@@ -290,10 +290,16 @@ int run(const conv_problem* p, int dtype, bool transpose, const void* x, const v
       a.groups = (int)g.g; a.cig = (int)g.cig; a.cog = (int)g.cog;
       a.pt = (int)g.pt; a.pl = (int)g.pl; a.ho = (int)g.ho; a.wo = (int)g.wo;
       a.th = (int)ceil_div(g.ho, 2); a.tw = (int)ceil_div(g.wo, 2);
-      a.tiles = cn * a.th * a.tw;
+      a.tr = pl.wino_tr; a.tc = pl.wino_tc;
+      a.nbr = (int)ceil_div(a.th, a.tr); a.nbc = (int)ceil_div(a.tw, a.tc);
       a.cb = pl.wino_cb;
-      a.mg_tpi = make_magic((unsigned)(a.th * a.tw));
-      a.mg_tw = make_magic((unsigned)a.tw);
+      const int rc = (2 * a.tr + 2) * (2 * a.tc + 2);
+      a.nsi = 16 * rc <= 256 * 10 ? 10 : 17;
+      a.mg_nb = make_magic((unsigned)(a.nbr * a.nbc));
+      a.mg_nbc = make_magic((unsigned)a.nbc);
+      a.mg_tc = make_magic((unsigned)a.tc);
+      a.mg_rc = make_magic((unsigned)rc);
+      a.mg_c = make_magic((unsigned)(2 * a.tc + 2));
       a.act = p->activation; a.alpha = p->act_alpha; a.beta = p->act_beta;
       e = launch_winograd(dt, a, s);
     } else if (pl.variant == CONV_VARIANT_IMPLICIT_GEMM_GROUPED) {

@@ -201,7 +201,8 @@ bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
 
 // Winograd F(2x2, 3x3): 16-bit operands, 3x3, stride 1, dilation 1, input
 // channels per group in whole steps of 16 (16-byte weight fragments), tile and
-// channel-tile counts inside the grid limits.
+// channel-tile counts inside the grid limits, and x and the transformed weights
+// below 2 GiB (the kernels address them with 32-bit byte offsets).
 bool winograd_applicable(const Geo& g, int dtype) {
   if (g.transpose || !half16(dtype) || g.kh != 3 || g.kw != 3 || g.sh != 1 || g.sw != 1 ||
       g.dh != 1 || g.dw != 1 || g.cig % 16)
@@ -210,7 +211,8 @@ bool winograd_applicable(const Geo& g, int dtype) {
   if (!mul_ok(g.n, ceil_div(g.ho, 2), &tiles) || !mul_ok(tiles, ceil_div(g.wo, 2), &tiles))
     return false;
   return tiles < (1LL << 31) - 64 && ceil_div(g.cog, 32) <= 65535 && g.g <= 65535 &&
-         mul_ok(16 * g.co, g.cig, &t);
+         mul_ok(16 * g.co, g.cig, &t) && t < (1LL << 30) && g.x_elems < (1LL << 30) &&
+         g.co * g.cig / 8 < (1LL << 31) - 64;
 }
 
 // Depthwise output tile: whole plane when the staged input fits, else smaller
@@ -390,8 +392,13 @@ int make_plan(const conv_problem* p, int dtype, const Geo& g, Plan* pl) {
     if (v == CONV_VARIANT_WINOGRAD) {  // only when asked for (see conv.h)
       if (!winograd_applicable(g, dtype) || p->split_override > 1) return CONV_ERR_ARG;
       pl->variant = v;
-      const int64_t tiles = g.n * ceil_div(g.ho, 2) * ceil_div(g.wo, 2);
-      pl->wino_cb = ceil_div(tiles, 32) * ceil_div(g.cog, 64) * g.g >= kPlanCUs ? 2 : 1;
+      // a workgroup's tiles: a band of whole tile rows of one image (a row of
+      // at most 32 tiles), else 32 tiles of one tile row
+      const int64_t th = ceil_div(g.ho, 2), tw = ceil_div(g.wo, 2);
+      pl->wino_tc = (int)std::min<int64_t>(tw, 32);
+      pl->wino_tr = (int)std::min<int64_t>(32 / pl->wino_tc, th);
+      const int64_t bands = g.n * ceil_div(th, pl->wino_tr) * ceil_div(tw, pl->wino_tc);
+      pl->wino_cb = bands * ceil_div(g.cog, 64) * g.g >= kPlanCUs ? 2 : 1;
       pl->scratch_per_image = (uint64_t)(16 * g.co * g.cig) * 2u;
       pl->scratch_whole = pl->scratch_per_image;
       pl->scratch_fixed = 1;
@@ -692,7 +699,8 @@ int conv_describe_variant(const conv_problem* p, int dtype, char* buf, uint64_t 
         snprintf(tmp, sizeof tmp, "depthwise_direct.%s.t%dx%d", dn, pl.toh, pl.tow);
       break;
     case CONV_VARIANT_WINOGRAD:
-      snprintf(tmp, sizeof tmp, "winograd_f2x2_3x3.%s.t32x%d", dn, 32 * pl.wino_cb);
+      snprintf(tmp, sizeof tmp, "winograd_f2x2_3x3.%s.band%dx%d.c%d", dn, pl.wino_tr, pl.wino_tc,
+               32 * pl.wino_cb);
       break;
     case CONV_VARIANT_IMPLICIT_GEMM_HALO:
       if (pl.halo.rowshift && pl.splits > 1)

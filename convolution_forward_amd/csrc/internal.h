@@ -233,9 +233,13 @@ struct WinoArgs {
   void* y;
   void* u;               // scratch: transformed weights [16][c_out][cig], 16-bit
   int n, c_in, h, w, c_out, groups, cig, cog, pt, pl, ho, wo;
-  int th, tw, tiles;     // 2x2 output tiles per column / row of an image, in the chunk
+  int th, tw;            // 2x2 output tiles per column / row of an image
+  int tr, tc;            // a workgroup's band: tr tile rows x tc tile columns (tr tc <= 32)
+  int nbr, nbc;          // bands per image column / row
   int cb;                // 32-channel blocks per workgroup (1 or 2)
-  Magic mg_tpi, mg_tw;   // divisions by th * tw and by tw
+  int nsi;               // staging items per thread and step: 10 or 17
+  Magic mg_nb, mg_nbc;   // divisions by nbr * nbc and by nbc
+  Magic mg_tc, mg_rc, mg_c;  // by tc, by the staged positions (2 tr + 2)(2 tc + 2), by 2 tc + 2
   int act;
   float alpha, beta;
 };

@@ -15,16 +15,24 @@
 // GEMMs M_xi[co][t] = sum_ci U_xi[co][ci] V_xi[ci][t] over the output tiles t
 // (2x2 outputs each), run on v_mfma_f32_32x32x16_{f16,bf16}.
 //
-//  * Weight kernel: U for every (co, ci) into scratch, [xi][co][ci] (16-bit),
-//    so each MFMA A fragment (8 consecutive input channels of one output
-//    channel) is one 16-byte load.
+//  * Weight kernel: U for every (co, ci) into scratch, 16-bit, laid out
+//    [xi][ci / 16][co][ci % 16]: each MFMA A fragment (8 consecutive input
+//    channels of one output channel) is one 16-byte load, and the 32 output
+//    channels of a fragment load are 1 KiB of contiguous memory (the lines a
+//    step reads are whole).  A thread transforms 8 input channels of one
+//    output channel (144 contiguous bytes of weights in, one 16-byte store per
+//    position out).
 //  * Main kernel: a workgroup owns 32 consecutive tiles (in (image, tile row,
 //    tile column) order) and 32 * CB output channels; each of its 4 waves owns
 //    4 of the 16 positions xi.  Per step of 16 input channels every thread
-//    gathers the 4x4 input patches of 2 (tile, channel) pairs, forms V in
-//    float32 (adds and subtracts only) and writes its 16 values, rounded once to
-//    the 16-bit type, into LDS laid out [xi][tile][channel] (a B fragment is
-//    one 16-byte read); V is double-buffered so one barrier per step suffices.
+//    gathers the 4x4 input patches of one tile for 2 adjacent channels, forms
+//    V in float32 (adds and subtracts only) and writes its 16 pairs of values,
+//    rounded once to the 16-bit type, into LDS laid out [xi][tile][channel]
+//    (a B fragment is one 16-byte read); V is double-buffered so one barrier
+//    per step suffices.  The input patches and the U fragments are loaded two
+//    steps ahead through buffer descriptors: the patch offsets are fixed for
+//    the launch (a tap in the padding reads 0 through an offset past the
+//    descriptor's range) and a step only adds a scalar offset.
 //  * Output: the accumulators go through LDS as float32 M[xi][co][t]; each
 //    thread applies A^T M A to whole tiles and the fused epilogue (bias,
 //    residual, activation, each rounded in float32) and stores the outputs
@@ -49,103 +57,221 @@ typedef unsigned u32x4_w __attribute__((ext_vector_type(4)));
 constexpr int WN_T = 32;   // tiles per workgroup
 constexpr int WN_KC = 16;  // input channels per step (the MFMA's k)
 constexpr int WN_VBUF = 16 * WN_T * WN_KC;  // elements of one V buffer
+constexpr int WN_OOB = (int)0x80000000;     // a byte offset past every descriptor's range
 
-// U[xi][co][ci] = (G g G^T)[xi] for every output channel co and input channel
-// ci of its group (ci fastest across threads: coalesced 2-byte stores).
-template <typename E>
-__global__ __launch_bounds__(256) void wino_weights_kernel(const WinoArgs a) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long plane = (long long)a.c_out * a.cig;
-  if (i >= plane) return;
-  const E* g = static_cast<const E*>(a.wt) + i * 9;  // [co][ci][3][3]
-  float w[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) w[k] = to_f32(g[k]);
-  float gg[4][3];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    gg[0][j] = w[j];
-    gg[1][j] = 0.5f * (w[j] + w[3 + j] + w[6 + j]);
-    gg[2][j] = 0.5f * (w[j] - w[3 + j] + w[6 + j]);
-    gg[3][j] = w[6 + j];
-  }
-  E* U = static_cast<E*>(a.u);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float u[4] = {gg[r][0], 0.5f * (gg[r][0] + gg[r][1] + gg[r][2]),
-                        0.5f * (gg[r][0] - gg[r][1] + gg[r][2]), gg[r][2]};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) U[(long long)(4 * r + c) * plane + i] = from_f32<E>(u[c]);
-  }
+// Raw buffer descriptor (gfx9 format word 0x00020000) over [p, p + bytes), its
+// operands made wave-uniform; an access whose per-lane offset is past the range
+// reads 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wino_rsrc(const void* p, int bytes) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-template <typename E, int CB>
+// The 16 bits of an element as float32.
+template <typename E>
+__device__ __forceinline__ float bits_to_f32(unsigned b) {
+  if constexpr (std::is_same_v<E, __bf16>) return __uint_as_float(b << 16);
+  else return (float)__builtin_bit_cast(_Float16, (unsigned short)b);
+}
+
+// U[xi][ci / 16][co][ci % 16] = (G g G^T)[xi] for every output channel co and
+// input channel ci of its group.  A thread takes one output channel and 8 consecutive input
+// channels: their 72 weights are 144 contiguous bytes of the OIHW tensor, and
+// each position xi receives 8 consecutive U values (one 16-byte store when the
+// weights are 16-byte aligned).
+template <typename E, bool VEC>
+__global__ __launch_bounds__(64) void wino_weights_kernel(const WinoArgs a) {
+  typedef E e8 __attribute__((ext_vector_type(8)));
+  const int octs = a.cig >> 3;
+  const int i = blockIdx.x * 64 + threadIdx.x;  // (co, octet), below c_out * cig / 8
+  if (i >= a.c_out * octs) return;
+  const int co = i / octs, ci0 = 8 * (i - co * octs);
+  const long long plane = (long long)a.c_out * a.cig;
+  const E* g = static_cast<const E*>(a.wt) + ((long long)co * a.cig + ci0) * 9;  // [ci][3][3]
+  E wv[72];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      const e8 v = *reinterpret_cast<const e8*>(g + 8 * k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[8 * k + e] = v[e];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 72; ++k) wv[k] = g[k];
+  }
+  e8 out[16];
+#pragma unroll
+  for (int c8 = 0; c8 < 8; ++c8) {
+    float w[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) w[k] = to_f32(wv[9 * c8 + k]);
+    float gg[4][3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      gg[0][j] = w[j];
+      gg[1][j] = 0.5f * (w[j] + w[3 + j] + w[6 + j]);
+      gg[2][j] = 0.5f * (w[j] - w[3 + j] + w[6 + j]);
+      gg[3][j] = w[6 + j];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      out[4 * r + 0][c8] = from_f32<E>(gg[r][0]);
+      out[4 * r + 1][c8] = from_f32<E>(0.5f * (gg[r][0] + gg[r][1] + gg[r][2]));
+      out[4 * r + 2][c8] = from_f32<E>(0.5f * (gg[r][0] - gg[r][1] + gg[r][2]));
+      out[4 * r + 3][c8] = from_f32<E>(gg[r][2]);
+    }
+  }
+  // 16-byte aligned: scratch, cig % 16 == 0
+  E* U = static_cast<E*>(a.u) + ((long long)(ci0 >> 4) * a.c_out + co) * 16 + (ci0 & 15);
+#pragma unroll
+  for (int xi = 0; xi < 16; ++xi) *reinterpret_cast<e8*>(U + xi * plane) = out[xi];
+}
+
+// Main kernel.  Workgroup: a band of tr x tc tiles of one image (tr whole tile
+// rows when a tile row has at most 32 tiles, else 32 tiles of one tile row) x
+// 32 CB output channels of one group; wave w multiplies the positions
+// xi = 4 w .. 4 w + 3.  Per step of 16 input channels:
+//  * the band's input window, (2 tr + 2) rows x (2 tc + 2) columns of the 16
+//    channels, is copied into LDS laid out [position][channel] (36 bytes per
+//    position: 16 channels + 4 bytes that spread the banks); each thread
+//    copies up to NSI elements whose offsets are fixed for the launch (a
+//    position in the padding reads 0 through an offset past the descriptor's
+//    range) plus a scalar step offset, loaded one step ahead;
+//  * thread (tile slot tl = tid / 8, channel pair cp = tid % 8) reads its
+//    tile's 4 x 4 patch of both channels (one 32-bit LDS read per position),
+//    forms V and writes each position's two values as one 32-bit word
+//    [xi][tile][channel] (a wave's writes cover 8 whole tiles: 256 contiguous
+//    bytes, every bank once);
+//  * the U fragments (16-byte loads, two steps ahead) times the V fragments.
+// Window and V are double-buffered: one barrier per step.
+template <typename E, int CB, int NSI>
 __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
+  typedef E e2 __attribute__((ext_vector_type(2)));
+  constexpr int PP = 36;                 // LDS bytes per staged position
+  constexpr int WPOS = 264;              // at most (2 tr + 2)(2 tc + 2) positions
+  constexpr int WBUF = WPOS * PP + 16;   // window buffer and its sink (items past the window)
+  constexpr int VOFF = 2 * WBUF;         // V buffers after the two windows
   __shared__ __attribute__((aligned(16))) unsigned char smem[16 * WN_T * 32 * 4];  // 64 KiB
-  E* vbuf = reinterpret_cast<E*>(smem);            // 2 x [16][32][16] (32 KiB)
-  float* mbuf = reinterpret_cast<float*>(smem);    // [16][32][32] (64 KiB), after the loop
+  static_assert(VOFF + 2 * WN_VBUF * 2 <= 16 * WN_T * 32 * 4, "window and V buffers fit");
+  E* vbuf = reinterpret_cast<E*>(smem + VOFF);    // 2 x [16][32][16]
+  float* mbuf = reinterpret_cast<float*>(smem);  // [16][32][32], after the loop
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * WN_T;
   const int co0 = blockIdx.y * 32 * CB;  // within the group
   const int grp = blockIdx.z;
-  const int tpi = a.th * a.tw;
-  const E* __restrict__ x = static_cast<const E*>(a.x);
-  const E* __restrict__ U = static_cast<const E*>(a.u);
-  const long long uplane = (long long)a.c_out * a.cig;
+  const int hw = a.h * a.w;
+  // band: image n, tile rows tr0 .., tile columns tc0 ..
+  const int bid = blockIdx.x;
+  const int n = (int)mdiv((unsigned)bid, a.mg_nb);
+  const int bb = bid - n * (a.nbr * a.nbc);
+  const int br = (int)mdiv((unsigned)bb, a.mg_nbc);
+  const int tr0 = br * a.tr, tc0 = (bb - br * a.nbc) * a.tc;
+  const int C = 2 * a.tc + 2;            // window columns
+  const int RC = (2 * a.tr + 2) * C;     // window positions
+  const int ih0 = 2 * tr0 - a.pt, iw0 = 2 * tc0 - a.pl;
 
-  // this thread's two staging pairs: channel ci_l = p >> 5, tile tl = p & 31
-  int tl[2], cil[2], ih0[2], iw0[2];
-  bool tok[2];
-  const E* xp[2];
+  // window items of this thread: element (channel, position) of the step
+  int gx[NSI], lx[NSI];
+  {
+    const int xbase = (n * a.c_in + grp * a.cig) * hw;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int p = tid + 256 * q;
-    cil[q] = p >> 5;
-    tl[q] = p & 31;
-    const int t = t0 + tl[q];
-    tok[q] = t < a.tiles;
-    const int tc = tok[q] ? t : 0;
-    const int n = (int)mdiv((unsigned)tc, a.mg_tpi);
-    const int rem = tc - n * tpi;
-    const int th = (int)mdiv((unsigned)rem, a.mg_tw);
-    const int tw = rem - th * a.tw;
-    ih0[q] = 2 * th - a.pt;
-    iw0[q] = 2 * tw - a.pl;
-    xp[q] = x + ((long long)n * a.c_in + (long long)grp * a.cig + cil[q]) * a.h * a.w;
+    for (int k = 0; k < NSI; ++k) {
+      const int i = tid + 256 * k;
+      const int ch = (int)mdiv((unsigned)i, a.mg_rc);
+      const int pos = i - ch * RC;
+      const int r = (int)mdiv((unsigned)pos, a.mg_c);
+      const int ih = ih0 + r, iw = iw0 + pos - r * C;
+      const bool live = ch < 16;
+      const bool ok = live && (unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w;
+      gx[k] = ok ? 2 * (xbase + ch * hw + ih * a.w + iw) : WN_OOB;
+      lx[k] = live ? pos * PP + 2 * ch : WPOS * PP;  // items past the window write the sink
+    }
   }
-  const long long cstride = (long long)WN_KC * a.h * a.w;  // one step of 16 channels
+  const __amdgpu_buffer_rsrc_t x_rsrc = wino_rsrc(a.x, 2 * a.n * a.c_in * hw);
+  const int cstep = 2 * WN_KC * hw;  // bytes from one step's channels to the next
 
-  auto stage = [&](int step, int buf) __attribute__((always_inline)) {
-    E* vb = vbuf + buf * WN_VBUF;
+  // this thread's tile slot in the band (slots past the band read the last
+  // tile's window; their results are dropped) and channel pair
+  const int tl = tid >> 3, cp = tid & 7;
+  const int tlc = min(tl, a.tr * a.tc - 1);
+  const int tlr = (int)mdiv((unsigned)tlc, a.mg_tc);
+  const int pbase = (2 * tlr * C + 2 * (tlc - tlr * a.tc)) * PP + 4 * cp;  // patch corner
+
+  // U fragments: output channel row (lane & 31) of each 32-channel block (an
+  // out-of-range channel reads the last valid one; its results are dropped),
+  // channels k0 + 8 * (lane >> 5) .. + 8, position 4 wave + i
+  const int kslot = (lane >> 5) * 8;
+  const int uplane = a.c_out * a.cig;
+  const __amdgpu_buffer_rsrc_t u_rsrc = wino_rsrc(a.u, 2 * 16 * uplane);
+  int uoff[4][CB];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float d[4][4];
-      const E* src = xp[q] + step * cstride;
+  for (int b = 0; b < CB; ++b) {
+    const int co = min(co0 + 32 * b + (lane & 31), a.cog - 1);
+    const int row = (grp * a.cog + co) * 16 + kslot;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int i = 0; i < 4; ++i) uoff[i][b] = 2 * ((4 * wave + i) * uplane + row);
+  }
+  const int ustep = 2 * 16 * a.c_out;  // bytes from one step's U block to the next
+
+  unsigned xr[NSI];         // the next step's window items, 16 bits each
+  u32x4_w af[2][4][CB];    // [set][position][channel block]
+  auto load_x = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int ih = ih0[q] + r, iw = iw0[q] + c;
-          d[r][c] = (tok[q] && (unsigned)ih < (unsigned)a.h && (unsigned)iw < (unsigned)a.w)
-                        ? to_f32(src[(long long)ih * a.w + iw])
-                        : 0.0f;
-        }
+    for (int k = 0; k < NSI; ++k) xr[k] = __builtin_amdgcn_raw_buffer_load_b16(x_rsrc, gx[k], s * cstep, 0);
+  };
+  auto put_x = [&](int set) __attribute__((always_inline)) {  // into window buffer `set`
+#pragma unroll
+    for (int k = 0; k < NSI; ++k)
+      *reinterpret_cast<unsigned short*>(smem + set * WBUF + lx[k]) = (unsigned short)xr[k];
+  };
+  auto load_u = [&](int s, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < CB; ++b)
+        af[set][i][b] = __builtin_bit_cast(
+            u32x4_w, __builtin_amdgcn_raw_buffer_load_b128(u_rsrc, uoff[i][b], s * ustep, 0));
+  };
+  // V = B^T d B of both channels from window buffer `set`, into V buffer `set`
+  auto transform = [&](int set) __attribute__((always_inline)) {
+    const unsigned char* wb = smem + set * WBUF + pbase;
+    float d[2][4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const unsigned w2 = *reinterpret_cast<const unsigned*>(wb + (r * C + c) * PP);
+        d[0][r][c] = bits_to_f32<E>(w2 & 0xFFFFu);
+        d[1][r][c] = bits_to_f32<E>(w2 >> 16);
+      }
+    float v[2][16];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
       float bd[4][4];  // B^T d
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        bd[0][c] = d[0][c] - d[2][c];
-        bd[1][c] = d[1][c] + d[2][c];
-        bd[2][c] = d[2][c] - d[1][c];
-        bd[3][c] = d[1][c] - d[3][c];
+        bd[0][c] = d[ch][0][c] - d[ch][2][c];
+        bd[1][c] = d[ch][1][c] + d[ch][2][c];
+        bd[2][c] = d[ch][2][c] - d[ch][1][c];
+        bd[3][c] = d[ch][1][c] - d[ch][3][c];
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {  // (B^T d) B
-        const float v[4] = {bd[r][0] - bd[r][2], bd[r][1] + bd[r][2], bd[r][2] - bd[r][1],
-                            bd[r][1] - bd[r][3]};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) vb[((4 * r + c) * WN_T + tl[q]) * WN_KC + cil[q]] = from_f32<E>(v[c]);
+        v[ch][4 * r + 0] = bd[r][0] - bd[r][2];
+        v[ch][4 * r + 1] = bd[r][1] + bd[r][2];
+        v[ch][4 * r + 2] = bd[r][2] - bd[r][1];
+        v[ch][4 * r + 3] = bd[r][1] - bd[r][3];
       }
+    }
+    E* vb = vbuf + set * WN_VBUF;
+#pragma unroll
+    for (int xi = 0; xi < 16; ++xi) {
+      const e2 p = {from_f32<E>(v[0][xi]), from_f32<E>(v[1][xi])};
+      *reinterpret_cast<e2*>(vb + (xi * WN_T + tl) * WN_KC + 2 * cp) = p;
     }
   };
 
@@ -157,46 +283,51 @@ __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][b][e] = 0.0f;
 
-  // A fragments: output channel row (lane & 31) of each 32-channel block (an
-  // out-of-range channel reads the last valid one; its results are dropped),
-  // channels k0 + 8 * (lane >> 5) .. + 8
-  const int kslot = (lane >> 5) * 8;
-  long long arow[CB];
-#pragma unroll
-  for (int b = 0; b < CB; ++b) {
-    const int co = min(co0 + 32 * b + (lane & 31), a.cog - 1);
-    arow[b] = ((long long)grp * a.cog + co) * a.cig + kslot;
-  }
-
-  const int nsteps = a.cig / WN_KC;
-  stage(0, 0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    u32x4_w af[4][CB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int b = 0; b < CB; ++b)
-        af[i][b] = *reinterpret_cast<const u32x4_w*>(U + (long long)(4 * wave + i) * uplane + arow[b] +
-                                                     s * WN_KC);
-    if (s + 1 < nsteps) stage(s + 1, buf ^ 1);
-    const E* vb = vbuf + buf * WN_VBUF;
+  auto mult = [&](int set) __attribute__((always_inline)) {
+    const E* vb = vbuf + set * WN_VBUF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4_w bf =
           *reinterpret_cast<const u32x4_w*>(vb + ((4 * wave + i) * WN_T + (lane & 31)) * WN_KC + kslot);
 #pragma unroll
-      for (int b = 0; b < CB; ++b) acc[i][b] = mfma_32x32x16<E>(af[i][b], bf, acc[i][b]);
+      for (int b = 0; b < CB; ++b) acc[i][b] = mfma_32x32x16<E>(af[set][i][b], bf, acc[i][b]);
     }
+  };
+  // Step s (buffers and U registers s & 1): window s + 1 from the registers
+  // into LDS and the registers refilled with step s + 2; window s -> V s;
+  // barrier; V s times U s and the U registers refilled with step s + 2.
+  // The loads a step waits for are then always the oldest ones outstanding.
+  // Refills past the last step reread it (unused).
+  const int nsteps = a.cig / WN_KC;
+  const int last = nsteps - 1;
+  auto step = [&](int s, int set) __attribute__((always_inline)) {
+    put_x(set ^ 1);
+    load_x(min(s + 2, last));
+    transform(set);
     __syncthreads();
+    mult(set);
+    load_u(min(s + 2, last), set);
+  };
+  load_x(0);
+  load_u(0, 0);
+  put_x(0);
+  load_x(min(1, last));
+  load_u(min(1, last), 1);  // as in the loop: the next window's items, then U
+  __syncthreads();
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(s, 0);
+    step(s + 1, 1);
   }
+  if (s < nsteps) step(s, 0);
+  __syncthreads();  // every wave is done with the buffers the output tiles overwrite
 
   // output transform and epilogue, one 32-channel block at a time
   const E* bias = static_cast<const E*>(a.bias);
   const E* res = static_cast<const E*>(a.res);
   E* y = static_cast<E*>(a.y);
   const int hwo = a.ho * a.wo;
+  const int nslots = a.tr * a.tc;
 #pragma unroll
   for (int b = 0; b < CB; ++b) {
 #pragma unroll
@@ -211,21 +342,19 @@ __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + 256 * q;
       const int col = idx >> 5, tt = idx & 31;
-      const int co = co0 + 32 * b + col, t = t0 + tt;
+      const int co = co0 + 32 * b + col;
+      const int ttr = (int)mdiv((unsigned)tt, a.mg_tc);
+      const int th = tr0 + ttr, tw = tc0 + tt - ttr * a.tc;
       float m[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) m[k] = mbuf[(k * 32 + col) * WN_T + tt];
-      if (co < a.cog && t < a.tiles) {
+      if (co < a.cog && tt < nslots && th < a.th && tw < a.tw) {
         float am[2][4];  // A^T M
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           am[0][c] = m[c] + m[4 + c] + m[8 + c];
           am[1][c] = m[4 + c] - m[8 + c] - m[12 + c];
         }
-        const int n = (int)mdiv((unsigned)t, a.mg_tpi);
-        const int rem = t - n * tpi;
-        const int th = (int)mdiv((unsigned)rem, a.mg_tw);
-        const int tw = rem - th * a.tw;
         const int cg = grp * a.cog + co;
         const float bv = bias ? to_f32(bias[cg]) : 0.0f;
         const long long obase = ((long long)n * a.c_out + cg) * hwo;
@@ -250,21 +379,26 @@ __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
   }
 }
 
+template <typename E, int CB>
+void launch_wino_main(const WinoArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.n * a.nbr * a.nbc), (unsigned)((a.cog + 32 * CB - 1) / (32 * CB)),
+                  (unsigned)a.groups);
+  if (a.nsi == 10) hipLaunchKernelGGL((wino_kernel<E, CB, 10>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((wino_kernel<E, CB, 17>), grid, dim3(256), 0, s, a);
+}
+
 template <typename E>
 hipError_t launch_winograd_t(const WinoArgs& a, hipStream_t s) {
-  const long long pairs = (long long)a.c_out * a.cig;
-  hipLaunchKernelGGL((wino_weights_kernel<E>), dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
-                     s, a);
+  const unsigned items = (unsigned)(a.c_out * (a.cig / 8));  // (output channel, 8 input channels)
+  const dim3 wgrid((items + 63) / 64);
+  if (reinterpret_cast<unsigned long long>(a.wt) % 16 == 0)
+    hipLaunchKernelGGL((wino_weights_kernel<E, true>), wgrid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((wino_weights_kernel<E, false>), wgrid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned tb = (unsigned)((a.tiles + WN_T - 1) / WN_T);
-  if (a.cb == 2) {
-    const dim3 grid(tb, (unsigned)((a.cog + 63) / 64), (unsigned)a.groups);
-    hipLaunchKernelGGL((wino_kernel<E, 2>), grid, dim3(256), 0, s, a);
-  } else {
-    const dim3 grid(tb, (unsigned)((a.cog + 31) / 32), (unsigned)a.groups);
-    hipLaunchKernelGGL((wino_kernel<E, 1>), grid, dim3(256), 0, s, a);
-  }
+  if (a.cb == 2) launch_wino_main<E, 2>(a, s);
+  else launch_wino_main<E, 1>(a, s);
   return hipGetLastError();
 }
 

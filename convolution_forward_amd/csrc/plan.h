@@ -54,6 +54,7 @@ struct Plan {
   int ct_fused;      // transpose: kernel = stride = 2 taps gathered by the GEMM epilogue
   int scratch_fixed; // scratch does not grow with the batch (Winograd weights): no chunks
   int wino_cb;       // Winograd: 32-channel blocks per workgroup
+  int wino_tr, wino_tc;  // Winograd: tile rows x tile columns of a workgroup's band (at most 32 tiles)
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

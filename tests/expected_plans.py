@@ -14,7 +14,7 @@ EXPECTED_PLANS = {
     "w5b_convtranspose2x2s2_f16": "transpose_gemm_col2im.f16.fused_k2s2.t128x64",
     "x1_late3x3_512_7x7_f16": "implicit_gemm_halo.f16.rowshift.r8.n32.split8",
     "x2_bottleneck3x3_bf16": "implicit_gemm_halo.bf16.rowshift.r14.n32",
-    "x3_bottleneck3x3_f16_winograd": "winograd_f2x2_3x3.f16.t32x32",
+    "x3_bottleneck3x3_f16_winograd": "winograd_f2x2_3x3.f16.band4x7.c64",
 }
 
 

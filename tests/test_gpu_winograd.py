@@ -117,6 +117,35 @@ def test_random_geometries(seed):
     assert_parity(dtype, y, yr, sr, b, r, what="winograd", act=g.act)
 
 
+# Band shapes of the main kernel: a tile row longer than 32 tiles (segments of
+# 32, the last one ragged), exactly 32, single-column images whose bands are 32
+# tile rows, and windows whose staging needs the larger item count.
+BAND_CASES = [
+    oracle.Geom(1, 32, 6, 70, 40, 3, 3, pt=1, pl=1, pb=1, pr=1),
+    oracle.Geom(1, 16, 5, 64, 24, 3, 3, pt=1, pl=1, pb=1, pr=1),
+    oracle.Geom(1, 16, 4, 131, 8, 3, 3, pt=0, pl=2, pb=1, pr=0),
+    oracle.Geom(2, 16, 80, 2, 24, 3, 3, pt=1, pl=1, pb=1, pr=1),
+    oracle.Geom(2, 48, 20, 20, 32, 3, 3, pt=1, pl=1, pb=1, pr=1, act="relu"),
+    oracle.Geom(3, 32, 13, 9, 72, 3, 3, pt=2, pl=0, pb=0, pr=2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BAND_CASES)))
+def test_band_shapes(case):
+    g = BAND_CASES[case]
+    dtype = ("f16", "bf16")[case % 2]
+    print(f"[winograd band {case}] {dtype} {_planned(g, dtype)} {g}", flush=True)
+    shp = oracle.out_shape(g)
+    rng = np.random.default_rng(700 + case)
+    x = _q(rng.uniform(-1, 1, (g.n, g.c_in, g.h, g.w)), dtype)
+    w = _q(rng.standard_normal((g.c_out, g.c_in, 3, 3)) * np.sqrt(2.0 / (9 * g.c_in)), dtype)
+    b = _q(rng.uniform(-0.1, 0.1, g.c_out), dtype)
+    r = _q(rng.uniform(-1, 1, shp), dtype)
+    y = run_gpu(g, dtype, x, w, b, r, variant="winograd")
+    yr, sr = oracle.conv2d(g, x, w, b, r)
+    assert_parity(dtype, y, yr, sr, b, r, what="winograd", act=g.act)
+
+
 def test_rerun_bits_and_noalloc():
     layer = workloads.BY_NAME["x3_bottleneck3x3_f16_winograd"].with_batch(3)
     inp = workloads.make_inputs(layer)
