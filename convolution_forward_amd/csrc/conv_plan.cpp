@@ -201,8 +201,8 @@ bool transpose_fused_applicable(const Geo& g, int dtype, bool residual) {
 
 // Winograd F(2x2, 3x3): 16-bit operands, 3x3, stride 1, dilation 1, input
 // channels per group in whole steps of 16 (16-byte weight fragments), tile and
-// channel-tile counts inside the grid limits, and x and the transformed weights
-// below 2 GiB (the kernels address them with 32-bit byte offsets).
+// channel-tile counts inside the grid limits, and x, y and the transformed
+// weights below 2 GiB (the kernels address them with 32-bit byte offsets).
 bool winograd_applicable(const Geo& g, int dtype) {
   if (g.transpose || !half16(dtype) || g.kh != 3 || g.kw != 3 || g.sh != 1 || g.sw != 1 ||
       g.dh != 1 || g.dw != 1 || g.cig % 16)
@@ -212,6 +212,7 @@ bool winograd_applicable(const Geo& g, int dtype) {
     return false;
   return tiles < (1LL << 31) - 64 && ceil_div(g.cog, 32) <= 65535 && g.g <= 65535 &&
          mul_ok(16 * g.co, g.cig, &t) && t < (1LL << 30) && g.x_elems < (1LL << 30) &&
+         g.y_elems < (1LL << 30) &&
          g.co * g.cig / 8 < (1LL << 31) - 64;
 }
 

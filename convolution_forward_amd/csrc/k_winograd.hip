@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64) void wino_weights_kernel(const WinoArgs a) {
 //    bytes, every bank once);
 //  * the U fragments (16-byte loads, two steps ahead) times the V fragments.
 // Window and V are double-buffered: one barrier per step.
-template <typename E, int CB, int NSI>
+template <typename E, int CB, int NSI, bool PAIR>
 __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
   typedef E e2 __attribute__((ext_vector_type(2)));
   constexpr int PP = 36;                 // LDS bytes per staged position
@@ -322,12 +322,60 @@ __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
   if (s < nsteps) step(s, 0);
   __syncthreads();  // every wave is done with the buffers the output tiles overwrite
 
-  // output transform and epilogue, one 32-channel block at a time
+  // Output transform and epilogue, one 32-channel block at a time.  A thread
+  // finishes 4 (channel, tile) items per block.  The offsets and residual of
+  // every block are loaded first, so the residual's latency overlaps the
+  // exchange of the sums through LDS; every access is branch-free: an output
+  // outside the image gets an offset past the descriptor (its residual reads
+  // 0, its store is dropped).  PAIR (even output width, 4-byte aligned y and
+  // residual): a tile row's two outputs move as one 32-bit word.  The stores
+  // are nontemporal (y is not read back).
   const E* bias = static_cast<const E*>(a.bias);
-  const E* res = static_cast<const E*>(a.res);
-  E* y = static_cast<E*>(a.y);
   const int hwo = a.ho * a.wo;
+  const int ybytes = 2 * a.n * a.c_out * hwo;
+  const __amdgpu_buffer_rsrc_t y_rsrc = wino_rsrc(a.y, ybytes);
+  const __amdgpu_buffer_rsrc_t r_rsrc = wino_rsrc(a.res ? a.res : a.y, a.res ? ybytes : 0);
   const int nslots = a.tr * a.tc;
+  int off[CB][4][4];  // [block][item][2 r + c]: byte offset of output (2 th + r, 2 tw + c)
+  float bv[CB][4];
+#pragma unroll
+  for (int b = 0; b < CB; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      const int col = idx >> 5, tt = idx & 31;
+      const int co = co0 + 32 * b + col;
+      const int ttr = (int)mdiv((unsigned)tt, a.mg_tc);
+      const int th = tr0 + ttr, tw = tc0 + tt - ttr * a.tc;
+      const bool ok = co < a.cog && tt < nslots && th < a.th && tw < a.tw;
+      const int cg = grp * a.cog + min(co, a.cog - 1);
+      const int obase = (n * a.c_out + cg) * hwo;
+      bv[b][q] = bias ? to_f32(bias[cg]) : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int oh = 2 * th + r, ow = 2 * tw + c;
+          off[b][q][2 * r + c] = ok && oh < a.ho && ow < a.wo ? 2 * (obase + oh * a.wo + ow) : WN_OOB;
+        }
+    }
+  unsigned rw[CB][4][4];  // residual bits (PAIR: word 2 r holds both outputs of row r)
+  if (a.res) {
+#pragma unroll
+    for (int b = 0; b < CB; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if constexpr (PAIR) {
+            rw[b][q][2 * r] = __builtin_amdgcn_raw_buffer_load_b32(r_rsrc, off[b][q][2 * r], 0, 0);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              rw[b][q][2 * r + c] = __builtin_amdgcn_raw_buffer_load_b16(r_rsrc, off[b][q][2 * r + c], 0, 0);
+          }
+        }
+  }
 #pragma unroll
   for (int b = 0; b < CB; ++b) {
 #pragma unroll
@@ -338,53 +386,59 @@ __global__ __launch_bounds__(256) void wino_kernel(const WinoArgs a) {
         mbuf[((4 * wave + i) * 32 + col) * WN_T + (lane & 31)] = acc[i][b][e];
       }
     __syncthreads();
+    float vv[16];  // [item][2 r + c]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + 256 * q;
       const int col = idx >> 5, tt = idx & 31;
-      const int co = co0 + 32 * b + col;
-      const int ttr = (int)mdiv((unsigned)tt, a.mg_tc);
-      const int th = tr0 + ttr, tw = tc0 + tt - ttr * a.tc;
       float m[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) m[k] = mbuf[(k * 32 + col) * WN_T + tt];
-      if (co < a.cog && tt < nslots && th < a.th && tw < a.tw) {
-        float am[2][4];  // A^T M
+      float am[2][4];  // A^T M
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          am[0][c] = m[c] + m[4 + c] + m[8 + c];
-          am[1][c] = m[4 + c] - m[8 + c] - m[12 + c];
-        }
-        const int cg = grp * a.cog + co;
-        const float bv = bias ? to_f32(bias[cg]) : 0.0f;
-        const long long obase = ((long long)n * a.c_out + cg) * hwo;
+      for (int c = 0; c < 4; ++c) {
+        am[0][c] = m[c] + m[4 + c] + m[8 + c];
+        am[1][c] = m[4 + c] - m[8 + c] - m[12 + c];
+      }
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const float yr[2] = {am[r][0] + am[r][1] + am[r][2], am[r][1] - am[r][2] - am[r][3]};
+      for (int r = 0; r < 2; ++r) {
+        const float yr[2] = {am[r][0] + am[r][1] + am[r][2], am[r][1] - am[r][2] - am[r][3]};
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int oh = 2 * th + r, ow = 2 * tw + c;
-            if (oh < a.ho && ow < a.wo) {
-              const long long oi = obase + (long long)oh * a.wo + ow;
-              float v = yr[c];
-              if (bias) v = v + bv;
-              if (res) v = v + to_f32(res[oi]);
-              y[oi] = from_f32<E>(apply_act(v, a.act, a.alpha, a.beta));
-            }
+        for (int c = 0; c < 2; ++c) {
+          float v = yr[c];
+          if (bias) v = v + bv[b][q];
+          if (a.res) {
+            const unsigned bits = PAIR ? (c ? rw[b][q][2 * r] >> 16 : rw[b][q][2 * r] & 0xFFFFu) : rw[b][q][2 * r + c];
+            v = v + bits_to_f32<E>(bits);
           }
+          vv[4 * q + 2 * r + c] = v;
         }
       }
     }
+    act_array(vv, a.act, a.alpha, a.beta);  // one uniform switch for all 16 outputs
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const unsigned short o0 = __builtin_bit_cast(unsigned short, from_f32<E>(vv[4 * q + 2 * r]));
+        const unsigned short o1 = __builtin_bit_cast(unsigned short, from_f32<E>(vv[4 * q + 2 * r + 1]));
+        if constexpr (PAIR) {
+          __builtin_amdgcn_raw_buffer_store_b32((unsigned)o0 | ((unsigned)o1 << 16), y_rsrc, off[b][q][2 * r], 0, 2);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b16(o0, y_rsrc, off[b][q][2 * r], 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b16(o1, y_rsrc, off[b][q][2 * r + 1], 0, 2);
+        }
+      }
     __syncthreads();
   }
 }
 
-template <typename E, int CB>
+template <typename E, int CB, bool PAIR>
 void launch_wino_main(const WinoArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.n * a.nbr * a.nbc), (unsigned)((a.cog + 32 * CB - 1) / (32 * CB)),
                   (unsigned)a.groups);
-  if (a.nsi == 10) hipLaunchKernelGGL((wino_kernel<E, CB, 10>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((wino_kernel<E, CB, 17>), grid, dim3(256), 0, s, a);
+  if (a.nsi == 10) hipLaunchKernelGGL((wino_kernel<E, CB, 10, PAIR>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((wino_kernel<E, CB, 17, PAIR>), grid, dim3(256), 0, s, a);
 }
 
 template <typename E>
@@ -397,8 +451,16 @@ hipError_t launch_winograd_t(const WinoArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((wino_weights_kernel<E, false>), wgrid, dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.cb == 2) launch_wino_main<E, 2>(a, s);
-  else launch_wino_main<E, 1>(a, s);
+  // outputs in 32-bit pairs: even output width, y and residual 4-byte aligned
+  const bool pair = a.wo % 2 == 0 &&
+                    ((reinterpret_cast<unsigned long long>(a.y) | reinterpret_cast<unsigned long long>(a.res)) & 3) == 0;
+  if (a.cb == 2) {
+    if (pair) launch_wino_main<E, 2, true>(a, s);
+    else launch_wino_main<E, 2, false>(a, s);
+  } else {
+    if (pair) launch_wino_main<E, 1, true>(a, s);
+    else launch_wino_main<E, 1, false>(a, s);
+  }
   return hipGetLastError();
 }
 
