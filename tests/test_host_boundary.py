@@ -413,3 +413,27 @@ def test_bf16_input_rounding_is_nearest_even_once():
     assert np.array_equal(r, want)
     bits = workloads.bf16_bits(r)
     assert np.array_equal(workloads.bf16_from_bits(bits).astype(np.float64), r)
+
+
+def test_winograd_band_plans():
+    """The Winograd variant's workgroup bands, from the shape alone: whole tile
+    rows of one image while a tile row has at most 32 tiles (4 x 7 tiles on
+    14 x 14 outputs), 32-tile segments of one row beyond that, 32 rows of
+    one-tile-wide images; 64-channel blocks when the bands fill the GPU;
+    refused where it does not apply (float32, 5 x 5, stride 2, input channels
+    per group not a multiple of 16) or where x would pass 2 GiB."""
+    def plan(n, c, h, w, co, dtype="f16", **kw):
+        p = cf.make_problem(n, c, h, w, co, kw.pop("k", 3), kw.pop("k2", 3), variant="winograd", **kw)
+        return cf.conv_describe_variant(p, dtype)
+    assert plan(32, 256, 14, 14, 256, pads=(1, 1, 1, 1)) == "winograd_f2x2_3x3.f16.band4x7.c64"
+    assert plan(1, 32, 6, 70, 40, "bf16", pads=(1, 1, 1, 1)) == "winograd_f2x2_3x3.bf16.band1x32.c32"
+    assert plan(2, 16, 80, 2, 24, pads=(1, 1, 1, 1)) == "winograd_f2x2_3x3.f16.band32x1.c32"
+    assert plan(2, 48, 20, 20, 32, pads=(1, 1, 1, 1)) == "winograd_f2x2_3x3.f16.band3x10.c32"
+    for bad in (dict(dtype="f32", pads=(1, 1, 1, 1)), dict(k=5, k2=5, pads=(2, 2, 2, 2)),
+                dict(stride=(2, 2), pads=(1, 1, 1, 1))):
+        with pytest.raises(cf.ConvError):
+            plan(2, 32, 14, 14, 32, **bad)
+    with pytest.raises(cf.ConvError):
+        plan(2, 24, 14, 14, 32, pads=(1, 1, 1, 1))
+    with pytest.raises(cf.ConvError):  # 2^30 input elements
+        plan(1024, 256, 64, 64, 16, pads=(1, 1, 1, 1))
